@@ -1,0 +1,584 @@
+/* orthrus_oracle.c -- the CPU oracle for the Orthrus dual-view decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may call, link or
+ * load this file; only tests/, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant generator
+ * with the HIP library.
+ *
+ * What it computes (source: "Orthrus: Memory-Efficient Parallel Token
+ * Generation via Dual-View Diffusion", as summarised on the HN item page
+ * "Idea" paragraph, the atlas.scime.ai page "Approach" section and the
+ * arXiv abstract on the opentrain.ai page):
+ *   - a frozen autoregressive (AR) Transformer view that builds the KV cache
+ *     (prefill) and verifies drafts causally;
+ *   - a trainable diffusion-attention path in every layer (its own Q/K/V/O
+ *     projections) that projects K mask positions in ONE forward pass over
+ *     the same cache, bidirectionally inside the block, writing nothing to
+ *     the cache;
+ *   - greedy argmax over the shared LM head, longest-matching-prefix
+ *     acceptance plus the AR bonus token, and commit of only the accepted
+ *     KV entries (openai-hub.net page, "KV Cache Overhead" section).
+ *
+ * Arithmetic: float64 everywhere, sums in increasing index order.  For bf16
+ * models the oracle rounds to bf16 exactly where the model stores bf16
+ * (weights as given; GEMM input activations; q and k after QK-norm + RoPE;
+ * cached K/V; attention output), taking each value to fp32 first and then to
+ * bf16 with round-to-nearest-even.  fp32 models round nothing.
+ *
+ * Layer definition (Qwen3-style, see the function comments): RMSNorm ->
+ * Q,K,V projections -> per-head QK RMSNorm -> rotate-half RoPE -> grouped
+ * query attention -> O projection + residual -> RMSNorm -> SwiGLU FFN +
+ * residual; final RMSNorm; untied LM head.
+ *
+ * The canonical weight buffer is a concatenation of tensors in a fixed
+ * order (oc_weight_layout); each tensor starts at a multiple of 256
+ * elements; matrices are row-major [out][in].
+ *
+ * The functions that have no pin other than GPU agreement -- the diffusion
+ * view's actual values (mask-row logits, hence the drafts) -- are marked
+ * "parity unpinned" below: the pages print no worked example for them.  Their
+ * structure is pinned (block bidirectionality, no cache writes, reduction to
+ * the AR view under tied weights and a causal block).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+  int32_t L, d, hq, hkv, hd, F, V, K;
+  double theta, eps;
+  int32_t bf16;   /* 1: bf16 weights (uint16 bit patterns) and bf16 storage points */
+} oc_cfg;
+
+enum {
+  T_EMBED = 0, T_LMHEAD = 1, T_FNORM = 2, T_MASK = 3, T_GLOBAL = 4,
+  /* per layer, offset from 4 + 17*l */
+  T_ANORM = 0, T_FFNNORM = 1, T_WQ = 2, T_WK = 3, T_WV = 4, T_WO = 5, T_QN = 6, T_KN = 7,
+  T_DQ = 8, T_DK = 9, T_DV = 10, T_DO = 11, T_DQN = 12, T_DKN = 13,
+  T_WG = 14, T_WU = 15, T_WD = 16, T_PER_LAYER = 17
+};
+
+/* numel of canonical tensor t (global index) */
+static size_t tensor_numel(const oc_cfg* c, int t) {
+  size_t d = c->d, qd = (size_t)c->hq * c->hd, kd = (size_t)c->hkv * c->hd;
+  if (t == T_EMBED || t == T_LMHEAD) return (size_t)c->V * d;
+  if (t == T_FNORM || t == T_MASK) return d;
+  int r = (t - T_GLOBAL) % T_PER_LAYER;
+  switch (r) {
+    case T_ANORM: case T_FFNNORM: return d;
+    case T_WQ: case T_DQ: return qd * d;
+    case T_WK: case T_WV: case T_DK: case T_DV: return kd * d;
+    case T_WO: case T_DO: return d * qd;
+    case T_QN: case T_KN: case T_DQN: case T_DKN: return (size_t)c->hd;
+    case T_WG: case T_WU: return (size_t)c->F * d;
+    case T_WD: return d * (size_t)c->F;
+  }
+  return 0;
+}
+
+int oc_num_tensors(const oc_cfg* c) { return T_GLOBAL + T_PER_LAYER * c->L; }
+
+/* Offset (elements) and numel of tensor t; t == -1 gives the total numel. */
+int oc_weight_layout(const oc_cfg* c, int t, size_t* off, size_t* numel) {
+  int nt = oc_num_tensors(c);
+  if (t < -1 || t >= nt) return -1;
+  size_t o = 0;
+  for (int i = 0; i < nt; ++i) {
+    if (i == t) { *off = o; *numel = tensor_numel(c, i); return 0; }
+    o += (tensor_numel(c, i) + 255) / 256 * 256;
+  }
+  *off = 0; *numel = o;
+  return 0;
+}
+
+/* ---------------------------------------------------------------- rounding */
+double oc_round_bf16(double x) {
+  union { float f; uint32_t u; } v;
+  v.f = (float)x;                         /* to fp32, nearest-even */
+  uint32_t rnd = ((v.u >> 16) & 1u) + 0x7FFFu;
+  v.u = ((v.u + rnd) >> 16) << 16;        /* to bf16, nearest-even */
+  return (double)v.f;
+}
+
+static double bf16_bits_to_double(uint16_t b) {
+  union { float f; uint32_t u; } v; v.u = (uint32_t)b << 16; return (double)v.f;
+}
+
+/* ------------------------------------------------------------ primitives */
+/* RMSNorm: y_i = x_i / sqrt(mean(x^2) + eps) * g_i. */
+void oc_rmsnorm(const double* x, const double* g, int n, double eps, double* y) {
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
+  double r = 1.0 / sqrt(ss / n + eps);
+  for (int i = 0; i < n; ++i) y[i] = x[i] * r * (g ? g[i] : 1.0);
+}
+
+/* Rotate-half RoPE at absolute position pos: the pair (i, i + hd/2) is
+ * rotated by the angle pos * theta^(-2i/hd). */
+void oc_rope(double* v, int hd, long pos, double theta) {
+  int h = hd / 2;
+  for (int i = 0; i < h; ++i) {
+    double ang = (double)pos * pow(theta, -2.0 * i / hd);
+    double cs = cos(ang), sn = sin(ang);
+    double x1 = v[i], x2 = v[i + h];
+    v[i] = x1 * cs - x2 * sn;
+    v[i + h] = x2 * cs + x1 * sn;
+  }
+}
+
+/* Scaled dot-product attention of one query over n keys:
+ * out = sum_j softmax_j(q.k_j / sqrt(hd)) v_j.  Keys/values are rows of
+ * stride hd.  Two passes (max, then sums) in float64. */
+void oc_attention(const double* q, const double* const* keys, const double* const* vals, int n,
+                  int hd, double* out) {
+  double* s = (double*)malloc(sizeof(double) * (n > 0 ? n : 1));
+  double scale = 1.0 / sqrt((double)hd);
+  double m = -INFINITY;
+  for (int j = 0; j < n; ++j) {
+    double acc = 0.0;
+    for (int t = 0; t < hd; ++t) acc += q[t] * keys[j][t];
+    s[j] = acc * scale;
+    if (s[j] > m) m = s[j];
+  }
+  double l = 0.0;
+  for (int j = 0; j < n; ++j) { s[j] = exp(s[j] - m); l += s[j]; }
+  for (int t = 0; t < hd; ++t) out[t] = 0.0;
+  for (int j = 0; j < n; ++j)
+    for (int t = 0; t < hd; ++t) out[t] += s[j] * vals[j][t];
+  for (int t = 0; t < hd; ++t) out[t] /= l;
+  free(s);
+}
+
+/* Contiguous-array wrapper of oc_attention for the tests. */
+void oc_attention_dense(const double* q, const double* K, const double* V, int n, int hd,
+                        double* out) {
+  const double** kp = (const double**)malloc(sizeof(void*) * (n > 0 ? n : 1));
+  const double** vp = (const double**)malloc(sizeof(void*) * (n > 0 ? n : 1));
+  for (int j = 0; j < n; ++j) { kp[j] = K + (size_t)j * hd; vp[j] = V + (size_t)j * hd; }
+  oc_attention(q, kp, vp, n, hd, out);
+  free(kp); free(vp);
+}
+
+double oc_silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* Greedy choice: the largest value, lowest index on exact ties; -1 on NaN. */
+int oc_argmax(const double* x, int n) {
+  int best = 0;
+  for (int i = 0; i < n; ++i) {
+    if (x[i] != x[i]) return -1;
+    if (x[i] > x[best]) best = i;
+  }
+  return n > 0 ? best : -1;
+}
+
+/* Longest-matching-prefix acceptance: d[0..K) are the drafts d_1..d_K,
+ * a[0..K] the AR tokens a_0..a_K (a_i = AR argmax after d_1..d_i).  Returns
+ * m = the largest j <= K with d_i == a_{i-1} for every i <= j. */
+int oc_accept(const int32_t* d, const int32_t* a, int K) {
+  int m = 0;
+  while (m < K && d[m] == a[m]) ++m;
+  return m;
+}
+
+/* ------------------------------------------------------------------ model */
+typedef struct {
+  oc_cfg c;
+  const void* w;
+  size_t* off;         /* per tensor offset (elements) */
+  double* attn_tap;    /* optional: [L][rows][hq*hd] attention outputs of the last call */
+  int attn_tap_rows;
+} oc_model;
+
+typedef struct {
+  const oc_model* m;
+  int cap, len;
+  double* k;   /* [L][hkv][cap][hd] */
+  double* v;
+} oc_seq;
+
+oc_model* oc_model_new(const oc_cfg* c, const void* weights) {
+  oc_model* m = (oc_model*)calloc(1, sizeof(oc_model));
+  m->c = *c;
+  m->w = weights;
+  int nt = oc_num_tensors(c);
+  m->off = (size_t*)malloc(sizeof(size_t) * nt);
+  for (int t = 0; t < nt; ++t) { size_t n; oc_weight_layout(c, t, &m->off[t], &n); }
+  return m;
+}
+
+void oc_model_free(oc_model* m) { if (m) { free(m->off); free(m); } }
+
+void oc_model_set_attn_tap(oc_model* m, double* tap, int rows) {
+  m->attn_tap = tap; m->attn_tap_rows = rows;
+}
+
+static inline double wget(const oc_model* m, int t, size_t i) {
+  size_t o = m->off[t] + i;
+  if (m->c.bf16) return bf16_bits_to_double(((const uint16_t*)m->w)[o]);
+  return (double)((const float*)m->w)[o];
+}
+
+static int lt(int l, int r) { return T_GLOBAL + T_PER_LAYER * l + r; }
+
+static void load_vec(const oc_model* m, int t, int n, double* out) {
+  for (int i = 0; i < n; ++i) out[i] = wget(m, t, (size_t)i);
+}
+
+static void store_round(const oc_model* m, double* x, size_t n) {
+  if (!m->c.bf16) return;
+  for (size_t i = 0; i < n; ++i) x[i] = oc_round_bf16(x[i]);
+}
+
+/* y[r][o] = sum_k x[r][k] * W[o][k] for R rows; W = tensor t, [out][in]. */
+static void linear(const oc_model* m, int t, const double* x, int R, int in, int out, double* y) {
+#pragma omp parallel
+  {
+    double* wrow = (double*)malloc(sizeof(double) * in);
+#pragma omp for schedule(static)
+    for (int o = 0; o < out; ++o) {
+      for (int k = 0; k < in; ++k) wrow[k] = wget(m, t, (size_t)o * in + k);
+      for (int r = 0; r < R; ++r) {
+        const double* xr = x + (size_t)r * in;
+        double acc = 0.0;
+        for (int k = 0; k < in; ++k) acc += xr[k] * wrow[k];
+        y[(size_t)r * out + o] = acc;
+      }
+    }
+    free(wrow);
+  }
+}
+
+oc_seq* oc_seq_new(const oc_model* m, int cap) {
+  oc_seq* s = (oc_seq*)calloc(1, sizeof(oc_seq));
+  s->m = m; s->cap = cap; s->len = 0;
+  size_t n = (size_t)m->c.L * m->c.hkv * cap * m->c.hd;
+  s->k = (double*)calloc(n, sizeof(double));
+  s->v = (double*)calloc(n, sizeof(double));
+  return s;
+}
+
+void oc_seq_free(oc_seq* s) { if (s) { free(s->k); free(s->v); free(s); } }
+int oc_seq_len(const oc_seq* s) { return s->len; }
+void oc_seq_set_len(oc_seq* s, int len) { s->len = len; }
+
+static double* kslot(const oc_seq* s, int l, int g, int p) {
+  const oc_cfg* c = &s->m->c;
+  return s->k + (((size_t)l * c->hkv + g) * s->cap + p) * c->hd;
+}
+static double* vslot(const oc_seq* s, int l, int g, int p) {
+  const oc_cfg* c = &s->m->c;
+  return s->v + (((size_t)l * c->hkv + g) * s->cap + p) * c->hd;
+}
+
+/* Sum of every cached K/V value in slots [0, upto) -- the tests use it to
+ * show that the draft pass leaves the committed cache untouched. */
+double oc_seq_checksum(const oc_seq* s, int upto) {
+  const oc_cfg* c = &s->m->c;
+  double acc = 0.0;
+  for (int l = 0; l < c->L; ++l)
+    for (int g = 0; g < c->hkv; ++g)
+      for (int p = 0; p < upto; ++p)
+        for (int t = 0; t < c->hd; ++t)
+          acc += kslot(s, l, g, p)[t] * (1.0 + 1e-3 * t) + vslot(s, l, g, p)[t] * (2.0 - 1e-3 * t);
+  return acc;
+}
+
+/* The rest of a layer after attention: O projection + residual, then the
+ * SwiGLU FFN + residual (frozen FFN, shared by both views). */
+static void layer_tail(const oc_model* m, int l, int to, double* h, double* o, int R) {
+  const oc_cfg* c = &m->c;
+  int d = c->d, qd = c->hq * c->hd, F = c->F;
+  double* y = (double*)malloc(sizeof(double) * (size_t)R * (d > 2 * F ? d : 2 * F));
+  store_round(m, o, (size_t)R * qd);
+  linear(m, to, o, R, qd, d, y);
+  for (size_t i = 0; i < (size_t)R * d; ++i) h[i] += y[i];
+  double* g = (double*)malloc(sizeof(double) * d);
+  double* u = (double*)malloc(sizeof(double) * (size_t)R * d);
+  load_vec(m, lt(l, T_FFNNORM), d, g);
+  for (int r = 0; r < R; ++r) oc_rmsnorm(h + (size_t)r * d, g, d, c->eps, u + (size_t)r * d);
+  store_round(m, u, (size_t)R * d);
+  double* gate = (double*)malloc(sizeof(double) * (size_t)R * F);
+  double* up = (double*)malloc(sizeof(double) * (size_t)R * F);
+  linear(m, lt(l, T_WG), u, R, d, F, gate);
+  linear(m, lt(l, T_WU), u, R, d, F, up);
+  for (size_t i = 0; i < (size_t)R * F; ++i) gate[i] = oc_silu(gate[i]) * up[i];
+  store_round(m, gate, (size_t)R * F);
+  linear(m, lt(l, T_WD), gate, R, F, d, y);
+  for (size_t i = 0; i < (size_t)R * d; ++i) h[i] += y[i];
+  free(y); free(g); free(u); free(gate); free(up);
+}
+
+/* Q/K/V projections of R normalised rows with the given tensors, then
+ * per-head QK RMSNorm and RoPE at pos[r]; q, k, v come back rounded to the
+ * storage precision. */
+static void qkv_proj(const oc_model* m, int l, int tq, int tk, int tv, int tqn, int tkn,
+                     const double* h, int R, const long* pos, double* q, double* k, double* v) {
+  const oc_cfg* c = &m->c;
+  int d = c->d, hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd;
+  double* g = (double*)malloc(sizeof(double) * d);
+  double* u = (double*)malloc(sizeof(double) * (size_t)R * d);
+  load_vec(m, lt(l, T_ANORM), d, g);
+  for (int r = 0; r < R; ++r) oc_rmsnorm(h + (size_t)r * d, g, d, c->eps, u + (size_t)r * d);
+  store_round(m, u, (size_t)R * d);
+  linear(m, tq, u, R, d, qd, q);
+  linear(m, tk, u, R, d, kd, k);
+  linear(m, tv, u, R, d, kd, v);
+  double* qn = (double*)malloc(sizeof(double) * hd);
+  double* kn = (double*)malloc(sizeof(double) * hd);
+  load_vec(m, tqn, hd, qn);
+  load_vec(m, tkn, hd, kn);
+  for (int r = 0; r < R; ++r) {
+    for (int hh = 0; hh < c->hq; ++hh) {
+      double* x = q + (size_t)r * qd + (size_t)hh * hd;
+      oc_rmsnorm(x, qn, hd, c->eps, x);
+      oc_rope(x, hd, pos[r], c->theta);
+    }
+    for (int gg = 0; gg < c->hkv; ++gg) {
+      double* x = k + (size_t)r * kd + (size_t)gg * hd;
+      oc_rmsnorm(x, kn, hd, c->eps, x);
+      oc_rope(x, hd, pos[r], c->theta);
+    }
+  }
+  store_round(m, q, (size_t)R * qd);
+  store_round(m, k, (size_t)R * kd);
+  store_round(m, v, (size_t)R * kd);
+  free(g); free(u); free(qn); free(kn);
+}
+
+static void final_logits(const oc_model* m, const double* h, int R, double* logits,
+                         int32_t* amax) {
+  const oc_cfg* c = &m->c;
+  int d = c->d, V = c->V;
+  double* g = (double*)malloc(sizeof(double) * d);
+  double* z = (double*)malloc(sizeof(double) * (size_t)R * d);
+  load_vec(m, T_FNORM, d, g);
+  for (int r = 0; r < R; ++r) oc_rmsnorm(h + (size_t)r * d, g, d, c->eps, z + (size_t)r * d);
+  store_round(m, z, (size_t)R * d);
+  double* lg = logits ? logits : (double*)malloc(sizeof(double) * (size_t)R * V);
+  linear(m, T_LMHEAD, z, R, d, V, lg);
+  if (amax)
+    for (int r = 0; r < R; ++r) amax[r] = oc_argmax(lg + (size_t)r * V, V);
+  if (!logits) free(lg);
+  free(g); free(z);
+}
+
+/* Frozen AR view over R consecutive tokens at positions pos0..pos0+R-1.
+ * Row r attends causally to cache slots [0, pos0+r]; its own K/V (and those
+ * of the rows before it) are written to the cache at pos0+r before the
+ * attention of each layer.  This single routine is prefill (R = prompt),
+ * plain greedy decoding (R = 1), the draft pass's anchor row (R = 1 at
+ * position len) and the verify pass (R = K at len+1).  Logits [R][V]
+ * (optional) and argmax tokens [R] are returned.  The sequence length is
+ * not changed (callers commit). */
+int oc_ar_rows(const oc_model* m, oc_seq* s, const int32_t* tokens, int R, int pos0,
+               double* logits, int32_t* amax) {
+  const oc_cfg* c = &m->c;
+  if (pos0 < 0 || pos0 + R > s->cap) return -2;
+  int d = c->d, hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd, grp = c->hq / c->hkv;
+  for (int r = 0; r < R; ++r)
+    if (tokens[r] < 0 || tokens[r] >= c->V) return -1;
+  double* h = (double*)malloc(sizeof(double) * (size_t)R * d);
+  for (int r = 0; r < R; ++r)
+    for (int i = 0; i < d; ++i) h[(size_t)r * d + i] = wget(m, T_EMBED, (size_t)tokens[r] * d + i);
+  long* pos = (long*)malloc(sizeof(long) * R);
+  for (int r = 0; r < R; ++r) pos[r] = pos0 + r;
+  double* q = (double*)malloc(sizeof(double) * (size_t)R * qd);
+  double* k = (double*)malloc(sizeof(double) * (size_t)R * kd);
+  double* v = (double*)malloc(sizeof(double) * (size_t)R * kd);
+  double* o = (double*)malloc(sizeof(double) * (size_t)R * qd);
+  for (int l = 0; l < c->L; ++l) {
+    qkv_proj(m, l, lt(l, T_WQ), lt(l, T_WK), lt(l, T_WV), lt(l, T_QN), lt(l, T_KN), h, R, pos, q,
+             k, v);
+    for (int r = 0; r < R; ++r)
+      for (int g = 0; g < c->hkv; ++g) {
+        memcpy(kslot(s, l, g, pos0 + r), k + (size_t)r * kd + (size_t)g * hd, sizeof(double) * hd);
+        memcpy(vslot(s, l, g, pos0 + r), v + (size_t)r * kd + (size_t)g * hd, sizeof(double) * hd);
+      }
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int r = 0; r < R; ++r)
+      for (int hh = 0; hh < c->hq; ++hh) {
+        int g = hh / grp, n = pos0 + r + 1;
+        const double** kp = (const double**)malloc(sizeof(void*) * n);
+        const double** vp = (const double**)malloc(sizeof(void*) * n);
+        for (int j = 0; j < n; ++j) { kp[j] = kslot(s, l, g, j); vp[j] = vslot(s, l, g, j); }
+        oc_attention(q + (size_t)r * qd + (size_t)hh * hd, kp, vp, n, hd,
+                     o + (size_t)r * qd + (size_t)hh * hd);
+        free(kp); free(vp);
+      }
+    if (m->attn_tap && R <= m->attn_tap_rows) {
+      double* tap = m->attn_tap + (size_t)l * m->attn_tap_rows * qd;
+      memcpy(tap, o, sizeof(double) * (size_t)R * qd);
+      store_round(m, tap, (size_t)R * qd);
+    }
+    layer_tail(m, l, lt(l, T_WO), h, o, R);
+  }
+  final_logits(m, h, R, logits, amax);
+  free(h); free(pos); free(q); free(k); free(v); free(o);
+  return 0;
+}
+
+/* Diffusion view over the block of K mask positions n+1..n+K (n = len), in
+ * one forward pass.  Every row starts from the mask embedding (or, for the
+ * structural test only, from the embeddings of given tokens), goes through
+ * the diffusion Q/K/V/O projections and QK-norm gains and the shared
+ * norms/FFN/LM head, and attends to the cache slots [0, n] plus all K block
+ * rows (bidirectional; causal = 1 restricts row i to block rows 0..i, for
+ * the structural test).  Block K/V stay in local scratch: nothing is written
+ * to the cache.  Parity unpinned (values): see the file header. */
+int oc_draft_rows(const oc_model* m, const oc_seq* s, int n, int K, const int32_t* in_tokens,
+                  int causal, double* logits, int32_t* amax) {
+  const oc_cfg* c = &m->c;
+  if (n < 0 || n >= s->cap || K <= 0) return -2;
+  int d = c->d, hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd, grp = c->hq / c->hkv;
+  double* h = (double*)malloc(sizeof(double) * (size_t)K * d);
+  for (int r = 0; r < K; ++r)
+    for (int i = 0; i < d; ++i)
+      h[(size_t)r * d + i] = in_tokens ? wget(m, T_EMBED, (size_t)in_tokens[r] * d + i)
+                                       : wget(m, T_MASK, (size_t)i);
+  long* pos = (long*)malloc(sizeof(long) * K);
+  for (int r = 0; r < K; ++r) pos[r] = n + 1 + r;
+  double* q = (double*)malloc(sizeof(double) * (size_t)K * qd);
+  double* bk = (double*)malloc(sizeof(double) * (size_t)K * kd);
+  double* bv = (double*)malloc(sizeof(double) * (size_t)K * kd);
+  double* o = (double*)malloc(sizeof(double) * (size_t)K * qd);
+  for (int l = 0; l < c->L; ++l) {
+    qkv_proj(m, l, lt(l, T_DQ), lt(l, T_DK), lt(l, T_DV), lt(l, T_DQN), lt(l, T_DKN), h, K, pos, q,
+             bk, bv);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int r = 0; r < K; ++r)
+      for (int hh = 0; hh < c->hq; ++hh) {
+        int g = hh / grp, nb = causal ? r + 1 : K, nk = n + 1 + nb;
+        const double** kp = (const double**)malloc(sizeof(void*) * nk);
+        const double** vp = (const double**)malloc(sizeof(void*) * nk);
+        for (int j = 0; j <= n; ++j) { kp[j] = kslot(s, l, g, j); vp[j] = vslot(s, l, g, j); }
+        for (int j = 0; j < nb; ++j) {
+          kp[n + 1 + j] = bk + (size_t)j * kd + (size_t)g * hd;
+          vp[n + 1 + j] = bv + (size_t)j * kd + (size_t)g * hd;
+        }
+        oc_attention(q + (size_t)r * qd + (size_t)hh * hd, kp, vp, nk, hd,
+                     o + (size_t)r * qd + (size_t)hh * hd);
+        free(kp); free(vp);
+      }
+    if (m->attn_tap && K <= m->attn_tap_rows) {
+      double* tap = m->attn_tap + (size_t)l * m->attn_tap_rows * qd;
+      memcpy(tap, o, sizeof(double) * (size_t)K * qd);
+      store_round(m, tap, (size_t)K * qd);
+    }
+    layer_tail(m, l, lt(l, T_DO), h, o, K);
+  }
+  final_logits(m, h, K, logits, amax);
+  free(h); free(pos); free(q); free(bk); free(bv); free(o);
+  return 0;
+}
+
+/* Prefill: the AR view over the whole prompt; len <- P; returns the first
+ * generated token (argmax of the last prompt row) or < 0 on error. */
+int oc_prefill(const oc_model* m, oc_seq* s, const int32_t* prompt, int P, double* last_logits) {
+  if (P <= 0 || P > s->cap) return -2;
+  int32_t* am = (int32_t*)malloc(sizeof(int32_t) * P);
+  double* lg = (double*)malloc(sizeof(double) * (size_t)P * m->c.V);
+  int rc = oc_ar_rows(m, s, prompt, P, 0, lg, am);
+  int tok = rc ? rc : am[P - 1];
+  if (!rc) {
+    s->len = P;
+    if (last_logits) memcpy(last_logits, lg + (size_t)(P - 1) * m->c.V, sizeof(double) * m->c.V);
+  }
+  free(am); free(lg);
+  return tok;
+}
+
+/* One draft -> verify -> accept -> commit step with block size K, as
+ * described by the pages: pass 1 runs the AR view on the pending token at
+ * position n (its argmax a_0; its K/V staged at slot n) and the diffusion
+ * view on K mask positions n+1..n+K (drafts d_1..d_K, nothing cached);
+ * pass 2 runs the AR view causally over d_1..d_K at n+1..n+K (a_1..a_K,
+ * K/V staged); m = the longest prefix with d_i == a_{i-1}; the step emits
+ * d_1..d_m and the bonus a_m; only slots n..n+m become committed.
+ * K == 0 is plain greedy decoding (one AR row, emits a_0).
+ * planted (optional) replaces the drafts after pass 1.
+ * Outputs: drafts[K], ar[K+1], logits_anchor[V], logits_draft[K][V],
+ * logits_verify[K][V] (each optional), emitted[K+1]; returns m or < 0. */
+int oc_step(const oc_model* m, oc_seq* s, int32_t pending, int K, const int32_t* planted,
+            int32_t* drafts, int32_t* ar, double* logits_anchor, double* logits_draft,
+            double* logits_verify, int32_t* emitted, int32_t* new_pending) {
+  int n = s->len;
+  if (n + K + 1 > s->cap) return -2;
+  int32_t a0;
+  int rc = oc_ar_rows(m, s, &pending, 1, n, logits_anchor, &a0);
+  if (rc) return rc;
+  ar[0] = a0;
+  if (K == 0) {
+    emitted[0] = a0;
+    s->len = n + 1;
+    *new_pending = a0;
+    return 0;
+  }
+  int32_t* d = (int32_t*)malloc(sizeof(int32_t) * K);
+  rc = oc_draft_rows(m, s, n, K, NULL, 0, logits_draft, d);
+  if (rc) { free(d); return rc; }
+  if (planted) memcpy(d, planted, sizeof(int32_t) * K);
+  for (int i = 0; i < K; ++i) if (d[i] < 0) { free(d); return -1; }
+  rc = oc_ar_rows(m, s, d, K, n + 1, logits_verify, ar + 1);
+  if (rc) { free(d); return rc; }
+  int acc = oc_accept(d, ar, K);
+  for (int i = 0; i < acc; ++i) emitted[i] = d[i];
+  emitted[acc] = ar[acc];
+  if (drafts) memcpy(drafts, d, sizeof(int32_t) * K);
+  s->len = n + 1 + acc;
+  *new_pending = ar[acc];
+  free(d);
+  return acc;
+}
+
+/* Plain greedy AR decoding: prefill, then one row at a time.  Writes the
+ * first n_new generated tokens (token 1 = argmax of the last prompt row). */
+int oc_ar_generate(const oc_model* m, const int32_t* prompt, int P, int n_new, int32_t* out) {
+  oc_seq* s = oc_seq_new(m, P + n_new + 1);
+  int tok = oc_prefill(m, s, prompt, P, NULL);
+  if (tok < 0) { oc_seq_free(s); return tok; }
+  for (int t = 0; t < n_new; ++t) {
+    out[t] = tok;
+    if (t + 1 == n_new) break;
+    int32_t nx;
+    int rc = oc_ar_rows(m, s, &tok, 1, s->len, NULL, &nx);
+    if (rc) { oc_seq_free(s); return rc; }
+    s->len += 1;
+    tok = nx;
+  }
+  oc_seq_free(s);
+  return 0;
+}
+
+/* Orthrus generation: prefill, then draft/verify/accept/commit steps until
+ * n_new tokens exist (the step that crosses n_new is truncated).  planted:
+ * optional [max_steps][K] table used instead of the drafts.  Per-step
+ * accept lengths go to accept_out[max_steps] (optional) and the cache length
+ * before each step to len_out; returns the number of steps or < 0. */
+int oc_generate(const oc_model* m, const int32_t* prompt, int P, int n_new, int K,
+                const int32_t* planted, int max_steps, int32_t* out, int32_t* accept_out,
+                int32_t* len_out) {
+  oc_seq* s = oc_seq_new(m, P + n_new + K + 2);
+  int tok = oc_prefill(m, s, prompt, P, NULL);
+  if (tok < 0) { oc_seq_free(s); return tok; }
+  int have = 0;
+  out[have++] = tok;
+  int32_t* em = (int32_t*)malloc(sizeof(int32_t) * (K + 1));
+  int32_t* ar = (int32_t*)malloc(sizeof(int32_t) * (K + 1));
+  int steps = 0;
+  while (have < n_new) {
+    if (steps >= max_steps) break;
+    if (len_out) len_out[steps] = s->len;
+    int32_t np;
+    int acc = oc_step(m, s, tok, K, planted ? planted + (size_t)steps * K : NULL, NULL, ar, NULL,
+                      NULL, NULL, em, &np);
+    if (acc < 0) { steps = acc; break; }
+    if (accept_out) accept_out[steps] = acc;
+    for (int i = 0; i <= acc && have < n_new; ++i) out[have++] = em[i];
+    tok = np;
+    ++steps;
+  }
+  free(em); free(ar);
+  oc_seq_free(s);
+  return steps;
+}
