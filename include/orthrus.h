@@ -1,0 +1,219 @@
+/* orthrus.h -- C ABI of the Orthrus dual-view decode step on MI355X (gfx950).
+ *
+ * The method ("Orthrus: Memory-Efficient Parallel Token Generation via
+ * Dual-View Diffusion"): a frozen autoregressive (AR) Transformer and a
+ * trainable diffusion-attention path in every layer share ONE KV cache.  The
+ * AR view pre-fills the cache (opentrain.ai page, abstract); the diffusion
+ * view projects a block of K mask positions in one forward pass over that
+ * cache (HN item page, "Idea"; atlas.scime.ai page, "Approach"); the AR view
+ * verifies the block in a second pass, the longest prefix matching its greedy
+ * argmax is accepted together with the AR bonus token, and only accepted
+ * entries are committed to the cache (openai-hub.net page, "KV Cache
+ * Overhead" and "Open-Source Code" steps).  The emitted sequence equals
+ * plain greedy AR decoding of the frozen model.
+ *
+ * One step, for each sequence b with committed length n = seq_len[b] and
+ * pending token x (the last emitted token, whose K/V is not yet cached):
+ *   orthrus_draft_block    pass 1: the anchor row (x at position n, frozen
+ *                          view, causal over slots [0, n], its K/V staged at
+ *                          slot n) gives a_0; K mask rows (positions
+ *                          n+1..n+K, diffusion view, attending to slots
+ *                          [0, n] and bidirectionally to the whole block)
+ *                          give the drafts d_1..d_K.  Block K/V live only in
+ *                          the block scratch; nothing of the block reaches the
+ *                          cache.
+ *   orthrus_verify_accept  pass 2: the frozen view over d_1..d_K at
+ *                          n+1..n+K, causal (row i sees slots [0, n+i]), K/V
+ *                          staged at n+1..n+K, gives a_1..a_K; then
+ *                          m = max{j <= K : d_i == a_{i-1} for all i <= j}.
+ *   orthrus_commit_kv      commits slots n..n+m (seq_len <- n+1+m), emits
+ *                          d_1..d_m and the bonus a_m, pending <- a_m.  Staged
+ *                          slots past n+m are discarded (overwritten later).
+ * block_k == 0 is plain greedy decoding with the same kernels: pass 1 is the
+ * anchor row alone, verify_accept only sets accept_len = 0, and commit emits
+ * a_0.
+ *
+ * Conventions
+ *  - Return codes: ORTHRUS_OK (0) or a negative ORTHRUS_E* code; the string
+ *    is orthrus_strerror(code).  All argument, capacity and call-order checks
+ *    run on the host BEFORE anything is enqueued, so an error leaves device
+ *    state untouched.  ORTHRUS_EHIP reports a failed HIP launch/copy
+ *    (orthrus_last_hip_error() gives the hipError_t value).
+ *  - Pointers: unless marked "host", every pointer argument is device memory
+ *    owned by the caller.  The library never allocates or frees device
+ *    memory; the sizes of the buffers it needs come from
+ *    orthrus_query_sizes().  "stream" is a hipStream_t (NULL = default
+ *    stream).  Every call only enqueues work on that stream (prefill and
+ *    create also do small host->device copies on it).
+ *  - Token ids are int32.  Ids outside [0, vocab) are clamped when embedded.
+ *  - One context is driven by one stream at a time; calls on a context must
+ *    be serialized by the caller.
+ *  - Call order per step: draft_block -> verify_accept -> commit_kv
+ *    (ORTHRUS_ESTATE otherwise).  The host keeps an upper bound on every
+ *    sequence's length (prompt_len, plus block_k + 1 per committed step) and
+ *    refuses a step that could write past max_ctx (ORTHRUS_ECAPACITY).
+ */
+#ifndef ORTHRUS_H
+#define ORTHRUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ORTHRUS_OK = 0,
+  ORTHRUS_EINVAL = -1,     /* bad shape, pointer, batch or token count */
+  ORTHRUS_ECAPACITY = -2,  /* a sequence could grow past max_ctx */
+  ORTHRUS_ESTATE = -3,     /* call out of order (e.g. verify without draft) */
+  ORTHRUS_EHIP = -4        /* a HIP call failed */
+};
+
+enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1 };
+
+/* Model and capacity.  The layer is Qwen3-style: RMSNorm (eps rms_eps), Q/K/V
+ * projections, per-head QK RMSNorm, rotate-half RoPE (base rope_theta),
+ * grouped-query attention (query head h reads KV head h / (n_q_heads /
+ * n_kv_heads)), O projection + residual, RMSNorm, SwiGLU FFN + residual;
+ * final RMSNorm and an untied LM head.  The diffusion path has its own
+ * Q/K/V/O projections and QK-norm gains; norms, FFN, embedding and LM head
+ * are shared.
+ * BF16 models: bf16 weights, bf16 KV cache, fp32 residual stream, fp32
+ * accumulation; requires head_dim 128, d_model, n_q_heads*head_dim and
+ * ffn_dim multiples of 256, and (block_k + 1) * group <= 144 and
+ * 32 * group <= 144 (group = n_q_heads / n_kv_heads).
+ * F32 models: everything fp32 (small check models). */
+typedef struct orthrus_config {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  int32_t block_k;        /* K, mask positions per block (0 = plain AR) */
+  double rope_theta;
+  double rms_eps;
+  int32_t dtype;          /* ORTHRUS_F32 or ORTHRUS_BF16 */
+  int32_t max_batch;      /* sequences per call, 1..256 */
+  int32_t max_ctx;        /* KV slots per sequence (cache capacity) */
+} orthrus_config;
+
+typedef struct orthrus_sizes {
+  uint64_t weights_bytes;    /* canonical weight buffer (see orthrus_weight_tensor) */
+  uint64_t packed_bytes;     /* library-layout copy of the weights */
+  uint64_t kv_bytes;         /* the shared KV cache */
+  uint64_t scratch_bytes;    /* block K/V scratch: 2*L*max_batch*Hkv*K*head_dim*elt */
+  uint64_t workspace_bytes;  /* activations, partial results, RoPE table */
+} orthrus_sizes;
+
+typedef struct orthrus_ctx orthrus_ctx;
+
+/* Buffer sizes for a config.  Host only; needs no GPU. */
+int orthrus_query_sizes(const orthrus_config* cfg, orthrus_sizes* out);
+
+/* Canonical weight buffer format: tensors concatenated in index order, each
+ * starting at a multiple of 256 elements, elements fp32 or bf16 (per dtype),
+ * matrices row-major [out][in].  Index 0 embedding [V][d], 1 LM head [V][d],
+ * 2 final-norm gain [d], 3 mask embedding [d] (the diffusion view's input at
+ * every mask position), then per layer l, at 4 + 17*l + j:
+ *   j=0 attention-norm gain [d], 1 FFN-norm gain [d], 2 Wq [Hq*hd][d],
+ *   3 Wk [Hkv*hd][d], 4 Wv [Hkv*hd][d], 5 Wo [d][Hq*hd], 6 q-norm gain [hd],
+ *   7 k-norm gain [hd], 8..13 the diffusion path's Wq, Wk, Wv, Wo, q-norm and
+ *   k-norm gains (same shapes), 14 W_gate [F][d], 15 W_up [F][d],
+ *   16 W_down [d][F].
+ * index == -1 returns the total element count.  Host only. */
+int orthrus_weight_tensor(const orthrus_config* cfg, int32_t index, uint64_t* offset_elems,
+                          uint64_t* numel);
+
+/* Validate cfg, bind the caller's buffers and pack the canonical weights
+ * (device, read only during this call; may be freed afterwards) into
+ * `packed`.  Builds the RoPE table (float64 angles on the host, stored
+ * fp32) into the workspace.  Errors: EINVAL (shape, null or misaligned
+ * pointer: every buffer must be 256-byte aligned), EHIP. */
+int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed, void* kv_cache,
+                   void* block_scratch, void* workspace, void* stream, orthrus_ctx** out);
+
+/* Release the context (host memory only; the caller frees its buffers). */
+int orthrus_destroy(orthrus_ctx* ctx);
+
+/* AR-view prefill of `batch` prompts (the frozen view builds the cache:
+ * opentrain.ai page, abstract).  tokens: device [batch][tokens_stride]
+ * int32; prompt_len: HOST [batch], each in [1, tokens_stride].  Writes the
+ * cache slots [0, prompt_len), sets seq_len[b] = prompt_len[b] and
+ * pending[b] = argmax of the last prompt row (the first generated token).
+ * Resets the call-order state.  Errors: EINVAL, ECAPACITY. */
+int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int32_t tokens_stride,
+                    const int32_t* prompt_len, int32_t* seq_len, int32_t* pending, void* stream);
+
+/* Pass 1 (see the top of this file).  seq_len, pending: [batch] (read);
+ * drafts: [batch][K] (written); ar_tokens: [batch][K+1], only column 0
+ * (a_0) is written.  Stages the anchor K/V at slot seq_len[b]; writes the
+ * block scratch; the committed cache [0, seq_len) is not modified.
+ * Errors: EINVAL, ECAPACITY, ESTATE (a draft is already outstanding). */
+int orthrus_draft_block(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                        const int32_t* pending, int32_t* drafts, int32_t* ar_tokens, void* stream);
+
+/* Pass 2 and acceptance.  drafts: [batch][K] (read; the caller may have
+ * replaced the drafted ids since draft_block); ar_tokens: [batch][K+1]
+ * (column 0 read, columns 1..K written); accept_len: [batch] (written, in
+ * [0, K]).  Stages K/V at slots seq_len+1 .. seq_len+K; commits nothing.
+ * Errors: EINVAL, ESTATE (no outstanding draft). */
+int orthrus_verify_accept(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                          const int32_t* drafts, int32_t* ar_tokens, int32_t* accept_len,
+                          void* stream);
+
+/* Commit.  accept_len [batch], ar_tokens [batch][K+1], drafts [batch][K]
+ * (read); seq_len [batch] (read, then set to seq_len + 1 + m); pending
+ * [batch] (set to a_m); commit_start [batch] (set to the old seq_len: the
+ * committed slots are [commit_start, commit_start + m]); out_tokens
+ * [batch*(K+1)] (the emitted tokens d_1..d_m, a_m of every sequence, packed
+ * in batch order); out_off [batch+1] (exclusive prefix sum of m+1; out_off
+ * [batch] = tokens emitted by the step).  Moves no KV bytes: the accepted
+ * entries are already in place.  Errors: EINVAL, ESTATE (no verified
+ * step). */
+int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len,
+                      const int32_t* ar_tokens, const int32_t* drafts, int32_t* seq_len,
+                      int32_t* pending, int32_t* commit_start, int32_t* out_tokens,
+                      int32_t* out_off, void* stream);
+
+/* Tighten the host's length bound of each sequence to seq_len_host[b]
+ * (HOST array, values the caller read back from seq_len after a commit).
+ * The bound otherwise grows by block_k + 1 per committed step, which is
+ * what a caller that never reads lengths back must provision in max_ctx.
+ * Values below 1 or above the current bound are rejected (EINVAL); the
+ * device side never reads or writes past max_ctx whatever the bound says.
+ * Host only; must not be called while a step is in flight (ESTATE). */
+int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len_host);
+
+/* Parity taps (optional; NULL disables).  logits: device fp32
+ * [rows_cap][vocab]; every later LM-head pass writes its rows' logits there
+ * (pass 1: the batch anchor rows first, then batch*K mask rows in sequence
+ * order; pass 2: batch*K rows in sequence order).  attn: device
+ * [n_layers][rows_cap][n_q_heads*head_dim] in the model dtype; every later
+ * pass writes each layer's attention output (the O projection's input).
+ * Errors: EINVAL. */
+int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_cap);
+
+/* Kernel (a) alone: block attention of `batch` sequences, bf16.  q: [batch]
+ * [rows][n_q_heads][128]; k_cache: [batch][n_kv_heads][cap][128]; v_cache
+ * in the library's tiled layout: [batch][n_kv_heads][cap/64][128][64] where
+ * key j of a 64-key tile sits at column (j/32)*32 + ((j%16)/4)*8 +
+ * ((j%32)/16)*4 + j%4; k_block: [batch][n_kv_heads][kpad][128]; v_block:
+ * [batch][n_kv_heads][128][kpad] in the same column order per 32 keys
+ * (kpad = block_len rounded up to 32).  Each row sees cache keys
+ * [0, ctx_len) and all block_len block keys (the pages' mask-row view).
+ * out: [batch][rows][n_q_heads][128] bf16.  workspace: at least
+ * orthrus_attention_workspace(...) bytes.  cap must be a multiple of 64.
+ * Errors: EINVAL, EHIP. */
+int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
+                            const void* q, const void* k_cache, const void* v_cache, int32_t cap,
+                            int32_t ctx_len, const void* k_block, const void* v_block,
+                            int32_t block_len, void* out, void* workspace, uint64_t workspace_bytes,
+                            void* stream);
+uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t ctx_len);
+
+const char* orthrus_strerror(int code);
+int orthrus_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ORTHRUS_H */

@@ -1,0 +1,590 @@
+// liborthrus C ABI: argument checks, buffer carving, weight packing, and the
+// orchestration of the two passes of a draft/verify step (see orthrus.h for
+// the contract of every entry point).
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr int kPrefillChunk = 32;     // prompt rows per sequence per prefill pass
+constexpr int kAlign = 256;
+
+inline uint64_t al(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+enum { ST_IDLE = 0, ST_DRAFTED = 1, ST_VERIFIED = 2 };
+
+// canonical tensor numel (see orthrus_weight_tensor)
+uint64_t canon_numel(const orthrus_config& c, int t) {
+  uint64_t d = c.d_model, qd = (uint64_t)c.n_q_heads * c.head_dim,
+           kd = (uint64_t)c.n_kv_heads * c.head_dim;
+  if (t == 0 || t == 1) return (uint64_t)c.vocab * d;
+  if (t == 2 || t == 3) return d;
+  switch ((t - 4) % 17) {
+    case 0: case 1: return d;
+    case 2: case 8: return qd * d;
+    case 3: case 4: case 9: case 10: return kd * d;
+    case 5: case 11: return d * qd;
+    case 6: case 7: case 12: case 13: return (uint64_t)c.head_dim;
+    case 14: case 15: return (uint64_t)c.ffn_dim * d;
+    case 16: return d * (uint64_t)c.ffn_dim;
+  }
+  return 0;
+}
+
+int n_tensors(const orthrus_config& c) { return 4 + 17 * c.n_layers; }
+
+uint64_t canon_offset(const orthrus_config& c, int t) {
+  uint64_t o = 0;
+  for (int i = 0; i < t; ++i) o += (canon_numel(c, i) + 255) / 256 * 256;
+  return o;
+}
+
+struct Layout {
+  // element size, dims
+  int esz, L, d, hq, hkv, hd, F, V, K, G, qd, kd, nqkv;
+  int cap, kpad, tmax, rmax, sc, nc, qr_max, lm_parts;
+  bool bf16;
+  // packed offsets (bytes)
+  uint64_t p_embed, p_lm, p_fnorm, p_mask;
+  std::vector<uint64_t> p_anorm, p_ffnnorm, p_qn, p_kn, p_dqn, p_dkn, p_qkv, p_dqkv, p_o, p_do,
+      p_gu, p_down;
+  uint64_t packed_bytes;
+  // workspace offsets (bytes)
+  uint64_t w_h, w_x, w_qkv, w_q, w_act, w_opart, w_ml, w_parts, w_logits, w_rope, w_i32,
+      workspace_bytes;
+  uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
+};
+
+int validate(const orthrus_config* c) {
+  if (!c) return ORTHRUS_EINVAL;
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
+      c->head_dim < 2 || c->ffn_dim < 1 || c->vocab < 2 || c->block_k < 0 || c->max_batch < 1 ||
+      c->max_batch > 256 || c->max_ctx < 2)
+    return ORTHRUS_EINVAL;
+  if (c->n_q_heads % c->n_kv_heads) return ORTHRUS_EINVAL;
+  if (c->head_dim % 2 || c->head_dim > 128) return ORTHRUS_EINVAL;
+  if (!(c->rope_theta > 1.0) || !(c->rms_eps > 0.0)) return ORTHRUS_EINVAL;
+  if (c->block_k > 63) return ORTHRUS_EINVAL;
+  int G = c->n_q_heads / c->n_kv_heads;
+  if (c->dtype == ORTHRUS_BF16) {
+    if (c->head_dim != 128) return ORTHRUS_EINVAL;
+    if (c->d_model % 256 || (c->n_q_heads * c->head_dim) % 256 || c->ffn_dim % 256)
+      return ORTHRUS_EINVAL;
+    if (c->vocab % 32) return ORTHRUS_EINVAL;
+    if ((c->block_k + 1) * G > 144 || kPrefillChunk * G > 144) return ORTHRUS_EINVAL;
+  } else if (c->dtype != ORTHRUS_F32) {
+    return ORTHRUS_EINVAL;
+  }
+  return ORTHRUS_OK;
+}
+
+void make_layout(const orthrus_config& c, Layout& y) {
+  y.bf16 = c.dtype == ORTHRUS_BF16;
+  y.esz = y.bf16 ? 2 : 4;
+  y.L = c.n_layers; y.d = c.d_model; y.hq = c.n_q_heads; y.hkv = c.n_kv_heads; y.hd = c.head_dim;
+  y.F = c.ffn_dim; y.V = c.vocab; y.K = c.block_k; y.G = y.hq / y.hkv;
+  y.qd = y.hq * y.hd; y.kd = y.hkv * y.hd; y.nqkv = y.qd + 2 * y.kd;
+  y.cap = round_up(c.max_ctx, 64);
+  y.kpad = y.K > 0 ? round_up(y.K, 32) : 0;
+  y.tmax = y.K + 1 > kPrefillChunk ? y.K + 1 : kPrefillChunk;
+  y.rmax = c.max_batch * y.tmax;
+  int sc = 256;
+  while (sc < 2048 && sc * 32 < y.cap) sc *= 2;
+  y.sc = sc;
+  y.nc = (y.cap + sc - 1) / sc;
+  y.qr_max = y.tmax * y.G;
+  y.lm_parts = y.bf16 ? gemm_bf16_argmax_parts(y.V) : gemm_f32_argmax_parts(y.V);
+
+  // ---- packed weights
+  uint64_t o = 0, E = y.esz;
+  auto take = [&](uint64_t bytes) { uint64_t r = o; o = al(o + bytes); return r; };
+  y.p_embed = take((uint64_t)y.V * y.d * E);
+  y.p_lm = take((uint64_t)y.V * y.d * E);
+  y.p_fnorm = take((uint64_t)y.d * E);
+  y.p_mask = take((uint64_t)y.d * E);
+  for (int l = 0; l < y.L; ++l) {
+    y.p_anorm.push_back(take((uint64_t)y.d * E));
+    y.p_ffnnorm.push_back(take((uint64_t)y.d * E));
+    y.p_qn.push_back(take((uint64_t)y.hd * E));
+    y.p_kn.push_back(take((uint64_t)y.hd * E));
+    y.p_dqn.push_back(take((uint64_t)y.hd * E));
+    y.p_dkn.push_back(take((uint64_t)y.hd * E));
+    y.p_qkv.push_back(take((uint64_t)y.nqkv * y.d * E));
+    y.p_dqkv.push_back(take((uint64_t)y.nqkv * y.d * E));
+    y.p_o.push_back(take((uint64_t)y.d * y.qd * E));
+    y.p_do.push_back(take((uint64_t)y.d * y.qd * E));
+    y.p_gu.push_back(take((uint64_t)2 * y.F * y.d * E));
+    y.p_down.push_back(take((uint64_t)y.d * y.F * E));
+  }
+  y.packed_bytes = o;
+
+  // ---- KV cache and block scratch
+  y.kv_layer_elems = (uint64_t)c.max_batch * y.hkv * y.cap * y.hd;
+  y.kv_bytes = 2 * y.L * y.kv_layer_elems * E;
+  y.scr_layer_elems = (uint64_t)c.max_batch * y.hkv * y.kpad * y.hd;
+  y.scratch_bytes = 2 * y.L * y.scr_layer_elems * E;
+
+  // ---- workspace
+  o = 0;
+  int xw = y.d > y.qd ? y.d : y.qd;
+  y.w_h = take((uint64_t)y.rmax * y.d * 4);
+  y.w_x = take((uint64_t)y.rmax * xw * E);
+  y.w_qkv = take((uint64_t)y.rmax * y.nqkv * 4);
+  y.w_q = take((uint64_t)y.rmax * y.qd * E);
+  y.w_act = take((uint64_t)y.rmax * y.F * E);
+  uint64_t part_rows = (uint64_t)c.max_batch * y.hkv * (y.nc + 1) * y.qr_max;
+  y.w_opart = y.bf16 ? take(part_rows * y.hd * 4) : take(0);
+  y.w_ml = y.bf16 ? take(part_rows * 2 * 4) : take(0);
+  y.w_parts = take((uint64_t)y.rmax * y.lm_parts * 8);
+  y.w_logits = y.bf16 ? take(0) : take((uint64_t)y.rmax * y.V * 4);
+  y.w_rope = take((uint64_t)y.cap * (y.hd / 2) * 8);
+  y.w_i32 = take((uint64_t)4 * c.max_batch * 4);
+  y.workspace_bytes = o;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
+
+}  // namespace
+
+struct orthrus_ctx {
+  orthrus_config cfg;
+  Layout y;
+  char* packed;
+  char* kv;
+  char* scr;
+  char* ws;
+  int state;
+  int step_batch;
+  std::vector<int64_t> bound;   // host upper bound of every sequence's length
+  float* dbg_logits;
+  void* dbg_attn;
+  int dbg_rows;
+};
+
+namespace {
+
+int hip_ok(hipError_t e) {
+  if (e != hipSuccess) { g_last_hip = (int)e; return ORTHRUS_EHIP; }
+  return ORTHRUS_OK;
+}
+
+int check_launch() { return hip_ok(hipGetLastError()); }
+
+template <typename T> T* W(orthrus_ctx* c, uint64_t off) { return (T*)(c->packed + off); }
+template <typename T> T* S(orthrus_ctx* c, uint64_t off) { return (T*)(c->ws + off); }
+
+void gemm(orthrus_ctx* c, uint64_t woff, uint64_t woff2, const void* X, int ldx, int M, int K,
+          int N, const GemmOut& o, hipStream_t s) {
+  if (c->y.bf16)
+    launch_gemm_bf16(c->packed + woff, (const uint16_t*)X, ldx, M, K, N, o, s);
+  else
+    launch_gemm_f32((const float*)(c->packed + woff), (const float*)(c->packed + woff2),
+                    (const float*)X, ldx, M, K, N, o, s);
+}
+
+GemmOut out_store(float* y, int ldy, int ep) {
+  GemmOut o{};
+  o.ep = ep; o.y = y; o.ldy = ldy;
+  return o;
+}
+
+// One forward pass of the rows described by P through every layer, ending
+// with the LM-head argmax when want_tokens.
+void run_pass(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
+              const int32_t* block_tok, int block_ld, bool want_tokens, int32_t* drafts,
+              int32_t* ar, int32_t* pending, hipStream_t s) {
+  const Layout& y = c->y;
+  const int rows = P.rows();
+  const int AB = P.A * P.B;
+  const float eps = (float)c->cfg.rms_eps;
+  float* h = S<float>(c, y.w_h);
+  char* x = S<char>(c, y.w_x);
+  float* qkv = S<float>(c, y.w_qkv);
+  char* q = S<char>(c, y.w_q);
+  char* act = S<char>(c, y.w_act);
+  const uint64_t E = y.esz;
+
+  launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed, c->packed + y.p_mask,
+               y.V, y.d, y.bf16, h, s);
+  for (int l = 0; l < y.L; ++l) {
+    launch_rmsnorm(h, rows, y.d, c->packed + y.p_anorm[l], y.bf16, eps, x, s);
+    // Q/K/V: anchor (and every non-draft) row with the frozen projections,
+    // mask rows with the diffusion projections
+    uint64_t qkv_sz = (uint64_t)y.nqkv * y.d * E;
+    (void)qkv_sz;
+    if (P.kind == PASS_DRAFT) {
+      uint64_t wq_f = y.p_qkv[l], wq_d = y.p_dqkv[l];
+      if (AB > 0)
+        gemm(c, wq_f, 0, x, y.d, AB, y.d, y.nqkv, out_store(qkv, y.nqkv, EP_STORE), s);
+      if (rows > AB)
+        gemm(c, wq_d, 0, x + (uint64_t)AB * y.d * E, y.d, rows - AB, y.d, y.nqkv,
+             out_store(qkv + (uint64_t)AB * y.nqkv, y.nqkv, EP_STORE), s);
+    } else {
+      gemm(c, y.p_qkv[l], 0, x, y.d, rows, y.d, y.nqkv, out_store(qkv, y.nqkv, EP_STORE), s);
+    }
+    char* kc = c->kv + (uint64_t)l * y.kv_layer_elems * E;
+    char* vc = c->kv + ((uint64_t)y.L + l) * y.kv_layer_elems * E;
+    char* ks = c->scr + (uint64_t)l * y.scr_layer_elems * E;
+    char* vs = c->scr + ((uint64_t)y.L + l) * y.scr_layer_elems * E;
+    launch_qkv_post(P, qkv, y.hq, y.hkv, y.hd, c->packed + y.p_qn[l], c->packed + y.p_kn[l],
+                    c->packed + y.p_dqn[l], c->packed + y.p_dkn[l], y.bf16, eps,
+                    S<float>(c, y.w_rope), q, kc, vc, y.cap, ks, vs, y.kpad, s);
+    AttnArgs a{};
+    a.P = P; a.q = q; a.kc = kc; a.vc = vc; a.cap = y.cap; a.ks = ks; a.vs = vs;
+    a.kpad = y.kpad; a.hq = y.hq; a.hkv = y.hkv; a.hd = y.hd; a.sc = y.sc; a.nc = y.nc;
+    a.qr_max = y.qr_max; a.opart = S<float>(c, y.w_opart); a.ml = S<float>(c, y.w_ml);
+    a.out = x; a.fixed_ctx = -1; a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
+    if (c->dbg_attn && rows <= c->dbg_rows) {
+      a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * E;
+      a.tap_rows = rows;
+    }
+    if (y.bf16) launch_attention_bf16(a, s); else launch_attention_f32(a, s);
+    // O projection + residual
+    if (P.kind == PASS_DRAFT) {
+      if (AB > 0) gemm(c, y.p_o[l], 0, x, y.qd, AB, y.qd, y.d, out_store(h, y.d, EP_RESID), s);
+      if (rows > AB)
+        gemm(c, y.p_do[l], 0, x + (uint64_t)AB * y.qd * E, y.qd, rows - AB, y.qd, y.d,
+             out_store(h + (uint64_t)AB * y.d, y.d, EP_RESID), s);
+    } else {
+      gemm(c, y.p_o[l], 0, x, y.qd, rows, y.qd, y.d, out_store(h, y.d, EP_RESID), s);
+    }
+    // FFN
+    launch_rmsnorm(h, rows, y.d, c->packed + y.p_ffnnorm[l], y.bf16, eps, x, s);
+    GemmOut og{};
+    og.ep = EP_SWIGLU; og.act = act; og.ldact = y.F;
+    gemm(c, y.p_gu[l], y.p_gu[l] + (uint64_t)y.F * y.d * E, x, y.d, rows, y.d,
+         y.bf16 ? 2 * y.F : y.F, og, s);
+    gemm(c, y.p_down[l], 0, act, y.F, rows, y.F, y.d, out_store(h, y.d, EP_RESID), s);
+  }
+  if (!want_tokens) return;
+  launch_rmsnorm(h, rows, y.d, c->packed + y.p_fnorm, y.bf16, eps, x, s);
+  GemmOut ol{};
+  ol.ep = EP_ARGMAX;
+  ol.part = S<float2>(c, y.w_parts);
+  ol.y = y.bf16 ? nullptr : S<float>(c, y.w_logits);
+  ol.ldy = y.V;
+  if (c->dbg_logits && rows <= c->dbg_rows) { ol.logits = c->dbg_logits; ol.ldl = y.V; }
+  gemm(c, y.p_lm, 0, x, y.d, rows, y.d, y.V, ol, s);
+  launch_lm_reduce(ol.part, rows, y.lm_parts, P, y.K, drafts, ar, pending, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int orthrus_query_sizes(const orthrus_config* cfg, orthrus_sizes* out) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!out) return ORTHRUS_EINVAL;
+  Layout y;
+  make_layout(*cfg, y);
+  out->weights_bytes = canon_offset(*cfg, n_tensors(*cfg)) * y.esz;
+  out->packed_bytes = y.packed_bytes;
+  out->kv_bytes = y.kv_bytes;
+  out->scratch_bytes = y.scratch_bytes;
+  out->workspace_bytes = y.workspace_bytes;
+  return ORTHRUS_OK;
+}
+
+int orthrus_weight_tensor(const orthrus_config* cfg, int32_t index, uint64_t* offset_elems,
+                          uint64_t* numel) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!offset_elems || !numel) return ORTHRUS_EINVAL;
+  int nt = n_tensors(*cfg);
+  if (index == -1) { *offset_elems = 0; *numel = canon_offset(*cfg, nt); return ORTHRUS_OK; }
+  if (index < 0 || index >= nt) return ORTHRUS_EINVAL;
+  *offset_elems = canon_offset(*cfg, index);
+  *numel = canon_numel(*cfg, index);
+  return ORTHRUS_OK;
+}
+
+int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed, void* kv_cache,
+                   void* block_scratch, void* workspace, void* stream, orthrus_ctx** out) {
+  int rc = validate(cfg);
+  if (rc) return rc;
+  if (!out || !weights || !packed || !kv_cache || !workspace) return ORTHRUS_EINVAL;
+  if (cfg->block_k > 0 && !block_scratch) return ORTHRUS_EINVAL;
+  if (!aligned(weights) || !aligned(packed) || !aligned(kv_cache) || !aligned(workspace) ||
+      (block_scratch && !aligned(block_scratch)))
+    return ORTHRUS_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  orthrus_ctx* c = new orthrus_ctx();
+  c->cfg = *cfg;
+  make_layout(*cfg, c->y);
+  c->packed = (char*)packed; c->kv = (char*)kv_cache; c->scr = (char*)block_scratch;
+  c->ws = (char*)workspace;
+  c->state = ST_IDLE; c->step_batch = 0;
+  c->bound.assign(cfg->max_batch, 0);
+  c->dbg_logits = nullptr; c->dbg_attn = nullptr; c->dbg_rows = 0;
+  const Layout& y = c->y;
+  const uint64_t E = y.esz;
+  const char* w = (const char*)weights;
+  auto src = [&](int t) { return w + canon_offset(*cfg, t) * E; };
+  auto copy = [&](uint64_t dst, int t) {
+    return hipMemcpyAsync(c->packed + dst, src(t), canon_numel(*cfg, t) * E,
+                          hipMemcpyDeviceToDevice, s);
+  };
+  hipError_t e = hipSuccess;
+  auto chk = [&](hipError_t x) { if (x != hipSuccess && e == hipSuccess) e = x; };
+  chk(copy(y.p_embed, 0));
+  chk(copy(y.p_fnorm, 2));
+  chk(copy(y.p_mask, 3));
+  if (y.bf16) launch_pack_bf16((const uint16_t*)src(1), y.V, y.d, c->packed + y.p_lm, 0, 1, s);
+  else chk(copy(y.p_lm, 1));
+  for (int l = 0; l < y.L; ++l) {
+    int b0 = 4 + 17 * l;
+    chk(copy(y.p_anorm[l], b0 + 0));
+    chk(copy(y.p_ffnnorm[l], b0 + 1));
+    chk(copy(y.p_qn[l], b0 + 6));
+    chk(copy(y.p_kn[l], b0 + 7));
+    chk(copy(y.p_dqn[l], b0 + 12));
+    chk(copy(y.p_dkn[l], b0 + 13));
+    if (y.bf16) {
+      const int KBd = y.d / 32;
+      auto pack_rows = [&](uint64_t dst, int t, int N, int K, int nb_off, int nb_stride) {
+        launch_pack_bf16((const uint16_t*)src(t), N, K, c->packed + dst, nb_off, nb_stride, s);
+      };
+      (void)KBd;
+      // [Wq; Wk; Wv] -> one packed matrix of nqkv output rows
+      pack_rows(y.p_qkv[l], b0 + 2, y.qd, y.d, 0, 1);
+      pack_rows(y.p_qkv[l], b0 + 3, y.kd, y.d, y.qd / 16, 1);
+      pack_rows(y.p_qkv[l], b0 + 4, y.kd, y.d, (y.qd + y.kd) / 16, 1);
+      pack_rows(y.p_dqkv[l], b0 + 8, y.qd, y.d, 0, 1);
+      pack_rows(y.p_dqkv[l], b0 + 9, y.kd, y.d, y.qd / 16, 1);
+      pack_rows(y.p_dqkv[l], b0 + 10, y.kd, y.d, (y.qd + y.kd) / 16, 1);
+      pack_rows(y.p_o[l], b0 + 5, y.d, y.qd, 0, 1);
+      pack_rows(y.p_do[l], b0 + 11, y.d, y.qd, 0, 1);
+      // gate block j -> packed block 2j, up block j -> 2j+1
+      pack_rows(y.p_gu[l], b0 + 14, y.F, y.d, 0, 2);
+      pack_rows(y.p_gu[l], b0 + 15, y.F, y.d, 1, 2);
+      pack_rows(y.p_down[l], b0 + 16, y.d, y.F, 0, 1);
+    } else {
+      uint64_t qb = (uint64_t)y.qd * y.d * E, kb = (uint64_t)y.kd * y.d * E;
+      chk(hipMemcpyAsync(c->packed + y.p_qkv[l], src(b0 + 2), qb, hipMemcpyDeviceToDevice, s));
+      chk(hipMemcpyAsync(c->packed + y.p_qkv[l] + qb, src(b0 + 3), kb, hipMemcpyDeviceToDevice, s));
+      chk(hipMemcpyAsync(c->packed + y.p_qkv[l] + qb + kb, src(b0 + 4), kb,
+                         hipMemcpyDeviceToDevice, s));
+      chk(hipMemcpyAsync(c->packed + y.p_dqkv[l], src(b0 + 8), qb, hipMemcpyDeviceToDevice, s));
+      chk(hipMemcpyAsync(c->packed + y.p_dqkv[l] + qb, src(b0 + 9), kb, hipMemcpyDeviceToDevice, s));
+      chk(hipMemcpyAsync(c->packed + y.p_dqkv[l] + qb + kb, src(b0 + 10), kb,
+                         hipMemcpyDeviceToDevice, s));
+      chk(copy(y.p_o[l], b0 + 5));
+      chk(copy(y.p_do[l], b0 + 11));
+      uint64_t fb = (uint64_t)y.F * y.d * E;
+      chk(hipMemcpyAsync(c->packed + y.p_gu[l], src(b0 + 14), fb, hipMemcpyDeviceToDevice, s));
+      chk(hipMemcpyAsync(c->packed + y.p_gu[l] + fb, src(b0 + 15), fb, hipMemcpyDeviceToDevice, s));
+      chk(copy(y.p_down[l], b0 + 16));
+    }
+  }
+  // RoPE table: angle pos * theta^(-2i/hd) in float64, stored as fp32 (cos, sin)
+  std::vector<float> rope((size_t)y.cap * y.hd);
+  for (int p = 0; p < y.cap; ++p)
+    for (int i = 0; i < y.hd / 2; ++i) {
+      double ang = (double)p * pow(cfg->rope_theta, -2.0 * i / y.hd);
+      rope[((size_t)p * (y.hd / 2) + i) * 2] = (float)cos(ang);
+      rope[((size_t)p * (y.hd / 2) + i) * 2 + 1] = (float)sin(ang);
+    }
+  chk(hipMemcpyAsync(c->ws + y.w_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice, s));
+  chk(hipGetLastError());
+  chk(hipStreamSynchronize(s));
+  if (e != hipSuccess) {
+    g_last_hip = (int)e;
+    delete c;
+    return ORTHRUS_EHIP;
+  }
+  *out = c;
+  return ORTHRUS_OK;
+}
+
+int orthrus_destroy(orthrus_ctx* ctx) {
+  if (!ctx) return ORTHRUS_EINVAL;
+  delete ctx;
+  return ORTHRUS_OK;
+}
+
+int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_cap) {
+  if (!ctx || rows_cap < 0) return ORTHRUS_EINVAL;
+  if ((logits || attn) && rows_cap == 0) return ORTHRUS_EINVAL;
+  ctx->dbg_logits = logits;
+  ctx->dbg_attn = attn;
+  ctx->dbg_rows = rows_cap;
+  return ORTHRUS_OK;
+}
+
+int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int32_t tokens_stride,
+                    const int32_t* prompt_len, int32_t* seq_len, int32_t* pending, void* stream) {
+  if (!ctx || !tokens || !prompt_len || !seq_len || !pending) return ORTHRUS_EINVAL;
+  if (batch < 1 || batch > ctx->cfg.max_batch || tokens_stride < 1) return ORTHRUS_EINVAL;
+  int pmax = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (prompt_len[b] < 1 || prompt_len[b] > tokens_stride) return ORTHRUS_EINVAL;
+    if (prompt_len[b] > pmax) pmax = prompt_len[b];
+  }
+  // prefill rows of every sequence run to pmax-1 (rows past a sequence's own
+  // prompt compute values that land in slots no later step reads)
+  if (pmax + 1 > ctx->y.cap || pmax > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  const Layout& y = ctx->y;
+  int32_t* i32 = S<int32_t>(ctx, y.w_i32);
+  int32_t* plen_dev = i32;
+  int32_t* last_tok = i32 + ctx->cfg.max_batch;
+  int rc = hip_ok(hipMemcpyAsync(plen_dev, prompt_len, sizeof(int32_t) * batch,
+                                 hipMemcpyHostToDevice, s));
+  if (rc) return rc;
+  rc = hip_ok(hipStreamSynchronize(s));
+  if (rc) return rc;
+  for (int p0 = 0; p0 < pmax - 1; p0 += kPrefillChunk) {
+    PassInfo P{};
+    P.kind = PASS_PREFILL; P.B = batch; P.A = 0;
+    P.Kx = (pmax - 1 - p0) < kPrefillChunk ? (pmax - 1 - p0) : kPrefillChunk;
+    P.p0 = p0; P.len = nullptr;
+    run_pass(ctx, P, nullptr, tokens, tokens_stride, false, nullptr, nullptr, nullptr, s);
+  }
+  launch_prefill_tail(batch, tokens, tokens_stride, plen_dev, seq_len, last_tok, s);
+  PassInfo P{};
+  P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = 0; P.p0 = 0; P.len = seq_len;
+  run_pass(ctx, P, last_tok, nullptr, 0, true, nullptr, nullptr, pending, s);
+  launch_len_add(batch, seq_len, 1, s);
+  rc = check_launch();
+  if (rc) return rc;
+  for (int b = 0; b < ctx->cfg.max_batch; ++b) ctx->bound[b] = b < batch ? prompt_len[b] : 0;
+  ctx->state = ST_IDLE;
+  return ORTHRUS_OK;
+}
+
+int orthrus_draft_block(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                        const int32_t* pending, int32_t* drafts, int32_t* ar_tokens,
+                        void* stream) {
+  if (!ctx || !seq_len || !pending || !ar_tokens) return ORTHRUS_EINVAL;
+  if (ctx->y.K > 0 && !drafts) return ORTHRUS_EINVAL;
+  if (batch < 1 || batch > ctx->cfg.max_batch) return ORTHRUS_EINVAL;
+  if (ctx->state != ST_IDLE) return ORTHRUS_ESTATE;
+  for (int b = 0; b < batch; ++b)
+    if (ctx->bound[b] < 1) return ORTHRUS_ESTATE;          // never prefilled
+  for (int b = 0; b < batch; ++b)
+    if (ctx->bound[b] + ctx->y.K + 1 > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
+  PassInfo P{};
+  P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = ctx->y.K; P.p0 = 0; P.len = seq_len;
+  run_pass(ctx, P, pending, nullptr, 0, true, drafts, ar_tokens, nullptr, (hipStream_t)stream);
+  int rc = check_launch();
+  if (rc) return rc;
+  ctx->state = ST_DRAFTED;
+  ctx->step_batch = batch;
+  return ORTHRUS_OK;
+}
+
+int orthrus_verify_accept(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                          const int32_t* drafts, int32_t* ar_tokens, int32_t* accept_len,
+                          void* stream) {
+  if (!ctx || !seq_len || !ar_tokens || !accept_len) return ORTHRUS_EINVAL;
+  if (ctx->y.K > 0 && !drafts) return ORTHRUS_EINVAL;
+  if (ctx->state != ST_DRAFTED) return ORTHRUS_ESTATE;
+  if (batch != ctx->step_batch) return ORTHRUS_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  const int K = ctx->y.K;
+  if (K > 0) {
+    PassInfo P{};
+    P.kind = PASS_VERIFY; P.B = batch; P.A = 0; P.Kx = K; P.p0 = 0; P.len = seq_len;
+    run_pass(ctx, P, nullptr, drafts, K, true, nullptr, ar_tokens, nullptr, s);
+  }
+  launch_accept(batch, K, drafts, ar_tokens, accept_len, s);
+  int rc = check_launch();
+  if (rc) return rc;
+  ctx->state = ST_VERIFIED;
+  return ORTHRUS_OK;
+}
+
+int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len,
+                      const int32_t* ar_tokens, const int32_t* drafts, int32_t* seq_len,
+                      int32_t* pending, int32_t* commit_start, int32_t* out_tokens,
+                      int32_t* out_off, void* stream) {
+  if (!ctx || !accept_len || !ar_tokens || !seq_len || !pending || !commit_start ||
+      !out_tokens || !out_off)
+    return ORTHRUS_EINVAL;
+  if (ctx->y.K > 0 && !drafts) return ORTHRUS_EINVAL;
+  if (ctx->state != ST_VERIFIED) return ORTHRUS_ESTATE;
+  if (batch != ctx->step_batch) return ORTHRUS_EINVAL;
+  launch_commit(batch, ctx->y.K, accept_len, ar_tokens, drafts, seq_len, pending, commit_start,
+                out_tokens, out_off, (hipStream_t)stream);
+  int rc = check_launch();
+  if (rc) return rc;
+  for (int b = 0; b < batch; ++b) ctx->bound[b] += ctx->y.K + 1;
+  ctx->state = ST_IDLE;
+  return ORTHRUS_OK;
+}
+
+int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len_host) {
+  if (!ctx || !seq_len_host || batch < 1 || batch > ctx->cfg.max_batch) return ORTHRUS_EINVAL;
+  if (ctx->state != ST_IDLE) return ORTHRUS_ESTATE;
+  for (int b = 0; b < batch; ++b)
+    if (seq_len_host[b] < 1 || seq_len_host[b] > ctx->bound[b]) return ORTHRUS_EINVAL;
+  for (int b = 0; b < batch; ++b) ctx->bound[b] = seq_len_host[b];
+  return ORTHRUS_OK;
+}
+
+uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
+                                     int32_t n_kv_heads, int32_t ctx_len) {
+  if (batch < 1 || rows < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || ctx_len < 0) return 0;
+  int sc = 256;
+  while (sc < 2048 && sc * 32 < ctx_len) sc *= 2;
+  int nc = (ctx_len + sc - 1) / sc;
+  uint64_t qr = (uint64_t)rows * (n_q_heads / n_kv_heads);
+  uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * qr;
+  return al(pr * 128 * 4) + al(pr * 2 * 4);
+}
+
+int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
+                            const void* q, const void* k_cache, const void* v_cache, int32_t cap,
+                            int32_t ctx_len, const void* k_block, const void* v_block,
+                            int32_t block_len, void* out, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
+  if (batch < 1 || rows < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads)
+    return ORTHRUS_EINVAL;
+  int G = n_q_heads / n_kv_heads;
+  if (rows * G > 144 || cap % 64 || ctx_len < 0 || ctx_len > cap || block_len < 0 ||
+      block_len > 64 || ctx_len + block_len < 1)
+    return ORTHRUS_EINVAL;
+  if (!q || !out || !workspace || (ctx_len > 0 && (!k_cache || !v_cache)) ||
+      (block_len > 0 && (!k_block || !v_block)))
+    return ORTHRUS_EINVAL;
+  uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
+  if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
+  int sc = 256;
+  while (sc < 2048 && sc * 32 < ctx_len) sc *= 2;
+  int nc = (ctx_len + sc - 1) / sc;
+  uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
+  AttnArgs a{};
+  a.P.kind = PASS_DRAFT; a.P.B = batch; a.P.A = 0; a.P.Kx = rows; a.P.p0 = 0; a.P.len = nullptr;
+  a.q = q; a.kc = k_cache; a.vc = v_cache; a.cap = cap; a.ks = k_block; a.vs = v_block;
+  a.kpad = round_up(block_len, 32); a.hq = n_q_heads; a.hkv = n_kv_heads; a.hd = 128;
+  a.sc = sc; a.nc = nc; a.qr_max = rows * G;
+  a.opart = (float*)workspace;
+  a.ml = (float*)((char*)workspace + al(pr * 128 * 4));
+  a.out = out; a.fixed_ctx = ctx_len; a.block_len = block_len;
+  launch_attention_bf16(a, (hipStream_t)stream);
+  return check_launch();
+}
+
+const char* orthrus_strerror(int code) {
+  switch (code) {
+    case ORTHRUS_OK: return "ok";
+    case ORTHRUS_EINVAL: return "invalid argument";
+    case ORTHRUS_ECAPACITY: return "a sequence could grow past max_ctx";
+    case ORTHRUS_ESTATE: return "call out of order";
+    case ORTHRUS_EHIP: return "HIP error";
+  }
+  return "unknown error";
+}
+
+int orthrus_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

@@ -1,0 +1,145 @@
+// Internal declarations of liborthrus: pass descriptors, kernel launchers and
+// the device helpers shared by the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "orthrus.h"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- passes
+// Row order inside a pass: for a draft pass the `A*B` anchor rows come first
+// (row b = sequence b), then B*Kx block rows (row A*B + b*Kx + i).  Verify and
+// prefill passes have no anchor rows (A = 0) and B*Kx rows.
+enum PassKind { PASS_DRAFT = 0, PASS_VERIFY = 1, PASS_PREFILL = 2 };
+
+struct PassInfo {
+  int kind;
+  int B;             // sequences
+  int A;             // 1 if anchor rows are present (draft passes)
+  int Kx;            // block rows per sequence (masks / verified drafts / prompt rows)
+  int p0;            // prefill: absolute position of block row 0
+  const int32_t* len;  // device seq_len[B] (draft / verify)
+  __host__ __device__ int rows() const { return A * B + B * Kx; }
+  __host__ __device__ int tokens_per_seq() const { return A + Kx; }
+};
+
+struct RowInfo {
+  int b, t, pos, limit, is_mask;
+};
+
+// Row r -> (sequence, token index within the sequence's rows, absolute
+// position, last visible cache slot, mask-row flag).
+__device__ __forceinline__ RowInfo row_info(const PassInfo& P, int r) {
+  RowInfo ri;
+  if (P.kind == PASS_DRAFT) {
+    if (r < P.A * P.B) {
+      ri.b = r; ri.t = 0; ri.pos = P.len[r]; ri.limit = ri.pos; ri.is_mask = 0;
+    } else {
+      int j = r - P.A * P.B;
+      ri.b = j / P.Kx;
+      int i = j - ri.b * P.Kx;
+      ri.t = P.A + i;
+      int n = P.len[ri.b];
+      ri.pos = n + 1 + i; ri.limit = n; ri.is_mask = 1;
+    }
+  } else {
+    ri.b = r / P.Kx;
+    int i = r - ri.b * P.Kx;
+    ri.t = i;
+    ri.pos = (P.kind == PASS_VERIFY ? P.len[ri.b] + 1 : P.p0) + i;
+    ri.limit = ri.pos; ri.is_mask = 0;
+  }
+  return ri;
+}
+
+__device__ __forceinline__ int row_of(const PassInfo& P, int b, int t) {
+  if (P.kind == PASS_DRAFT) return t < P.A ? b : P.A * P.B + b * P.Kx + (t - P.A);
+  return b * P.Kx + t;
+}
+
+// Column of key j (0..63) inside a 64-key V tile stored transposed
+// ([head_dim][64]): within each 32-key group the 4-key runs are interleaved
+// so that one 16-byte LDS read gives a lane the 8 keys its MFMA B-operand
+// slot needs (keys q*4..q*4+3 and 16+q*4..16+q*4+3 for lane group q).
+__host__ __device__ __forceinline__ int vt_col(int j) {
+  int g = j >> 5, k = j & 31;
+  return g * 32 + ((k & 15) >> 2) * 8 + (k >> 4) * 4 + (k & 3);
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += ((u >> 16) & 1u) + 0x7FFFu;        // round to nearest even (inputs are finite)
+  return (uint16_t)(u >> 16);
+}
+
+// ----------------------------------------------------------- launchers
+struct Model;   // defined in api.hip
+
+// common kernels
+void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, int nb_stride,
+                      hipStream_t s);
+void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
+                  int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
+                  float* h, hipStream_t s);
+void launch_rmsnorm(const float* h, int rows, int d, const void* gain, bool bf16, float eps,
+                    void* out, hipStream_t s);
+void launch_qkv_post(const PassInfo& P, const float* qkv, int hq, int hkv, int hd,
+                     const void* qn, const void* kn, const void* dqn, const void* dkn, bool bf16,
+                     float eps, const float* rope, void* q_out, void* kc, void* vc, int cap,
+                     void* ks, void* vs, int kpad, hipStream_t s);
+void launch_lm_reduce(const float2* part, int rows, int nparts, const PassInfo& P, int K,
+                      int32_t* drafts, int32_t* ar_tokens, int32_t* pending, hipStream_t s);
+void launch_accept(int B, int K, const int32_t* drafts, const int32_t* ar, int32_t* accept_len,
+                   hipStream_t s);
+void launch_commit(int B, int K, const int32_t* accept_len, const int32_t* ar,
+                   const int32_t* drafts, int32_t* seq_len, int32_t* pending,
+                   int32_t* commit_start, int32_t* out_tokens, int32_t* out_off, hipStream_t s);
+void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev,
+                         int32_t* seq_len, int32_t* last_tok, hipStream_t s);
+void launch_len_add(int B, int32_t* seq_len, int add, hipStream_t s);
+void launch_copy_rows_f32_to_bf16(const float* src, int rows, int cols, uint16_t* dst,
+                                  hipStream_t s);
+
+// GEMMs.  Y = X . W^T over rows [0, M) of X (row stride ldx elements).
+enum Epilogue { EP_STORE = 0, EP_RESID = 1, EP_SWIGLU = 2, EP_ARGMAX = 3 };
+struct GemmOut {
+  int ep;
+  float* y; int ldy;            // EP_STORE / EP_RESID (fp32)
+  void* act; int ldact;         // EP_SWIGLU (model dtype)
+  float2* part;                 // EP_ARGMAX partials [M][nparts]
+  float* logits; int ldl;       // optional logits tap (EP_ARGMAX)
+};
+// bf16: W is packed (16x32 MFMA blocks); the reduction order per output is
+// fixed (8 K-slices summed in order) and independent of M.
+void launch_gemm_bf16(const void* Wp, const uint16_t* X, int ldx, int M, int K, int N,
+                      const GemmOut& o, hipStream_t s);
+int gemm_bf16_argmax_parts(int N);
+// fp32: W canonical row-major [N][K] (for SwiGLU: gate at W, up at W2).
+void launch_gemm_f32(const float* W, const float* W2, const float* X, int ldx, int M, int K,
+                     int N, const GemmOut& o, hipStream_t s);
+int gemm_f32_argmax_parts(int N);
+
+// Attention.  q [rows][hq][hd] (model dtype); cache layer base pointers.
+struct AttnArgs {
+  PassInfo P;
+  const void* q;
+  const void* kc; const void* vc; int cap;
+  const void* ks; const void* vs; int kpad;   // block scratch (draft passes)
+  int hq, hkv, hd;
+  int sc;           // keys per chunk (multiple of 64)
+  int nc;           // cache chunks
+  int qr_max;       // q-rows per (sequence, kv head) capacity of the partial buffers
+  float* opart;     // [B][hkv][nc+1][qr_max][hd]
+  float* ml;        // [B][hkv][nc+1][qr_max][2]
+  void* out;        // [rows][hq*hd] model dtype
+  void* tap; int tap_rows;   // optional attention-output tap for this layer
+  int fixed_ctx;    // >= 0: microbenchmark mode, every row sees cache [0, fixed_ctx)
+  int block_len;    // keys in the block scratch
+};
+void launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+void launch_attention_f32(const AttnArgs& a, hipStream_t s);

@@ -1,0 +1,138 @@
+"""A decode engine over liborthrus with torch as the device-memory and stream
+provider.  Host-side sequencing only (prefill, then draft -> verify -> commit
+steps); all computation is in the library's kernels."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as C
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _buf(nbytes: int, device) -> torch.Tensor:
+    # 256-byte aligned raw device buffer (the caching allocator aligns to 512)
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+class Engine:
+    """One context: packed weights, KV cache, block scratch and workspace.
+
+    weights: a device tensor holding the canonical weight buffer (see
+    orthrus_weight_tensor); it is only read during construction."""
+
+    def __init__(self, cfg: C.OrthrusConfig, weights: torch.Tensor, device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.sizes = C.orthrus_query_sizes(cfg)
+        self.K = cfg.block_k
+        self.packed = _buf(self.sizes.packed_bytes, self.device)
+        self.kv = _buf(self.sizes.kv_bytes, self.device)
+        self.scratch = _buf(self.sizes.scratch_bytes, self.device)
+        self.ws = _buf(self.sizes.workspace_bytes, self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        self.ctx = C.orthrus_create(cfg, weights.data_ptr(), self.packed.data_ptr(),
+                                    self.kv.data_ptr(), self.scratch.data_ptr(),
+                                    self.ws.data_ptr(), self.stream.cuda_stream)
+        B, K = cfg.max_batch, max(self.K, 1)
+        i32 = dict(dtype=torch.int32, device=self.device)
+        self.seq_len = torch.zeros(B, **i32)
+        self.pending = torch.zeros(B, **i32)
+        self.drafts = torch.zeros(B, K, **i32)
+        self.ar = torch.zeros(B, self.K + 1, **i32)
+        self.accept = torch.zeros(B, **i32)
+        self.commit_start = torch.zeros(B, **i32)
+        self.out_tokens = torch.zeros(B * (self.K + 1), **i32)
+        self.out_off = torch.zeros(B + 1, **i32)
+        self.B = 0
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            C.orthrus_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def s(self) -> int:
+        return self.stream.cuda_stream
+
+    def set_debug(self, logits: torch.Tensor | None, attn: torch.Tensor | None, rows: int):
+        C.orthrus_set_debug(self.ctx, _ptr(logits), _ptr(attn), rows)
+
+    def prefill(self, prompts: np.ndarray, prompt_len=None):
+        prompts = np.ascontiguousarray(prompts, np.int32)
+        B, P = prompts.shape
+        plen = np.full(B, P, np.int32) if prompt_len is None else np.asarray(prompt_len, np.int32)
+        tok = torch.from_numpy(prompts).to(self.device)
+        self._prompt_dev = tok
+        C.orthrus_prefill(self.ctx, B, tok.data_ptr(), P, plen, self.seq_len.data_ptr(),
+                          self.pending.data_ptr(), self.s)
+        self.B = B
+
+    def draft(self):
+        C.orthrus_draft_block(self.ctx, self.B, self.seq_len.data_ptr(), self.pending.data_ptr(),
+                              self.drafts.data_ptr() if self.K else None, self.ar.data_ptr(),
+                              self.s)
+
+    def verify(self):
+        C.orthrus_verify_accept(self.ctx, self.B, self.seq_len.data_ptr(),
+                                self.drafts.data_ptr() if self.K else None, self.ar.data_ptr(),
+                                self.accept.data_ptr(), self.s)
+
+    def commit(self):
+        C.orthrus_commit_kv(self.ctx, self.B, self.accept.data_ptr(), self.ar.data_ptr(),
+                            self.drafts.data_ptr() if self.K else None, self.seq_len.data_ptr(),
+                            self.pending.data_ptr(), self.commit_start.data_ptr(),
+                            self.out_tokens.data_ptr(), self.out_off.data_ptr(), self.s)
+
+    def step(self, planted: torch.Tensor | None = None):
+        self.draft()
+        if planted is not None:
+            self.drafts[:self.B].copy_(planted)
+        self.verify()
+        self.commit()
+
+    def generate(self, prompts: np.ndarray, n_new: int, planted=None, record=False):
+        """Greedy generation of n_new tokens per sequence (token 1 is the
+        prefill's).  planted: optional [steps][B][K] int32 drafts.  Returns
+        (tokens [B][n_new], per-step records)."""
+        self.prefill(prompts)
+        B = self.B
+        outs = [[int(t)] for t in self.pending[:B].cpu().tolist()]
+        recs = []
+        s = 0
+        while min(len(o) for o in outs) < n_new:
+            n_before = self.seq_len[:B].clone() if record else None
+            pl = None
+            if planted is not None:
+                if s >= planted.shape[0]:
+                    break
+                pl = torch.as_tensor(planted[s], dtype=torch.int32, device=self.device)
+            self.draft()
+            if record:
+                drafted = self.drafts[:B].clone()
+            if pl is not None:
+                self.drafts[:B].copy_(pl)
+            self.verify()
+            self.commit()
+            off = self.out_off[:B + 1].cpu().numpy()
+            C.orthrus_sync_lengths(self.ctx, B, self.seq_len[:B].cpu().numpy())
+            tok = self.out_tokens[:off[-1]].cpu().numpy()
+            for b in range(B):
+                outs[b].extend(tok[off[b]:off[b + 1]].tolist())
+            if record:
+                recs.append(dict(n=n_before.cpu().numpy(), drafted=drafted.cpu().numpy(),
+                                 drafts=self.drafts[:B].cpu().numpy(),
+                                 ar=self.ar[:B].cpu().numpy(), m=self.accept[:B].cpu().numpy(),
+                                 commit_start=self.commit_start[:B].cpu().numpy(),
+                                 len=self.seq_len[:B].cpu().numpy()))
+            s += 1
+        return np.array([o[:n_new] for o in outs], np.int32), recs

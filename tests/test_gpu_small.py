@@ -1,0 +1,139 @@
+"""GPU parity on the small bf16 model (the bf16 MFMA kernels at the big
+model's head size and GQA group): the draft/verify output equals the GPU's
+own plain greedy decoding exactly; tokens, drafts and accept lengths equal
+the oracle's wherever the oracle's top-1/top-2 margin exceeds the tolerance;
+logits within 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.mark.parametrize("B", [1, 3])
+def test_small_orthrus_equals_gpu_greedy(B):
+    sh = workloads.SHAPES["small"]
+    prompt = workloads.prompts(B, 40, sh["V"], seed=5)
+    eng = U.engine("small", max_batch=B, max_ctx=1024)
+    ar = U.engine("small", K=0, max_batch=B, max_ctx=1024)
+    got, recs = eng.generate(prompt, 96, record=True)
+    want, _ = ar.generate(prompt, 96)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("kind", ["all", "none", "geom6", "uniform32"])
+def test_small_planted_drafts(kind):
+    """Planted drafts force the accept length; output stays greedy and every
+    step accepts exactly the planted count (commit and discard paths)."""
+    sh = workloads.SHAPES["small"]
+    K, B = sh["K"], 2
+    prompt = workloads.prompts(B, 24, sh["V"], seed=6)
+    ar = U.engine("small", K=0, max_batch=B, max_ctx=2048)
+    traj, _ = ar.generate(prompt, 400)
+    steps = 8
+    if kind == "all":
+        a = np.full((steps, B), K, np.int32)
+    elif kind == "none":
+        a = np.zeros((steps, B), np.int32)
+    else:
+        a = workloads.plant_lengths(steps, B, K, kind)
+    planted = workloads.plant_drafts(traj, 1, a, K, sh["V"])
+    eng = U.engine("small", max_batch=B, max_ctx=2048)
+    n_new = 1 + int((a + 1).sum(0).min())
+    got, recs = eng.generate(prompt, n_new, planted=planted, record=True)
+    assert np.array_equal(got, traj[:, :n_new])
+    for s, r in enumerate(recs):
+        assert np.array_equal(r["m"], a[s])
+        assert np.array_equal(r["len"], r["n"] + 1 + a[s])
+
+
+def test_small_anchor_and_verify_rows_bitwise_equal_plain_decoding():
+    """Batch invariance: the anchor row (computed with 32 mask rows) and the
+    verify rows (32 at once) give the same logits, bit for bit, as one-row
+    greedy decoding of the same tokens."""
+    sh = workloads.SHAPES["small"]
+    K, V = sh["K"], sh["V"]
+    prompt = workloads.prompts(1, 30, V, seed=7)
+    ar = U.engine("small", K=0, max_ctx=512)
+    lg_ar = torch.zeros(1, V, device="cuda")
+    ar.set_debug(lg_ar, None, 1)
+    ar.prefill(prompt)
+    rows_ar = []
+    toks = [int(ar.pending[0])]
+    for _ in range(K + 1):
+        ar.step()
+        torch.cuda.synchronize()
+        rows_ar.append(lg_ar[0].clone())
+        toks.append(int(ar.pending[0]))
+    eng = U.engine("small", max_ctx=512)
+    lg = torch.zeros(K + 1, V, device="cuda")
+    eng.set_debug(lg, None, K + 1)
+    eng.prefill(prompt)
+    eng.draft()
+    torch.cuda.synchronize()
+    assert torch.equal(lg[0], rows_ar[0])                 # anchor row
+    eng.drafts[0].copy_(torch.tensor(toks[1:K + 1], dtype=torch.int32))
+    eng.verify()
+    torch.cuda.synchronize()
+    for i in range(K):
+        assert torch.equal(lg[i], rows_ar[i + 1]), i      # verify row i
+    assert int(eng.accept[0]) == K
+
+
+def test_small_step_parity_with_oracle():
+    """Step by step against the oracle while the two agree on every token;
+    a disagreement is only allowed at an oracle near-tie (margin <= tol) with
+    the GPU choosing the oracle's runner-up, and ends the comparison."""
+    sh = workloads.SHAPES["small"]
+    K, V = sh["K"], sh["V"]
+    prompt = workloads.prompts(1, 48, V, seed=8)
+    om = U.oracle_model("small")
+    seq = om.seq(600)
+    pend_o, lg0 = seq.prefill(prompt[0], want_logits=True)
+    eng = U.engine("small", max_ctx=600)
+    lg = torch.zeros(K + 1, V, device="cuda")
+    eng.set_debug(lg, None, K + 1)
+    eng.prefill(prompt)
+    assert int(eng.pending[0]) == pend_o or U.margin(lg0) <= TOL
+    compared = 0
+    for step in range(10):
+        eng.draft()
+        torch.cuda.synchronize()
+        gd = lg.cpu().numpy().astype(np.float64)
+        g_drafts = eng.drafts[0].cpu().numpy().copy()
+        eng.verify()
+        torch.cuda.synchronize()
+        gv = lg[:K].cpu().numpy().astype(np.float64)
+        eng.commit()
+        torch.cuda.synchronize()
+        r = seq.step(pend_o, K)
+        assert np.abs(gd[0] - r["logits_anchor"]).max() < TOL
+        assert np.abs(gd[1:] - r["logits_draft"]).max() < TOL
+        diverged = False
+        for i in range(K):
+            if g_drafts[i] != r["drafts"][i]:
+                row = r["logits_draft"][i]
+                assert U.margin(row) <= TOL and np.argsort(row)[-2] == g_drafts[i]
+                diverged = True
+                break
+        if diverged:
+            break
+        # verify rows are comparable up to the accepted prefix and one more
+        g_ar = eng.ar[0].cpu().numpy()
+        m = r["m"]
+        np.testing.assert_array_less(np.abs(gv[:m + 1] - r["logits_verify"][:m + 1]).max(), TOL)
+        if not np.array_equal(g_ar[:m + 2], r["ar"][:m + 2]):
+            j = int(np.nonzero(g_ar[:m + 2] != r["ar"][:m + 2])[0][0])
+            row = r["logits_anchor"] if j == 0 else r["logits_verify"][j - 1]
+            assert U.margin(row) <= TOL
+            break
+        assert int(eng.accept[0]) == m
+        assert int(eng.seq_len[0]) == r["len"]
+        pend_o = r["pending"]
+        compared += 1
+    assert compared >= 3
