@@ -1,3 +1,267 @@
-"""placeholder"""
+#!/usr/bin/env python3
+"""Throughput of the Orthrus draft -> verify -> accept -> commit step on one
+MI355X, on a random-init Qwen3-8B-shaped model (synthetic, seeded).
+
+A step is one pass of the whole hot path for every sequence of the batch:
+pass 1 (anchor + K mask rows through all layers, LM-head argmax), the
+planted-draft copy, pass 2 (K verify rows), acceptance and commit.  Drafts
+are planted from the model's own greedy trajectory so that each step
+accepts a seeded number of tokens (the random model's own drafts would
+almost never be accepted); the timed loop does all the work of a real step.
+
+Prints ONE JSON line (everything else goes to stderr):
+  value          verified tokens/s = sum over steps and sequences of (m+1) / time
+  roofline       the dominant kernel (the draft pass's gate/up SwiGLU GEMM):
+                 algorithmic bytes per launch / its average duration, timed
+                 with HIP events around its launches inside the timed region
+  cpu_baseline   the CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_gateup_draft_pmc.json")
+
+
 def tpf_from_accept(mean_accept: float) -> float:
+    """Tokens per forward: a step emits m+1 tokens with two forward passes."""
     return (mean_accept + 1.0) / 2.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "lossless_decoding_amd", "csrc", "k_gemm.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def workload_desc(name, wl, sh):
+    law = {"geom6": "planted accept length min(Geom(1/7), 32), mean 6",
+           "uniform32": "planted accept length uniform{0..32}"}[wl["plant"]]
+    return (f"{name}: Qwen3-8B-shaped random-init model (L={sh['L']}, d={sh['d']}, "
+            f"{sh['hq']}q/{sh['hkv']}kv heads x {sh['hd']}, SwiGLU {sh['F']}, vocab {sh['V']}, "
+            f"bf16), batch {wl['B']}, prompt {wl['P']} uniform-random tokens, K={sh['K']}, {law}")
+
+
+def cpu_baseline(sh, wl, mean_tokens_per_step):
+    """Oracle (plain fp64 C, as it stands) on one full draft+verify step of
+    one sequence at the full model shape after a short prefill."""
+    import numpy as np
+
+    import oracle
+    from synth import workloads
+
+    t0 = time.time()
+    shp = oracle.ModelShape(**sh)
+    lay, total = oracle.weight_layout(shp)
+    w = workloads.fill_weights(lay, total, True)
+    log(f"[cpu] weights generated in {time.time() - t0:.1f}s")
+    m = oracle.Model(shp, w)
+    P0 = 4
+    prompt = workloads.prompts(1, P0, sh["V"])[0]
+    seq = m.seq(P0 + sh["K"] + 4)
+    t1 = time.time()
+    pending = seq.prefill(prompt)
+    t2 = time.time()
+    r = seq.step(pending, sh["K"])
+    t3 = time.time()
+    step_s = t3 - t2
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    log(f"[cpu] prefill {P0} rows {t2 - t1:.1f}s, one step {step_s:.1f}s, m={r['m']}")
+    return {
+        "value": mean_tokens_per_step / step_s,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"one draft+verify step (2 passes, 36 layers, K={sh['K']}, 1 sequence) of the "
+                   f"fp64 oracle after a {P0}-token prefill, {step_s:.1f} s; tokens/s = the "
+                   f"workload's mean tokens per step ({mean_tokens_per_step:.3f}) / step time"),
+        "step_seconds": step_s,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=120)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="qwen3_8b_b1_p512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown-steps", type=int, default=8)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from lossless_decoding_amd import _lib as C
+    from lossless_decoding_amd.engine import Engine
+    from synth import workloads
+    from synth.device import fill_weights_device
+
+    wl = workloads.WORKLOADS[args.workload]
+    sh = workloads.SHAPES[wl["shape"]]
+    B, P, K, V = wl["B"], wl["P"], sh["K"], sh["V"]
+    W, S = args.warmup, args.steps
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    a = workloads.plant_lengths(W + S, B, K, wl["plant"])
+    need = 1 + int((a + 1).sum(0).max()) + K + 2          # trajectory tokens per sequence
+    max_ctx = P + (W + S) * (K + 1) + 64                  # host bound grows K+1 per step
+    t0 = time.time()
+    cfg = C.OrthrusConfig.make(sh["L"], sh["d"], sh["hq"], sh["hkv"], sh["hd"], sh["F"], V, K,
+                               True, B, max_ctx)
+    lay, total = C.weight_layout(cfg)
+    w = fill_weights_device(lay, total, True)
+    eng = Engine(cfg, w)
+    cfg0 = C.OrthrusConfig.make(sh["L"], sh["d"], sh["hq"], sh["hkv"], sh["hd"], sh["F"], V, 0,
+                                True, B, P + need + 8)
+    ar = Engine(cfg0, w)
+    del w
+    torch.cuda.synchronize()
+    log(f"[setup] weights + two contexts in {time.time() - t0:.1f}s "
+        f"(packed {eng.sizes.packed_bytes / 1e9:.2f} GB, KV {eng.sizes.kv_bytes / 1e9:.2f} GB)")
+
+    prompts = workloads.prompts(B, P, V)
+    # greedy trajectory from the plain-decoding context (same kernels, K = 0)
+    t0 = time.time()
+    ar.prefill(prompts)
+    traj = torch.zeros(need, B, dtype=torch.int32, device=dev)
+    traj[0] = ar.pending[:B]
+    for j in range(1, need):
+        ar.draft(); ar.verify(); ar.commit()
+        traj[j] = ar.pending[:B]
+    traj = traj.t().contiguous().cpu().numpy()
+    ar_s = time.time() - t0
+    log(f"[setup] greedy trajectory of {need} tokens x {B} in {ar_s:.1f}s")
+    ar.close()
+    del ar
+    planted = torch.from_numpy(workloads.plant_drafts(traj, 1, a, K, V)).to(dev)
+
+    # ---------------------------------------------------------------- timed
+    eng.prefill(prompts)
+    for s in range(W):
+        eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
+    cls = C.timing_class("draft", "gate_up")
+    C.orthrus_timing_enable(eng.ctx, 1 << cls, S * sh["L"] + 16)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for s in range(W, W + S):
+        eng.draft()
+        eng.drafts[:B].copy_(planted[s])
+        eng.verify()
+        eng.commit()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    tim, dropped = C.orthrus_timing_read(eng.ctx)
+    C.orthrus_timing_enable(eng.ctx, 0, 0)
+
+    tokens = int((a[W:W + S] + 1).sum())
+    ms_step = ms / S
+    # correctness of the timed run: lengths and the emitted stream match greedy decoding
+    seq_len = eng.seq_len[:B].cpu().numpy()
+    want_len = P + (a + 1).sum(0)
+    pend = eng.pending[:B].cpu().numpy()
+    e_end = 1 + (a + 1).sum(0)
+    lossless = bool((seq_len == want_len).all() and
+                    all(pend[b] == traj[b, e_end[b] - 1] for b in range(B)))
+    log(f"[timed] {S} steps in {ms:.1f} ms ({ms_step:.3f} ms/step, wall {wall * 1e3:.1f} ms), "
+        f"{tokens} tokens, lossless={lossless}")
+
+    # dominant kernel: the draft pass's gate/up SwiGLU GEMM (M = B*(K+1) rows)
+    gu_ms, gu_n = tim.get(("draft", "gate_up"), (0.0, 0))
+    M1 = B * (K + 1)
+    gu_bytes = 2 * sh["F"] * sh["d"] * 2 + M1 * sh["d"] * 2 + M1 * sh["F"] * 2
+    gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
+    achieved = gu_bytes / gu_avg_s / 1e9 if gu_n else 0.0
+    traffic = None
+    if os.path.exists(PROFILE_PMC):
+        pm = json.load(open(PROFILE_PMC))
+        if pm.get("kernel_source_hash") == kernel_source_hash() and \
+                pm.get("workload") == args.workload:
+            traffic = pm.get("hbm_bytes_per_launch")
+
+    # per-class breakdown over a few more steps (all classes timed)
+    breakdown = {}
+    if args.breakdown_steps > 0:
+        # a few more steps with every class timed (acceptance differs: the
+        # planted rows no longer line up with the trajectory; cost does not)
+        C.orthrus_sync_lengths(eng.ctx, B, seq_len)
+        extra = min(args.breakdown_steps, (max_ctx - int(seq_len.max()) - 64) // (K + 1))
+        C.orthrus_timing_enable(eng.ctx, (1 << 24) - 1, max(extra, 1) * 800 + 64)
+        for j in range(extra):
+            eng.draft(); eng.drafts[:B].copy_(planted[W + j]); eng.verify(); eng.commit()
+        torch.cuda.synchronize()
+        tb, _ = C.orthrus_timing_read(eng.ctx)
+        C.orthrus_timing_enable(eng.ctx, 0, 0)
+        if extra > 0:
+            breakdown = {f"{p}.{r}": round(v[0] / extra, 4) for (p, r), v in sorted(tb.items())}
+        log(f"[breakdown] ms per step by class over {extra} steps: {breakdown}")
+
+    out = {
+        "metric": "verified tokens/s (and draft+verify steps/s) on 1 GPU; % of HBM roofline",
+        "value": round(tokens / (ms / 1e3), 3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and prompts, planted drafts)",
+        "config": {"workload": workload_desc(args.workload, wl, sh), "batch": B,
+                   "prompt_len": P, "block_k": K, "parallelism": "none (1 GPU)"},
+        "steps_per_s": round(S / (ms / 1e3), 3),
+        "tokens_per_step": round(tokens / S, 4),
+        "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
+        "lossless_vs_greedy": lossless,
+        "roofline": {
+            "kernel": f"k_gemm_bf16<{min(4, (M1 + 15) // 16)},2,EP_SWIGLU> (draft-pass gate/up "
+                      f"SwiGLU GEMM, M={M1}, N={2 * sh['F']}, K={sh['d']})",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": gu_bytes,
+            "avg_launch_us": round(gu_avg_s * 1e6, 3),
+            "launches": gu_n,
+            "events_dropped": dropped,
+        },
+        "ms_per_step_by_class": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(sh, wl, tokens / S / B)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -82,7 +82,7 @@ enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1 };
  * are shared.
  * BF16 models: bf16 weights, bf16 KV cache, fp32 residual stream, fp32
  * accumulation; requires head_dim 128, d_model, n_q_heads*head_dim and
- * ffn_dim multiples of 256, and (block_k + 1) * group <= 144 and
+ * ffn_dim multiples of 256, vocab a multiple of 128, and (block_k + 1) * group <= 144 and
  * 32 * group <= 144 (group = n_q_heads / n_kv_heads).
  * F32 models: everything fp32 (small check models). */
 typedef struct orthrus_config {
@@ -182,10 +182,28 @@ int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len
  * Host only; must not be called while a step is in flight (ESTATE). */
 int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len_host);
 
+/* Launch timing for profiling.  When enabled, the library records a pair
+ * of hipEvents (host-created; no device memory) around every launch of the
+ * selected classes on the call's stream.  Class = pass*8 + role with pass
+ * 0 draft, 1 verify, 2 prefill and role 0 QKV GEMM, 1 attention (+ merge),
+ * 2 O GEMM, 3 gate/up SwiGLU GEMM, 4 down GEMM, 5 LM head + argmax, 6 the
+ * small kernels (embed, RMSNorm, QK-norm/RoPE/KV write), 7 accept and
+ * commit (pass 1 only).  class_mask bit k selects class k; capacity = event
+ * pairs kept (launches past it are not timed).  class_mask 0 turns timing
+ * off.  orthrus_timing_read synchronizes on the recorded events, adds each
+ * pair's elapsed time to ms[class] (milliseconds) and counts launches[class]
+ * (both arrays ORTHRUS_TIMING_CLASSES long), then starts a new record;
+ * ECAPACITY if launches were dropped.  Errors: EINVAL, EHIP. */
+#define ORTHRUS_TIMING_CLASSES 24
+int orthrus_timing_enable(orthrus_ctx* ctx, uint32_t class_mask, int32_t capacity);
+int orthrus_timing_read(orthrus_ctx* ctx, double* ms, int64_t* launches);
+
 /* Parity taps (optional; NULL disables).  logits: device fp32
- * [rows_cap][vocab]; every later LM-head pass writes its rows' logits there
- * (pass 1: the batch anchor rows first, then batch*K mask rows in sequence
- * order; pass 2: batch*K rows in sequence order).  attn: device
+ * [rows_cap][vocab]; every later LM-head pass writes its rows' logits there,
+ * by pass row: pass 1 has the batch*K mask rows in sequence order (row
+ * b*K + i), then padding up to RA = batch*K rounded up to a multiple of 16,
+ * then the anchor rows (row RA + b); pass 2 has batch*K rows (b*K + i).
+ * Padding rows are unspecified.  attn: device
  * [n_layers][rows_cap][n_q_heads*head_dim] in the model dtype; every later
  * pass writes each layer's attention output (the O projection's input).
  * Errors: EINVAL. */

@@ -17,7 +17,7 @@ ORTHRUS_F32, ORTHRUS_BF16 = 0, 1
 EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_verify_accept", "orthrus_commit_kv",
-    "orthrus_set_debug", "orthrus_sync_lengths", "orthrus_block_attention", "orthrus_attention_workspace",
+    "orthrus_set_debug", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_attention_workspace",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
 
@@ -79,6 +79,8 @@ def lib():
         L.orthrus_commit_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orthrus_set_debug.argtypes = [vp, vp, vp, i32]
         L.orthrus_sync_lengths.argtypes = [vp, i32, vp]
+        L.orthrus_timing_enable.argtypes = [vp, ctypes.c_uint32, i32]
+        L.orthrus_timing_read.argtypes = [vp, vp, vp]
         L.orthrus_block_attention.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp,
                                               i32, vp, vp, u64, vp]
         L.orthrus_attention_workspace.argtypes = [i32, i32, i32, i32, i32]
@@ -150,6 +152,33 @@ def orthrus_set_debug(ctx, logits, attn, rows_cap):
 def orthrus_sync_lengths(ctx, batch, seq_len_host: np.ndarray):
     sl = np.ascontiguousarray(seq_len_host, np.int32)
     _check("orthrus_sync_lengths", lib().orthrus_sync_lengths(ctx, batch, sl.ctypes.data))
+
+
+TIMING_CLASSES = 24
+TIMING_PASSES = ("draft", "verify", "prefill")
+TIMING_ROLES = ("qkv", "attention", "o_proj", "gate_up", "down", "lm_head", "small", "accept_commit")
+
+
+def timing_class(pass_name: str, role: str) -> int:
+    return TIMING_PASSES.index(pass_name) * 8 + TIMING_ROLES.index(role)
+
+
+def orthrus_timing_enable(ctx, class_mask: int, capacity: int):
+    _check("orthrus_timing_enable", lib().orthrus_timing_enable(ctx, class_mask, capacity))
+
+
+def orthrus_timing_read(ctx):
+    """{(pass, role): (ms_total, launches)} for every class with launches."""
+    ms = np.zeros(TIMING_CLASSES, np.float64)
+    n = np.zeros(TIMING_CLASSES, np.int64)
+    rc = lib().orthrus_timing_read(ctx, ms.ctypes.data, n.ctypes.data)
+    if rc not in (ORTHRUS_OK, ORTHRUS_ECAPACITY):
+        _check("orthrus_timing_read", rc)
+    out = {}
+    for k in range(TIMING_CLASSES):
+        if n[k]:
+            out[(TIMING_PASSES[k // 8], TIMING_ROLES[k % 8])] = (float(ms[k]), int(n[k]))
+    return out, rc == ORTHRUS_ECAPACITY
 
 
 def orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len) -> int:

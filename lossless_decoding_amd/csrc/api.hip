@@ -50,7 +50,7 @@ uint64_t canon_offset(const orthrus_config& c, int t) {
 struct Layout {
   // element size, dims
   int esz, L, d, hq, hkv, hd, F, V, K, G, qd, kd, nqkv;
-  int cap, kpad, tmax, rmax, sc, nc, qr_max, lm_parts;
+  int cap, kpad, tmax, rmax, sc, nc, qr_max, nss, ngroups_max;
   bool bf16;
   // packed offsets (bytes)
   uint64_t p_embed, p_lm, p_fnorm, p_mask;
@@ -59,7 +59,7 @@ struct Layout {
   uint64_t packed_bytes;
   // workspace offsets (bytes)
   uint64_t w_h, w_x, w_qkv, w_q, w_act, w_opart, w_ml, w_parts, w_logits, w_rope, w_i32,
-      workspace_bytes;
+      w_ss, w_part, w_cnt, cnt_bytes, w_amax, workspace_bytes;
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
 };
 
@@ -78,7 +78,7 @@ int validate(const orthrus_config* c) {
     if (c->head_dim != 128) return ORTHRUS_EINVAL;
     if (c->d_model % 256 || (c->n_q_heads * c->head_dim) % 256 || c->ffn_dim % 256)
       return ORTHRUS_EINVAL;
-    if (c->vocab % 32) return ORTHRUS_EINVAL;
+    if (c->vocab % 128) return ORTHRUS_EINVAL;
     if ((c->block_k + 1) * G > 144 || kPrefillChunk * G > 144) return ORTHRUS_EINVAL;
   } else if (c->dtype != ORTHRUS_F32) {
     return ORTHRUS_EINVAL;
@@ -95,13 +95,23 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.cap = round_up(c.max_ctx, 64);
   y.kpad = y.K > 0 ? round_up(y.K, 32) : 0;
   y.tmax = y.K + 1 > kPrefillChunk ? y.K + 1 : kPrefillChunk;
-  y.rmax = c.max_batch * y.tmax;
-  int sc = 256;
-  while (sc < 2048 && sc * 32 < y.cap) sc *= 2;
+  // physical rows: draft passes pad the mask rows to a multiple of 16
+  int draft_rows = round_up(c.max_batch * y.K, 16) + c.max_batch;
+  int other_rows = c.max_batch * (y.K > kPrefillChunk ? y.K : kPrefillChunk);
+  y.rmax = draft_rows > other_rows ? draft_rows : other_rows;
+  // attention key chunk: fixed per context so that a row's result does not
+  // depend on which pass computes it
+  int sc = 64;
+  while (sc < 2048 && sc * 64 < y.cap) sc *= 2;
   y.sc = sc;
   y.nc = (y.cap + sc - 1) / sc;
   y.qr_max = y.tmax * y.G;
-  y.lm_parts = y.bf16 ? gemm_bf16_argmax_parts(y.V) : gemm_f32_argmax_parts(y.V);
+  y.nss = y.d / 128;
+  {
+    int ns[4] = {y.nqkv, y.d, 2 * y.F, y.V};
+    y.ngroups_max = 0;
+    for (int i = 0; i < 4; ++i) if (ns[i] / 128 > y.ngroups_max) y.ngroups_max = ns[i] / 128;
+  }
 
   // ---- packed weights
   uint64_t o = 0, E = y.esz;
@@ -137,22 +147,42 @@ void make_layout(const orthrus_config& c, Layout& y) {
   int xw = y.d > y.qd ? y.d : y.qd;
   y.w_h = take((uint64_t)y.rmax * y.d * 4);
   y.w_x = take((uint64_t)y.rmax * xw * E);
-  y.w_qkv = take((uint64_t)y.rmax * y.nqkv * 4);
+  y.w_qkv = y.bf16 ? take(0) : take((uint64_t)y.rmax * y.nqkv * 4);
   y.w_q = take((uint64_t)y.rmax * y.qd * E);
   y.w_act = take((uint64_t)y.rmax * y.F * E);
   uint64_t part_rows = (uint64_t)c.max_batch * y.hkv * (y.nc + 1) * y.qr_max;
   y.w_opart = y.bf16 ? take(part_rows * y.hd * 4) : take(0);
   y.w_ml = y.bf16 ? take(part_rows * 2 * 4) : take(0);
-  y.w_parts = take((uint64_t)y.rmax * y.lm_parts * 8);
+  y.w_parts = y.bf16 ? take(0) : take((uint64_t)y.rmax * 8);
   y.w_logits = y.bf16 ? take(0) : take((uint64_t)y.rmax * y.V * 4);
   y.w_rope = take((uint64_t)y.cap * (y.hd / 2) * 8);
   y.w_i32 = take((uint64_t)4 * c.max_batch * 4);
+  if (y.bf16) {
+    y.w_ss = take((uint64_t)y.rmax * y.nss * 4);
+    // split-K partials of the narrow GEMMs (fewer than 128 column groups)
+    uint64_t nmax = 0;
+    int ns[4] = {y.nqkv, y.d, 2 * y.F, y.V};
+    for (int i = 0; i < 4; ++i)
+      if (ns[i] / 128 < 128 && (uint64_t)ns[i] > nmax) nmax = ns[i];
+    // partials are kept per padded 64-row group: [8][round_up(rows, 64)][N]
+    y.w_part = take(8 * (uint64_t)round_up(y.rmax, 64) * nmax * 4);
+    y.cnt_bytes = ((uint64_t)((y.rmax + 63) / 64) * y.ngroups_max + 1) * 4;
+    y.w_cnt = take(y.cnt_bytes);
+    y.w_amax = take((uint64_t)y.rmax * (y.V / 128) * 8);
+  } else {
+    y.w_ss = y.w_part = y.w_cnt = y.w_amax = take(0);
+    y.cnt_bytes = 0;
+  }
   y.workspace_bytes = o;
 }
 
 bool aligned(const void* p) { return ((uintptr_t)p % kAlign) == 0; }
 
 }  // namespace
+
+inline void set_rm(PassInfo& P) {
+  P.RM = P.kind == PASS_DRAFT ? round_up(P.B * P.Kx, 16) : 0;
+}
 
 struct orthrus_ctx {
   orthrus_config cfg;
@@ -167,6 +197,11 @@ struct orthrus_ctx {
   float* dbg_logits;
   void* dbg_attn;
   int dbg_rows;
+  // opt-in launch timing: event pairs around launches of the selected classes
+  uint32_t tmask;
+  std::vector<hipEvent_t> ev;     // 2 per pair
+  std::vector<int> ev_cls;
+  int ev_used;
 };
 
 namespace {
@@ -178,16 +213,29 @@ int hip_ok(hipError_t e) {
 
 int check_launch() { return hip_ok(hipGetLastError()); }
 
+// timing classes: pass * 8 + role
+enum { R_QKV = 0, R_ATTN = 1, R_O = 2, R_GU = 3, R_DOWN = 4, R_LM = 5, R_SMALL = 6, R_ACC = 7 };
+inline int pass_base(int kind) { return kind * 8; }
+
+struct Tick {
+  orthrus_ctx* c; int i; hipStream_t s;
+  Tick(orthrus_ctx* c_, int cls, hipStream_t s_) : c(c_), i(-1), s(s_) {
+    if (!(c->tmask >> cls & 1u) || c->ev_used * 2 >= (int)c->ev.size()) return;
+    i = c->ev_used++;
+    c->ev_cls[i] = cls;
+    hipEventRecord(c->ev[2 * i], s);
+  }
+  ~Tick() { if (i >= 0) hipEventRecord(c->ev[2 * i + 1], s); }
+};
+
 template <typename T> T* W(orthrus_ctx* c, uint64_t off) { return (T*)(c->packed + off); }
 template <typename T> T* S(orthrus_ctx* c, uint64_t off) { return (T*)(c->ws + off); }
 
+// fp32 GEMM on canonical row-major weights (check models)
 void gemm(orthrus_ctx* c, uint64_t woff, uint64_t woff2, const void* X, int ldx, int M, int K,
           int N, const GemmOut& o, hipStream_t s) {
-  if (c->y.bf16)
-    launch_gemm_bf16(c->packed + woff, (const uint16_t*)X, ldx, M, K, N, o, s);
-  else
-    launch_gemm_f32((const float*)(c->packed + woff), (const float*)(c->packed + woff2),
-                    (const float*)X, ldx, M, K, N, o, s);
+  launch_gemm_f32((const float*)(c->packed + woff), (const float*)(c->packed + woff2),
+                  (const float*)X, ldx, M, K, N, o, s);
 }
 
 GemmOut out_store(float* y, int ldy, int ep) {
@@ -198,12 +246,14 @@ GemmOut out_store(float* y, int ldy, int ep) {
 
 // One forward pass of the rows described by P through every layer, ending
 // with the LM-head argmax when want_tokens.
-void run_pass(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
-              const int32_t* block_tok, int block_ld, bool want_tokens, int32_t* drafts,
-              int32_t* ar, int32_t* pending, hipStream_t s) {
+void run_pass_f32(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
+                  const int32_t* block_tok, int block_ld, bool want_tokens, int32_t* drafts,
+                  int32_t* ar, int32_t* pending, hipStream_t s) {
   const Layout& y = c->y;
   const int rows = P.rows();
-  const int AB = P.A * P.B;
+  const int BK = P.kind == PASS_DRAFT ? P.B * P.Kx : 0;   // mask rows (draft)
+  const int RM = P.kind == PASS_DRAFT ? P.RM : 0;
+  const int NA = P.kind == PASS_DRAFT ? P.A * P.B : 0;    // anchor rows
   const float eps = (float)c->cfg.rms_eps;
   float* h = S<float>(c, y.w_h);
   char* x = S<char>(c, y.w_x);
@@ -211,22 +261,20 @@ void run_pass(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   char* q = S<char>(c, y.w_q);
   char* act = S<char>(c, y.w_act);
   const uint64_t E = y.esz;
-
-  launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed, c->packed + y.p_mask,
-               y.V, y.d, y.bf16, h, s);
+  const int pb = pass_base(P.kind);
+  {
+    Tick t(c, pb + R_SMALL, s);
+    launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed,
+                 c->packed + y.p_mask, y.V, y.d, false, h, nullptr, s);
+  }
   for (int l = 0; l < y.L; ++l) {
-    launch_rmsnorm(h, rows, y.d, c->packed + y.p_anorm[l], y.bf16, eps, x, s);
-    // Q/K/V: anchor (and every non-draft) row with the frozen projections,
-    // mask rows with the diffusion projections
-    uint64_t qkv_sz = (uint64_t)y.nqkv * y.d * E;
-    (void)qkv_sz;
+    launch_rmsnorm(h, rows, y.d, c->packed + y.p_anorm[l], false, eps, x, s);
     if (P.kind == PASS_DRAFT) {
-      uint64_t wq_f = y.p_qkv[l], wq_d = y.p_dqkv[l];
-      if (AB > 0)
-        gemm(c, wq_f, 0, x, y.d, AB, y.d, y.nqkv, out_store(qkv, y.nqkv, EP_STORE), s);
-      if (rows > AB)
-        gemm(c, wq_d, 0, x + (uint64_t)AB * y.d * E, y.d, rows - AB, y.d, y.nqkv,
-             out_store(qkv + (uint64_t)AB * y.nqkv, y.nqkv, EP_STORE), s);
+      if (BK > 0)
+        gemm(c, y.p_dqkv[l], 0, x, y.d, BK, y.d, y.nqkv, out_store(qkv, y.nqkv, EP_STORE), s);
+      if (NA > 0)
+        gemm(c, y.p_qkv[l], 0, x + (uint64_t)RM * y.d * E, y.d, NA, y.d, y.nqkv,
+             out_store(qkv + (uint64_t)RM * y.nqkv, y.nqkv, EP_STORE), s);
     } else {
       gemm(c, y.p_qkv[l], 0, x, y.d, rows, y.d, y.nqkv, out_store(qkv, y.nqkv, EP_STORE), s);
     }
@@ -235,45 +283,156 @@ void run_pass(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     char* ks = c->scr + (uint64_t)l * y.scr_layer_elems * E;
     char* vs = c->scr + ((uint64_t)y.L + l) * y.scr_layer_elems * E;
     launch_qkv_post(P, qkv, y.hq, y.hkv, y.hd, c->packed + y.p_qn[l], c->packed + y.p_kn[l],
-                    c->packed + y.p_dqn[l], c->packed + y.p_dkn[l], y.bf16, eps,
+                    c->packed + y.p_dqn[l], c->packed + y.p_dkn[l], false, eps,
                     S<float>(c, y.w_rope), q, kc, vc, y.cap, ks, vs, y.kpad, s);
+    AttnArgs a{};
+    a.P = P; a.q = q; a.kc = kc; a.vc = vc; a.cap = y.cap; a.ks = ks; a.vs = vs;
+    a.kpad = y.kpad; a.hq = y.hq; a.hkv = y.hkv; a.hd = y.hd; a.sc = y.sc; a.nc = y.nc;
+    a.qr_max = y.qr_max; a.out = x; a.fixed_ctx = -1;
+    a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
+    if (c->dbg_attn && rows <= c->dbg_rows) {
+      a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * E;
+      a.tap_rows = rows;
+    }
+    launch_attention_f32(a, s);
+    if (P.kind == PASS_DRAFT) {
+      if (BK > 0) gemm(c, y.p_do[l], 0, x, y.qd, BK, y.qd, y.d, out_store(h, y.d, EP_RESID), s);
+      if (NA > 0)
+        gemm(c, y.p_o[l], 0, x + (uint64_t)RM * y.qd * E, y.qd, NA, y.qd, y.d,
+             out_store(h + (uint64_t)RM * y.d, y.d, EP_RESID), s);
+    } else {
+      gemm(c, y.p_o[l], 0, x, y.qd, rows, y.qd, y.d, out_store(h, y.d, EP_RESID), s);
+    }
+    launch_rmsnorm(h, rows, y.d, c->packed + y.p_ffnnorm[l], false, eps, x, s);
+    GemmOut og{};
+    og.ep = EP_SWIGLU; og.act = act; og.ldact = y.F;
+    gemm(c, y.p_gu[l], y.p_gu[l] + (uint64_t)y.F * y.d * E, x, y.d, rows, y.d, y.F, og, s);
+    gemm(c, y.p_down[l], 0, act, y.F, rows, y.F, y.d, out_store(h, y.d, EP_RESID), s);
+  }
+  if (!want_tokens) return;
+  launch_rmsnorm(h, rows, y.d, c->packed + y.p_fnorm, false, eps, x, s);
+  GemmOut ol{};
+  ol.ep = EP_ARGMAX;
+  ol.part = S<float2>(c, y.w_parts);
+  ol.y = S<float>(c, y.w_logits);
+  ol.ldy = y.V;
+  if (c->dbg_logits && rows <= c->dbg_rows) { ol.logits = c->dbg_logits; ol.ldl = y.V; }
+  gemm(c, y.p_lm, 0, x, y.d, rows, y.d, y.V, ol, s);
+  launch_lm_reduce(ol.part, rows, 1, P, y.K, drafts, ar, pending, s);
+}
+
+void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
+                   const int32_t* block_tok, int block_ld, bool want_tokens, int32_t* drafts,
+                   int32_t* ar, int32_t* pending, hipStream_t s) {
+  const Layout& y = c->y;
+  const int rows = P.rows();
+  const int BK = P.kind == PASS_DRAFT ? P.B * P.Kx : 0;
+  const int RM = P.kind == PASS_DRAFT ? P.RM : 0;
+  const int NA = P.kind == PASS_DRAFT ? P.A * P.B : 0;
+  const float eps = (float)c->cfg.rms_eps;
+  float* h = S<float>(c, y.w_h);
+  float* ss = S<float>(c, y.w_ss);
+  uint16_t* x = S<uint16_t>(c, y.w_x);
+  uint16_t* q = S<uint16_t>(c, y.w_q);
+  uint16_t* act = S<uint16_t>(c, y.w_act);
+  const int pb = pass_base(P.kind);
+  {
+    Tick t(c, pb + R_SMALL, s);
+    launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed,
+                 c->packed + y.p_mask, y.V, y.d, true, h, ss, s);
+  }
+  GemmArgs g0{};
+  g0.part = S<float>(c, y.w_part);
+  g0.cnt = S<unsigned>(c, y.w_cnt);
+  g0.eps = eps;
+  g0.P = P; g0.hq = y.hq; g0.hkv = y.hkv;
+  g0.rope = S<float2>(c, y.w_rope); g0.q_out = q; g0.cap = y.cap; g0.kpad = y.kpad;
+  g0.nss = y.nss; g0.nss_out = y.nss;
+  auto normed = [&](GemmArgs g, uint64_t gain_off, int K) {
+    g.h = h; g.ss = ss; g.gain = (const uint16_t*)(c->packed + gain_off); g.dn = K;
+    return g;
+  };
+  auto run = [&](GemmArgs g, uint64_t w, int row0, int M, int K, int N, int ep) {
+    g.W = (const u32x4_t*)(c->packed + w);
+    g.row0 = row0; g.M = M; g.K = K; g.N = N; g.ep = ep;
+    launch_gemm_bf16(g, s);
+  };
+  for (int l = 0; l < y.L; ++l) {
+    const uint64_t E = 2;
+    uint16_t* kc = (uint16_t*)(c->kv + (uint64_t)l * y.kv_layer_elems * E);
+    uint16_t* vc = (uint16_t*)(c->kv + ((uint64_t)y.L + l) * y.kv_layer_elems * E);
+    uint16_t* ks = (uint16_t*)(c->scr + (uint64_t)l * y.scr_layer_elems * E);
+    uint16_t* vs = (uint16_t*)(c->scr + ((uint64_t)y.L + l) * y.scr_layer_elems * E);
+    // Q/K/V projection + QK-norm + RoPE + K/V placement; mask rows use the
+    // diffusion projections, every other row the frozen ones
+    {
+      Tick t(c, pb + R_QKV, s);
+      GemmArgs g = normed(g0, y.p_anorm[l], y.d);
+      g.qn = (const uint16_t*)(c->packed + y.p_qn[l]);
+      g.kn = (const uint16_t*)(c->packed + y.p_kn[l]);
+      g.dqn = (const uint16_t*)(c->packed + y.p_dqn[l]);
+      g.dkn = (const uint16_t*)(c->packed + y.p_dkn[l]);
+      g.kc = kc; g.vc = vc; g.ks = ks; g.vs = vs;
+      if (P.kind == PASS_DRAFT) {
+        if (BK > 0) run(g, y.p_dqkv[l], 0, BK, y.d, y.nqkv, EP_QKV);
+        if (NA > 0) run(g, y.p_qkv[l], RM, NA, y.d, y.nqkv, EP_QKV);
+      } else {
+        run(g, y.p_qkv[l], 0, rows, y.d, y.nqkv, EP_QKV);
+      }
+    }
     AttnArgs a{};
     a.P = P; a.q = q; a.kc = kc; a.vc = vc; a.cap = y.cap; a.ks = ks; a.vs = vs;
     a.kpad = y.kpad; a.hq = y.hq; a.hkv = y.hkv; a.hd = y.hd; a.sc = y.sc; a.nc = y.nc;
     a.qr_max = y.qr_max; a.opart = S<float>(c, y.w_opart); a.ml = S<float>(c, y.w_ml);
     a.out = x; a.fixed_ctx = -1; a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
     if (c->dbg_attn && rows <= c->dbg_rows) {
-      a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * E;
+      a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * 2;
       a.tap_rows = rows;
     }
-    if (y.bf16) launch_attention_bf16(a, s); else launch_attention_f32(a, s);
-    // O projection + residual
-    if (P.kind == PASS_DRAFT) {
-      if (AB > 0) gemm(c, y.p_o[l], 0, x, y.qd, AB, y.qd, y.d, out_store(h, y.d, EP_RESID), s);
-      if (rows > AB)
-        gemm(c, y.p_do[l], 0, x + (uint64_t)AB * y.qd * E, y.qd, rows - AB, y.qd, y.d,
-             out_store(h + (uint64_t)AB * y.d, y.d, EP_RESID), s);
-    } else {
-      gemm(c, y.p_o[l], 0, x, y.qd, rows, y.qd, y.d, out_store(h, y.d, EP_RESID), s);
+    {
+      Tick t(c, pb + R_ATTN, s);
+      launch_attention_bf16(a, s);
     }
-    // FFN
-    launch_rmsnorm(h, rows, y.d, c->packed + y.p_ffnnorm[l], y.bf16, eps, x, s);
-    GemmOut og{};
-    og.ep = EP_SWIGLU; og.act = act; og.ldact = y.F;
-    gemm(c, y.p_gu[l], y.p_gu[l] + (uint64_t)y.F * y.d * E, x, y.d, rows, y.d,
-         y.bf16 ? 2 * y.F : y.F, og, s);
-    gemm(c, y.p_down[l], 0, act, y.F, rows, y.F, y.d, out_store(h, y.d, EP_RESID), s);
+    // O projection + residual (+ sums of squares for the FFN norm)
+    {
+      Tick t(c, pb + R_O, s);
+      GemmArgs g = g0;
+      g.X = x; g.ldx = y.qd; g.y = h; g.ldy = y.d; g.ss_out = ss;
+      if (P.kind == PASS_DRAFT) {
+        if (BK > 0) run(g, y.p_do[l], 0, BK, y.qd, y.d, EP_RESID);
+        if (NA > 0) run(g, y.p_o[l], RM, NA, y.qd, y.d, EP_RESID);
+      } else {
+        run(g, y.p_o[l], 0, rows, y.qd, y.d, EP_RESID);
+      }
+    }
+    {
+      Tick t(c, pb + R_GU, s);
+      GemmArgs g = normed(g0, y.p_ffnnorm[l], y.d);
+      g.act = act; g.ldact = y.F;
+      run(g, y.p_gu[l], 0, rows, y.d, 2 * y.F, EP_SWIGLU);
+    }
+    {
+      Tick t(c, pb + R_DOWN, s);
+      GemmArgs g = g0;
+      g.X = act; g.ldx = y.F; g.y = h; g.ldy = y.d; g.ss_out = ss;
+      run(g, y.p_down[l], 0, rows, y.F, y.d, EP_RESID);
+    }
   }
   if (!want_tokens) return;
-  launch_rmsnorm(h, rows, y.d, c->packed + y.p_fnorm, y.bf16, eps, x, s);
-  GemmOut ol{};
-  ol.ep = EP_ARGMAX;
-  ol.part = S<float2>(c, y.w_parts);
-  ol.y = y.bf16 ? nullptr : S<float>(c, y.w_logits);
-  ol.ldy = y.V;
-  if (c->dbg_logits && rows <= c->dbg_rows) { ol.logits = c->dbg_logits; ol.ldl = y.V; }
-  gemm(c, y.p_lm, 0, x, y.d, rows, y.d, y.V, ol, s);
-  launch_lm_reduce(ol.part, rows, y.lm_parts, P, y.K, drafts, ar, pending, s);
+  Tick tl(c, pb + R_LM, s);
+  GemmArgs g = normed(g0, y.p_fnorm, y.d);
+  g.amax = S<float2>(c, y.w_amax);
+  g.Kb = y.K; g.drafts = drafts; g.ar = ar; g.pending = pending;
+  if (c->dbg_logits && rows <= c->dbg_rows) { g.logits = c->dbg_logits; g.ldl = y.V; }
+  run(g, y.p_lm, 0, rows, y.d, y.V, EP_ARGMAX);
+}
+
+void run_pass(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
+              const int32_t* block_tok, int block_ld, bool want_tokens, int32_t* drafts,
+              int32_t* ar, int32_t* pending, hipStream_t s) {
+  if (c->y.bf16) run_pass_bf16(c, P, anchor_tok, block_tok, block_ld, want_tokens, drafts, ar,
+                               pending, s);
+  else run_pass_f32(c, P, anchor_tok, block_tok, block_ld, want_tokens, drafts, ar, pending, s);
 }
 
 }  // namespace
@@ -325,6 +484,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
   c->state = ST_IDLE; c->step_batch = 0;
   c->bound.assign(cfg->max_batch, 0);
   c->dbg_logits = nullptr; c->dbg_attn = nullptr; c->dbg_rows = 0;
+  c->tmask = 0; c->ev_used = 0;
   const Layout& y = c->y;
   const uint64_t E = y.esz;
   const char* w = (const char*)weights;
@@ -394,6 +554,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
       rope[((size_t)p * (y.hd / 2) + i) * 2 + 1] = (float)sin(ang);
     }
   chk(hipMemcpyAsync(c->ws + y.w_rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice, s));
+  if (y.cnt_bytes) chk(hipMemsetAsync(c->ws + y.w_cnt, 0, y.cnt_bytes, s));
   chk(hipGetLastError());
   chk(hipStreamSynchronize(s));
   if (e != hipSuccess) {
@@ -407,6 +568,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
 
 int orthrus_destroy(orthrus_ctx* ctx) {
   if (!ctx) return ORTHRUS_EINVAL;
+  for (hipEvent_t e : ctx->ev) hipEventDestroy(e);
   delete ctx;
   return ORTHRUS_OK;
 }
@@ -447,11 +609,13 @@ int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int3
     P.kind = PASS_PREFILL; P.B = batch; P.A = 0;
     P.Kx = (pmax - 1 - p0) < kPrefillChunk ? (pmax - 1 - p0) : kPrefillChunk;
     P.p0 = p0; P.len = nullptr;
+    set_rm(P);
     run_pass(ctx, P, nullptr, tokens, tokens_stride, false, nullptr, nullptr, nullptr, s);
   }
   launch_prefill_tail(batch, tokens, tokens_stride, plen_dev, seq_len, last_tok, s);
   PassInfo P{};
   P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = 0; P.p0 = 0; P.len = seq_len;
+  set_rm(P);
   run_pass(ctx, P, last_tok, nullptr, 0, true, nullptr, nullptr, pending, s);
   launch_len_add(batch, seq_len, 1, s);
   rc = check_launch();
@@ -474,6 +638,7 @@ int orthrus_draft_block(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
     if (ctx->bound[b] + ctx->y.K + 1 > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
   PassInfo P{};
   P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = ctx->y.K; P.p0 = 0; P.len = seq_len;
+  set_rm(P);
   run_pass(ctx, P, pending, nullptr, 0, true, drafts, ar_tokens, nullptr, (hipStream_t)stream);
   int rc = check_launch();
   if (rc) return rc;
@@ -494,9 +659,13 @@ int orthrus_verify_accept(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_le
   if (K > 0) {
     PassInfo P{};
     P.kind = PASS_VERIFY; P.B = batch; P.A = 0; P.Kx = K; P.p0 = 0; P.len = seq_len;
+    set_rm(P);
     run_pass(ctx, P, nullptr, drafts, K, true, nullptr, ar_tokens, nullptr, s);
   }
-  launch_accept(batch, K, drafts, ar_tokens, accept_len, s);
+  {
+    Tick t(ctx, pass_base(PASS_VERIFY) + R_ACC, s);
+    launch_accept(batch, K, drafts, ar_tokens, accept_len, s);
+  }
   int rc = check_launch();
   if (rc) return rc;
   ctx->state = ST_VERIFIED;
@@ -513,13 +682,49 @@ int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len
   if (ctx->y.K > 0 && !drafts) return ORTHRUS_EINVAL;
   if (ctx->state != ST_VERIFIED) return ORTHRUS_ESTATE;
   if (batch != ctx->step_batch) return ORTHRUS_EINVAL;
-  launch_commit(batch, ctx->y.K, accept_len, ar_tokens, drafts, seq_len, pending, commit_start,
-                out_tokens, out_off, (hipStream_t)stream);
+  {
+    Tick t(ctx, pass_base(PASS_VERIFY) + R_ACC, (hipStream_t)stream);
+    launch_commit(batch, ctx->y.K, accept_len, ar_tokens, drafts, seq_len, pending,
+                  commit_start, out_tokens, out_off, (hipStream_t)stream);
+  }
   int rc = check_launch();
   if (rc) return rc;
   for (int b = 0; b < batch; ++b) ctx->bound[b] += ctx->y.K + 1;
   ctx->state = ST_IDLE;
   return ORTHRUS_OK;
+}
+
+int orthrus_timing_enable(orthrus_ctx* ctx, uint32_t class_mask, int32_t capacity) {
+  if (!ctx || capacity < 0) return ORTHRUS_EINVAL;
+  if (class_mask && capacity == 0) return ORTHRUS_EINVAL;
+  for (hipEvent_t e : ctx->ev) hipEventDestroy(e);
+  ctx->ev.clear(); ctx->ev_cls.clear(); ctx->ev_used = 0; ctx->tmask = 0;
+  if (!class_mask) return ORTHRUS_OK;
+  ctx->ev.resize((size_t)2 * capacity);
+  ctx->ev_cls.resize(capacity);
+  for (auto& e : ctx->ev) {
+    int rc = hip_ok(hipEventCreate(&e));
+    if (rc) { e = nullptr; return rc; }
+  }
+  ctx->tmask = class_mask;
+  return ORTHRUS_OK;
+}
+
+int orthrus_timing_read(orthrus_ctx* ctx, double* ms, int64_t* launches) {
+  if (!ctx || !ms || !launches) return ORTHRUS_EINVAL;
+  for (int k = 0; k < ORTHRUS_TIMING_CLASSES; ++k) { ms[k] = 0.0; launches[k] = 0; }
+  for (int i = 0; i < ctx->ev_used; ++i) {
+    int rc = hip_ok(hipEventSynchronize(ctx->ev[2 * i + 1]));
+    if (rc) return rc;
+    float t = 0.f;
+    rc = hip_ok(hipEventElapsedTime(&t, ctx->ev[2 * i], ctx->ev[2 * i + 1]));
+    if (rc) return rc;
+    ms[ctx->ev_cls[i]] += t;
+    launches[ctx->ev_cls[i]] += 1;
+  }
+  int dropped = ctx->ev_used * 2 >= (int)ctx->ev.size() ? 1 : 0;
+  ctx->ev_used = 0;
+  return dropped ? ORTHRUS_ECAPACITY : ORTHRUS_OK;
 }
 
 int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len_host) {
@@ -564,6 +769,7 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
   AttnArgs a{};
   a.P.kind = PASS_DRAFT; a.P.B = batch; a.P.A = 0; a.P.Kx = rows; a.P.p0 = 0; a.P.len = nullptr;
+  a.P.RM = batch * rows;
   a.q = q; a.kc = k_cache; a.vc = v_cache; a.cap = cap; a.ks = k_block; a.vs = v_block;
   a.kpad = round_up(block_len, 32); a.hq = n_q_heads; a.hkv = n_kv_heads; a.hd = 128;
   a.sc = sc; a.nc = nc; a.qr_max = rows * G;

@@ -11,9 +11,11 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- passes
-// Row order inside a pass: for a draft pass the `A*B` anchor rows come first
-// (row b = sequence b), then B*Kx block rows (row A*B + b*Kx + i).  Verify and
-// prefill passes have no anchor rows (A = 0) and B*Kx rows.
+// Physical row order inside a pass.  Draft pass: the B*Kx mask rows first
+// (row b*Kx + i), padding up to RM = a multiple of 16, then the A*B anchor
+// rows (row RM + b).  Verify and prefill passes: B*Kx rows (row b*Kx + i).
+// Putting the mask rows first makes both GEMM row groups start on a 16-row
+// MFMA tile.
 enum PassKind { PASS_DRAFT = 0, PASS_VERIFY = 1, PASS_PREFILL = 2 };
 
 struct PassInfo {
@@ -22,29 +24,33 @@ struct PassInfo {
   int A;             // 1 if anchor rows are present (draft passes)
   int Kx;            // block rows per sequence (masks / verified drafts / prompt rows)
   int p0;            // prefill: absolute position of block row 0
+  int RM;            // draft: first anchor row (B*Kx rounded up to 16)
   const int32_t* len;  // device seq_len[B] (draft / verify)
-  __host__ __device__ int rows() const { return A * B + B * Kx; }
+  __host__ __device__ int rows() const { return kind == PASS_DRAFT ? RM + A * B : B * Kx; }
   __host__ __device__ int tokens_per_seq() const { return A + Kx; }
 };
 
 struct RowInfo {
-  int b, t, pos, limit, is_mask;
+  int b, t, pos, limit, is_mask, pad;
 };
 
-// Row r -> (sequence, token index within the sequence's rows, absolute
-// position, last visible cache slot, mask-row flag).
+// Physical row r -> (sequence, token index within the sequence's rows
+// [anchor first], absolute position, last visible cache slot, mask-row flag,
+// padding flag).
 __device__ __forceinline__ RowInfo row_info(const PassInfo& P, int r) {
   RowInfo ri;
+  ri.pad = 0;
   if (P.kind == PASS_DRAFT) {
-    if (r < P.A * P.B) {
-      ri.b = r; ri.t = 0; ri.pos = P.len[r]; ri.limit = ri.pos; ri.is_mask = 0;
-    } else {
-      int j = r - P.A * P.B;
-      ri.b = j / P.Kx;
-      int i = j - ri.b * P.Kx;
+    if (r >= P.RM) {
+      ri.b = r - P.RM; ri.t = 0; ri.pos = P.len[ri.b]; ri.limit = ri.pos; ri.is_mask = 0;
+    } else if (r < P.B * P.Kx) {
+      ri.b = r / P.Kx;
+      int i = r - ri.b * P.Kx;
       ri.t = P.A + i;
       int n = P.len[ri.b];
       ri.pos = n + 1 + i; ri.limit = n; ri.is_mask = 1;
+    } else {
+      ri.b = 0; ri.t = 0; ri.pos = 0; ri.limit = -1; ri.is_mask = 0; ri.pad = 1;
     }
   } else {
     ri.b = r / P.Kx;
@@ -56,8 +62,8 @@ __device__ __forceinline__ RowInfo row_info(const PassInfo& P, int r) {
   return ri;
 }
 
-__device__ __forceinline__ int row_of(const PassInfo& P, int b, int t) {
-  if (P.kind == PASS_DRAFT) return t < P.A ? b : P.A * P.B + b * P.Kx + (t - P.A);
+__host__ __device__ __forceinline__ int row_of(const PassInfo& P, int b, int t) {
+  if (P.kind == PASS_DRAFT) return t < P.A ? P.RM + b : b * P.Kx + (t - P.A);
   return b * P.Kx + t;
 }
 
@@ -78,14 +84,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 }
 
 // ----------------------------------------------------------- launchers
-struct Model;   // defined in api.hip
-
 // common kernels
 void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, int nb_stride,
                       hipStream_t s);
 void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
                   int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
-                  float* h, hipStream_t s);
+                  float* h, float* ss, hipStream_t s);
 void launch_rmsnorm(const float* h, int rows, int d, const void* gain, bool bf16, float eps,
                     void* out, hipStream_t s);
 void launch_qkv_post(const PassInfo& P, const float* qkv, int hq, int hkv, int hd,
@@ -102,27 +106,43 @@ void launch_commit(int B, int K, const int32_t* accept_len, const int32_t* ar,
 void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev,
                          int32_t* seq_len, int32_t* last_tok, hipStream_t s);
 void launch_len_add(int B, int32_t* seq_len, int add, hipStream_t s);
-void launch_copy_rows_f32_to_bf16(const float* src, int rows, int cols, uint16_t* dst,
-                                  hipStream_t s);
 
 // GEMMs.  Y = X . W^T over rows [0, M) of X (row stride ldx elements).
-enum Epilogue { EP_STORE = 0, EP_RESID = 1, EP_SWIGLU = 2, EP_ARGMAX = 3 };
-struct GemmOut {
+enum Epilogue { EP_STORE = 0, EP_RESID = 1, EP_SWIGLU = 2, EP_ARGMAX = 3, EP_QKV = 4 };
+struct GemmOut {                // fp32 path
   int ep;
   float* y; int ldy;            // EP_STORE / EP_RESID (fp32)
-  void* act; int ldact;         // EP_SWIGLU (model dtype)
-  float2* part;                 // EP_ARGMAX partials [M][nparts]
+  void* act; int ldact;         // EP_SWIGLU
+  float2* part;                 // EP_ARGMAX partials [M][1]
   float* logits; int ldl;       // optional logits tap (EP_ARGMAX)
 };
-// bf16: W is packed (16x32 MFMA blocks); the reduction order per output is
-// fixed (8 K-slices summed in order) and independent of M.
-void launch_gemm_bf16(const void* Wp, const uint16_t* X, int ldx, int M, int K, int N,
-                      const GemmOut& o, hipStream_t s);
-int gemm_bf16_argmax_parts(int N);
+
+// bf16 path: one launch covers GEMM rows [0, M) = pass rows [row0, row0+M).
+struct GemmArgs {
+  const u32x4_t* W;             // packed weight (16x32 MFMA fragments)
+  int M, K, N, row0;
+  // input: bf16 rows X, or RMSNorm(h) built from fp32 h, per-128-column
+  // sums of squares ss [rows][nss] and the bf16 gain (length dn = K)
+  const uint16_t* X; int ldx;
+  const float* h; const float* ss; int nss; const uint16_t* gain; float eps; int dn;
+  // split-K partials [8][M][N] and completion counters (zero between launches)
+  float* part; unsigned* cnt;
+  int ep;
+  float* y; int ldy; float* ss_out; int nss_out;      // EP_RESID
+  uint16_t* act; int ldact;                            // EP_SWIGLU
+  PassInfo P; int hq, hkv;                             // EP_QKV (and EP_ARGMAX row mapping)
+  const uint16_t* qn; const uint16_t* kn; const uint16_t* dqn; const uint16_t* dkn;
+  const float2* rope; uint16_t* q_out; uint16_t* kc; uint16_t* vc; int cap;
+  uint16_t* ks; uint16_t* vs; int kpad;
+  float2* amax; float* logits; int ldl; int Kb;       // EP_ARGMAX
+  int32_t* drafts; int32_t* ar; int32_t* pending;
+  int split;                    // 1: force the split-K form, 2: force all slices per workgroup
+};
+void launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+int gemm_bf16_groups(int N);
 // fp32: W canonical row-major [N][K] (for SwiGLU: gate at W, up at W2).
 void launch_gemm_f32(const float* W, const float* W2, const float* X, int ldx, int M, int K,
                      int N, const GemmOut& o, hipStream_t s);
-int gemm_f32_argmax_parts(int N);
 
 // Attention.  q [rows][hq][hd] (model dtype); cache layer base pointers.
 struct AttnArgs {

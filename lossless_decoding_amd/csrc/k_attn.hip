@@ -250,7 +250,11 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
   const int hd = a.hd, G = a.hq / a.hkv, g = h / G;
   int b, t;
   if (a.fixed_ctx >= 0) { b = r / P.Kx; t = r - b * P.Kx; }
-  else { RowInfo ri = row_info(P, r); b = ri.b; t = ri.t; }
+  else {
+    RowInfo ri = row_info(P, r);
+    if (ri.pad) return;
+    b = ri.b; t = ri.t;
+  }
   const SeqLimits L = seq_limits(a, b);
   int limit, sees;
   token_view(a, L, t, limit, sees);
@@ -301,6 +305,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(AttnArgs a) {
   const PassInfo& P = a.P;
   const int hd = a.hd, G = a.hq / a.hkv, g = h / G;
   RowInfo ri = row_info(P, r);
+  if (ri.pad) return;
   const SeqLimits L = seq_limits(a, ri.b);
   int limit, sees;
   token_view(a, L, ri.t, limit, sees);

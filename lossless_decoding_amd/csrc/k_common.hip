@@ -36,42 +36,63 @@ void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, 
 }
 
 // ----------------------------------------------------------- embedding
-__global__ void k_embed(PassInfo P, const int32_t* __restrict__ anchor_tok,
-                        const int32_t* __restrict__ block_tok, int block_ld,
-                        const void* __restrict__ embed, const void* __restrict__ mask_emb, int V,
-                        int d, int bf16, float* __restrict__ h) {
-  int r = blockIdx.x;
-  int tok = -1;   // -1: the mask embedding (mask rows of a draft pass)
-  if (r < P.A * P.B) {
-    tok = anchor_tok[r];
-  } else if (P.kind != PASS_DRAFT) {
+// h[row] = E[token] (token rows) or the mask embedding (mask rows); padding
+// rows get zeros.  With ss != NULL also writes the per-128-column sums of
+// squares of the row (wave w sums columns 128c + lane and 128c + 64 + lane,
+// then a fixed butterfly), the input of the next fused RMSNorm.
+__global__ __launch_bounds__(256) void k_embed(PassInfo P, const int32_t* __restrict__ anchor_tok,
+                                               const int32_t* __restrict__ block_tok, int block_ld,
+                                               const void* __restrict__ embed,
+                                               const void* __restrict__ mask_emb, int V, int d,
+                                               int bf16, float* __restrict__ h,
+                                               float* __restrict__ ss) {
+  const int r = blockIdx.x;
+  int kind;          // 0 token, 1 mask, 2 padding
+  int tok = 0;
+  if (P.kind == PASS_DRAFT) {
+    if (r >= P.RM) { kind = 0; tok = anchor_tok[r - P.RM]; }
+    else if (r < P.B * P.Kx) kind = 1;
+    else kind = 2;
+  } else {
     int b = r / P.Kx, i = r - b * P.Kx;
+    kind = 0;
     tok = block_tok[(size_t)b * block_ld + (P.kind == PASS_PREFILL ? P.p0 : 0) + i];
   }
-  const bool mask_row = P.kind == PASS_DRAFT && r >= P.A * P.B;
-  if (!mask_row) tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
   float* out = h + (size_t)r * d;
   for (int i = threadIdx.x; i < d; i += blockDim.x) {
-    float v;
-    if (bf16) {
-      const uint16_t* src = tok < 0 ? (const uint16_t*)mask_emb
-                                    : (const uint16_t*)embed + (size_t)tok * d;
-      v = bf2f(src[i]);
-    } else {
-      const float* src = tok < 0 ? (const float*)mask_emb : (const float*)embed + (size_t)tok * d;
-      v = src[i];
+    float v = 0.f;
+    if (kind != 2) {
+      if (bf16) {
+        const uint16_t* src = kind == 1 ? (const uint16_t*)mask_emb
+                                        : (const uint16_t*)embed + (size_t)tok * d;
+        v = bf2f(src[i]);
+      } else {
+        const float* src = kind == 1 ? (const float*)mask_emb : (const float*)embed + (size_t)tok * d;
+        v = src[i];
+      }
     }
     out[i] = v;
+  }
+  if (!ss) return;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nss = d / 128;
+  for (int c = wave; c < nss; c += 4) {
+    float x1 = out[c * 128 + lane], x2 = out[c * 128 + 64 + lane];
+    float t = x1 * x1 + x2 * x2;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
+    if (lane == 0) ss[(size_t)r * nss + c] = t;
   }
 }
 
 void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
                   int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
-                  float* h, hipStream_t s) {
+                  float* h, float* ss, hipStream_t s) {
   int rows = P.rows();
   if (rows <= 0) return;
   hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, P, anchor_tok, block_tok, block_ld,
-                     embed, mask_emb, V, d, (int)bf16, h);
+                     embed, mask_emb, V, d, (int)bf16, h, ss);
 }
 
 // -------------------------------------------------------------- RMSNorm
@@ -126,7 +147,7 @@ __global__ __launch_bounds__(64) void k_qkv_post(
     void* __restrict__ ks, void* __restrict__ vs, int kpad) {
   const int r = blockIdx.x, slot = blockIdx.y, lane = threadIdx.x;
   const RowInfo ri = row_info(P, r);
-  if (ri.pos >= cap) return;     // unreachable under the host's length bound
+  if (ri.pad || ri.pos >= cap) return;     // padding row, or past the cache (host bound excludes it)
   const int qd = hq * hd, kd = hkv * hd, half = hd / 2;
   const bool isq = slot < hq;
   const int head = isq ? slot : slot - hq;
@@ -224,16 +245,16 @@ __global__ void k_lm_reduce(const float2* __restrict__ part, int rows, int npart
     float v = p[j].x;
     if (v > best) { best = v; idx = __float_as_int(p[j].y); }
   }
+  const RowInfo ri = row_info(P, r);
+  if (ri.pad) return;
   if (P.kind == PASS_DRAFT) {
-    if (r < P.A * P.B) {
-      if (pending) pending[r] = idx; else ar[(size_t)r * (K + 1)] = idx;
+    if (!ri.is_mask) {
+      if (pending) pending[ri.b] = idx; else ar[(size_t)ri.b * (K + 1)] = idx;
     } else {
-      int j = r - P.A * P.B;
-      drafts[j] = idx;     // rows are sequence-major: j = b*K + i
+      drafts[(size_t)ri.b * K + (ri.t - P.A)] = idx;
     }
-  } else {
-    int b = r / P.Kx, i = r - (r / P.Kx) * P.Kx;
-    ar[(size_t)b * (K + 1) + 1 + i] = idx;
+  } else if (P.kind == PASS_VERIFY) {
+    ar[(size_t)ri.b * (K + 1) + 1 + ri.t] = idx;
   }
 }
 

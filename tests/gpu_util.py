@@ -44,6 +44,12 @@ def oracle_model(name, seed=workloads.WEIGHT_SEED, **over):
     return _OCACHE[key]
 
 
+def anchor_row(K, B=1, b=0):
+    """Physical row of sequence b's anchor in a draft pass: the B*K mask rows
+    come first, padded to a multiple of 16."""
+    return (B * K + 15) // 16 * 16 + b
+
+
 def margin(logits_row):
     """top-1 minus top-2 of one logits row."""
     s = np.sort(np.asarray(logits_row, np.float64))

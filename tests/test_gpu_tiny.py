@@ -41,7 +41,8 @@ def test_tiny_step_parity_with_oracle():
     tap = om.set_attn_tap(K + 1)
     pend_o = seq.prefill(prompt[0])
     eng = U.engine("tiny", max_ctx=400)
-    rows = K + 1
+    RA = U.anchor_row(K)
+    rows = RA + 1
     lg = torch.zeros(rows, V, device="cuda")
     at = torch.zeros(L, rows, qd, device="cuda")
     eng.set_debug(lg, at, rows)
@@ -61,8 +62,8 @@ def test_tiny_step_parity_with_oracle():
         eng.commit()
         torch.cuda.synchronize()
         r = seq.step(pend_o, K)
-        np.testing.assert_allclose(g_draft[0], r["logits_anchor"], atol=TOL, rtol=0)
-        np.testing.assert_allclose(g_draft[1:], r["logits_draft"], atol=TOL, rtol=0)
+        np.testing.assert_allclose(g_draft[RA], r["logits_anchor"], atol=TOL, rtol=0)
+        np.testing.assert_allclose(g_draft[:K], r["logits_draft"], atol=TOL, rtol=0)
         np.testing.assert_allclose(g_verify, r["logits_verify"], atol=TOL, rtol=0)
         np.testing.assert_allclose(g_attn, tap[:, :K], atol=TOL, rtol=0)
         assert np.array_equal(g_drafts, r["drafts"])
