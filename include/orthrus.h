@@ -93,6 +93,11 @@ typedef struct orthrus_config {
   int32_t dtype;          /* ORTHRUS_F32 or ORTHRUS_BF16 */
   int32_t max_batch;      /* sequences per call, 1..256 */
   int32_t max_ctx;        /* KV slots per sequence (cache capacity) */
+  int32_t attn_chunk;     /* keys per attention chunk: 0 = chosen from max_ctx, else a power
+                             of two in [64, 4096].  Attention partials are folded per chunk
+                             of absolute cache positions, so two contexts give bit-identical
+                             rows (e.g. a block_k = 32 context and its block_k = 0 greedy
+                             twin) only if their attn_chunk values are equal. */
 } orthrus_config;
 
 typedef struct orthrus_sizes {

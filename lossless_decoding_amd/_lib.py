@@ -38,12 +38,13 @@ class OrthrusConfig(ctypes.Structure):
                 ("vocab", ctypes.c_int32), ("block_k", ctypes.c_int32),
                 ("rope_theta", ctypes.c_double), ("rms_eps", ctypes.c_double),
                 ("dtype", ctypes.c_int32), ("max_batch", ctypes.c_int32),
-                ("max_ctx", ctypes.c_int32)]
+                ("max_ctx", ctypes.c_int32), ("attn_chunk", ctypes.c_int32)]
 
     @classmethod
-    def make(cls, L, d, hq, hkv, hd, F, V, K, bf16, max_batch, max_ctx, theta=1e6, eps=1e-6):
+    def make(cls, L, d, hq, hkv, hd, F, V, K, bf16, max_batch, max_ctx, theta=1e6, eps=1e-6,
+             attn_chunk=0):
         return cls(L, d, hq, hkv, hd, F, V, K, theta, eps, ORTHRUS_BF16 if bf16 else ORTHRUS_F32,
-                   max_batch, max_ctx)
+                   max_batch, max_ctx, attn_chunk)
 
 
 class OrthrusSizes(ctypes.Structure):

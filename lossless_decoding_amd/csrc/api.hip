@@ -73,6 +73,9 @@ int validate(const orthrus_config* c) {
   if (c->head_dim % 2 || c->head_dim > 128) return ORTHRUS_EINVAL;
   if (!(c->rope_theta > 1.0) || !(c->rms_eps > 0.0)) return ORTHRUS_EINVAL;
   if (c->block_k > 63) return ORTHRUS_EINVAL;
+  if (c->attn_chunk != 0 &&
+      (c->attn_chunk < 64 || c->attn_chunk > 4096 || (c->attn_chunk & (c->attn_chunk - 1))))
+    return ORTHRUS_EINVAL;
   int G = c->n_q_heads / c->n_kv_heads;
   if (c->dtype == ORTHRUS_BF16) {
     if (c->head_dim != 128) return ORTHRUS_EINVAL;
@@ -101,8 +104,11 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.rmax = draft_rows > other_rows ? draft_rows : other_rows;
   // attention key chunk: fixed per context so that a row's result does not
   // depend on which pass computes it
-  int sc = 64;
-  while (sc < 2048 && sc * 64 < y.cap) sc *= 2;
+  int sc = c.attn_chunk;
+  if (sc == 0) {
+    sc = 64;
+    while (sc < 2048 && sc * 64 < y.cap) sc *= 2;
+  }
   y.sc = sc;
   y.nc = (y.cap + sc - 1) / sc;
   y.qr_max = y.tmax * y.G;

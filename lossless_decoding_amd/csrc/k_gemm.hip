@@ -66,9 +66,9 @@ __device__ __forceinline__ void amax_comb(float& v, int& i, float v2, int i2) {
 
 template <int MT, int EP, int SPW>
 __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
-  // LDS: activation chunk in fragment order (MT*16 rows x 256 k bf16), reused
+  // LDS: activation block in fragment order (MT*16 rows x 512 k bf16), reused
   // by the epilogue as an fp32 tile of MT*16 x 128.
-  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * 256];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * 512];
   __shared__ float sInv[64];
   __shared__ float sRed[WAVES * 64];
   __shared__ int sIdx[WAVES * 64];
@@ -115,24 +115,32 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
     tot[mt] = cur[mt];
   }
 
+  // Weights stream in chunks of CLB k-blocks into two register sets, loaded
+  // two chunks ahead; activations are staged into LDS in blocks of SAB
+  // k-blocks (up to 512 k), so the weight loads stay in flight across the
+  // staging barriers.
   const int nchunk_slice = KS / CL;
   const int nchunks = nchunk_slice * SPW;
   const int kbase0 = s_first * KS;
-  u32x4_t wreg[8], wnext[8];
+  const int SAB = (KS >> 5) < 16 ? (KS >> 5) : 16;   // staged k-blocks
+  u32x4_t wA[8], wB[8];
+  auto wload = [&](u32x4_t (&w)[8], int c) {
+    const int kb = (kbase0 >> 5) + c * CLB;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    wnext[j] = u32x4_t{0u, 0u, 0u, 0u};
-    if (j < CLB) wreg[j] = __builtin_nontemporal_load(wp + (size_t)((kbase0 >> 5) + j) * 64);
-    else wreg[j] = wnext[j];
-  }
+    for (int j = 0; j < 8; ++j)
+      if (j < CLB) w[j] = __builtin_nontemporal_load(wp + (size_t)(kb + j) * 64);
+  };
+#pragma unroll
+  for (int j = 0; j < 8; ++j) { wA[j] = u32x4_t{0u, 0u, 0u, 0u}; wB[j] = wA[j]; }
+  wload(wA, 0);
+  if (nchunks > 1) wload(wB, 1);
 
-  for (int c = 0; c < nchunks; ++c) {
-    const int k0 = kbase0 + c * CL;
-    // ---- stage the activation chunk [MT*16 rows][CL] in fragment order
+  auto stage = [&](int kb0) {        // stage k-blocks [kb0, kb0 + SAB) of the activations
     __syncthreads();
-    const int units = MT * 16 * CL / 8;      // 16-byte units
+    const int k0 = kb0 * 32;
+    const int units = MT * 16 * SAB * 4;      // 16-byte units
     for (int u = tid; u < units; u += 512) {
-      int row = u / (CL / 8), kq = u - row * (CL / 8);
+      int row = u / (SAB * 4), kq = u - row * (SAB * 4);
       int kb = kq >> 2, q = kq & 3;
       int r = m0 + row;
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
@@ -155,38 +163,40 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
         }
       }
       int mt = row >> 4, ln = q * 16 + (row & 15);
-      *(u32x4_t*)(sX + ((size_t)(mt * CLB + kb) * 64 + ln) * 8) = v;
+      *(u32x4_t*)(sX + ((size_t)(mt * SAB + kb) * 64 + ln) * 8) = v;
     }
     __syncthreads();
-    // ---- prefetch the next chunk's weights
-    if (c + 1 < nchunks) {
-      const int kb1 = (k0 + CL) >> 5;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (j < CLB) wnext[j] = __builtin_nontemporal_load(wp + (size_t)(kb1 + j) * 64);
-    }
-    // ---- MFMA chain over the chunk
+  };
+  auto compute = [&](const u32x4_t (&w)[8], int c) {
+    const int kbl = (c * CLB) % SAB;           // first k-block of the chunk inside the stage
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < CLB) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-          u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * CLB + j) * 64 + lane) * 8);
-          cur[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wreg[j]), as_bf16x8(xv),
+          u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SAB + kbl + j) * 64 + lane) * 8);
+          cur[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[j]), as_bf16x8(xv),
                                                             cur[mt], 0, 0, 0);
         }
       }
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) wreg[j] = wnext[j];
-    // ---- slice boundary: add the slice sum in slice order
-    if (SPW == NSL && (c + 1) % nchunk_slice == 0) {
+    if (SPW == NSL && (c + 1) % nchunk_slice == 0) {   // slice done: add in slice order
       const int s = (c + 1) / nchunk_slice - 1;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         tot[mt] = s == 0 ? cur[mt] : add4(tot[mt], cur[mt]);
         cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
       }
+    }
+  };
+  for (int c = 0; c < nchunks; c += 2) {
+    if ((c * CLB) % SAB == 0) stage((kbase0 >> 5) + c * CLB);
+    compute(wA, c);
+    if (c + 2 < nchunks) wload(wA, c + 2);
+    if (c + 1 < nchunks) {
+      if (((c + 1) * CLB) % SAB == 0) stage((kbase0 >> 5) + (c + 1) * CLB);
+      compute(wB, c + 1);
+      if (c + 3 < nchunks) wload(wB, c + 3);
     }
   }
   if (SPW == NSL) {

@@ -75,7 +75,8 @@ def test_tpf_accounting_matches_pages():
 
 
 @pytest.mark.parametrize("field,val", [("n_layers", 0), ("head_dim", 64), ("d_model", 500),
-                                       ("block_k", 64), ("max_batch", 0), ("n_kv_heads", 3)])
+                                       ("block_k", 64), ("max_batch", 0), ("n_kv_heads", 3),
+                                       ("attn_chunk", 100), ("attn_chunk", 32), ("vocab", 2000)])
 def test_invalid_configs_rejected(field, val):
     c = cfg_of("small")
     setattr(c, field, val)
