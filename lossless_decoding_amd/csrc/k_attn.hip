@@ -196,15 +196,22 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       const bool any = mnew != -INFINITY;
       const float mref = any ? mnew : 0.f;
       const float alpha = any ? exp2f(mrow[j] - mref) : 1.f;
+      // P enters the P.V product as two bf16 terms, hi = bf16(p) and
+      // lo = bf16(p - hi) (p - hi is exact in fp32), so the product carries
+      // about 16 significant bits of p instead of 8.  Rounding p itself to
+      // bf16 would make the result depend on the running maximum it was
+      // taken against, i.e. on how the keys were split into tiles and chunks.
       float ps = 0.f;
-      bf16x8_t pf[2];
+      bf16x8_t pf[2], pl[2];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float p = exp2f(s[kb][i] - mref);
           ps += p;
-          pf[kb >> 1][(kb & 1) * 4 + i] = (__bf16)p;
+          __bf16 hi = (__bf16)p;
+          pf[kb >> 1][(kb & 1) * 4 + i] = hi;
+          pl[kb >> 1][(kb & 1) * 4 + i] = (__bf16)(p - (float)hi);
         }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
@@ -218,6 +225,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8_t vf = ld_bf16x8(sV + (db * 16 + lr) * VT_STRIDE + ks * 32 + lq * 8);
           o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks], o, 0, 0, 0);
+          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[ks], o, 0, 0, 0);
         }
         oacc[j][db] = o;
       }

@@ -182,11 +182,12 @@ class Model:
         self.w = np.ascontiguousarray(weights)
         self._c = shape.c()
         self.h = lib().oc_model_new(ctypes.byref(self._c), self.w.ctypes.data)
+        self._free = lib().oc_model_free     # held so that teardown needs no module globals
         self._tap = None
 
     def __del__(self):
         if getattr(self, "h", None):
-            lib().oc_model_free(self.h)
+            self._free(self.h)
             self.h = None
 
     def set_attn_tap(self, rows: int):
@@ -224,11 +225,12 @@ class Seq:
     def __init__(self, model: Model, cap: int):
         self.m = model
         self.h = lib().oc_seq_new(model.h, cap)
+        self._free = lib().oc_seq_free
         self.cap = cap
 
     def __del__(self):
         if getattr(self, "h", None):
-            lib().oc_seq_free(self.h)
+            self._free(self.h)
             self.h = None
 
     @property

@@ -14,7 +14,8 @@ def cfg_of(name, K=None, max_batch=1, max_ctx=512, attn_chunk=128, **over):
     """Test contexts share one attention chunk size so that a K context and
     its K = 0 greedy twin are bit-comparable."""
     s = dict(workloads.SHAPES[name]); s.update(over)
-    return C.OrthrusConfig.make(s["L"], s["d"], s["hq"], s["hkv"], s["hd"], s["F"], s["V"],
+    L = s.pop("n_layers", s["L"])
+    return C.OrthrusConfig.make(L, s["d"], s["hq"], s["hkv"], s["hd"], s["F"], s["V"],
                                 s["K"] if K is None else K, s["bf16"], max_batch, max_ctx,
                                 attn_chunk=attn_chunk)
 
