@@ -203,6 +203,9 @@ def main():
     M1 = B * (K + 1)
     gu_bytes = 2 * sh["F"] * sh["d"] * 2 + M1 * sh["d"] * 2 + M1 * sh["F"] * 2
     gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
+    # the instantiation the library launches for it (row tiles, waves per workgroup)
+    gu_mt = min(4, (M1 + 15) // 16)
+    gu_wv = 6 if (2 * sh["F"] // 16) % 6 == 0 and gu_mt <= 3 else 8
     achieved = gu_bytes / gu_avg_s / 1e9 if gu_n else 0.0
     traffic = None
     if os.path.exists(PROFILE_PMC):
@@ -258,7 +261,7 @@ def main():
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
         "lossless_vs_greedy": lossless,
         "roofline": {
-            "kernel": f"k_gemm_bf16<{min(4, (M1 + 15) // 16)},2,EP_SWIGLU> (draft-pass gate/up "
+            "kernel": f"k_gemm_bf16<{gu_mt}, EP_SWIGLU, {gu_wv}, false> (draft-pass gate/up "
                       f"SwiGLU GEMM, M={M1}, N={2 * sh['F']}, K={sh['d']})",
             "bound": "hbm",
             "achieved": round(achieved, 1),

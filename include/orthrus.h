@@ -82,7 +82,7 @@ enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1 };
  * are shared.
  * BF16 models: bf16 weights, bf16 KV cache, fp32 residual stream, fp32
  * accumulation; requires head_dim 128, d_model, n_q_heads*head_dim and
- * ffn_dim multiples of 256, vocab a multiple of 128, and (block_k + 1) * group <= 144 and
+ * ffn_dim multiples of 256, d_model <= 8192, vocab a multiple of 128, and (block_k + 1) * group <= 144 and
  * 32 * group <= 144 (group = n_q_heads / n_kv_heads).
  * F32 models: everything fp32 (small check models). */
 typedef struct orthrus_config {

@@ -50,7 +50,7 @@ uint64_t canon_offset(const orthrus_config& c, int t) {
 struct Layout {
   // element size, dims
   int esz, L, d, hq, hkv, hd, F, V, K, G, qd, kd, nqkv;
-  int cap, kpad, tmax, rmax, sc, nc, qr_max, nss, ngroups_max;
+  int cap, kpad, tmax, rmax, sc, nc, qr_max, ngroups_max;
   bool bf16;
   // packed offsets (bytes)
   uint64_t p_embed, p_lm, p_fnorm, p_mask;
@@ -59,7 +59,7 @@ struct Layout {
   uint64_t packed_bytes;
   // workspace offsets (bytes)
   uint64_t w_h, w_x, w_qkv, w_q, w_act, w_opart, w_ml, w_parts, w_logits, w_rope, w_i32,
-      w_ss, w_part, w_cnt, cnt_bytes, w_amax, workspace_bytes;
+      w_part, w_cnt, cnt_bytes, w_amax, workspace_bytes;
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
 };
 
@@ -82,6 +82,7 @@ int validate(const orthrus_config* c) {
     if (c->d_model % 256 || (c->n_q_heads * c->head_dim) % 256 || c->ffn_dim % 256)
       return ORTHRUS_EINVAL;
     if (c->vocab % 128) return ORTHRUS_EINVAL;
+    if (c->d_model > 8192) return ORTHRUS_EINVAL;
     if ((c->block_k + 1) * G > 144 || kPrefillChunk * G > 144) return ORTHRUS_EINVAL;
   } else if (c->dtype != ORTHRUS_F32) {
     return ORTHRUS_EINVAL;
@@ -112,7 +113,6 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.sc = sc;
   y.nc = (y.cap + sc - 1) / sc;
   y.qr_max = y.tmax * y.G;
-  y.nss = y.d / 128;
   {
     int ns[4] = {y.nqkv, y.d, 2 * y.F, y.V};
     y.ngroups_max = 0;
@@ -164,7 +164,6 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.w_rope = take((uint64_t)y.cap * (y.hd / 2) * 8);
   y.w_i32 = take((uint64_t)4 * c.max_batch * 4);
   if (y.bf16) {
-    y.w_ss = take((uint64_t)y.rmax * y.nss * 4);
     // split-K partials of the narrow GEMMs (fewer than 128 column groups)
     uint64_t nmax = 0;
     int ns[4] = {y.nqkv, y.d, 2 * y.F, y.V};
@@ -172,11 +171,12 @@ void make_layout(const orthrus_config& c, Layout& y) {
       if (ns[i] / 128 < 128 && (uint64_t)ns[i] > nmax) nmax = ns[i];
     // partials are kept per padded 64-row group: [8][round_up(rows, 64)][N]
     y.w_part = take(8 * (uint64_t)round_up(y.rmax, 64) * nmax * 4);
+    // completion counters of the split-K GEMM column groups (+1 grid counter)
     y.cnt_bytes = ((uint64_t)((y.rmax + 63) / 64) * y.ngroups_max + 1) * 4;
     y.w_cnt = take(y.cnt_bytes);
     y.w_amax = take((uint64_t)y.rmax * (y.V / 128) * 8);
   } else {
-    y.w_ss = y.w_part = y.w_cnt = y.w_amax = take(0);
+    y.w_part = y.w_cnt = y.w_amax = take(0);
     y.cnt_bytes = 0;
   }
   y.workspace_bytes = o;
@@ -271,7 +271,7 @@ void run_pass_f32(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   {
     Tick t(c, pb + R_SMALL, s);
     launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed,
-                 c->packed + y.p_mask, y.V, y.d, false, h, nullptr, s);
+                 c->packed + y.p_mask, y.V, y.d, false, h, s);
   }
   for (int l = 0; l < y.L; ++l) {
     launch_rmsnorm(h, rows, y.d, c->packed + y.p_anorm[l], false, eps, x, s);
@@ -337,15 +337,14 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   const int NA = P.kind == PASS_DRAFT ? P.A * P.B : 0;
   const float eps = (float)c->cfg.rms_eps;
   float* h = S<float>(c, y.w_h);
-  float* ss = S<float>(c, y.w_ss);
-  uint16_t* x = S<uint16_t>(c, y.w_x);
+  uint16_t* x = S<uint16_t>(c, y.w_x);   // RMSNorm output (ld d) / attention output (ld qd)
   uint16_t* q = S<uint16_t>(c, y.w_q);
   uint16_t* act = S<uint16_t>(c, y.w_act);
   const int pb = pass_base(P.kind);
   {
     Tick t(c, pb + R_SMALL, s);
     launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed,
-                 c->packed + y.p_mask, y.V, y.d, true, h, ss, s);
+                 c->packed + y.p_mask, y.V, y.d, true, h, s);
   }
   GemmArgs g0{};
   g0.part = S<float>(c, y.w_part);
@@ -353,10 +352,9 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   g0.eps = eps;
   g0.P = P; g0.hq = y.hq; g0.hkv = y.hkv;
   g0.rope = S<float2>(c, y.w_rope); g0.q_out = q; g0.cap = y.cap; g0.kpad = y.kpad;
-  g0.nss = y.nss; g0.nss_out = y.nss;
-  auto normed = [&](GemmArgs g, uint64_t gain_off, int K) {
-    g.h = h; g.ss = ss; g.gain = (const uint16_t*)(c->packed + gain_off); g.dn = K;
-    return g;
+  auto norm = [&](uint64_t gain_off) {
+    Tick t(c, pb + R_SMALL, s);
+    launch_rownorm_bf16(h, rows, y.d, (const uint16_t*)(c->packed + gain_off), eps, x, s);
   };
   auto run = [&](GemmArgs g, uint64_t w, int row0, int M, int K, int N, int ep) {
     g.W = (const u32x4_t*)(c->packed + w);
@@ -369,11 +367,13 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     uint16_t* vc = (uint16_t*)(c->kv + ((uint64_t)y.L + l) * y.kv_layer_elems * E);
     uint16_t* ks = (uint16_t*)(c->scr + (uint64_t)l * y.scr_layer_elems * E);
     uint16_t* vs = (uint16_t*)(c->scr + ((uint64_t)y.L + l) * y.scr_layer_elems * E);
-    // Q/K/V projection + QK-norm + RoPE + K/V placement; mask rows use the
-    // diffusion projections, every other row the frozen ones
+    // RMSNorm, then Q/K/V projection + QK-norm + RoPE + K/V placement; mask
+    // rows use the diffusion projections, every other row the frozen ones
+    norm(y.p_anorm[l]);
     {
       Tick t(c, pb + R_QKV, s);
-      GemmArgs g = normed(g0, y.p_anorm[l], y.d);
+      GemmArgs g = g0;
+      g.X = x; g.ldx = y.d;
       g.qn = (const uint16_t*)(c->packed + y.p_qn[l]);
       g.kn = (const uint16_t*)(c->packed + y.p_kn[l]);
       g.dqn = (const uint16_t*)(c->packed + y.p_dqn[l]);
@@ -399,11 +399,11 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       Tick t(c, pb + R_ATTN, s);
       launch_attention_bf16(a, s);
     }
-    // O projection + residual (+ sums of squares for the FFN norm)
+    // O projection + residual
     {
       Tick t(c, pb + R_O, s);
       GemmArgs g = g0;
-      g.X = x; g.ldx = y.qd; g.y = h; g.ldy = y.d; g.ss_out = ss;
+      g.X = x; g.ldx = y.qd; g.y = h; g.ldy = y.d;
       if (P.kind == PASS_DRAFT) {
         if (BK > 0) run(g, y.p_do[l], 0, BK, y.qd, y.d, EP_RESID);
         if (NA > 0) run(g, y.p_o[l], RM, NA, y.qd, y.d, EP_RESID);
@@ -411,22 +411,26 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
         run(g, y.p_o[l], 0, rows, y.qd, y.d, EP_RESID);
       }
     }
+    norm(y.p_ffnnorm[l]);
     {
       Tick t(c, pb + R_GU, s);
-      GemmArgs g = normed(g0, y.p_ffnnorm[l], y.d);
+      GemmArgs g = g0;
+      g.X = x; g.ldx = y.d;
       g.act = act; g.ldact = y.F;
       run(g, y.p_gu[l], 0, rows, y.d, 2 * y.F, EP_SWIGLU);
     }
     {
       Tick t(c, pb + R_DOWN, s);
       GemmArgs g = g0;
-      g.X = act; g.ldx = y.F; g.y = h; g.ldy = y.d; g.ss_out = ss;
+      g.X = act; g.ldx = y.F; g.y = h; g.ldy = y.d;
       run(g, y.p_down[l], 0, rows, y.F, y.d, EP_RESID);
     }
   }
   if (!want_tokens) return;
+  norm(y.p_fnorm);
   Tick tl(c, pb + R_LM, s);
-  GemmArgs g = normed(g0, y.p_fnorm, y.d);
+  GemmArgs g = g0;
+  g.X = x; g.ldx = y.d;
   g.amax = S<float2>(c, y.w_amax);
   g.Kb = y.K; g.drafts = drafts; g.ar = ar; g.pending = pending;
   if (c->dbg_logits && rows <= c->dbg_rows) { g.logits = c->dbg_logits; g.ldl = y.V; }

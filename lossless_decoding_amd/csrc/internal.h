@@ -89,7 +89,9 @@ void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, 
                       hipStream_t s);
 void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
                   int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
-                  float* h, float* ss, hipStream_t s);
+                  float* h, hipStream_t s);
+void launch_rownorm_bf16(const float* h, int rows, int d, const uint16_t* gain, float eps,
+                         uint16_t* out, hipStream_t s);
 void launch_rmsnorm(const float* h, int rows, int d, const void* gain, bool bf16, float eps,
                     void* out, hipStream_t s);
 void launch_qkv_post(const PassInfo& P, const float* qkv, int hq, int hkv, int hd,
@@ -121,22 +123,18 @@ struct GemmOut {                // fp32 path
 struct GemmArgs {
   const u32x4_t* W;             // packed weight (16x32 MFMA fragments)
   int M, K, N, row0;
-  // input: bf16 rows X, or RMSNorm(h) built from fp32 h, per-128-column
-  // sums of squares ss [rows][nss] and the bf16 gain (length dn = K)
-  const uint16_t* X; int ldx;
-  const float* h; const float* ss; int nss; const uint16_t* gain; float eps; int dn;
+  const uint16_t* X; int ldx;   // bf16 input rows
   // split-K partials [8][M][N] and completion counters (zero between launches)
   float* part; unsigned* cnt;
   int ep;
-  float* y; int ldy; float* ss_out; int nss_out;      // EP_RESID
+  float* y; int ldy;                                  // EP_RESID
   uint16_t* act; int ldact;                            // EP_SWIGLU
-  PassInfo P; int hq, hkv;                             // EP_QKV (and EP_ARGMAX row mapping)
+  PassInfo P; int hq, hkv; float eps;                  // EP_QKV (and EP_ARGMAX row mapping)
   const uint16_t* qn; const uint16_t* kn; const uint16_t* dqn; const uint16_t* dkn;
   const float2* rope; uint16_t* q_out; uint16_t* kc; uint16_t* vc; int cap;
   uint16_t* ks; uint16_t* vs; int kpad;
   float2* amax; float* logits; int ldl; int Kb;       // EP_ARGMAX
   int32_t* drafts; int32_t* ar; int32_t* pending;
-  int split;                    // 1: force the split-K form, 2: force all slices per workgroup
 };
 void launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 int gemm_bf16_groups(int N);

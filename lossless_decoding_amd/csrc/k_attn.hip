@@ -1,27 +1,27 @@
 // Block attention over the shared KV cache (the draft pass's anchor + mask
 // rows, the verify pass's causal rows, prefill rows).
 //
-// bf16 path.  One workgroup per (sequence, KV head, key chunk).  All query
-// rows of the pass for that sequence and every query head of the GQA group
-// (T tokens x G heads, at most 144 rows = 9 row tiles of 16) share each
-// 64-key K/V tile staged in LDS, so the cache is streamed once per pass.
+// bf16 path.  A workgroup handles (key chunk, KV head, sequence,
+// group of four 16-row query tiles); the query rows of a sequence are its
+// tokens x the G query heads of the KV head, so each 64-key K/V tile staged
+// in LDS serves the whole GQA group.  A wave owns one query tile.
 // MFMA: S^T = K . Q^T (keys x rows) and O^T = V^T . P^T (dims x rows), so a
 // lane always holds one query row and the softmax statistics stay in-lane.
-// Online softmax in fp32 (base-2 exponent).  Chunks are SC keys aligned to
-// absolute cache positions; each chunk's partial (max, sum, unnormalised
-// output) is folded in increasing chunk order by the merge kernel, and the
-// draft block's keys are folded last.  A row's result therefore depends only
-// on which keys it sees, never on the other rows of the pass: fully masked
-// tiles and chunks are exact no-ops, masked keys are removed by selection
-// (never by multiplying stale values), and keys past the pass's last
-// written slot are zeroed when staged.
+// Online softmax in fp32 (base-2 exponent); the next K/V tile is loaded into
+// registers while the current one is computed.  Chunks are SC keys aligned
+// to absolute cache positions; each writes its partial (max, sum,
+// unnormalised output) and the merge kernel combines a row's partials in
+// increasing chunk order, the draft block's keys last.  A row's result
+// therefore depends only on which keys it sees, never on the other rows of
+// the pass: fully masked tiles and chunks are exact no-ops, masked keys are
+// removed by selection (never by multiplying stale values), and keys past
+// the pass's last written slot are zeroed when staged.
 //
 // fp32 path: one wave per (row, query head), keys in order (check models).
 #include "internal.h"
 
 #define KT_STRIDE 136   // bf16 per key row of the staged K tile (128 + 8 pad)
 #define VT_STRIDE 72    // bf16 per dimension row of the staged V^T tile (64 + 8 pad)
-#define AT_MAX_RT_PER_WAVE 3
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   uint4 v = *(const uint4*)p;
@@ -63,57 +63,61 @@ __device__ __forceinline__ void token_view(const AttnArgs& a, const SeqLimits& L
   limit = P.kind == PASS_VERIFY ? L.n + 1 + t : P.p0 + t;
 }
 
+// number of 4-tile query row groups of a pass
+__host__ __device__ inline int attn_row_groups(int qr) { return ((qr + 15) / 16 + 3) / 4; }
+
 __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[64 * KT_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[128 * VT_STRIDE];
-  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int c = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
   const PassInfo& P = a.P;
   const int T = a.fixed_ctx >= 0 ? P.Kx : P.tokens_per_seq();
   const int G = a.hq / a.hkv;
   const int QR = T * G;
   const int NRT = (QR + 15) >> 4;
+  const int NRG = attn_row_groups(QR);
+  const int b = blockIdx.z / NRG, rg = blockIdx.z - b * NRG;
   const bool blk = (c == a.nc);
   const int hd = 128;
   const int H = a.hq * hd;
 
-  if (blk && !(a.block_len > 0 && (a.fixed_ctx >= 0 || (P.kind == PASS_DRAFT && P.Kx > 0))))
-    return;
+  // which chunks take part: every chunk up to the sequence's last visible
+  // slot, plus the block chunk when the pass has a draft block
+  const bool has_blk = a.block_len > 0 && (a.fixed_ctx >= 0 || (P.kind == PASS_DRAFT && P.Kx > 0));
   const SeqLimits L = seq_limits(a, b);
+  const int lastk = L.maxlim < a.cap - 1 ? L.maxlim : a.cap - 1;
+  const int nch = lastk >= 0 ? lastk / a.sc + 1 : 0;
+  if (blk ? !has_blk : c >= nch) return;
   int k_begin, k_end;
   if (!blk) {
     k_begin = c * a.sc;
-    if (k_begin > L.maxlim) return;
-    k_end = min(min(k_begin + a.sc, L.maxlim + 1), a.cap);
+    k_end = min(k_begin + a.sc, lastk + 1);
   } else {
     k_begin = 0;
     k_end = a.block_len;
   }
 
-  // query fragments (B operand of S^T = K.Q^T): row qr = rt*16 + lr
-  bf16x8_t qf[AT_MAX_RT_PER_WAVE][4];
-  int lim[AT_MAX_RT_PER_WAVE], seesb[AT_MAX_RT_PER_WAVE];
-  floatx4_t oacc[AT_MAX_RT_PER_WAVE][8];
-  float mrow[AT_MAX_RT_PER_WAVE], lrow[AT_MAX_RT_PER_WAVE];
+  // this wave's query tile: row qr = rt*16 + lr (B operand of S^T = K.Q^T)
+  const int rt = rg * 4 + wave;
+  const int qr = rt * 16 + lr;
+  const bool wact = rt < NRT;                 // uniform per wave
+  bf16x8_t qf[4];
+  int lim = -1, seesb = 0;
+  floatx4_t oacc[8];
+  float mrow = -INFINITY, lrow = 0.f;
 #pragma unroll
-  for (int j = 0; j < AT_MAX_RT_PER_WAVE; ++j) {
-    int rt = wave + 4 * j;
-    int qr = rt * 16 + lr;
-    lim[j] = -1; seesb[j] = 0;
-    mrow[j] = -INFINITY; lrow[j] = 0.f;
+  for (int db = 0; db < 8; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if (wact && qr < QR) {
+    const int t = qr / G, hh = g * G + (qr - t * G);
+    const int r = row_of(P, b, t);
+    token_view(a, L, t, lim, seesb);
+    const uint16_t* qp = (const uint16_t*)a.q + (size_t)r * H + hh * hd + lq * 8;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) oacc[j][db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    if (rt < NRT && qr < QR) {
-      int t = qr / G, hh = g * G + (qr - t * G);
-      int r = row_of(P, b, t);
-      token_view(a, L, t, lim[j], seesb[j]);
-      const uint16_t* qp = (const uint16_t*)a.q + (size_t)r * H + hh * hd + lq * 8;
+    for (int ds = 0; ds < 4; ++ds) qf[ds] = ld_bf16x8(qp + ds * 32);
+  } else {
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) qf[j][ds] = ld_bf16x8(qp + ds * 32);
-    } else {
-#pragma unroll
-      for (int ds = 0; ds < 4; ++ds) qf[j][ds] = bf16x8_t{};
-    }
+    for (int ds = 0; ds < 4; ++ds) qf[ds] = bf16x8_t{};
   }
 
   const uint16_t* kbase;
@@ -127,43 +131,51 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   }
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
 
-  for (int kt = k_begin; kt < k_end; kt += 64) {
+  // K (64 x 128) and V^T (128 x 64) of one tile: 4 + 4 16-byte pieces per thread
+  uint4 kr[4], vr[4];
+  auto load_tile = [&](int kt) __attribute__((always_inline)) {
     const int nvalid = min(64, k_end - kt);
-    // ---- stage K (64 x 128) and V^T (128 x 64) into LDS, zeroing keys >= nvalid
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int ci = tid + j * 256;
-      int key = ci >> 4, col = (ci & 15) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < nvalid) v = *(const uint4*)(kbase + (size_t)(kt + key) * hd + col);
-      *(uint4*)(sK + key * KT_STRIDE + col) = v;
+      const int ci = tid + j * 256;
+      const int key = ci >> 4, col = (ci & 15) * 8;
+      kr[j] = make_uint4(0, 0, 0, 0);
+      if (key < nvalid) kr[j] = *(const uint4*)(kbase + (size_t)(kt + key) * hd + col);
+      const int d = ci >> 3, vc8 = (ci & 7) * 8;
+      vr[j] = make_uint4(0, 0, 0, 0);
+      if (!blk) vr[j] = *(const uint4*)(vbase + (size_t)(kt >> 6) * 64 * hd + (size_t)d * 64 + vc8);
+      else if (vc8 < a.kpad) vr[j] = *(const uint4*)(vbase + (size_t)d * a.kpad + vc8);
     }
+  };
+  auto store_tile = [&](int kt) __attribute__((always_inline)) {
+    const int nvalid = min(64, k_end - kt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int ci = tid + j * 256;
-      int d = ci >> 3, col = (ci & 7) * 8;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (!blk) {
-        v = *(const uint4*)(vbase + (size_t)(kt >> 6) * 64 * hd + (size_t)d * 64 + col);
-      } else if (col < a.kpad) {
-        v = *(const uint4*)(vbase + (size_t)d * a.kpad + col);
-      }
-      if (nvalid < 64) {
+      const int ci = tid + j * 256;
+      const int key = ci >> 4, col = (ci & 15) * 8;
+      *(uint4*)(sK + key * KT_STRIDE + col) = kr[j];
+      const int d = ci >> 3, vc8 = (ci & 7) * 8;
+      uint4 v = vr[j];
+      if (nvalid < 64) {                 // zero the columns of keys past the end
         uint16_t e[8];
         __builtin_memcpy(e, &v, 16);
 #pragma unroll
         for (int x = 0; x < 8; ++x)
-          if (vt_key(col + x) >= nvalid) e[x] = 0;
+          if (vt_key(vc8 + x) >= nvalid) e[x] = 0;
         __builtin_memcpy(&v, e, 16);
       }
-      *(uint4*)(sV + d * VT_STRIDE + col) = v;
+      *(uint4*)(sV + d * VT_STRIDE + vc8) = v;
     }
-    __syncthreads();
+  };
 
-#pragma unroll
-    for (int j = 0; j < AT_MAX_RT_PER_WAVE; ++j) {
-      int rt = wave + 4 * j;
-      if (rt >= NRT) continue;
+  load_tile(k_begin);
+  for (int kt = k_begin; kt < k_end; kt += 64) {
+    const int nvalid = min(64, k_end - kt);
+    __syncthreads();                     // the previous tile is no longer read
+    store_tile(kt);
+    __syncthreads();
+    if (kt + 64 < k_end) load_tile(kt + 64);
+    if (wact) {
       // S^T for 4 blocks of 16 keys
       floatx4_t s[4];
 #pragma unroll
@@ -172,7 +184,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int ds = 0; ds < 4; ++ds) {
           bf16x8_t kf = ld_bf16x8(sK + (kb * 16 + lr) * KT_STRIDE + ds * 32 + lq * 8);
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[j][ds], s[kb], 0, 0, 0);
+          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ds], s[kb], 0, 0, 0);
         }
       }
       // mask by selection and scale to base 2
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           int kl = kb * 16 + lq * 4 + i;
-          bool ok = kl < nvalid && (blk ? seesb[j] != 0 : (kt + kl) <= lim[j]);
+          bool ok = kl < nvalid && (blk ? seesb != 0 : (kt + kl) <= lim);
           float v = ok ? s[kb][i] * sl2 : -INFINITY;
           s[kb][i] = v;
           mt = fmaxf(mt, v);
@@ -192,10 +204,10 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       // Branch-free update: the MFMAs below read operands from every lane,
       // so no lane may skip them.  A row with nothing visible yet keeps
       // m = -inf, l = 0, o = 0 exactly (alpha = 1, p = 0).
-      const float mnew = fmaxf(mrow[j], mt);
+      const float mnew = fmaxf(mrow, mt);
       const bool any = mnew != -INFINITY;
       const float mref = any ? mnew : 0.f;
-      const float alpha = any ? exp2f(mrow[j] - mref) : 1.f;
+      const float alpha = any ? exp2f(mrow - mref) : 1.f;
       // P enters the P.V product as two bf16 terms, hi = bf16(p) and
       // lo = bf16(p - hi) (p - hi is exact in fp32), so the product carries
       // about 16 significant bits of p instead of 8.  Rounding p itself to
@@ -215,11 +227,11 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
         }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      lrow[j] = lrow[j] * alpha + ps;
-      mrow[j] = any ? mnew : mrow[j];
+      lrow = lrow * alpha + ps;
+      mrow = any ? mnew : mrow;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        floatx4_t o = oacc[j][db];
+        floatx4_t o = oacc[db];
         o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -227,33 +239,37 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
           o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks], o, 0, 0, 0);
           o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[ks], o, 0, 0, 0);
         }
-        oacc[j][db] = o;
+        oacc[db] = o;
       }
     }
-    __syncthreads();
   }
 
-  // partials: opart[((b*hkv+g)*(nc+1)+c)*qr_max + qr][d], ml[...][2]
-  const size_t pbase = ((size_t)(b * a.hkv + g) * (a.nc + 1) + c) * a.qr_max;
+  // ---- partial of this chunk: opart[((b*hkv+g)*(nc+1)+c)*qr_max + qr][d],
+  // ml[...][2]
+  if (wact && qr < QR) {
+    const size_t pi = ((size_t)(b * a.hkv + g) * (a.nc + 1) + c) * a.qr_max + qr;
+    float* op = a.opart + pi * hd;
 #pragma unroll
-  for (int j = 0; j < AT_MAX_RT_PER_WAVE; ++j) {
-    int rt = wave + 4 * j;
-    int qr = rt * 16 + lr;
-    if (rt >= NRT || qr >= QR) continue;
-    float* op = a.opart + (pbase + qr) * hd;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) *(floatx4_t*)(op + db * 16 + lq * 4) = oacc[j][db];
+    for (int db = 0; db < 8; ++db) *(floatx4_t*)(op + db * 16 + lq * 4) = oacc[db];
     if (lq == 0) {
-      a.ml[(pbase + qr) * 2 + 0] = mrow[j];
-      a.ml[(pbase + qr) * 2 + 1] = lrow[j];
+      a.ml[pi * 2 + 0] = mrow;
+      a.ml[pi * 2 + 1] = lrow;
     }
   }
 }
 
-// Fold the chunk partials of one (row, query head) in increasing chunk
-// order, then the block chunk for rows that see the draft block.
-__global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
-  const int r = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+// Combine the chunk partials of one (row, query head); one wave each, four
+// per block.  Phase 1: the maximum M of the chunk maxima the row sees (its
+// cache chunks, then the block chunk).  Phase 2: l = sum_c l_c 2^(m_c - M)
+// and o = sum_c o_c 2^(m_c - M), summed in increasing chunk order (block
+// last).  All loads of a phase are independent, so the merge costs two
+// memory round trips; the result depends only on the row's own partials.
+__global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
+  __shared__ float sw[4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + wave;
+  if (pair >= npairs) return;
+  const int r = pair / a.hq, h = pair - r * a.hq;
   const PassInfo& P = a.P;
   const int hd = a.hd, G = a.hq / a.hkv, g = h / G;
   int b, t;
@@ -266,45 +282,73 @@ __global__ __launch_bounds__(64) void k_attn_merge(AttnArgs a) {
   const SeqLimits L = seq_limits(a, b);
   int limit, sees;
   token_view(a, L, t, limit, sees);
+  const bool has_blk = a.block_len > 0 && (a.fixed_ctx >= 0 || (P.kind == PASS_DRAFT && P.Kx > 0));
   const int qr = t * G + (h - g * G);
   if (limit >= a.cap) limit = a.cap - 1;
-  const int nchunks = limit >= 0 ? limit / a.sc + 1 : 0;
-  float m = -INFINITY, l = 0.f;
-  float o0 = 0.f, o1 = 0.f;
+  const int nrow = limit >= 0 ? limit / a.sc + 1 : 0;
+  const int ntot = nrow + ((sees && has_blk) ? 1 : 0);   // partials this row folds
   const size_t sbase = (size_t)(b * a.hkv + g) * (a.nc + 1);
-  for (int c = 0; c <= nchunks; ++c) {
-    int cc = c;
-    if (c == nchunks) {
-      if (!(sees && a.block_len > 0)) break;
-      cc = a.nc;
+  auto pidx = [&](int j) { return (sbase + (j < nrow ? j : a.nc)) * a.qr_max + qr; };
+  // phase 1: maxima (64 partials per pass over the lanes)
+  float M = -INFINITY;
+  for (int j0 = 0; j0 < ntot; j0 += 64) {
+    const int j = j0 + lane;
+    const float mc = j < ntot ? a.ml[pidx(j) * 2] : -INFINITY;
+    M = fmaxf(M, mc);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  // phase 2: weights 2^(m_c - M) (0 for fully masked partials), then sums
+  float l = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int j0 = 0; j0 < ntot; j0 += 64) {
+    const int j = j0 + lane;
+    float wgt = 0.f, lw = 0.f;
+    if (j < ntot) {
+      const size_t pi = pidx(j);
+      const float mc = a.ml[pi * 2], lc = a.ml[pi * 2 + 1];
+      wgt = mc == -INFINITY ? 0.f : exp2f(mc - M);
+      lw = lc * wgt;
     }
-    size_t pi = (sbase + cc) * a.qr_max + qr;
-    float mc = a.ml[pi * 2], lc = a.ml[pi * 2 + 1];
-    if (mc == -INFINITY) continue;
-    float mn = fmaxf(m, mc);
-    float al = exp2f(m - mn), be = exp2f(mc - mn);
-    const float* op = a.opart + pi * hd;
-    l = l * al + lc * be;
-    o0 = o0 * al + op[lane * 2] * be;
-    o1 = o1 * al + op[lane * 2 + 1] * be;
-    m = mn;
+    sw[wave][lane] = wgt;
+    // l in chunk order: gather the 64 products on every lane, add in order
+    const int n = min(64, ntot - j0);
+    float lws[1];
+    lws[0] = lw;
+    for (int k = 0; k < n; ++k) l += __shfl(lws[0], k, 64);
+    __builtin_amdgcn_wave_barrier();
+    // o: lane owns dimensions 2 lane, 2 lane + 1; loads in batches of 8
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[u] = k0 + u < n ? *(const float2*)(a.opart + pidx(j0 + k0 + u) * hd + lane * 2)
+                          : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (k0 + u < n) {
+          const float wu = sw[wave][k0 + u];
+          o0 += v[u].x * wu;
+          o1 += v[u].y * wu;
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
-  float inv = 1.0f / l;
-  size_t ob = (size_t)r * a.hq * hd + (size_t)h * hd + lane * 2;
-  uint16_t y0 = f2bf(o0 * inv), y1 = f2bf(o1 * inv);
-  ((uint16_t*)a.out)[ob] = y0;
-  ((uint16_t*)a.out)[ob + 1] = y1;
-  if (a.tap && r < a.tap_rows) {
-    ((uint16_t*)a.tap)[ob] = y0;
-    ((uint16_t*)a.tap)[ob + 1] = y1;
-  }
+  const float inv = 1.0f / l;
+  const size_t ob = (size_t)r * a.hq * hd + (size_t)h * hd + lane * 2;
+  const uint32_t y = (uint32_t)f2bf(o0 * inv) | ((uint32_t)f2bf(o1 * inv) << 16);
+  *(uint32_t*)((uint16_t*)a.out + ob) = y;
+  if (a.tap && r < a.tap_rows) *(uint32_t*)((uint16_t*)a.tap + ob) = y;
 }
 
 void launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   const int B = a.P.B;
-  hipLaunchKernelGGL(k_attn_bf16, dim3(a.nc + 1, a.hkv, B), dim3(256), 0, s, a);
-  int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
-  hipLaunchKernelGGL(k_attn_merge, dim3(rows, a.hq), dim3(64), 0, s, a);
+  const int T = a.fixed_ctx >= 0 ? a.P.Kx : a.P.tokens_per_seq();
+  const int nrg = attn_row_groups(T * (a.hq / a.hkv));
+  hipLaunchKernelGGL(k_attn_bf16, dim3(a.nc + 1, a.hkv, B * nrg), dim3(256), 0, s, a);
+  const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
+  const int npairs = rows * a.hq;
+  hipLaunchKernelGGL(k_attn_merge, dim3((npairs + 3) / 4), dim3(256), 0, s, a, npairs);
 }
 
 // ------------------------------------------------------------- fp32

@@ -37,15 +37,12 @@ void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, 
 
 // ----------------------------------------------------------- embedding
 // h[row] = E[token] (token rows) or the mask embedding (mask rows); padding
-// rows get zeros.  With ss != NULL also writes the per-128-column sums of
-// squares of the row (wave w sums columns 128c + lane and 128c + 64 + lane,
-// then a fixed butterfly), the input of the next fused RMSNorm.
+// rows get zeros.
 __global__ __launch_bounds__(256) void k_embed(PassInfo P, const int32_t* __restrict__ anchor_tok,
                                                const int32_t* __restrict__ block_tok, int block_ld,
                                                const void* __restrict__ embed,
                                                const void* __restrict__ mask_emb, int V, int d,
-                                               int bf16, float* __restrict__ h,
-                                               float* __restrict__ ss) {
+                                               int bf16, float* __restrict__ h) {
   const int r = blockIdx.x;
   int kind;          // 0 token, 1 mask, 2 padding
   int tok = 0;
@@ -74,25 +71,69 @@ __global__ __launch_bounds__(256) void k_embed(PassInfo P, const int32_t* __rest
     }
     out[i] = v;
   }
-  if (!ss) return;
-  __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nss = d / 128;
-  for (int c = wave; c < nss; c += 4) {
-    float x1 = out[c * 128 + lane], x2 = out[c * 128 + 64 + lane];
-    float t = x1 * x1 + x2 * x2;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o, 64);
-    if (lane == 0) ss[(size_t)r * nss + c] = t;
-  }
 }
 
 void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
                   int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
-                  float* h, float* ss, hipStream_t s) {
+                  float* h, hipStream_t s) {
   int rows = P.rows();
   if (rows <= 0) return;
   hipLaunchKernelGGL(k_embed, dim3(rows), dim3(256), 0, s, P, anchor_tok, block_tok, block_ld,
-                     embed, mask_emb, V, d, (int)bf16, h, ss);
+                     embed, mask_emb, V, d, (int)bf16, h);
+}
+
+// ------------------------------------------------- RMSNorm -> bf16 rows
+// out[r] = bf16(h[r] / rms(h[r]) * g), the bf16 input of the next GEMM.  One
+// 256-thread block per row; thread t owns the float4 groups t, t + 256, ...
+// (all loaded before use).  Its sum of squares runs over its groups in
+// order, then a fixed butterfly inside the wave and the four wave sums in
+// wave order: the result depends only on the row.
+template <int NV>
+__global__ __launch_bounds__(256) void k_rownorm_bf16(const float* __restrict__ h, int d,
+                                                      const uint16_t* __restrict__ gain, float eps,
+                                                      uint16_t* __restrict__ out) {
+  __shared__ float red[4];
+  const int r = blockIdx.x, t = threadIdx.x;
+  const float* x = h + (size_t)r * d;
+  float4 v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = (j * 256 + t) * 4;
+    v[j] = i < d ? *(const float4*)(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = (j * 256 + t) * 4;
+    if (i < d) {
+      const uint2 g = *(const uint2*)(gain + i);
+      const float g0 = __uint_as_float(g.x << 16), g1 = __uint_as_float(g.x & 0xffff0000u);
+      const float g2 = __uint_as_float(g.y << 16), g3 = __uint_as_float(g.y & 0xffff0000u);
+      uint2 o;
+      o.x = (uint32_t)f2bf(v[j].x * inv * g0) | ((uint32_t)f2bf(v[j].y * inv * g1) << 16);
+      o.y = (uint32_t)f2bf(v[j].z * inv * g2) | ((uint32_t)f2bf(v[j].w * inv * g3) << 16);
+      *(uint2*)(out + (size_t)r * d + i) = o;
+    }
+  }
+}
+
+// d a multiple of 4, at most 8192
+void launch_rownorm_bf16(const float* h, int rows, int d, const uint16_t* gain, float eps,
+                         uint16_t* out, hipStream_t s) {
+  if (rows <= 0) return;
+  const int nv = (d + 1023) / 1024;
+  if (nv <= 1) hipLaunchKernelGGL(k_rownorm_bf16<1>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
+  else if (nv <= 2) hipLaunchKernelGGL(k_rownorm_bf16<2>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
+  else if (nv <= 4) hipLaunchKernelGGL(k_rownorm_bf16<4>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
+  else hipLaunchKernelGGL(k_rownorm_bf16<8>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
 }
 
 // -------------------------------------------------------------- RMSNorm

@@ -4,31 +4,38 @@
 // bf16 path (MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulation).
 //  * Operands: the packed weight is the A operand (16 output features x 32
 //    k per 1 KB fragment, one coalesced wave load); the activations are the
-//    B operand, staged once per workgroup into LDS in fragment order.
-//  * Work split: a workgroup owns 128 output columns (8 waves x 16) and up
-//    to 64 rows.  K is cut into 8 equal slices.  Each slice is a chain of
-//    MFMAs in increasing k starting from zero; the 8 slice sums are added
-//    in slice order, ((s0+s1)+s2)+...+s7.  Narrow GEMMs
-//    give every slice its own workgroup (8x the workgroups, to stream the
-//    weights with the whole chip) and the last workgroup of a column group
-//    adds the partials; wide GEMMs keep all slices in one workgroup.  Both
-//    produce the same bits, and nothing in the order depends on the number
-//    of rows -- a row's output is identical whether computed alone (plain
-//    decoding), as the anchor of a draft block or as one of K verify rows.
-//  * Prologue: an input that is RMSNorm(h) is normalised while staging
-//    (1/rms from per-128-column partial sums of squares, added in order).
+//    B operand, staged into LDS in fragment order.
+//  * Arithmetic: K is cut into 8 equal slices.  Each slice is a chain of
+//    MFMAs in increasing k starting from zero; the 8 slice sums are added in
+//    slice order, ((s0+s1)+s2)+...+s7.  Nothing in this order depends on the
+//    number of rows, how the work is split or which rows share a launch, so
+//    a row's output is identical whether computed alone (plain decoding), as
+//    the anchor of a draft block or as one of K verify rows.
+//  * Work split: a wave owns one 16-column tile; a workgroup of WV waves
+//    owns WV*16 columns and up to 64 rows.  Narrow GEMMs (fewer than 128
+//    groups of 128 columns) give every K slice its own workgroup and the
+//    last workgroup of a column group adds the 8 partials; wide GEMMs keep
+//    all slices in one workgroup.
+//  * Streaming: every wave keeps D weight fragments in flight in a register
+//    ring.  Activations are staged 512 k at a time; the next stage is loaded
+//    into registers one stage ahead, so waiting for it never waits for weight
+//    loads issued after it (memory counters complete in order).
+//  * Input: bf16 rows (RMSNorm outputs, attention output, SwiGLU product).
 //  * Epilogues: QK-norm + RoPE + KV placement (QKV projection; a column
-//    group is one head), residual add + partial sums of squares for the
-//    next RMSNorm (O and down projections), SwiGLU (gate/up), and per-row
+//    group is one head), residual add (O and down projections), SwiGLU
+//    (gate/up), and per-row
 //    argmax with lowest-index ties (LM head; the grid's last workgroup
 //    turns the partials into tokens).
 //
 // fp32 path: one thread per output with a sequential k loop (check models).
 #include "internal.h"
 
+
 #define NSL 8                 // K slices
-#define WAVES 8
-#define COLS 128              // output columns per workgroup
+#define SKB 16                // k-blocks of 32 per activation stage
+#define BUF_FLAGS 0x00020000  // buffer descriptor word 3: 32-bit data format
+#define BUF_NT 2              // cache policy: nontemporal (streamed once)
+#define OOR 0x40000000        // buffer offset past every descriptor's range
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t r;
@@ -64,26 +71,28 @@ __device__ __forceinline__ void amax_comb(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
-template <int MT, int EP, int SPW>
-__global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
-  // LDS: activation block in fragment order (MT*16 rows x 512 k bf16), reused
-  // by the epilogue as an fp32 tile of MT*16 x 128.
-  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * 512];
-  __shared__ float sInv[64];
-  __shared__ float sRed[WAVES * 64];
-  __shared__ int sIdx[WAVES * 64];
+template <int MT, int EP, int WV, bool SPLIT>
+__global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf16(GemmArgs a) {
+  constexpr int NT = WV * 64;
+  constexpr int COLS = WV * 16;
+  constexpr int NFR = MT * SKB;               // activation fragments per stage
+  constexpr int NF = (NFR + WV - 1) / WV;     // ... per wave
+  // LDS: one activation stage in fragment order [mt][k-block][lane][8]; it
+  // also holds the fp32 output tile (MT*16 x COLS) in the epilogue.
+  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * SKB * 32];
+  __shared__ float sRed[WV * 64];
+  __shared__ int sIdx[WV * 64];
   __shared__ int sLast;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
-  const int KB = a.K >> 5;                   // k-blocks of 32
-  const int KS = a.K / NSL;                  // slice length
-  const int CL = KS < 256 ? KS : 256;        // k per LDS chunk
-  const int CLB = CL >> 5;                   // k-blocks per chunk (<= 8)
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = a.K >> 5;                    // k-blocks of 32
+  const int KSB = KB / NSL;                   // k-blocks per slice
   const int ngroups = a.N / COLS;
   int ng, s_first;
-  if (SPW == NSL) {
+  if (!SPLIT) {
     ng = blockIdx.x; s_first = 0;
-  } else if ((ngroups & 7) == 0) {           // keep a column group's slices on one XCD
+  } else if ((ngroups & 7) == 0) {            // keep a column group's slices on one XCD
     const int id = blockIdx.x;
     s_first = (id >> 3) & 7;
     ng = ((id >> 6) << 3) | (id & 7);
@@ -91,22 +100,54 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
     s_first = blockIdx.x % NSL;
     ng = blockIdx.x / NSL;
   }
-  const int m0 = blockIdx.y * 64;            // GEMM-local first row of this workgroup
-  const int nbk = ng * WAVES + wave;         // this wave's 16-column block
-  const u32x4_t* wp = a.W + (size_t)nbk * KB * 64 + lane;
+  const int m0 = blockIdx.y * 64;             // GEMM-local first row of this workgroup
+  const int kb_lo = SPLIT ? s_first * KSB : 0;
+  const int nkb = SPLIT ? KSB : KB;           // k-blocks of this workgroup
+  const int nbk = ng * WV + wave;             // this wave's 16-column tile
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + ((size_t)nbk * KB + kb_lo) * 64), (short)0, nkb * 1024, BUF_FLAGS);
 
-  // 1/rms of every row (normalised-input GEMMs): partial sums added in order
-  if (a.h && tid < MT * 16) {
-    int r = m0 + tid;
-    float inv = 0.f;
-    if (r < a.M) {
-      const float* ss = a.ss + (size_t)(a.row0 + r) * a.nss;
-      float t = 0.f;
-      for (int j = 0; j < a.nss; ++j) t += ss[j];
-      inv = 1.0f / sqrtf(t / (float)a.dn + a.eps);
+  // stage st: k-blocks [st*SKB, st*SKB + SKB) of this workgroup's range; the
+  // lane of fragment (mt, j) holds row mt*16 + lr, k = 32 j + 8 lq .. + 7.
+  // Activations and weights are read with buffer loads whose descriptors
+  // cover exactly the valid rows / this wave's k-range: out-of-range loads
+  // return zero without touching memory, so every load is issued
+  // unconditionally, the number of loads between a ring load and its use
+  // never depends on the data, and the memory-counter waits stay exact.
+  const int vrows = a.M - m0 < 64 ? a.M - m0 : 64;           // valid rows of this workgroup
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + (size_t)(a.row0 + m0) * a.ldx), (short)0, vrows * a.ldx * 2, BUF_FLAGS);
+  const int a_vo = lr * a.ldx * 2 + lq * 16;                  // lane part of the offset
+  u32x4_t sr[NF];
+  auto load_stage = [&](int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int fr = (wave + f * WV) % NFR;
+      const int mt = fr / SKB, kbl = st * SKB + fr % SKB;
+      // k-blocks past this workgroup's range are pushed out of the
+      // descriptor (range checks apply to the VGPR offset)
+      const int so = kbl < nkb ? (mt * 16 * a.ldx + (kb_lo + kbl) * 32) * 2 : OOR;
+      sr[f] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo + so, 0, 0);
     }
-    sInv[tid] = inv;
-  }
+  };
+  auto write_stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int fr = wave + f * WV;
+      if (fr < NFR) *(u32x4_t*)(sX + ((size_t)fr * 64 + lane) * 8) = sr[f];
+    }
+  };
+  const int nst = (nkb + SKB - 1) / SKB;      // activation stages
+  load_stage(0);
+  // weight ring: slot i holds k-block st*SKB + i of the stage being computed;
+  // loads past this wave's k-range fall outside the descriptor (zero, no
+  // memory access)
+  u32x4_t w[SKB];
+#pragma unroll
+  for (int i = 0; i < SKB; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + i * 1024, 0, BUF_NT);
+
+  write_stage();
+  __syncthreads();
 
   floatx4_t cur[MT], tot[MT];
 #pragma unroll
@@ -114,92 +155,37 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
     cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     tot[mt] = cur[mt];
   }
-
-  // Weights stream in chunks of CLB k-blocks into two register sets, loaded
-  // two chunks ahead; activations are staged into LDS in blocks of SAB
-  // k-blocks (up to 512 k), so the weight loads stay in flight across the
-  // staging barriers.
-  const int nchunk_slice = KS / CL;
-  const int nchunks = nchunk_slice * SPW;
-  const int kbase0 = s_first * KS;
-  const int SAB = (KS >> 5) < 16 ? (KS >> 5) : 16;   // staged k-blocks
-  u32x4_t wA[8], wB[8];
-  auto wload = [&](u32x4_t (&w)[8], int c) {
-    const int kb = (kbase0 >> 5) + c * CLB;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < CLB) w[j] = __builtin_nontemporal_load(wp + (size_t)(kb + j) * 64);
-  };
-#pragma unroll
-  for (int j = 0; j < 8; ++j) { wA[j] = u32x4_t{0u, 0u, 0u, 0u}; wB[j] = wA[j]; }
-  wload(wA, 0);
-  if (nchunks > 1) wload(wB, 1);
-
-  auto stage = [&](int kb0) {        // stage k-blocks [kb0, kb0 + SAB) of the activations
-    __syncthreads();
-    const int k0 = kb0 * 32;
-    const int units = MT * 16 * SAB * 4;      // 16-byte units
-    for (int u = tid; u < units; u += 512) {
-      int row = u / (SAB * 4), kq = u - row * (SAB * 4);
-      int kb = kq >> 2, q = kq & 3;
-      int r = m0 + row;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (r < a.M) {
-        int prw = a.row0 + r;
-        if (a.h) {
-          const float* hp = a.h + (size_t)prw * a.dn + k0 + kq * 8;
-          float4 x0 = *(const float4*)hp, x1 = *(const float4*)(hp + 4);
-          uint16_t g[8];
-          *(u32x4_t*)g = *(const u32x4_t*)(a.gain + k0 + kq * 8);
-          float inv = sInv[row];
-          uint16_t e[8];
-          e[0] = f2bf(x0.x * inv * bf2f(g[0])); e[1] = f2bf(x0.y * inv * bf2f(g[1]));
-          e[2] = f2bf(x0.z * inv * bf2f(g[2])); e[3] = f2bf(x0.w * inv * bf2f(g[3]));
-          e[4] = f2bf(x1.x * inv * bf2f(g[4])); e[5] = f2bf(x1.y * inv * bf2f(g[5]));
-          e[6] = f2bf(x1.z * inv * bf2f(g[6])); e[7] = f2bf(x1.w * inv * bf2f(g[7]));
-          __builtin_memcpy(&v, e, 16);
-        } else {
-          v = *(const u32x4_t*)(a.X + (size_t)prw * a.ldx + k0 + kq * 8);
-        }
-      }
-      int mt = row >> 4, ln = q * 16 + (row & 15);
-      *(u32x4_t*)(sX + ((size_t)(mt * SAB + kb) * 64 + ln) * 8) = v;
+  // Per stage: switch the LDS stage, prefetch the next one, then SKB MFMA
+  // steps, each refilling its ring slot with the k-block one stage ahead.
+  // The loads are the same on every path.  Past the end of a partial last
+  // stage both operands are zero, so the extra MFMAs add exact zeros.
+  for (int st = 0; st < nst; ++st) {
+    if (st > 0) {
+      __syncthreads();                 // every wave is done with the previous stage
+      write_stage();
+      __syncthreads();
     }
-    __syncthreads();
-  };
-  auto compute = [&](const u32x4_t (&w)[8], int c) {
-    const int kbl = (c * CLB) % SAB;           // first k-block of the chunk inside the stage
+    load_stage(st + 1);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < CLB) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SAB + kbl + j) * 64 + lane) * 8);
-          cur[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[j]), as_bf16x8(xv),
-                                                            cur[mt], 0, 0, 0);
-        }
-      }
-    }
-    if (SPW == NSL && (c + 1) % nchunk_slice == 0) {   // slice done: add in slice order
-      const int s = (c + 1) / nchunk_slice - 1;
+    for (int i = 0; i < SKB; ++i) {
+      const int kk = st * SKB + i;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        tot[mt] = s == 0 ? cur[mt] : add4(tot[mt], cur[mt]);
-        cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        const u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SKB + i) * 64 + lane) * 8);
+        cur[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[i]), as_bf16x8(xv),
+                                                          cur[mt], 0, 0, 0);
+      }
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + (kk + SKB) * 1024, 0, BUF_NT);
+      if (!SPLIT && kk < nkb && (kk + 1) % KSB == 0) {   // slice done: add in slice order
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          tot[mt] = kk + 1 == KSB ? cur[mt] : add4(tot[mt], cur[mt]);
+          cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
-  };
-  for (int c = 0; c < nchunks; c += 2) {
-    if ((c * CLB) % SAB == 0) stage((kbase0 >> 5) + c * CLB);
-    compute(wA, c);
-    if (c + 2 < nchunks) wload(wA, c + 2);
-    if (c + 1 < nchunks) {
-      if (((c + 1) * CLB) % SAB == 0) stage((kbase0 >> 5) + (c + 1) * CLB);
-      compute(wB, c + 1);
-      if (c + 3 < nchunks) wload(wB, c + 3);
-    }
   }
-  if (SPW == NSL) {
+  if (!SPLIT) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) cur[mt] = tot[mt];
   }
@@ -208,14 +194,14 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
   // The partials and counters use agent-scope (coherent) stores and loads; an
   // explicit wait for the stores plus the barrier orders them before the
   // counter increment, so no L2 writeback is needed.
-  if (SPW == 1) {
+  if (SPLIT) {
     // partial layout [slice][m-group][col group][mt][wave][i][lane]: each
     // coherent dword store of a wave covers 256 contiguous bytes
-    const size_t pstride = (size_t)gridDim.y * ngroups * MT * WAVES * 256;
-    float* pbase = a.part + ((size_t)blockIdx.y * ngroups + ng) * MT * WAVES * 256;
+    const size_t pstride = (size_t)gridDim.y * ngroups * MT * WV * 256;
+    float* pbase = a.part + ((size_t)blockIdx.y * ngroups + ng) * MT * WV * 256;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float* pp = pbase + s_first * pstride + ((size_t)mt * WAVES + wave) * 256 + lane;
+      float* pp = pbase + s_first * pstride + ((size_t)mt * WV + wave) * 256 + lane;
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_agent(pp + i * 64, cur[mt][i]);
     }
@@ -235,9 +221,13 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
       floatx4_t p[NSL];
 #pragma unroll
       for (int s = 0; s < NSL; ++s) {
-        const float* pp = pbase + s * pstride + ((size_t)mt * WAVES + wave) * 256 + lane;
+        const float* pp = pbase + s * pstride + ((size_t)mt * WV + wave) * 256 + lane;
+        if (s == s_first) {
+          p[s] = cur[mt];
+        } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[s][i] = ld_agent(pp + i * 64);
+          for (int i = 0; i < 4; ++i) p[s][i] = ld_agent(pp + i * 64);
+        }
       }
       floatx4_t t = p[0];
 #pragma unroll
@@ -251,28 +241,16 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
   float* tile = (float*)sX;                  // [MT*16][COLS] fp32 scratch
   __syncthreads();
   if (EP == EP_RESID) {
-    // h += y; per-row sum of squares of the new values over this column group
+    // h += y
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      int r = m0 + mt * 16 + lr;
-      float sq = 0.f;
+      const int r = m0 + mt * 16 + lr;
       if (r < a.M) {
         float* yp = a.y + (size_t)(a.row0 + r) * a.ldy + nbk * 16 + lq * 4;
         float4 o = *(float4*)yp;
         o.x += cur[mt][0]; o.y += cur[mt][1]; o.z += cur[mt][2]; o.w += cur[mt][3];
         *(float4*)yp = o;
-        sq = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
       }
-      sq += __shfl_xor(sq, 16, 64);
-      sq += __shfl_xor(sq, 32, 64);
-      if (lq == 0) sRed[wave * 64 + mt * 16 + lr] = sq;
-    }
-    __syncthreads();
-    if (tid < MT * 16 && m0 + tid < a.M) {
-      float t = 0.f;
-#pragma unroll
-      for (int w = 0; w < WAVES; ++w) t += sRed[w * 64 + tid];
-      a.ss_out[(size_t)(a.row0 + m0 + tid) * a.nss_out + ng] = t;
     }
     return;
   }
@@ -290,7 +268,7 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
         int r = m0 + mt * 16 + lr;
         if (r >= a.M) continue;
         floatx4_t u = *(const floatx4_t*)(tile + ((mt * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4);
-        int j = (ng * 4 + (wave >> 1)) * 16 + lq * 4;
+        int j = (ng * (WV / 2) + (wave >> 1)) * 16 + lq * 4;
         uint16_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[mt][i]) * u[i]);
@@ -321,7 +299,7 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
     if (tid < MT * 16 && m0 + tid < a.M) {
       float bv = sRed[tid];
       int bi = sIdx[tid];
-      for (int w = 1; w < WAVES; ++w) amax_comb(bv, bi, sRed[w * 64 + tid], sIdx[w * 64 + tid]);
+      for (int w = 1; w < WV; ++w) amax_comb(bv, bi, sRed[w * 64 + tid], sIdx[w * 64 + tid]);
       float2* ap = a.amax + (size_t)(a.row0 + m0 + tid) * ngroups + ng;
       st_agent(&ap->x, bv);
       st_agent(&ap->y, __int_as_float(bi));
@@ -338,7 +316,7 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
     }
     __syncthreads();
     if (!sLast) return;
-    for (int r = wave; r < a.M; r += WAVES) {
+    for (int r = wave; r < a.M; r += WV) {
       const int prow = a.row0 + r;
       const float2* pp = a.amax + (size_t)prow * ngroups;
       float bv = -INFINITY;
@@ -378,7 +356,7 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
     const int hd = 128, half = 64;
     const bool isq = ng < a.hq, isk = !isq && ng < a.hq + a.hkv;
     const int head = isq ? ng : (isk ? ng - a.hq : ng - a.hq - a.hkv);
-    for (int rl = wave; rl < MT * 16; rl += WAVES) {
+    for (int rl = wave; rl < MT * 16; rl += WV) {
       const int r = m0 + rl;
       if (r >= a.M) break;
       const int prow = a.row0 + r;
@@ -430,39 +408,46 @@ __global__ __launch_bounds__(512, 4) void k_gemm_bf16(GemmArgs a) {
   }
 }
 
-template <int EP, int SPW>
+template <int EP, int WV, bool SPLIT>
 static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
+  const dim3 block(WV * 64);
   switch (MT) {
-    case 1: hipLaunchKernelGGL((k_gemm_bf16<1, EP, SPW>), grid, dim3(512), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, SPW>), grid, dim3(512), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, SPW>), grid, dim3(512), 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<4, EP, SPW>), grid, dim3(512), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm_bf16<1, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT>), grid, block, 0, s, a); break;
   }
 }
 
-int gemm_bf16_groups(int N) { return N / COLS; }
+int gemm_bf16_groups(int N) { return N / 128; }
 
+// Shape rules: N a multiple of 128, K a multiple of 256 (8 slices of whole
+// k-blocks).
 void launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0) return;
   const int MT = a.M >= 64 ? 4 : (a.M + 15) / 16;
-  const int ng = a.N / COLS;
-  bool wide = ng >= 128;                     // enough workgroups without splitting K
-  if (a.split == 1) wide = false;
-  if (a.split == 2) wide = true;
-  dim3 grid(wide ? ng : ng * NSL, (a.M + 63) / 64);
+  const dim3 gy(1, (a.M + 63) / 64);
+  const bool wide = a.N / 128 >= 128;      // enough workgroups without splitting K
+  if (!wide) {
+    const dim3 grid(a.N / 128 * NSL, gy.y);
+    switch (a.ep) {
+      case EP_RESID: dispatch_mt<EP_RESID, 8, true>(MT, grid, a, s); break;
+      case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
+      case EP_QKV: dispatch_mt<EP_QKV, 8, true>(MT, grid, a, s); break;
+      default: dispatch_mt<EP_ARGMAX, 8, true>(MT, grid, a, s); break;
+    }
+    return;
+  }
   switch (a.ep) {
-    case EP_RESID:
-      if (wide) dispatch_mt<EP_RESID, NSL>(MT, grid, a, s); else dispatch_mt<EP_RESID, 1>(MT, grid, a, s);
-      break;
     case EP_SWIGLU:
-      if (wide) dispatch_mt<EP_SWIGLU, NSL>(MT, grid, a, s); else dispatch_mt<EP_SWIGLU, 1>(MT, grid, a, s);
+      // 96-column workgroups when they divide N: the Qwen3-8B gate/up GEMM
+      // (N = 24576) then has exactly one workgroup per compute unit
+      if ((a.N / 16) % 6 == 0 && MT <= 3) dispatch_mt<EP_SWIGLU, 6, false>(MT, dim3(a.N / 96, gy.y), a, s);
+      else dispatch_mt<EP_SWIGLU, 8, false>(MT, dim3(a.N / 128, gy.y), a, s);
       break;
-    case EP_QKV:
-      if (wide) dispatch_mt<EP_QKV, NSL>(MT, grid, a, s); else dispatch_mt<EP_QKV, 1>(MT, grid, a, s);
-      break;
-    default:
-      if (wide) dispatch_mt<EP_ARGMAX, NSL>(MT, grid, a, s); else dispatch_mt<EP_ARGMAX, 1>(MT, grid, a, s);
-      break;
+    case EP_RESID: dispatch_mt<EP_RESID, 8, false>(MT, dim3(a.N / 128, gy.y), a, s); break;
+    case EP_QKV: dispatch_mt<EP_QKV, 8, false>(MT, dim3(a.N / 128, gy.y), a, s); break;
+    default: dispatch_mt<EP_ARGMAX, 8, false>(MT, dim3(a.N / 128, gy.y), a, s); break;
   }
 }
 
