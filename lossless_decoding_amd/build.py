@@ -11,7 +11,7 @@ SOURCES = ["api.hip", "k_common.hip", "k_gemm.hip", "k_attn.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are disabled for all device code.
-COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 

@@ -170,9 +170,11 @@ void make_layout(const orthrus_config& c, Layout& y) {
     for (int i = 0; i < 4; ++i)
       if (ns[i] / 128 < 128 && (uint64_t)ns[i] > nmax) nmax = ns[i];
     // partials are kept per padded 64-row group: [8][round_up(rows, 64)][N]
-    y.w_part = take(8 * (uint64_t)round_up(y.rmax, 64) * nmax * 4);
+    // (+1 row group: a draft launch splits its rows into two segments)
+    const uint64_t rgroups = (uint64_t)(y.rmax + 63) / 64 + 1;
+    y.w_part = take(8 * rgroups * 64 * nmax * 4);
     // completion counters of the split-K GEMM column groups (+1 grid counter)
-    y.cnt_bytes = ((uint64_t)((y.rmax + 63) / 64) * y.ngroups_max + 1) * 4;
+    y.cnt_bytes = (rgroups * y.ngroups_max + 1) * 4;
     y.w_cnt = take(y.cnt_bytes);
     y.w_amax = take((uint64_t)y.rmax * (y.V / 128) * 8);
   } else {
@@ -229,9 +231,9 @@ struct Tick {
     if (!(c->tmask >> cls & 1u) || c->ev_used * 2 >= (int)c->ev.size()) return;
     i = c->ev_used++;
     c->ev_cls[i] = cls;
-    hipEventRecord(c->ev[2 * i], s);
+    (void)hipEventRecord(c->ev[2 * i], s);
   }
-  ~Tick() { if (i >= 0) hipEventRecord(c->ev[2 * i + 1], s); }
+  ~Tick() { if (i >= 0) (void)hipEventRecord(c->ev[2 * i + 1], s); }
 };
 
 template <typename T> T* W(orthrus_ctx* c, uint64_t off) { return (T*)(c->packed + off); }
@@ -361,6 +363,14 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     g.row0 = row0; g.M = M; g.K = K; g.N = N; g.ep = ep;
     launch_gemm_bf16(g, s);
   };
+  // draft: mask rows [0, BK) with the diffusion weights and the anchor rows
+  // [RM, RM + NA) with the frozen ones, one launch
+  auto run2 = [&](GemmArgs g, uint64_t wd, uint64_t wf, int K, int N, int ep) {
+    g.W = (const u32x4_t*)(c->packed + wd); g.row0 = 0; g.M = BK;
+    g.W2 = (const u32x4_t*)(c->packed + wf); g.row02 = RM; g.M2 = NA;
+    g.K = K; g.N = N; g.ep = ep;
+    launch_gemm_bf16(g, s);
+  };
   for (int l = 0; l < y.L; ++l) {
     const uint64_t E = 2;
     uint16_t* kc = (uint16_t*)(c->kv + (uint64_t)l * y.kv_layer_elems * E);
@@ -380,8 +390,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       g.dkn = (const uint16_t*)(c->packed + y.p_dkn[l]);
       g.kc = kc; g.vc = vc; g.ks = ks; g.vs = vs;
       if (P.kind == PASS_DRAFT) {
-        if (BK > 0) run(g, y.p_dqkv[l], 0, BK, y.d, y.nqkv, EP_QKV);
-        if (NA > 0) run(g, y.p_qkv[l], RM, NA, y.d, y.nqkv, EP_QKV);
+        run2(g, y.p_dqkv[l], y.p_qkv[l], y.d, y.nqkv, EP_QKV);
       } else {
         run(g, y.p_qkv[l], 0, rows, y.d, y.nqkv, EP_QKV);
       }
@@ -405,8 +414,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       GemmArgs g = g0;
       g.X = x; g.ldx = y.qd; g.y = h; g.ldy = y.d;
       if (P.kind == PASS_DRAFT) {
-        if (BK > 0) run(g, y.p_do[l], 0, BK, y.qd, y.d, EP_RESID);
-        if (NA > 0) run(g, y.p_o[l], RM, NA, y.qd, y.d, EP_RESID);
+        run2(g, y.p_do[l], y.p_o[l], y.qd, y.d, EP_RESID);
       } else {
         run(g, y.p_o[l], 0, rows, y.qd, y.d, EP_RESID);
       }
@@ -578,7 +586,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
 
 int orthrus_destroy(orthrus_ctx* ctx) {
   if (!ctx) return ORTHRUS_EINVAL;
-  for (hipEvent_t e : ctx->ev) hipEventDestroy(e);
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   delete ctx;
   return ORTHRUS_OK;
 }
@@ -707,7 +715,7 @@ int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len
 int orthrus_timing_enable(orthrus_ctx* ctx, uint32_t class_mask, int32_t capacity) {
   if (!ctx || capacity < 0) return ORTHRUS_EINVAL;
   if (class_mask && capacity == 0) return ORTHRUS_EINVAL;
-  for (hipEvent_t e : ctx->ev) hipEventDestroy(e);
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
   ctx->ev.clear(); ctx->ev_cls.clear(); ctx->ev_used = 0; ctx->tmask = 0;
   if (!class_mask) return ORTHRUS_OK;
   ctx->ev.resize((size_t)2 * capacity);

@@ -123,6 +123,8 @@ struct GemmOut {                // fp32 path
 struct GemmArgs {
   const u32x4_t* W;             // packed weight (16x32 MFMA fragments)
   int M, K, N, row0;
+  const u32x4_t* W2; int M2, row02;   // optional second segment (other weights and rows)
+  int gy0;                      // row blocks of the first segment (set by the launcher)
   const uint16_t* X; int ldx;   // bf16 input rows
   // split-K partials [8][M][N] and completion counters (zero between launches)
   float* part; unsigned* cnt;

@@ -73,7 +73,6 @@ __device__ __forceinline__ void amax_comb(float& v, int& i, float v2, int i2) {
 
 template <int MT, int EP, int WV, bool SPLIT>
 __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf16(GemmArgs a) {
-  constexpr int NT = WV * 64;
   constexpr int COLS = WV * 16;
   constexpr int NFR = MT * SKB;               // activation fragments per stage
   constexpr int NF = (NFR + WV - 1) / WV;     // ... per wave
@@ -100,12 +99,19 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     s_first = blockIdx.x % NSL;
     ng = blockIdx.x / NSL;
   }
-  const int m0 = blockIdx.y * 64;             // GEMM-local first row of this workgroup
+  // row blocks [0, gy0) belong to segment 0, the rest to segment 1 (its own
+  // weights and rows: the draft pass runs the mask rows' diffusion
+  // projection and the anchor rows' frozen one in one launch)
+  const bool seg1 = (int)blockIdx.y >= a.gy0;
+  const u32x4_t* const Wt = seg1 ? a.W2 : a.W;
+  const int Mr = seg1 ? a.M2 : a.M;
+  const int row0 = seg1 ? a.row02 : a.row0;
+  const int m0 = (seg1 ? blockIdx.y - a.gy0 : blockIdx.y) * 64;   // first row of this workgroup
   const int kb_lo = SPLIT ? s_first * KSB : 0;
   const int nkb = SPLIT ? KSB : KB;           // k-blocks of this workgroup
   const int nbk = ng * WV + wave;             // this wave's 16-column tile
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.W + ((size_t)nbk * KB + kb_lo) * 64), (short)0, nkb * 1024, BUF_FLAGS);
+      (void*)(Wt + ((size_t)nbk * KB + kb_lo) * 64), (short)0, nkb * 1024, BUF_FLAGS);
 
   // stage st: k-blocks [st*SKB, st*SKB + SKB) of this workgroup's range; the
   // lane of fragment (mt, j) holds row mt*16 + lr, k = 32 j + 8 lq .. + 7.
@@ -114,9 +120,9 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   // return zero without touching memory, so every load is issued
   // unconditionally, the number of loads between a ring load and its use
   // never depends on the data, and the memory-counter waits stay exact.
-  const int vrows = a.M - m0 < 64 ? a.M - m0 : 64;           // valid rows of this workgroup
+  const int vrows = Mr - m0 < 64 ? Mr - m0 : 64;           // valid rows of this workgroup
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.X + (size_t)(a.row0 + m0) * a.ldx), (short)0, vrows * a.ldx * 2, BUF_FLAGS);
+      (void*)(a.X + (size_t)(row0 + m0) * a.ldx), (short)0, vrows * a.ldx * 2, BUF_FLAGS);
   const int a_vo = lr * a.ldx * 2 + lq * 16;                  // lane part of the offset
   u32x4_t sr[NF];
   auto load_stage = [&](int st) __attribute__((always_inline)) {
@@ -245,8 +251,8 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = m0 + mt * 16 + lr;
-      if (r < a.M) {
-        float* yp = a.y + (size_t)(a.row0 + r) * a.ldy + nbk * 16 + lq * 4;
+      if (r < Mr) {
+        float* yp = a.y + (size_t)(row0 + r) * a.ldy + nbk * 16 + lq * 4;
         float4 o = *(float4*)yp;
         o.x += cur[mt][0]; o.y += cur[mt][1]; o.z += cur[mt][2]; o.w += cur[mt][3];
         *(float4*)yp = o;
@@ -266,7 +272,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         int r = m0 + mt * 16 + lr;
-        if (r >= a.M) continue;
+        if (r >= Mr) continue;
         floatx4_t u = *(const floatx4_t*)(tile + ((mt * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4);
         int j = (ng * (WV / 2) + (wave >> 1)) * 16 + lq * 4;
         uint16_t o[4];
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
         for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[mt][i]) * u[i]);
         uint2 pk;
         __builtin_memcpy(&pk, o, 8);
-        *(uint2*)(a.act + (size_t)(a.row0 + r) * a.ldact + j) = pk;
+        *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
       }
     }
     return;
@@ -287,8 +293,8 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       int bi = nbk * 16 + lq * 4;
 #pragma unroll
       for (int i = 1; i < 4; ++i) amax_comb(bv, bi, cur[mt][i], nbk * 16 + lq * 4 + i);
-      if (a.logits && r < a.M)
-        *(floatx4_t*)(a.logits + (size_t)(a.row0 + r) * a.ldl + nbk * 16 + lq * 4) = cur[mt];
+      if (a.logits && r < Mr)
+        *(floatx4_t*)(a.logits + (size_t)(row0 + r) * a.ldl + nbk * 16 + lq * 4) = cur[mt];
       float v2 = __shfl_xor(bv, 16, 64); int i2 = __shfl_xor(bi, 16, 64);
       amax_comb(bv, bi, v2, i2);
       v2 = __shfl_xor(bv, 32, 64); i2 = __shfl_xor(bi, 32, 64);
@@ -296,11 +302,11 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       if (lq == 0) { sRed[wave * 64 + mt * 16 + lr] = bv; sIdx[wave * 64 + mt * 16 + lr] = bi; }
     }
     __syncthreads();
-    if (tid < MT * 16 && m0 + tid < a.M) {
+    if (tid < MT * 16 && m0 + tid < Mr) {
       float bv = sRed[tid];
       int bi = sIdx[tid];
       for (int w = 1; w < WV; ++w) amax_comb(bv, bi, sRed[w * 64 + tid], sIdx[w * 64 + tid]);
-      float2* ap = a.amax + (size_t)(a.row0 + m0 + tid) * ngroups + ng;
+      float2* ap = a.amax + (size_t)(row0 + m0 + tid) * ngroups + ng;
       st_agent(&ap->x, bv);
       st_agent(&ap->y, __int_as_float(bi));
     }
@@ -316,8 +322,8 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     }
     __syncthreads();
     if (!sLast) return;
-    for (int r = wave; r < a.M; r += WV) {
-      const int prow = a.row0 + r;
+    for (int r = wave; r < Mr; r += WV) {
+      const int prow = row0 + r;
       const float2* pp = a.amax + (size_t)prow * ngroups;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
@@ -358,8 +364,8 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     const int head = isq ? ng : (isk ? ng - a.hq : ng - a.hq - a.hkv);
     for (int rl = wave; rl < MT * 16; rl += WV) {
       const int r = m0 + rl;
-      if (r >= a.M) break;
-      const int prow = a.row0 + r;
+      if (r >= Mr) break;
+      const int prow = row0 + r;
       const RowInfo ri = row_info(P, prow);
       if (ri.pad || ri.pos >= a.cap) continue;
       float x1 = tile[rl * COLS + lane], x2 = tile[rl * COLS + lane + half];
@@ -422,11 +428,16 @@ static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
 int gemm_bf16_groups(int N) { return N / 128; }
 
 // Shape rules: N a multiple of 128, K a multiple of 256 (8 slices of whole
-// k-blocks).
-void launch_gemm_bf16(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 0) return;
-  const int MT = a.M >= 64 ? 4 : (a.M + 15) / 16;
-  const dim3 gy(1, (a.M + 63) / 64);
+// k-blocks).  A second segment (W2, M2, row02: same N, K and input buffer)
+// runs in the same launch; the argmax epilogue takes one segment only.
+void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
+  GemmArgs a = a0;
+  if (!a.W2 || a.M2 <= 0) { a.W2 = nullptr; a.M2 = 0; }
+  if (a.M <= 0 && a.M2 <= 0) return;
+  const int Mx = a.M > a.M2 ? a.M : a.M2;
+  const int MT = Mx >= 64 ? 4 : (Mx + 15) / 16;
+  a.gy0 = (a.M + 63) / 64;
+  const dim3 gy(1, a.gy0 + (a.M2 + 63) / 64);
   const bool wide = a.N / 128 >= 128;      // enough workgroups without splitting K
   if (!wide) {
     const dim3 grid(a.N / 128 * NSL, gy.y);
