@@ -59,7 +59,7 @@ struct Layout {
   uint64_t packed_bytes;
   // workspace offsets (bytes)
   uint64_t w_h, w_x, w_qkv, w_q, w_act, w_opart, w_ml, w_parts, w_logits, w_rope, w_i32,
-      w_part, w_cnt, cnt_bytes, w_amax, workspace_bytes;
+      w_part, w_rpart, w_cnt, cnt_bytes, w_amax, workspace_bytes;
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
 };
 
@@ -173,12 +173,14 @@ void make_layout(const orthrus_config& c, Layout& y) {
     // (+1 row group: a draft launch splits its rows into two segments)
     const uint64_t rgroups = (uint64_t)(y.rmax + 63) / 64 + 1;
     y.w_part = take(8 * rgroups * 64 * nmax * 4);
+    // slice partials of the residual GEMMs (O, down): [8][rows][d]
+    y.w_rpart = take(8 * (uint64_t)y.rmax * y.d * 4);
     // completion counters of the split-K GEMM column groups (+1 grid counter)
     y.cnt_bytes = (rgroups * y.ngroups_max + 1) * 4;
     y.w_cnt = take(y.cnt_bytes);
     y.w_amax = take((uint64_t)y.rmax * (y.V / 128) * 8);
   } else {
-    y.w_part = y.w_cnt = y.w_amax = take(0);
+    y.w_part = y.w_rpart = y.w_cnt = y.w_amax = take(0);
     y.cnt_bytes = 0;
   }
   y.workspace_bytes = o;
@@ -354,10 +356,17 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   g0.eps = eps;
   g0.P = P; g0.hq = y.hq; g0.hkv = y.hkv;
   g0.rope = S<float2>(c, y.w_rope); g0.q_out = q; g0.cap = y.cap; g0.kpad = y.kpad;
-  auto norm = [&](uint64_t gain_off) {
+  // residual add of the O / down slice partials (nsl = 8) and the RMSNorm
+  // that produces the next GEMM's bf16 input
+  float* rpart = S<float>(c, y.w_rpart);
+  const size_t rps = (size_t)y.rmax * y.d;
+  auto rnorm = [&](int nsl, uint64_t gain_off) {
     Tick t(c, pb + R_SMALL, s);
-    launch_rownorm_bf16(h, rows, y.d, (const uint16_t*)(c->packed + gain_off), eps, x, s);
+    launch_resid_norm_bf16(P, h, y.d, rpart, rps, nsl, (const uint16_t*)(c->packed + gain_off),
+                           eps, x, s);
   };
+  g0.rpart = rpart; g0.rps = rps;
+  rnorm(0, y.p_anorm[0]);
   auto run = [&](GemmArgs g, uint64_t w, int row0, int M, int K, int N, int ep) {
     g.W = (const u32x4_t*)(c->packed + w);
     g.row0 = row0; g.M = M; g.K = K; g.N = N; g.ep = ep;
@@ -379,7 +388,6 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     uint16_t* vs = (uint16_t*)(c->scr + ((uint64_t)y.L + l) * y.scr_layer_elems * E);
     // RMSNorm, then Q/K/V projection + QK-norm + RoPE + K/V placement; mask
     // rows use the diffusion projections, every other row the frozen ones
-    norm(y.p_anorm[l]);
     {
       Tick t(c, pb + R_QKV, s);
       GemmArgs g = g0;
@@ -408,7 +416,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       Tick t(c, pb + R_ATTN, s);
       launch_attention_bf16(a, s);
     }
-    // O projection + residual
+    // O projection (slice partials), then residual + FFN RMSNorm
     {
       Tick t(c, pb + R_O, s);
       GemmArgs g = g0;
@@ -419,7 +427,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
         run(g, y.p_o[l], 0, rows, y.qd, y.d, EP_RESID);
       }
     }
-    norm(y.p_ffnnorm[l]);
+    rnorm(8, y.p_ffnnorm[l]);
     {
       Tick t(c, pb + R_GU, s);
       GemmArgs g = g0;
@@ -433,9 +441,11 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       g.X = act; g.ldx = y.F; g.y = h; g.ldy = y.d;
       run(g, y.p_down[l], 0, rows, y.F, y.d, EP_RESID);
     }
+    // residual + the next RMSNorm: the next layer's attention norm, or the
+    // final norm in front of the LM head
+    rnorm(8, l + 1 < y.L ? y.p_anorm[l + 1] : y.p_fnorm);
   }
   if (!want_tokens) return;
-  norm(y.p_fnorm);
   Tick tl(c, pb + R_LM, s);
   GemmArgs g = g0;
   g.X = x; g.ldx = y.d;

@@ -90,8 +90,12 @@ void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, 
 void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
                   int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
                   float* h, hipStream_t s);
-void launch_rownorm_bf16(const float* h, int rows, int d, const uint16_t* gain, float eps,
-                         uint16_t* out, hipStream_t s);
+// h[r] += ((p0 + p1) + ... + p7)[r] (nslices 8, part [8][rows][d] with slice
+// stride ps; nslices 0: no residual), then out[r] = bf16(RMSNorm(h[r]) * g).
+// Padding rows of a draft pass are left alone.
+void launch_resid_norm_bf16(const PassInfo& P, float* h, int d, const float* part, size_t ps,
+                            int nslices, const uint16_t* gain, float eps, uint16_t* out,
+                            hipStream_t s);
 void launch_rmsnorm(const float* h, int rows, int d, const void* gain, bool bf16, float eps,
                     void* out, hipStream_t s);
 void launch_qkv_post(const PassInfo& P, const float* qkv, int hq, int hkv, int hd,
@@ -129,7 +133,8 @@ struct GemmArgs {
   // split-K partials [8][M][N] and completion counters (zero between launches)
   float* part; unsigned* cnt;
   int ep;
-  float* y; int ldy;                                  // EP_RESID
+  float* y; int ldy;                                  // EP_RESID (wide: y += result)
+  float* rpart; size_t rps;     // EP_RESID split-K: slice partials [8][rows][N] (slice stride rps)
   uint16_t* act; int ldact;                            // EP_SWIGLU
   PassInfo P; int hq, hkv; float eps;                  // EP_QKV (and EP_ARGMAX row mapping)
   const uint16_t* qn; const uint16_t* kn; const uint16_t* dqn; const uint16_t* dkn;

@@ -82,24 +82,52 @@ void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* b
                      embed, mask_emb, V, d, (int)bf16, h);
 }
 
-// ------------------------------------------------- RMSNorm -> bf16 rows
-// out[r] = bf16(h[r] / rms(h[r]) * g), the bf16 input of the next GEMM.  One
-// 256-thread block per row; thread t owns the float4 groups t, t + 256, ...
-// (all loaded before use).  Its sum of squares runs over its groups in
-// order, then a fixed butterfly inside the wave and the four wave sums in
-// wave order: the result depends only on the row.
+// Residual add of the split-K partials + RMSNorm -> bf16 rows.  One
+// 512-thread block per row; thread t owns the float4 groups t, t + 512, ...
+// All loads are issued before use.  The partial sum runs in slice order and
+// is then added to h (the same arithmetic as a fused residual epilogue);
+// the sum of squares runs over the thread's groups in order, then a fixed
+// butterfly inside the wave and the eight wave sums in wave order.
 template <int NV>
-__global__ __launch_bounds__(256) void k_rownorm_bf16(const float* __restrict__ h, int d,
-                                                      const uint16_t* __restrict__ gain, float eps,
-                                                      uint16_t* __restrict__ out) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __restrict__ h, int d,
+                                                         const float* __restrict__ part, size_t ps,
+                                                         int nslices,
+                                                         const uint16_t* __restrict__ gain,
+                                                         float eps, uint16_t* __restrict__ out) {
+  __shared__ float red[8];
   const int r = blockIdx.x, t = threadIdx.x;
-  const float* x = h + (size_t)r * d;
+  if (P.kind == PASS_DRAFT && row_info(P, r).pad) {     // keep padding rows' input at zero
+    for (int i = t * 4; i < d; i += 2048) *(uint2*)(out + (size_t)r * d + i) = make_uint2(0u, 0u);
+    return;
+  }
+  float* x = h + (size_t)r * d;
   float4 v[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int i = (j * 256 + t) * 4;
+    const int i = (j * 512 + t) * 4;
     v[j] = i < d ? *(const float4*)(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (nslices == 8) {
+    float4 p[8][NV];
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        const int i = (j * 512 + t) * 4;
+        p[sl][j] = i < d ? *(const float4*)(part + sl * ps + (size_t)r * d + i)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      float4 s4 = p[0][j];
+#pragma unroll
+      for (int sl = 1; sl < 8; ++sl) {
+        s4.x += p[sl][j].x; s4.y += p[sl][j].y; s4.z += p[sl][j].z; s4.w += p[sl][j].w;
+      }
+      v[j].x += s4.x; v[j].y += s4.y; v[j].z += s4.z; v[j].w += s4.w;
+      const int i = (j * 512 + t) * 4;
+      if (i < d) *(float4*)(x + i) = v[j];
+    }
   }
   float ss = 0.f;
 #pragma unroll
@@ -108,11 +136,13 @@ __global__ __launch_bounds__(256) void k_rownorm_bf16(const float* __restrict__ 
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
   if ((t & 63) == 0) red[t >> 6] = ss;
   __syncthreads();
-  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  float tot = red[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) tot += red[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int i = (j * 256 + t) * 4;
+    const int i = (j * 512 + t) * 4;
     if (i < d) {
       const uint2 g = *(const uint2*)(gain + i);
       const float g0 = __uint_as_float(g.x << 16), g1 = __uint_as_float(g.x & 0xffff0000u);
@@ -126,14 +156,18 @@ __global__ __launch_bounds__(256) void k_rownorm_bf16(const float* __restrict__ 
 }
 
 // d a multiple of 4, at most 8192
-void launch_rownorm_bf16(const float* h, int rows, int d, const uint16_t* gain, float eps,
-                         uint16_t* out, hipStream_t s) {
+void launch_resid_norm_bf16(const PassInfo& P, float* h, int d, const float* part, size_t ps,
+                            int nslices, const uint16_t* gain, float eps, uint16_t* out,
+                            hipStream_t s) {
+  const int rows = P.rows();
   if (rows <= 0) return;
-  const int nv = (d + 1023) / 1024;
-  if (nv <= 1) hipLaunchKernelGGL(k_rownorm_bf16<1>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
-  else if (nv <= 2) hipLaunchKernelGGL(k_rownorm_bf16<2>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
-  else if (nv <= 4) hipLaunchKernelGGL(k_rownorm_bf16<4>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
-  else hipLaunchKernelGGL(k_rownorm_bf16<8>, dim3(rows), dim3(256), 0, s, h, d, gain, eps, out);
+  const int nv = (d + 2047) / 2048;
+  if (nv <= 1)
+    hipLaunchKernelGGL(k_resid_norm_bf16<1>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
+  else if (nv <= 2)
+    hipLaunchKernelGGL(k_resid_norm_bf16<2>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
+  else
+    hipLaunchKernelGGL(k_resid_norm_bf16<4>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
 }
 
 // -------------------------------------------------------------- RMSNorm

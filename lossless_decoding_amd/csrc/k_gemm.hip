@@ -22,10 +22,10 @@
 //    loads issued after it (memory counters complete in order).
 //  * Input: bf16 rows (RMSNorm outputs, attention output, SwiGLU product).
 //  * Epilogues: QK-norm + RoPE + KV placement (QKV projection; a column
-//    group is one head), residual add (O and down projections), SwiGLU
-//    (gate/up), and per-row
+//    group is one head), SwiGLU (gate/up), per-row
 //    argmax with lowest-index ties (LM head; the grid's last workgroup
-//    turns the partials into tokens).
+//    turns the partials into tokens).  The O and down projections write
+//    their 8 slice partials; the next kernel adds them to the residual.
 //
 // fp32 path: one thread per output with a sequential k loop (check models).
 #include "internal.h"
@@ -196,6 +196,19 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     for (int mt = 0; mt < MT; ++mt) cur[mt] = tot[mt];
   }
 
+  // ---- split-K residual GEMMs (O and down projections): the slice partial
+  // goes to [slice][row][N]; the residual + RMSNorm kernel that follows adds
+  // the 8 partials in slice order, so no workgroup waits for another here.
+  if (SPLIT && EP == EP_RESID) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int r = m0 + mt * 16 + lr;
+      if (r < Mr)
+        *(floatx4_t*)(a.rpart + (size_t)s_first * a.rps + (size_t)(row0 + r) * a.N + nbk * 16 + lq * 4) =
+            cur[mt];
+    }
+    return;
+  }
   // ---- split-K: write the slice partial; the last slice workgroup adds all 8.
   // The partials and counters use agent-scope (coherent) stores and loads; an
   // explicit wait for the stores plus the barrier orders them before the
