@@ -83,67 +83,70 @@ void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* b
 }
 
 // Residual add of the split-K partials + RMSNorm -> bf16 rows.  One
-// 512-thread block per row; thread t owns the float4 groups t, t + 512, ...
-// All loads are issued before use.  The partial sum runs in slice order and
-// is then added to h (the same arithmetic as a fused residual epilogue);
-// the sum of squares runs over the thread's groups in order, then a fixed
-// butterfly inside the wave and the eight wave sums in wave order.
-template <int NV>
+// 512-thread block per row; the row is cut into 256-element chunks, wave w
+// takes chunks w, w + 8, ..., lane l holds elements 4l .. 4l + 3.  All loads
+// are issued before use.  The partial sum runs in slice order and is then
+// added to h (the same arithmetic as a fused residual epilogue).  The sum
+// of squares is canonical: per chunk, the lane's four squares in order and
+// a fixed butterfly, then the chunk sums in chunk order (the GEMM prelude
+// computes the same value).
+template <int NCW>
 __global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __restrict__ h, int d,
                                                          const float* __restrict__ part, size_t ps,
                                                          int nslices,
                                                          const uint16_t* __restrict__ gain,
                                                          float eps, uint16_t* __restrict__ out) {
-  __shared__ float red[8];
-  const int r = blockIdx.x, t = threadIdx.x;
+  __shared__ float red[32];
+  const int r = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63, nch = d >> 8;
   if (P.kind == PASS_DRAFT && row_info(P, r).pad) {     // keep padding rows' input at zero
     for (int i = t * 4; i < d; i += 2048) *(uint2*)(out + (size_t)r * d + i) = make_uint2(0u, 0u);
     return;
   }
   float* x = h + (size_t)r * d;
-  float4 v[NV];
+  float4 v[NCW];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int i = (j * 512 + t) * 4;
-    v[j] = i < d ? *(const float4*)(x + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < NCW; ++j) {
+    const int c = wave + j * 8;
+    v[j] = c < nch ? *(const float4*)(x + c * 256 + lane * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (nslices == 8) {
-    float4 p[8][NV];
+    float4 p[8][NCW];
 #pragma unroll
     for (int sl = 0; sl < 8; ++sl)
 #pragma unroll
-      for (int j = 0; j < NV; ++j) {
-        const int i = (j * 512 + t) * 4;
-        p[sl][j] = i < d ? *(const float4*)(part + sl * ps + (size_t)r * d + i)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j = 0; j < NCW; ++j) {
+        const int c = wave + j * 8;
+        p[sl][j] = c < nch ? *(const float4*)(part + sl * ps + (size_t)r * d + c * 256 + lane * 4)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
+    for (int j = 0; j < NCW; ++j) {
       float4 s4 = p[0][j];
 #pragma unroll
       for (int sl = 1; sl < 8; ++sl) {
         s4.x += p[sl][j].x; s4.y += p[sl][j].y; s4.z += p[sl][j].z; s4.w += p[sl][j].w;
       }
       v[j].x += s4.x; v[j].y += s4.y; v[j].z += s4.z; v[j].w += s4.w;
-      const int i = (j * 512 + t) * 4;
-      if (i < d) *(float4*)(x + i) = v[j];
+      const int c = wave + j * 8;
+      if (c < nch) *(float4*)(x + c * 256 + lane * 4) = v[j];
     }
   }
-  float ss = 0.f;
 #pragma unroll
-  for (int j = 0; j < NV; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  for (int j = 0; j < NCW; ++j) {
+    const int c = wave + j * 8;
+    float sq = v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if ((t & 63) == 0) red[t >> 6] = ss;
+    for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+    if (c < nch && lane == 0) red[c] = sq;
+  }
   __syncthreads();
   float tot = red[0];
-#pragma unroll
-  for (int w = 1; w < 8; ++w) tot += red[w];
+  for (int c = 1; c < nch; ++c) tot += red[c];
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int i = (j * 512 + t) * 4;
-    if (i < d) {
+  for (int j = 0; j < NCW; ++j) {
+    const int c = wave + j * 8, i = c * 256 + lane * 4;
+    if (c < nch) {
       const uint2 g = *(const uint2*)(gain + i);
       const float g0 = __uint_as_float(g.x << 16), g1 = __uint_as_float(g.x & 0xffff0000u);
       const float g2 = __uint_as_float(g.y << 16), g3 = __uint_as_float(g.y & 0xffff0000u);
@@ -155,16 +158,16 @@ __global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __re
   }
 }
 
-// d a multiple of 4, at most 8192
+// d a multiple of 256, at most 8192
 void launch_resid_norm_bf16(const PassInfo& P, float* h, int d, const float* part, size_t ps,
                             int nslices, const uint16_t* gain, float eps, uint16_t* out,
                             hipStream_t s) {
   const int rows = P.rows();
   if (rows <= 0) return;
-  const int nv = (d + 2047) / 2048;
-  if (nv <= 1)
+  const int ncw = ((d >> 8) + 7) / 8;          // chunks per wave
+  if (ncw <= 1)
     hipLaunchKernelGGL(k_resid_norm_bf16<1>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
-  else if (nv <= 2)
+  else if (ncw <= 2)
     hipLaunchKernelGGL(k_resid_norm_bf16<2>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
   else
     hipLaunchKernelGGL(k_resid_norm_bf16<4>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
