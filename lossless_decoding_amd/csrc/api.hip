@@ -59,7 +59,7 @@ struct Layout {
   uint64_t packed_bytes;
   // workspace offsets (bytes)
   uint64_t w_h, w_x, w_qkv, w_q, w_act, w_opart, w_ml, w_parts, w_logits, w_rope, w_i32,
-      w_part, w_rpart, w_cnt, cnt_bytes, w_amax, workspace_bytes;
+      w_part, w_rpart, w_cnt, cnt_bytes, w_amax, workspace_bytes, part_bytes;
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
 };
 
@@ -173,6 +173,7 @@ void make_layout(const orthrus_config& c, Layout& y) {
     // (+1 row group: a draft launch splits its rows into two segments)
     const uint64_t rgroups = (uint64_t)(y.rmax + 63) / 64 + 1;
     y.w_part = take(8 * rgroups * 64 * nmax * 4);
+    y.part_bytes = 8 * rgroups * 64 * nmax * 4;      // addressed with 32-bit offsets
     // slice partials of the residual GEMMs (O, down): [8][rows][d]
     y.w_rpart = take(8 * (uint64_t)y.rmax * y.d * 4);
     // completion counters of the split-K GEMM column groups (+1 grid counter)
@@ -181,6 +182,7 @@ void make_layout(const orthrus_config& c, Layout& y) {
     y.w_amax = take((uint64_t)y.rmax * (y.V / 128) * 8);
   } else {
     y.w_part = y.w_rpart = y.w_cnt = y.w_amax = take(0);
+    y.part_bytes = 0;
     y.cnt_bytes = 0;
   }
   y.workspace_bytes = o;
@@ -473,6 +475,7 @@ int orthrus_query_sizes(const orthrus_config* cfg, orthrus_sizes* out) {
   if (!out) return ORTHRUS_EINVAL;
   Layout y;
   make_layout(*cfg, y);
+  if (y.part_bytes >= (1ull << 31)) return ORTHRUS_EINVAL;   // batch too large for one context
   out->weights_bytes = canon_offset(*cfg, n_tensors(*cfg)) * y.esz;
   out->packed_bytes = y.packed_bytes;
   out->kv_bytes = y.kv_bytes;
@@ -507,6 +510,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
   orthrus_ctx* c = new orthrus_ctx();
   c->cfg = *cfg;
   make_layout(*cfg, c->y);
+  if (c->y.part_bytes >= (1ull << 31)) { delete c; return ORTHRUS_EINVAL; }
   c->packed = (char*)packed; c->kv = (char*)kv_cache; c->scr = (char*)block_scratch;
   c->ws = (char*)workspace;
   c->state = ST_IDLE; c->step_batch = 0;

@@ -36,6 +36,7 @@
 #define BUF_FLAGS 0x00020000  // buffer descriptor word 3: 32-bit data format
 #define BUF_NT 2              // cache policy: nontemporal (streamed once)
 #define OOR 0x40000000        // buffer offset past every descriptor's range
+#define BUF_SC1 16            // cache policy: device scope (data of other workgroups)
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) {
   bf16x8_t r;
@@ -210,20 +211,24 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     return;
   }
   // ---- split-K: write the slice partial; the last slice workgroup adds all 8.
-  // The partials and counters use agent-scope (coherent) stores and loads; an
+  // Partials and counters use device-scope (coherent) stores and loads; an
   // explicit wait for the stores plus the barrier orders them before the
   // counter increment, so no L2 writeback is needed.
   if (SPLIT) {
-    // partial layout [slice][m-group][col group][mt][wave][i][lane]: each
-    // coherent dword store of a wave covers 256 contiguous bytes
+    // partial layout [slice][m-group][col group][mt][wave][lane][4]: one
+    // 16-byte device-scope store / load per lane and row tile (a wave moves
+    // 1 KB contiguous)
     const size_t pstride = (size_t)gridDim.y * ngroups * MT * WV * 256;
     float* pbase = a.part + ((size_t)blockIdx.y * ngroups + ng) * MT * WV * 256;
+    const __amdgpu_buffer_rsrc_t rPt =
+        __builtin_amdgcn_make_buffer_rsrc((void*)pbase, (short)0, 0x7fffffff, BUF_FLAGS);
+    auto poff = [&](int s, int mt) {
+      return (int)((s * pstride + ((size_t)mt * WV + wave) * 256) * 4) + lane * 16;
+    };
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      float* pp = pbase + s_first * pstride + ((size_t)mt * WV + wave) * 256 + lane;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st_agent(pp + i * 64, cur[mt][i]);
-    }
+    for (int mt = 0; mt < MT; ++mt)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[mt]), rPt,
+                                             poff(s_first, mt), 0, BUF_SC1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
@@ -240,13 +245,9 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       floatx4_t p[NSL];
 #pragma unroll
       for (int s = 0; s < NSL; ++s) {
-        const float* pp = pbase + s * pstride + ((size_t)mt * WV + wave) * 256 + lane;
-        if (s == s_first) {
-          p[s] = cur[mt];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[s][i] = ld_agent(pp + i * 64);
-        }
+        if (s == s_first) p[s] = cur[mt];
+        else p[s] = __builtin_bit_cast(floatx4_t,
+                                       __builtin_amdgcn_raw_buffer_load_b128(rPt, poff(s, mt), 0, BUF_SC1));
       }
       floatx4_t t = p[0];
 #pragma unroll
