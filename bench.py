@@ -38,6 +38,99 @@ def tpf_from_accept(mean_accept: float) -> float:
     return (mean_accept + 1.0) / 2.0
 
 
+MFMA_PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, published
+
+
+def KV_BYTES_PER_TOKEN(sh):
+    """K and V of one token, all layers, bf16."""
+    return sh["L"] * 2 * sh["hkv"] * sh["hd"] * 2
+
+
+def step_weight_bytes(sh):
+    """Weight bytes one draft + verify step streams (bf16): pass 1 reads the
+    frozen and the diffusion Q/K/V/O, the FFN and the LM head; pass 2 the
+    frozen Q/K/V/O, the FFN and the LM head."""
+    d, qd, kd, F, V, L = sh["d"], sh["hq"] * sh["hd"], sh["hkv"] * sh["hd"], sh["F"], sh["V"], sh["L"]
+    qkvo = d * qd + 2 * d * kd + qd * d
+    ffn = 3 * d * F
+    return 2 * (L * (2 * qkvo + ffn) + d * V) + 2 * (L * (qkvo + ffn) + d * V)
+
+
+def step_gemm_flops(sh, B, K):
+    """GEMM flops of one step: pass 1 has B anchor rows on the frozen
+    projections and B*K mask rows on the diffusion ones, all B*(K+1) rows
+    through the FFN and LM head; pass 2 has B*K rows through the frozen
+    model."""
+    d, qd, kd, F, V, L = sh["d"], sh["hq"] * sh["hd"], sh["hkv"] * sh["hd"], sh["F"], sh["V"], sh["L"]
+    qkvo = d * qd + 2 * d * kd + qd * d
+    ffn = 3 * d * F
+    draft = B * (K + 1) * (L * (qkvo + ffn) + d * V)
+    verify = B * K * (L * (qkvo + ffn) + d * V)
+    return 2 * (draft + verify)
+
+
+def kernel_a_bench(dev, points=((4, 16384), (16, 4096)), rows=32, hq=32, hkv=8, kb=32, reps=20):
+    """Kernel (a) alone (orthrus_block_attention) at the configurations with
+    at least 256 MB of cache K/V: `rows` mask rows per sequence see Lk cache
+    keys and kb block keys.  Seeded N(0, 1) bf16 inputs; four independent
+    buffer sets are rotated so that the 256 MB Infinity Cache does not hold
+    the keys between launches.  Algorithmic bytes = cache K/V + block K/V +
+    Q + output."""
+    import torch
+
+    import synth
+    from lossless_decoding_amd import _lib as C
+    from lossless_decoding_amd.layout import tile_v, tile_block_v
+    from synth import workloads
+    from synth.device import fill_normal_device
+
+    res = []
+    for B, lk in points:
+        sets = []
+        for i in range(4):
+            st = workloads.attn_inputs_stream(B, lk) + 100 * i
+            q = torch.empty(B, rows, hq, 128, dtype=torch.bfloat16, device=dev)
+            fill_normal_device(q, workloads.ATTN_SEED, st, 1.0, synth.P_ATTN)
+            kc = torch.empty(B, hkv, lk, 128, dtype=torch.bfloat16, device=dev)
+            fill_normal_device(kc, workloads.ATTN_SEED, st + 1, 1.0, synth.P_ATTN)
+            vc = torch.empty_like(kc)
+            fill_normal_device(vc, workloads.ATTN_SEED, st + 2, 1.0, synth.P_ATTN)
+            vt = tile_v(vc)
+            del vc
+            kbk = torch.empty(B, hkv, kb, 128, dtype=torch.bfloat16, device=dev)
+            fill_normal_device(kbk, workloads.ATTN_SEED, st + 3, 1.0, synth.P_ATTN)
+            vbk = torch.empty_like(kbk)
+            fill_normal_device(vbk, workloads.ATTN_SEED, st + 4, 1.0, synth.P_ATTN)
+            sets.append((q, kc, vt, kbk, tile_block_v(vbk, 32)))
+        out = torch.empty(B, rows, hq, 128, dtype=torch.bfloat16, device=dev)
+        wsb = C.orthrus_attention_workspace(B, rows, hq, hkv, lk)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def go(i):
+            q, kc, vt, kbk, vbt = sets[i % 4]
+            C.orthrus_block_attention(B, rows, hq, hkv, q.data_ptr(), kc.data_ptr(), vt.data_ptr(), lk,
+                                      lk, kbk.data_ptr(), vbt.data_ptr(), kb, out.data_ptr(),
+                                      ws.data_ptr(), wsb, stream)
+        for i in range(4):
+            go(i)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            go(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        alg = B * hkv * (lk + kb) * 128 * 2 * 2 + 2 * B * rows * hq * 128 * 2
+        res.append({"batch": B, "cache_keys": lk, "block_keys": kb, "rows": rows, "us": round(us, 2),
+                    "algorithmic_bytes": alg, "achieved_GBps": round(alg / us / 1e3, 1),
+                    "frac_of_8TBps": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)})
+        log(f"[kernel a] B={B} Lk={lk}: {us:.1f} us, {alg / us / 1e3:.0f} GB/s")
+        del sets, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -102,6 +195,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_b1_p512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=8)
+    ap.add_argument("--no-kernel-a", action="store_true",
+                    help="skip the block-attention kernel measurement")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run plain 1 GiB device copies (PMC byte-counter calibration)")
     args = ap.parse_args()
@@ -154,12 +249,20 @@ def main():
     ar.prefill(prompts)
     traj = torch.zeros(need, B, dtype=torch.int32, device=dev)
     traj[0] = ar.pending[:B]
+    # the same kernels in plain greedy decoding (K = 0): one token per
+    # sequence per step, timed for the speedup figure
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
     for j in range(1, need):
         ar.draft(); ar.verify(); ar.commit()
         traj[j] = ar.pending[:B]
+    a1.record()
+    torch.cuda.synchronize()
+    plain_tps = B * (need - 1) / (a0.elapsed_time(a1) / 1e3)
     traj = traj.t().contiguous().cpu().numpy()
     ar_s = time.time() - t0
-    log(f"[setup] greedy trajectory of {need} tokens x {B} in {ar_s:.1f}s")
+    log(f"[setup] greedy trajectory of {need} tokens x {B} in {ar_s:.1f}s "
+        f"(plain decoding {plain_tps:.1f} tokens/s)")
     ar.close()
     del ar
     planted = torch.from_numpy(workloads.plant_drafts(traj, 1, a, K, V)).to(dev)
@@ -241,6 +344,16 @@ def main():
         del src, dst
         log("[calibrate] 3 plain copies of 1 GiB")
 
+    # whole-step roofline: algorithmic bytes of the timed steps (weights of
+    # both passes + the cache keys each pass must read) at 8 TB/s
+    wb = step_weight_bytes(sh)
+    n0 = P + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(a + 1, axis=0)])[W:W + S]
+    kv_b = float(((2 * n0 + K + 2) * KV_BYTES_PER_TOKEN(sh)).sum())
+    step_bytes = S * wb + kv_b
+    step_roof_ms = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    gemm_flops = step_gemm_flops(sh, B, K) * S
+    kernel_a = kernel_a_bench(dev) if not args.no_kernel_a else None
+
     out = {
         "metric": "verified tokens/s (and draft+verify steps/s) on 1 GPU; % of HBM roofline",
         "value": round(tokens / (ms / 1e3), 3),
@@ -260,6 +373,12 @@ def main():
         "tokens_per_step": round(tokens / S, 4),
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
         "lossless_vs_greedy": lossless,
+        "plain_decoding_tokens_per_s": round(plain_tps, 3),
+        "speedup_vs_plain_decoding": round(tokens / (ms / 1e3) / plain_tps, 4),
+        "step_roofline": {"bytes_per_step": round(step_bytes / S), "roofline_ms": round(step_roof_ms / S, 4),
+                          "frac": round(step_roof_ms / ms, 4),
+                          "gemm_tflops_per_s": round(gemm_flops / (ms / 1e3) / 1e12, 2),
+                          "mfma_frac_bf16": round(gemm_flops / (ms / 1e3) / MFMA_PEAK_BF16, 4)},
         "roofline": {
             "kernel": f"k_gemm_bf16<{gu_mt}, EP_SWIGLU, {gu_wv}, false> (draft-pass gate/up "
                       f"SwiGLU GEMM, M={M1}, N={2 * sh['F']}, K={sh['d']})",
@@ -275,6 +394,7 @@ def main():
             "events_dropped": dropped,
         },
         "ms_per_step_by_class": breakdown,
+        "kernel_a": kernel_a,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(sh, wl, tokens / S / B)

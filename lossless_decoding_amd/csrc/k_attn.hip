@@ -131,23 +131,34 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
   }
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
 
-  // K (64 x 128) and V^T (128 x 64) of one tile: 4 + 4 16-byte pieces per thread
-  uint4 kr[4], vr[4];
-  auto load_tile = [&](int kt) __attribute__((always_inline)) {
-    const int nvalid = min(64, k_end - kt);
+  // K (64 x 128) and V^T (128 x 64) of one tile: 4 + 4 16-byte pieces per
+  // thread.  Two register sets alternate, so the tile two steps ahead is in
+  // flight while one is computed.  The loads are buffer loads whose
+  // descriptors end at this chunk's last key (K: whole keys; V: whole 64-key
+  // tiles, the partial last tile is zeroed when staged): loads past the end
+  // return zero without touching memory, so every load is issued
+  // unconditionally and the memory-counter waits never drain the other set.
+  const int kv_hi = blk ? a.block_len : k_end;                 // keys [0, kv_hi) exist
+  const __amdgpu_buffer_rsrc_t rK =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kv_hi * hd * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vbase, (short)0, blk ? hd * a.kpad * 2 : ((kv_hi + 63) >> 6) * 64 * hd * 2, 0x00020000);
+  uint4 kA[4], vA[4], kB[4], vB[4];
+  auto load_tile = [&](uint4 (&kr)[4], uint4 (&vr)[4], int kt) __attribute__((always_inline)) {
+    const bool live = kt < k_end;                              // uniform
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int ci = tid + j * 256;
       const int key = ci >> 4, col = (ci & 15) * 8;
-      kr[j] = make_uint4(0, 0, 0, 0);
-      if (key < nvalid) kr[j] = *(const uint4*)(kbase + (size_t)(kt + key) * hd + col);
+      const int ko = live ? ((kt + key) * hd + col) * 2 : 0x40000000;
+      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, ko, 0, 0));
       const int d = ci >> 3, vc8 = (ci & 7) * 8;
-      vr[j] = make_uint4(0, 0, 0, 0);
-      if (!blk) vr[j] = *(const uint4*)(vbase + (size_t)(kt >> 6) * 64 * hd + (size_t)d * 64 + vc8);
-      else if (vc8 < a.kpad) vr[j] = *(const uint4*)(vbase + (size_t)d * a.kpad + vc8);
+      const int vo = !live ? 0x40000000
+                           : (blk ? (d * a.kpad + vc8) * 2 : ((kt >> 6) * 64 * hd + d * 64 + vc8) * 2);
+      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rV, vo, 0, 0));
     }
   };
-  auto store_tile = [&](int kt) __attribute__((always_inline)) {
+  auto store_tile = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], int kt) __attribute__((always_inline)) {
     const int nvalid = min(64, k_end - kt);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -168,13 +179,15 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
     }
   };
 
-  load_tile(k_begin);
-  for (int kt = k_begin; kt < k_end; kt += 64) {
+  // One tile step: stage the tile, refill its register set two tiles ahead,
+  // compute.  A step past the end (odd tile count) sees no key: every score
+  // is masked, alpha = 1 and p = 0, so it changes nothing.
+  auto step = [&](uint4 (&kr)[4], uint4 (&vr)[4], int kt) __attribute__((always_inline)) {
     const int nvalid = min(64, k_end - kt);
     __syncthreads();                     // the previous tile is no longer read
-    store_tile(kt);
+    store_tile(kr, vr, kt);
     __syncthreads();
-    if (kt + 64 < k_end) load_tile(kt + 64);
+    load_tile(kr, vr, kt + 128);
     if (wact) {
       // S^T for 4 blocks of 16 keys
       floatx4_t s[4];
@@ -187,27 +200,38 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
           s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ds], s[kb], 0, 0, 0);
         }
       }
-      // mask by selection and scale to base 2
-      float mt = -INFINITY;
+      // Visibility: when every key of the tile is visible to every row of
+      // the wave (the common case at long context) nothing is masked;
+      // otherwise invisible keys get the score -inf.  Both paths then compute
+      // the same values: the maximum of the raw scores, scaled to base 2
+      // (scaling by a positive constant keeps the maximum), and
+      // p = 2^(s * scale - m) with one fused multiply-add.
+      const bool all_vis = !blk && nvalid == 64 && __all(kt + 63 <= lim);
+      if (!all_vis) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kl = kb * 16 + lq * 4 + i;
+            const bool ok = kl < nvalid && (blk ? seesb != 0 : (kt + kl) <= lim);
+            s[kb][i] = ok ? s[kb][i] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          int kl = kb * 16 + lq * 4 + i;
-          bool ok = kl < nvalid && (blk ? seesb != 0 : (kt + kl) <= lim);
-          float v = ok ? s[kb][i] * sl2 : -INFINITY;
-          s[kb][i] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mt = mx * sl2;
       // Branch-free update: the MFMAs below read operands from every lane,
       // so no lane may skip them.  A row with nothing visible yet keeps
       // m = -inf, l = 0, o = 0 exactly (alpha = 1, p = 0).
       const float mnew = fmaxf(mrow, mt);
       const bool any = mnew != -INFINITY;
       const float mref = any ? mnew : 0.f;
-      const float alpha = any ? exp2f(mrow - mref) : 1.f;
+      const float alpha = any ? __builtin_amdgcn_exp2f(mrow - mref) : 1.f;
       // P enters the P.V product as two bf16 terms, hi = bf16(p) and
       // lo = bf16(p - hi) (p - hi is exact in fp32), so the product carries
       // about 16 significant bits of p instead of 8.  Rounding p itself to
@@ -219,7 +243,9 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float p = exp2f(s[kb][i] - mref);
+          // v_exp_f32 directly: the argument is <= 0 and results below
+          // 2^-126 (flushed) are negligible softmax weights
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], sl2, -mref));
           ps += p;
           __bf16 hi = (__bf16)p;
           pf[kb >> 1][(kb & 1) * 4 + i] = hi;
@@ -228,11 +254,17 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
       lrow = lrow * alpha + ps;
+      // rescale only if some row's maximum grew (otherwise every alpha is 1)
+      if (__any(mnew != mrow)) {
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          oacc[db][0] *= alpha; oacc[db][1] *= alpha; oacc[db][2] *= alpha; oacc[db][3] *= alpha;
+        }
+      }
       mrow = any ? mnew : mrow;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         floatx4_t o = oacc[db];
-        o[0] *= alpha; o[1] *= alpha; o[2] *= alpha; o[3] *= alpha;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8_t vf = ld_bf16x8(sV + (db * 16 + lr) * VT_STRIDE + ks * 32 + lq * 8);
@@ -242,6 +274,12 @@ __global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
         oacc[db] = o;
       }
     }
+  };
+  load_tile(kA, vA, k_begin);
+  load_tile(kB, vB, k_begin + 64);
+  for (int kt = k_begin; kt < k_end; kt += 128) {
+    step(kA, vA, kt);
+    step(kB, vB, kt + 64);
   }
 
   // ---- partial of this chunk: opart[((b*hkv+g)*(nc+1)+c)*qr_max + qr][d],

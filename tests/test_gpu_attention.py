@@ -11,33 +11,11 @@ import synth
 from lossless_decoding_amd import _lib as C
 from synth import workloads
 from synth.device import fill_normal_device
+from lossless_decoding_amd.layout import tile_v, tile_block_v
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-2
 HD = 128
-
-
-def vt_cols():
-    j = np.arange(64)
-    return (j // 32) * 32 + ((j % 16) // 4) * 8 + ((j % 32) // 16) * 4 + j % 4
-
-
-def tile_v(v: torch.Tensor) -> torch.Tensor:
-    """[..., L (multiple of 64), 128] logical -> [..., L/64, 128, 64] tiled."""
-    *lead, L, d = v.shape
-    t = v.reshape(*lead, L // 64, 64, d).transpose(-1, -2)       # [.., tiles, 128, 64 keys]
-    out = torch.empty_like(t)
-    out[..., torch.as_tensor(vt_cols(), device=v.device)] = t
-    return out.contiguous()
-
-
-def tile_block_v(v: torch.Tensor, kpad: int) -> torch.Tensor:
-    """[..., Kb, 128] -> [..., 128, kpad] with the same key-to-column map."""
-    *lead, Kb, d = v.shape
-    out = torch.zeros(*lead, d, kpad, dtype=v.dtype, device=v.device)
-    cols = torch.as_tensor(vt_cols()[:Kb] if Kb <= 64 else None, device=v.device)
-    out[..., cols] = v.transpose(-1, -2)
-    return out
 
 
 def make(B, rows, hq, hkv, lk, kb, seed_base):
