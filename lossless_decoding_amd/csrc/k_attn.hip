@@ -66,7 +66,7 @@ __device__ __forceinline__ void token_view(const AttnArgs& a, const SeqLimits& L
 // number of 4-tile query row groups of a pass
 __host__ __device__ inline int attn_row_groups(int qr) { return ((qr + 15) / 16 + 3) / 4; }
 
-__global__ __launch_bounds__(256) void k_attn_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[64 * KT_STRIDE];
   __shared__ __attribute__((aligned(16))) uint16_t sV[128 * VT_STRIDE];
   const int c = blockIdx.x, g = blockIdx.y;
