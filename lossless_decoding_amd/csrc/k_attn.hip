@@ -20,8 +20,14 @@
 // fp32 path: one wave per (row, query head), keys in order (check models).
 #include "internal.h"
 
-#define KT_STRIDE 136   // bf16 per key row of the staged K tile (128 + 8 pad)
-#define VT_STRIDE 72    // bf16 per dimension row of the staged V^T tile (64 + 8 pad)
+// Staged tiles in LDS: K as 64 key rows of 256 bytes, V^T as 128 dimension
+// rows of 128 bytes (64 keys in the cache's column order).  The 16-byte units
+// of a row are XOR-permuted by the row index (K: unit ^ (key & 15), V^T:
+// unit ^ (dim & 7)), which keeps the MFMA fragment reads (16 rows x 16 bytes
+// per group of lanes) free of LDS bank conflicts; padded rows would block the
+// direct memory-to-LDS loads, which fill 1 KB of LDS in lane order.
+__device__ __forceinline__ int k_lds_off(int key, int cu) { return key * 256 + ((cu ^ (key & 15)) << 4); }
+__device__ __forceinline__ int v_lds_off(int d, int ku) { return d * 128 + ((ku ^ (d & 7)) << 4); }
 
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   uint4 v = *(const uint4*)p;
@@ -63,12 +69,25 @@ __device__ __forceinline__ void token_view(const AttnArgs& a, const SeqLimits& L
   limit = P.kind == PASS_VERIFY ? L.n + 1 + t : P.p0 + t;
 }
 
-// number of 4-tile query row groups of a pass
-__host__ __device__ inline int attn_row_groups(int qr) { return ((qr + 15) / 16 + 3) / 4; }
+// number of query row groups of a pass: a workgroup's four waves own two
+// 16-row query tiles each
+__host__ __device__ inline int attn_row_groups(int qr) { return ((qr + 15) / 16 + 7) / 8; }
+
+// A row's softmax reference m (base 2) is raised only when a tile holds a
+// score above m + REF_SLACK; otherwise the tile's weights 2^(s - m) stay
+// below 2^REF_SLACK and are used against the old reference.  The decision is
+// taken per row from that row's own scores, so the arithmetic a row sees is
+// still a function of its keys alone.
+#define REF_SLACK 8.0f
+
+template <int N> struct IntC { static constexpr int value = N; };
 
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[64 * KT_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[128 * VT_STRIDE];
+  // two stages of (K tile, V^T tile), 16 KB each
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[64 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[128 * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[64 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[128 * 64];
   const int c = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
   const PassInfo& P = a.P;
@@ -98,27 +117,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     k_end = a.block_len;
   }
 
-  // this wave's query tile: row qr = rt*16 + lr (B operand of S^T = K.Q^T)
-  const int rt = rg * 4 + wave;
-  const int qr = rt * 16 + lr;
-  const bool wact = rt < NRT;                 // uniform per wave
-  bf16x8_t qf[4];
-  int lim = -1, seesb = 0;
-  floatx4_t oacc[8];
-  float mrow = -INFINITY, lrow = 0.f;
+  // This wave's query tiles rt0 and rt0 + 1 (B operands of S^T = K.Q^T);
+  // lane row qr = rt*16 + lr.  A padding row (qr >= QR) gets a zero query
+  // that sees every key: it computes harmless values that are never stored.
+  const int rt0 = rg * 8 + wave * 2;
+  const int nt = rt0 >= NRT ? 0 : (rt0 + 1 < NRT ? 2 : 1);     // uniform per wave
+  bf16x8_t qf[2][4];
+  int lim[2], seesb[2];
+  floatx4_t oacc[2][8];
+  float mref[2], thr[2], lsum[2];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  if (wact && qr < QR) {
-    const int t = qr / G, hh = g * G + (qr - t * G);
-    const int r = row_of(P, b, t);
-    token_view(a, L, t, lim, seesb);
-    const uint16_t* qp = (const uint16_t*)a.q + (size_t)r * H + hh * hd + lq * 8;
+  for (int t = 0; t < 2; ++t) {
+    mref[t] = -INFINITY; thr[t] = -INFINITY; lsum[t] = 0.f;
+    lim[t] = 0x7fffffff; seesb[t] = 1;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qf[ds] = ld_bf16x8(qp + ds * 32);
-  } else {
+    for (int db = 0; db < 8; ++db) oacc[t][db] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const int qr = (rt0 + t) * 16 + lr;
+    if (t < nt && qr < QR) {
+      const int tk = qr / G, hh = g * G + (qr - tk * G);
+      const int r = row_of(P, b, tk);
+      token_view(a, L, tk, lim[t], seesb[t]);
+      const uint16_t* qp = (const uint16_t*)a.q + (size_t)r * H + hh * hd + lq * 8;
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qf[ds] = bf16x8_t{};
+      for (int ds = 0; ds < 4; ++ds) qf[t][ds] = ld_bf16x8(qp + ds * 32);
+    } else {
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) qf[t][ds] = bf16x8_t{};
+    }
   }
+  const int lmin = nt == 2 ? min(lim[0], lim[1]) : lim[0];
 
   const uint16_t* kbase;
   const uint16_t* vbase;
@@ -131,167 +158,239 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   }
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
 
-  // K (64 x 128) and V^T (128 x 64) of one tile: 4 + 4 16-byte pieces per
-  // thread.  Two register sets alternate, so the tile two steps ahead is in
-  // flight while one is computed.  The loads are buffer loads whose
-  // descriptors end at this chunk's last key (K: whole keys; V: whole 64-key
-  // tiles, the partial last tile is zeroed when staged): loads past the end
-  // return zero without touching memory, so every load is issued
-  // unconditionally and the memory-counter waits never drain the other set.
+  // Tiles go from memory straight into LDS (buffer loads with an LDS
+  // destination): per tile each wave moves 4 KB of K and 4 KB of V^T, one
+  // kilobyte per instruction (64 lanes x 16 bytes, in lane order), each lane
+  // fetching the piece that the XOR permutation puts at its position.  The
+  // descriptors cover one tile: K pieces past the chunk's last key, V^T pieces
+  // past the tile and every piece of a tile past the end read as zero without
+  // touching memory.  V^T columns of keys past the end within the last tile
+  // hold whatever the cache holds there; they are zeroed in LDS.
   const int kv_hi = blk ? a.block_len : k_end;                 // keys [0, kv_hi) exist
-  const __amdgpu_buffer_rsrc_t rK =
-      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kv_hi * hd * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)vbase, (short)0, blk ? hd * a.kpad * 2 : ((kv_hi + 63) >> 6) * 64 * hd * 2, 0x00020000);
-  uint4 kA[4], vA[4], kB[4], vB[4];
-  auto load_tile = [&](uint4 (&kr)[4], uint4 (&vr)[4], int kt) __attribute__((always_inline)) {
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  int koff[4], voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int key = wv * 16 + j * 4 + (lane >> 4);
+    koff[j] = key * 256 + (((lane & 15) ^ (key & 15)) << 4);   // unit (lane & 15) ^ (key & 15) of the key
+    const int d = wv * 32 + j * 8 + (lane >> 3);
+    const int ku = (lane & 7) ^ (d & 7);
+    voff[j] = blk ? (d * a.kpad + ku * 8) * 2 : d * 128 + ku * 16;
+  }
+  auto issue = [&](auto s1c, int kt) __attribute__((always_inline)) {
+    constexpr bool S1 = decltype(s1c)::value;
+    uint16_t* dK = S1 ? sK1 : sK0;
+    uint16_t* dV = S1 ? sV1 : sV0;
     const bool live = kt < k_end;                              // uniform
+    const int nk = live ? min(64, kv_hi - kt) : 0;
+    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kbase + (size_t)kt * hd), (short)0, nk * hd * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(blk ? vbase : vbase + (size_t)(kt >> 6) * 64 * hd), (short)0,
+        live ? (blk ? hd * a.kpad * 2 : 64 * hd * 2) : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int ci = tid + j * 256;
-      const int key = ci >> 4, col = (ci & 15) * 8;
-      const int ko = live ? ((kt + key) * hd + col) * 2 : 0x40000000;
-      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, ko, 0, 0));
-      const int d = ci >> 3, vc8 = (ci & 7) * 8;
-      const int vo = !live ? 0x40000000
-                           : (blk ? (d * a.kpad + vc8) * 2 : ((kt >> 6) * 64 * hd + d * 64 + vc8) * 2);
-      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rV, vo, 0, 0));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rK, (__attribute__((address_space(3))) void*)(dK + (wv * 4 + j) * 512), 16, koff[j], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rV, (__attribute__((address_space(3))) void*)(dV + (wv * 4 + j) * 512), 16, voff[j], 0, 0, 0);
     }
   };
-  auto store_tile = [&](const uint4 (&kr)[4], const uint4 (&vr)[4], int kt) __attribute__((always_inline)) {
-    const int nvalid = min(64, k_end - kt);
+  // zero the V^T columns of keys >= nvalid (the last, partial tile)
+  auto zero_v = [&](uint16_t* V, int nvalid) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ci = tid + j * 256;
-      const int key = ci >> 4, col = (ci & 15) * 8;
-      *(uint4*)(sK + key * KT_STRIDE + col) = kr[j];
-      const int d = ci >> 3, vc8 = (ci & 7) * 8;
-      uint4 v = vr[j];
-      if (nvalid < 64) {                 // zero the columns of keys past the end
-        uint16_t e[8];
-        __builtin_memcpy(e, &v, 16);
+    for (int m = 0; m < 4; ++m) {
+      const int u = tid + m * 256;                             // 16-byte unit of the tile
+      const int d = u >> 3, ku = (u & 7) ^ (d & 7);
+      uint4 v = *(uint4*)(V + u * 8);
+      uint16_t e[8];
+      __builtin_memcpy(e, &v, 16);
 #pragma unroll
-        for (int x = 0; x < 8; ++x)
-          if (vt_key(vc8 + x) >= nvalid) e[x] = 0;
-        __builtin_memcpy(&v, e, 16);
-      }
-      *(uint4*)(sV + d * VT_STRIDE + vc8) = v;
+      for (int x = 0; x < 8; ++x)
+        if (vt_key(ku * 8 + x) >= nvalid) e[x] = 0;
+      __builtin_memcpy(&v, e, 16);
+      *(uint4*)(V + u * 8) = v;
     }
   };
+  // fragment offsets (bytes) of this lane: K for ds = 0..3 (+ kb*4096),
+  // V^T for ks = 0..1 (+ db*2048)
+  int kfo[4], vfo[2];
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) kfo[ds] = k_lds_off(lr, ds * 4 + lq);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) vfo[ks] = v_lds_off(lr, ks * 4 + lq);
 
-  // One tile step: stage the tile, refill its register set two tiles ahead,
-  // compute.  A step past the end (odd tile count) sees no key: every score
-  // is masked, alpha = 1 and p = 0, so it changes nothing.
-  auto step = [&](uint4 (&kr)[4], uint4 (&vr)[4], int kt) __attribute__((always_inline)) {
-    const int nvalid = min(64, k_end - kt);
-    __syncthreads();                     // the previous tile is no longer read
-    store_tile(kr, vr, kt);
-    __syncthreads();
-    load_tile(kr, vr, kt + 128);
-    if (wact) {
-      // S^T for 4 blocks of 16 keys
-      floatx4_t s[4];
+  // The tile's work for the wave's NT query tiles.  Every K and V^T
+  // fragment read from LDS feeds one MFMA per query tile.
+  auto compute = [&](auto s1c, auto ntc, int kt, int nvalid) __attribute__((always_inline)) {
+    constexpr bool S1 = decltype(s1c)::value;
+    constexpr int NT = decltype(ntc)::value;
+    const char* sKb = (const char*)(S1 ? sK1 : sK0);
+    const char* sVb = (const char*)(S1 ? sV1 : sV0);
+    // S^T for 4 blocks of 16 keys
+    floatx4_t s[NT][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int ds = 0; ds < 4; ++ds) {
-          bf16x8_t kf = ld_bf16x8(sK + (kb * 16 + lr) * KT_STRIDE + ds * 32 + lq * 8);
-          s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ds], s[kb], 0, 0, 0);
-        }
+      for (int kb = 0; kb < 4; ++kb) s[t][kb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) {
+        const bf16x8_t kf = ld_bf16x8((const uint16_t*)(sKb + kb * 4096 + kfo[ds]));
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          s[t][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][ds], s[t][kb], 0, 0, 0);
       }
-      // Visibility: when every key of the tile is visible to every row of
-      // the wave (the common case at long context) nothing is masked;
-      // otherwise invisible keys get the score -inf.  Both paths then compute
-      // the same values: the maximum of the raw scores, scaled to base 2
-      // (scaling by a positive constant keeps the maximum), and
-      // p = 2^(s * scale - m) with one fused multiply-add.
-      const bool all_vis = !blk && nvalid == 64 && __all(kt + 63 <= lim);
-      if (!all_vis) {
+    // Visibility: when every key of the tile is visible to every row of the
+    // wave (the common case at long context) nothing is masked; otherwise
+    // invisible keys get the score -inf.
+    const bool all_vis = !blk && nvalid == 64 && __all(kt + 63 <= lmin);
+    if (!all_vis) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int kl = kb * 16 + lq * 4 + i;
-            const bool ok = kl < nvalid && (blk ? seesb != 0 : (kt + kl) <= lim);
-            s[kb][i] = ok ? s[kb][i] : -INFINITY;
+            const bool ok = kl < nvalid && (blk ? seesb[t] != 0 : (kt + kl) <= lim[t]);
+            s[t][kb][i] = ok ? s[t][kb][i] : -INFINITY;
           }
-      }
+    }
+    // Reference update.  A row needs one when some lane of the row (its
+    // four lanes hold lanes lr, lr+16, lr+32, lr+48) has a scaled score
+    // above m + REF_SLACK; the ballot, folded to 16 row bits, says which.
+    // Only then the row maximum is formed across the lanes and the row's
+    // o and l are rescaled (a row that needs none keeps m and is multiplied
+    // by exactly 1).
+    float lm[NT];
+    uint32_t rowbits[NT];
+    uint32_t anyrow = 0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mt = mx * sl2;
-      // Branch-free update: the MFMAs below read operands from every lane,
-      // so no lane may skip them.  A row with nothing visible yet keeps
-      // m = -inf, l = 0, o = 0 exactly (alpha = 1, p = 0).
-      const float mnew = fmaxf(mrow, mt);
-      const bool any = mnew != -INFINITY;
-      const float mref = any ? mnew : 0.f;
-      const float alpha = any ? __builtin_amdgcn_exp2f(mrow - mref) : 1.f;
-      // P enters the P.V product as two bf16 terms, hi = bf16(p) and
-      // lo = bf16(p - hi) (p - hi is exact in fp32), so the product carries
-      // about 16 significant bits of p instead of 8.  Rounding p itself to
-      // bf16 would make the result depend on the running maximum it was
-      // taken against, i.e. on how the keys were split into tiles and chunks.
-      float ps = 0.f;
-      bf16x8_t pf[2], pl[2];
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[t][kb][i]);
+      lm[t] = mx;
+      const uint64_t bal = __ballot(mx * sl2 > thr[t]);
+      rowbits[t] = (uint32_t)(bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xffffu;
+      anyrow |= rowbits[t];
+    }
+    if (anyrow) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // v_exp_f32 directly: the argument is <= 0 and results below
-          // 2^-126 (flushed) are negligible softmax weights
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], sl2, -mref));
-          ps += p;
-          __bf16 hi = (__bf16)p;
-          pf[kb >> 1][(kb & 1) * 4 + i] = hi;
-          pl[kb >> 1][(kb & 1) * 4 + i] = (__bf16)(p - (float)hi);
-        }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      lrow = lrow * alpha + ps;
-      // rescale only if some row's maximum grew (otherwise every alpha is 1)
-      if (__any(mnew != mrow)) {
+      for (int t = 0; t < NT; ++t) {
+        if (rowbits[t] == 0) continue;
+        float rm = lm[t];
+        rm = fmaxf(rm, __shfl_xor(rm, 16, 64));
+        rm = fmaxf(rm, __shfl_xor(rm, 32, 64));
+        const bool rn = (rowbits[t] >> lr) & 1u;
+        const float mnew = rn ? fmaxf(mref[t], rm * sl2) : mref[t];
+        // m = -inf (nothing seen yet): 2^-inf = 0, and o, l are still 0
+        const float alpha = rn ? __builtin_amdgcn_exp2f(mref[t] - mnew) : 1.f;
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          oacc[db][0] *= alpha; oacc[db][1] *= alpha; oacc[db][2] *= alpha; oacc[db][3] *= alpha;
+          oacc[t][db][0] *= alpha; oacc[t][db][1] *= alpha;
+          oacc[t][db][2] *= alpha; oacc[t][db][3] *= alpha;
         }
+        lsum[t] *= alpha;
+        mref[t] = mnew;
+        thr[t] = mnew + REF_SLACK;
       }
-      mrow = any ? mnew : mrow;
+    }
+    // Weights p = 2^(s * scale - m), one fused multiply-add and v_exp_f32
+    // each (arguments <= REF_SLACK; results below 2^-126 are negligible
+    // weights and flush to 0).  A row whose m is still -inf has only -inf
+    // scores so far, so its p are 0.  l is summed per lane (the lane's keys
+    // in a fixed order) and across the row's lanes once, at the end.
+    // P enters the P.V product as two bf16 terms, hi = bf16(p) and
+    // lo = bf16(p - hi) (p - hi is exact in fp32), so the product carries
+    // about 16 significant bits of p instead of 8.
+    // Done in two halves of 32 keys (kb 0-1, then kb 2-3), so only half of
+    // P is live at a time; each accumulator still sums its terms in the
+    // same order (keys 0-31 hi, lo, then keys 32-63 hi, lo).
+    float mr[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mr[t] = mref[t] == -INFINITY ? 0.f : mref[t];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t pf[NT], pl[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kb = ks * 2 + kh;
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][kb][i], sl2, -mr[t]));
+            lsum[t] += p;
+            const __bf16 hi = (__bf16)p;
+            pf[t][kh * 4 + i] = hi;
+            pl[t][kh * 4 + i] = (__bf16)(p - (float)hi);
+          }
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        floatx4_t o = oacc[db];
+        const bf16x8_t vf = ld_bf16x8((const uint16_t*)(sVb + db * 2048 + vfo[ks]));
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          bf16x8_t vf = ld_bf16x8(sV + (db * 16 + lr) * VT_STRIDE + ks * 32 + lq * 8);
-          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks], o, 0, 0, 0);
-          o = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[ks], o, 0, 0, 0);
+        for (int t = 0; t < NT; ++t) {
+          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[t], oacc[t][db], 0, 0, 0);
+          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[t], oacc[t][db], 0, 0, 0);
         }
-        oacc[db] = o;
       }
     }
   };
-  load_tile(kA, vA, k_begin);
-  load_tile(kB, vB, k_begin + 64);
-  for (int kt = k_begin; kt < k_end; kt += 128) {
-    step(kA, vA, kt);
-    step(kB, vB, kt + 64);
-  }
 
-  // ---- partial of this chunk: opart[((b*hkv+g)*(nc+1)+c)*qr_max + qr][d],
-  // ml[...][2]
-  if (wact && qr < QR) {
-    const size_t pi = ((size_t)(b * a.hkv + g) * (a.nc + 1) + c) * a.qr_max + qr;
-    float* op = a.opart + pi * hd;
+  // One tile step: wait until the tile is in LDS (own loads, then the
+  // barrier for everyone's; the barrier also ends every wave's reads of the
+  // other stage), start the next tile's loads into the other stage, compute.
+  // Every wave runs the same steps, with the number of query tiles it owns.
+  // No load is issued past the chunk's last tile, so none is in flight when
+  // the loop ends.
+  auto run = [&](auto ntc) __attribute__((always_inline)) {
+    auto step = [&](auto s1c, int kt) __attribute__((always_inline)) {
+      constexpr bool S1 = decltype(s1c)::value;
+      const int nvalid = min(64, k_end - kt);
+      __builtin_amdgcn_s_waitcnt(0x0f70);                     // vmcnt(0)
+      __syncthreads();
+      if (nvalid > 0 && nvalid < 64) {
+        zero_v(S1 ? sV1 : sV0, nvalid);
+        __syncthreads();
+      }
+      if (kt + 64 < k_end) issue(IntC<!S1>{}, kt + 64);
+      if constexpr (decltype(ntc)::value > 0)
+        if (nvalid > 0) compute(s1c, ntc, kt, nvalid);
+    };
+    issue(IntC<0>{}, k_begin);
+    for (int kt = k_begin; kt < k_end; kt += 128) {
+      step(IntC<0>{}, kt);
+      step(IntC<1>{}, kt + 64);
+    }
+  };
+  if (nt == 2) run(IntC<2>{});
+  else if (nt == 1) run(IntC<1>{});
+  else run(IntC<0>{});
+
+  // ---- partials of this chunk: opart[((b*hkv+g)*(nc+1)+c)*qr_max + qr][d],
+  // ml[...][2] = (m, l); l is summed over the row's four lanes in a fixed
+  // butterfly
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *(floatx4_t*)(op + db * 16 + lq * 4) = oacc[db];
-    if (lq == 0) {
-      a.ml[pi * 2 + 0] = mrow;
-      a.ml[pi * 2 + 1] = lrow;
+  for (int t = 0; t < 2; ++t) {
+    if (t >= nt) break;
+    float l = lsum[t];
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    const int qr = (rt0 + t) * 16 + lr;
+    if (qr < QR) {
+      const size_t pi = ((size_t)(b * a.hkv + g) * (a.nc + 1) + c) * a.qr_max + qr;
+      float* op = a.opart + pi * hd;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) *(floatx4_t*)(op + db * 16 + lq * 4) = oacc[t][db];
+      if (lq == 0) {
+        a.ml[pi * 2 + 0] = mref[t];
+        a.ml[pi * 2 + 1] = l;
+      }
     }
   }
 }
