@@ -210,7 +210,7 @@ def main():
     import torch
 
     from lossless_decoding_amd import _lib as C
-    from lossless_decoding_amd.engine import Engine
+    from lossless_decoding_amd.engine import Engine, attn_chunk_for
     from synth import workloads
     from synth.device import fill_weights_device
 
@@ -227,9 +227,7 @@ def main():
     t0 = time.time()
     # both contexts fold attention over the same key chunks, so their rows are
     # bit-identical (the lossless check below compares them token for token)
-    chunk = 64
-    while chunk < 2048 and chunk * 64 < max_ctx:
-        chunk *= 2
+    chunk = attn_chunk_for(max_ctx)
     cfg = C.OrthrusConfig.make(sh["L"], sh["d"], sh["hq"], sh["hkv"], sh["hd"], sh["F"], V, K,
                                True, B, max_ctx, attn_chunk=chunk)
     lay, total = C.weight_layout(cfg)

@@ -211,7 +211,8 @@ int orthrus_timing_read(orthrus_ctx* ctx, double* ms, int64_t* launches);
  * Padding rows are unspecified.  attn: device
  * [n_layers][rows_cap][n_q_heads*head_dim] in the model dtype; every later
  * pass writes each layer's attention output (the O projection's input).
- * Errors: EINVAL. */
+ * A pass with more rows than rows_cap writes neither tap (both keep what an
+ * earlier pass wrote).  Errors: EINVAL. */
 int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_cap);
 
 /* Kernel (a) alone: block attention of `batch` sequences, bf16.  q: [batch]

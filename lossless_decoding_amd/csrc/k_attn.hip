@@ -82,12 +82,31 @@ __host__ __device__ inline int attn_row_groups(int qr) { return ((qr + 15) / 16 
 
 template <int N> struct IntC { static constexpr int value = N; };
 
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
-  // two stages of (K tile, V^T tile), 16 KB each
+#ifndef ATT_STAGES
+#define ATT_STAGES 2
+#endif
+
+__global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
+  // ATT_STAGES stages of (K tile, V^T tile), 16 KB each
   __shared__ __attribute__((aligned(16))) uint16_t sK0[64 * 128];
   __shared__ __attribute__((aligned(16))) uint16_t sV0[128 * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sK1[64 * 128];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[128 * 64];
+#if ATT_STAGES > 2
+  __shared__ __attribute__((aligned(16))) uint16_t sK2[64 * 128];
+  __shared__ __attribute__((aligned(16))) uint16_t sV2[128 * 64];
+#else
+  uint16_t* const sK2 = sK0;
+  uint16_t* const sV2 = sV0;
+#endif
+  auto kst = [&](auto stc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(stc)::value;
+    if constexpr (S == 0) return sK0; else if constexpr (S == 1) return sK1; else return sK2;
+  };
+  auto vst = [&](auto stc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(stc)::value;
+    if constexpr (S == 0) return sV0; else if constexpr (S == 1) return sV1; else return sV2;
+  };
   const int c = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
   const PassInfo& P = a.P;
@@ -178,9 +197,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
     voff[j] = blk ? (d * a.kpad + ku * 8) * 2 : d * 128 + ku * 16;
   }
   auto issue = [&](auto s1c, int kt) __attribute__((always_inline)) {
-    constexpr bool S1 = decltype(s1c)::value;
-    uint16_t* dK = S1 ? sK1 : sK0;
-    uint16_t* dV = S1 ? sV1 : sV0;
+    uint16_t* dK = kst(s1c);
+    uint16_t* dV = vst(s1c);
     const bool live = kt < k_end;                              // uniform
     const int nk = live ? min(64, kv_hi - kt) : 0;
     const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
@@ -223,20 +241,20 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   // The tile's work for the wave's NT query tiles.  Every K and V^T
   // fragment read from LDS feeds one MFMA per query tile.
   auto compute = [&](auto s1c, auto ntc, int kt, int nvalid) __attribute__((always_inline)) {
-    constexpr bool S1 = decltype(s1c)::value;
     constexpr int NT = decltype(ntc)::value;
-    const char* sKb = (const char*)(S1 ? sK1 : sK0);
-    const char* sVb = (const char*)(S1 ? sV1 : sV0);
+    const char* sKb = (const char*)kst(s1c);
+    const char* sVb = (const char*)vst(s1c);
     // S^T for 4 blocks of 16 keys
     floatx4_t s[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) s[t][kb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    // dimension steps outer, so consecutive MFMAs use different accumulators
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) {
+      for (int kb = 0; kb < 4; ++kb) {
         const bf16x8_t kf = ld_bf16x8((const uint16_t*)(sKb + kb * 4096 + kfo[ds]));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
@@ -330,14 +348,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
             pf[t][kh * 4 + i] = hi;
             pl[t][kh * 4 + i] = (__bf16)(p - (float)hi);
           }
+      // two dimension blocks at a time, hi terms before lo terms, so an
+      // MFMA never waits on the one just issued (same per-accumulator order)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8_t vf = ld_bf16x8((const uint16_t*)(sVb + db * 2048 + vfo[ks]));
+      for (int db = 0; db < 8; db += 2) {
+        const bf16x8_t vf0 = ld_bf16x8((const uint16_t*)(sVb + db * 2048 + vfo[ks]));
+        const bf16x8_t vf1 = ld_bf16x8((const uint16_t*)(sVb + (db + 1) * 2048 + vfo[ks]));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[t], oacc[t][db], 0, 0, 0);
-          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pl[t], oacc[t][db], 0, 0, 0);
-        }
+        for (int t = 0; t < NT; ++t)
+          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pf[t], oacc[t][db], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pf[t], oacc[t][db + 1], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pl[t], oacc[t][db], 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pl[t], oacc[t][db + 1], 0, 0, 0);
       }
     }
   };
@@ -348,17 +376,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
   // Every wave runs the same steps, with the number of query tiles it owns.
   // No load is issued past the chunk's last tile, so none is in flight when
   // the loop ends.
+#if ATT_STAGES == 2
   auto run = [&](auto ntc) __attribute__((always_inline)) {
     auto step = [&](auto s1c, int kt) __attribute__((always_inline)) {
-      constexpr bool S1 = decltype(s1c)::value;
+      constexpr int S1 = decltype(s1c)::value;
       const int nvalid = min(64, k_end - kt);
       __builtin_amdgcn_s_waitcnt(0x0f70);                     // vmcnt(0)
       __syncthreads();
       if (nvalid > 0 && nvalid < 64) {
-        zero_v(S1 ? sV1 : sV0, nvalid);
+        zero_v(vst(s1c), nvalid);
         __syncthreads();
       }
-      if (kt + 64 < k_end) issue(IntC<!S1>{}, kt + 64);
+      if (kt + 64 < k_end) issue(IntC<1 - S1>{}, kt + 64);
       if constexpr (decltype(ntc)::value > 0)
         if (nvalid > 0) compute(s1c, ntc, kt, nvalid);
     };
@@ -368,6 +397,35 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(AttnArgs a) {
       step(IntC<1>{}, kt + 64);
     }
   };
+#else
+  // Three stages: two tiles in flight while one is computed.  Every step
+  // issues the tile two ahead (past the end: no memory access, zeros), so
+  // exactly one later tile's 8 loads per wave are outstanding when a step
+  // waits for its own; the loop drains the rest before the partials.
+  auto run = [&](auto ntc) __attribute__((always_inline)) {
+    auto step = [&](auto sc_, int kt) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc_)::value;
+      const int nvalid = min(64, k_end - kt);
+      __builtin_amdgcn_s_waitcnt(0x0f78);                     // vmcnt(8)
+      __syncthreads();
+      if (nvalid > 0 && nvalid < 64) {
+        zero_v(vst(sc_), nvalid);
+        __syncthreads();
+      }
+      issue(IntC<(S + 2) % 3>{}, kt + 128);
+      if constexpr (decltype(ntc)::value > 0)
+        if (nvalid > 0) compute(sc_, ntc, kt, nvalid);
+    };
+    issue(IntC<0>{}, k_begin);
+    issue(IntC<1>{}, k_begin + 64);
+    for (int kt = k_begin; kt < k_end; kt += 192) {
+      step(IntC<0>{}, kt);
+      step(IntC<1>{}, kt + 64);
+      step(IntC<2>{}, kt + 128);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);                       // vmcnt(0)
+  };
+#endif
   if (nt == 2) run(IntC<2>{});
   else if (nt == 1) run(IntC<1>{});
   else run(IntC<0>{});

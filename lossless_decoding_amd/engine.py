@@ -9,6 +9,17 @@ import torch
 from . import _lib as C
 
 
+def attn_chunk_for(max_ctx: int) -> int:
+    """Attention key-chunk size for a context of max_ctx slots: the smallest
+    power of two from 64 up to 2048 that cuts max_ctx into at most 64 chunks.
+    Two contexts give bit-identical attention rows only with the same chunk
+    size, so a context and its greedy (K = 0) twin should share this value."""
+    chunk = 64
+    while chunk < 2048 and chunk * 64 < max_ctx:
+        chunk *= 2
+    return chunk
+
+
 def _ptr(t: torch.Tensor | None) -> int | None:
     return None if t is None else t.data_ptr()
 

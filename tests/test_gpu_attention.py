@@ -80,16 +80,20 @@ def test_block_attention_small_all_rows(lk, kb):
 
 
 @pytest.mark.slow
-def test_block_attention_full_size_sampled():
-    """The largest microbenchmark point: 16 sequences x 32768 cached keys, 32
-    block queries of 32 heads over 8 KV heads and 32 block keys; sampled
+@pytest.mark.parametrize("B,rows,lk", [(16, 32, 32768), (16, 33, 8192), (8, 33, 32768)])
+def test_block_attention_full_size_sampled(B, rows, lk):
+    """Full sizes: the largest microbenchmark point (16 sequences x 32768
+    cached keys, 32 query tokens) and the draft pass of the two large decode
+    workloads (16 x 8192 and 8 x 32768 cached keys, 33 query tokens: anchor
+    and 32 masks); 32 query heads over 8 KV heads, 32 block keys.  Sampled
     (sequence, row, head) outputs against the oracle."""
-    B, rows, hq, hkv, lk, kb = 16, 32, 32, 8, 32768, 32
+    hq, hkv, kb = 32, 8, 32
     G = hq // hkv
+    print(f"[attention] B={B} rows={rows} lk={lk}", flush=True)
     q, kc, vc, kbk, vbk, cap = make(B, rows, hq, hkv, lk, kb, 0)
     out = run(B, rows, hq, hkv, lk, kb, q, kc, vc, kbk, vbk, cap)
-    rng = np.random.default_rng(0)
-    for _ in range(6):
+    rng = np.random.default_rng(lk + rows)
+    for _ in range(8):
         b, r, h = int(rng.integers(B)), int(rng.integers(rows)), int(rng.integers(hq))
         g = h // G
         keys = torch.cat([kc[b, g, :lk], kbk[b, g, :kb]]).float().cpu().numpy().astype(np.float64)
