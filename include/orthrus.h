@@ -93,11 +93,13 @@ typedef struct orthrus_config {
   int32_t dtype;          /* ORTHRUS_F32 or ORTHRUS_BF16 */
   int32_t max_batch;      /* sequences per call, 1..256 */
   int32_t max_ctx;        /* KV slots per sequence (cache capacity) */
-  int32_t attn_chunk;     /* keys per attention chunk: 0 = chosen from max_ctx, else a power
-                             of two in [64, 4096].  Attention partials are folded per chunk
-                             of absolute cache positions, so two contexts give bit-identical
-                             rows (e.g. a block_k = 32 context and its block_k = 0 greedy
-                             twin) only if their attn_chunk values are equal. */
+  int32_t attn_chunk;     /* keys per attention chunk: 0 = orthrus_default_attn_chunk(
+                             max_batch, max_ctx), else a power of two in [64, 4096].
+                             Attention partials are folded per chunk of absolute cache
+                             positions, so two contexts give bit-identical rows (e.g. a
+                             block_k = 32 context and its block_k = 0 greedy twin, or a batch
+                             and one of its sequences alone) only if their attn_chunk values
+                             are equal. */
 } orthrus_config;
 
 typedef struct orthrus_sizes {
@@ -233,6 +235,14 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
                             void* stream);
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len);
+
+/* The attention key chunk a context gets for attn_chunk = 0: the smallest
+ * power of two in [64, 4096] that cuts max_ctx (rounded up to 64) into at
+ * most 64 chunks and max_batch x chunks to at most 160 (the chunk partials,
+ * 64 KB per chunk and KV head, are written and read back once per pass).
+ * Kernel (a) alone (orthrus_block_attention) uses the same rule with
+ * (batch, ctx_len).  Errors: EINVAL (returned as a negative value). */
+int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx);
 
 const char* orthrus_strerror(int code);
 int orthrus_last_hip_error(void);

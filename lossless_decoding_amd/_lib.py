@@ -18,6 +18,7 @@ EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_verify_accept", "orthrus_commit_kv",
     "orthrus_set_debug", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_attention_workspace",
+    "orthrus_default_attn_chunk",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
 
@@ -86,6 +87,8 @@ def lib():
                                               i32, vp, vp, u64, vp]
         L.orthrus_attention_workspace.argtypes = [i32, i32, i32, i32, i32]
         L.orthrus_attention_workspace.restype = u64
+        L.orthrus_default_attn_chunk.argtypes = [i32, i32]
+        L.orthrus_default_attn_chunk.restype = i32
         L.orthrus_strerror.argtypes = [ctypes.c_int]
         L.orthrus_strerror.restype = ctypes.c_char_p
         L.orthrus_last_hip_error.argtypes = []
@@ -184,6 +187,12 @@ def orthrus_timing_read(ctx):
 
 def orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len) -> int:
     return lib().orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len)
+
+
+def orthrus_default_attn_chunk(max_batch, max_ctx) -> int:
+    r = lib().orthrus_default_attn_chunk(max_batch, max_ctx)
+    _check("orthrus_default_attn_chunk", min(r, 0))
+    return r
 
 
 def orthrus_block_attention(batch, rows, hq, hkv, q, k_cache, v_cache, cap, ctx_len, k_block,

@@ -63,6 +63,21 @@ struct Layout {
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
 };
 
+// Default attention key chunk: the smallest power of two in [64, 4096] that
+// cuts a sequence of `slots` keys into at most 64 chunks and the batch into
+// at most 160 (batch x chunks), so the chunk partials (64 KB per chunk and
+// KV head) stay small next to the keys they summarise while short contexts
+// still spread over the chip.
+static int default_attn_chunk(int batch, int slots) {
+  int sc = 64;
+  while (sc < 4096) {
+    const long nch = (slots + sc - 1) / sc;
+    if (nch <= 64 && (long)batch * nch <= 160) break;
+    sc *= 2;
+  }
+  return sc;
+}
+
 int validate(const orthrus_config* c) {
   if (!c) return ORTHRUS_EINVAL;
   if (c->n_layers < 1 || c->d_model < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 ||
@@ -106,10 +121,7 @@ void make_layout(const orthrus_config& c, Layout& y) {
   // attention key chunk: fixed per context so that a row's result does not
   // depend on which pass computes it
   int sc = c.attn_chunk;
-  if (sc == 0) {
-    sc = 64;
-    while (sc < 2048 && sc * 64 < y.cap) sc *= 2;
-  }
+  if (sc == 0) sc = default_attn_chunk(c.max_batch, y.cap);
   y.sc = sc;
   y.nc = (y.cap + sc - 1) / sc;
   y.qr_max = y.tmax * y.G;
@@ -358,8 +370,9 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   g0.eps = eps;
   g0.P = P; g0.hq = y.hq; g0.hkv = y.hkv;
   g0.rope = S<float2>(c, y.w_rope); g0.q_out = q; g0.cap = y.cap; g0.kpad = y.kpad;
-  // residual add of the O / down slice partials (nsl = 8) and the RMSNorm
-  // that produces the next GEMM's bf16 input
+  // residual add of the O / down slice partials (nsl = 8 when those GEMMs
+  // split K; otherwise they added into h themselves) and the RMSNorm that
+  // produces the next GEMM's bf16 input
   float* rpart = S<float>(c, y.w_rpart);
   const size_t rps = (size_t)y.rmax * y.d;
   auto rnorm = [&](int nsl, uint64_t gain_off) {
@@ -429,7 +442,8 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
         run(g, y.p_o[l], 0, rows, y.qd, y.d, EP_RESID);
       }
     }
-    rnorm(8, y.p_ffnnorm[l]);
+    rnorm(P.kind == PASS_DRAFT ? gemm_bf16_split_slices(BK, NA, y.d, EP_RESID)
+                               : gemm_bf16_split_slices(rows, 0, y.d, EP_RESID), y.p_ffnnorm[l]);
     {
       Tick t(c, pb + R_GU, s);
       GemmArgs g = g0;
@@ -445,7 +459,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     }
     // residual + the next RMSNorm: the next layer's attention norm, or the
     // final norm in front of the LM head
-    rnorm(8, l + 1 < y.L ? y.p_anorm[l + 1] : y.p_fnorm);
+    rnorm(gemm_bf16_split_slices(rows, 0, y.d, EP_RESID), l + 1 < y.L ? y.p_anorm[l + 1] : y.p_fnorm);
   }
   if (!want_tokens) return;
   Tick tl(c, pb + R_LM, s);
@@ -771,8 +785,7 @@ int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len) {
   if (batch < 1 || rows < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || ctx_len < 0) return 0;
-  int sc = 256;
-  while (sc < 2048 && sc * 32 < ctx_len) sc *= 2;
+  int sc = default_attn_chunk(batch, ctx_len);
   int nc = (ctx_len + sc - 1) / sc;
   uint64_t qr = (uint64_t)rows * (n_q_heads / n_kv_heads);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * qr;
@@ -795,8 +808,7 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
     return ORTHRUS_EINVAL;
   uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
   if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
-  int sc = 256;
-  while (sc < 2048 && sc * 32 < ctx_len) sc *= 2;
+  int sc = default_attn_chunk(batch, ctx_len);
   int nc = (ctx_len + sc - 1) / sc;
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
   AttnArgs a{};
@@ -810,6 +822,11 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   a.out = out; a.fixed_ctx = ctx_len; a.block_len = block_len;
   launch_attention_bf16(a, (hipStream_t)stream);
   return check_launch();
+}
+
+int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx) {
+  if (max_batch < 1 || max_ctx < 1) return ORTHRUS_EINVAL;
+  return default_attn_chunk(max_batch, round_up(max_ctx, 64));
 }
 
 const char* orthrus_strerror(int code) {

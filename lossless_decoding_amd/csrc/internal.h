@@ -129,6 +129,8 @@ struct GemmArgs {
   int M, K, N, row0;
   const u32x4_t* W2; int M2, row02;   // optional second segment (other weights and rows)
   int gy0;                      // row blocks of the first segment (set by the launcher)
+  int gyt;                      // row blocks of both segments (set by the launcher)
+  int flat;                     // 1-D grid over (column group, row block) (set by the launcher)
   const uint16_t* X; int ldx;   // bf16 input rows
   // split-K partials [8][M][N] and completion counters (zero between launches)
   float* part; unsigned* cnt;
@@ -145,6 +147,9 @@ struct GemmArgs {
 };
 void launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 int gemm_bf16_groups(int N);
+// 0, or the K slices whose partials an EP_RESID launch of these rows leaves
+// for the residual + RMSNorm kernel
+int gemm_bf16_split_slices(int M, int M2, int N, int ep);
 // fp32: W canonical row-major [N][K] (for SwiGLU: gate at W, up at W2).
 void launch_gemm_f32(const float* W, const float* W2, const float* X, int ldx, int M, int K,
                      int N, const GemmOut& o, hipStream_t s);

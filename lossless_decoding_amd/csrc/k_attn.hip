@@ -1,21 +1,23 @@
 // Block attention over the shared KV cache (the draft pass's anchor + mask
 // rows, the verify pass's causal rows, prefill rows).
 //
-// bf16 path.  A workgroup handles (key chunk, KV head, sequence,
-// group of four 16-row query tiles); the query rows of a sequence are its
-// tokens x the G query heads of the KV head, so each 64-key K/V tile staged
-// in LDS serves the whole GQA group.  A wave owns one query tile.
+// bf16 path.  A workgroup handles (key chunk, KV head, sequence, group of
+// eight 16-row query tiles); the query rows of a sequence are its tokens x
+// the G query heads of the KV head, so each 64-key K/V tile staged in LDS
+// serves the whole GQA group.  A wave owns two query tiles.
 // MFMA: S^T = K . Q^T (keys x rows) and O^T = V^T . P^T (dims x rows), so a
 // lane always holds one query row and the softmax statistics stay in-lane.
-// Online softmax in fp32 (base-2 exponent); the next K/V tile is loaded into
-// registers while the current one is computed.  Chunks are SC keys aligned
-// to absolute cache positions; each writes its partial (max, sum,
-// unnormalised output) and the merge kernel combines a row's partials in
-// increasing chunk order, the draft block's keys last.  A row's result
-// therefore depends only on which keys it sees, never on the other rows of
-// the pass: fully masked tiles and chunks are exact no-ops, masked keys are
-// removed by selection (never by multiplying stale values), and keys past
-// the pass's last written slot are zeroed when staged.
+// Softmax in fp32 with a base-2 exponent against a per-row reference that is
+// raised only when a tile's scores exceed it by more than 2^8.  K/V tiles go
+// from memory straight into a two-stage LDS ring while the other stage is
+// computed.  Chunks are SC keys aligned to absolute cache positions; each
+// writes its partial (reference, sum, unnormalised output) and the merge
+// kernel combines a row's partials in increasing chunk order, the draft
+// block's keys last.  A row's result therefore depends only on which keys
+// it sees, never on the other rows of the pass: fully masked tiles and
+// chunks are exact no-ops, masked keys are removed by selection (never by
+// multiplying stale values), and keys past the pass's last written slot are
+// zeroed when staged.
 //
 // fp32 path: one wave per (row, query head), keys in order (check models).
 #include "internal.h"
@@ -107,7 +109,6 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     constexpr int S = decltype(stc)::value;
     if constexpr (S == 0) return sV0; else if constexpr (S == 1) return sV1; else return sV2;
   };
-  const int c = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
   const PassInfo& P = a.P;
   const int T = a.fixed_ctx >= 0 ? P.Kx : P.tokens_per_seq();
@@ -115,7 +116,25 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
   const int QR = T * G;
   const int NRT = (QR + 15) >> 4;
   const int NRG = attn_row_groups(QR);
-  const int b = blockIdx.z / NRG, rg = blockIdx.z - b * NRG;
+  // 1-D grid: every (cache chunk, KV head, sequence x row group) first, then
+  // the short block-chunk workgroups, which fill the tail
+  int c, g, zz;
+  {
+    const int ncache = a.nc * a.hkv * P.B * NRG;
+    int id = blockIdx.x;
+    if (id < ncache) {
+      c = id % a.nc;
+      const int r = id / a.nc;
+      g = r % a.hkv;
+      zz = r / a.hkv;
+    } else {
+      id -= ncache;
+      c = a.nc;
+      g = id % a.hkv;
+      zz = id / a.hkv;
+    }
+  }
+  const int b = zz / NRG, rg = zz - b * NRG;
   const bool blk = (c == a.nc);
   const int hd = 128;
   const int H = a.hq * hd;
@@ -540,7 +559,7 @@ void launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
   const int B = a.P.B;
   const int T = a.fixed_ctx >= 0 ? a.P.Kx : a.P.tokens_per_seq();
   const int nrg = attn_row_groups(T * (a.hq / a.hkv));
-  hipLaunchKernelGGL(k_attn_bf16, dim3(a.nc + 1, a.hkv, B * nrg), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_attn_bf16, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
   const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
   const int npairs = rows * a.hq;
   hipLaunchKernelGGL(k_attn_merge, dim3((npairs + 3) / 4), dim3(256), 0, s, a, npairs);

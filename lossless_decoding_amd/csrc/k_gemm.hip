@@ -12,12 +12,13 @@
 //    a row's output is identical whether computed alone (plain decoding), as
 //    the anchor of a draft block or as one of K verify rows.
 //  * Work split: a wave owns one 16-column tile; a workgroup of WV waves
-//    owns WV*16 columns and up to 64 rows.  Narrow GEMMs (fewer than 128
-//    groups of 128 columns) give every K slice its own workgroup and the
-//    last workgroup of a column group adds the 8 partials; wide GEMMs keep
-//    all slices in one workgroup.
+//    owns WV*16 columns and up to max(64, 16*MT) rows (MT = 8 for passes
+//    of more than 128 rows, which halves the weight re-reads).  Launches
+//    with fewer than 128 (column group, row group) workgroups give every K
+//    slice its own workgroup and the last workgroup of a column group adds
+//    the 8 partials; the others keep all slices in one workgroup.
 //  * Streaming: every wave keeps D weight fragments in flight in a register
-//    ring.  Activations are staged 512 k at a time; the next stage is loaded
+//    ring.  Activations are staged 512 k at a time (256 at MT 8); the next stage is loaded
 //    into registers one stage ahead, so waiting for it never waits for weight
 //    loads issued after it (memory counters complete in order).
 //  * Input: bf16 rows (RMSNorm outputs, attention output, SwiGLU product).
@@ -75,13 +76,16 @@ __device__ __forceinline__ void amax_comb(float& v, int& i, float v2, int i2) {
 template <int MT, int EP, int WV, bool SPLIT>
 __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf16(GemmArgs a) {
   constexpr int COLS = WV * 16;
-  constexpr int NFR = MT * SKB;               // activation fragments per stage
+  constexpr int RPW = MT * 16 > 64 ? MT * 16 : 64;     // rows per workgroup
+  constexpr int SK = MT <= 4 ? SKB : SKB / 2;          // k-blocks per stage (64 KB of LDS at MT 8)
+  constexpr int NFR = MT * SK;                // activation fragments per stage
   constexpr int NF = (NFR + WV - 1) / WV;     // ... per wave
   // LDS: one activation stage in fragment order [mt][k-block][lane][8]; it
   // also holds the fp32 output tile (MT*16 x COLS) in the epilogue.
-  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * SKB * 32];
-  __shared__ float sRed[WV * 64];
-  __shared__ int sIdx[WV * 64];
+  static_assert(MT * 16 * COLS * 4 <= MT * 16 * SK * 32 * 2, "epilogue tile exceeds the stage");
+  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * SK * 32];
+  __shared__ float sRed[WV * RPW];
+  __shared__ int sIdx[WV * RPW];
   __shared__ int sLast;
 
   const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
@@ -89,39 +93,51 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   const int KB = a.K >> 5;                    // k-blocks of 32
   const int KSB = KB / NSL;                   // k-blocks per slice
   const int ngroups = a.N / COLS;
-  int ng, s_first;
+  int ng, s_first, by;
   if (!SPLIT) {
-    ng = blockIdx.x; s_first = 0;
+    s_first = 0;
+    if (a.flat) {
+      // 1-D grid: the row blocks of one column group are consecutive
+      // workgroups of one XCD (workgroup id mod 8), so its weights come from
+      // memory once and from that XCD's L2 for the other row blocks
+      const int id = blockIdx.x, j = id >> 3;
+      by = j % a.gyt;
+      ng = (j / a.gyt) * 8 + (id & 7);
+    } else {
+      ng = blockIdx.x; by = blockIdx.y;
+    }
   } else if ((ngroups & 7) == 0) {            // keep a column group's slices on one XCD
     const int id = blockIdx.x;
     s_first = (id >> 3) & 7;
     ng = ((id >> 6) << 3) | (id & 7);
+    by = blockIdx.y;
   } else {
     s_first = blockIdx.x % NSL;
     ng = blockIdx.x / NSL;
+    by = blockIdx.y;
   }
   // row blocks [0, gy0) belong to segment 0, the rest to segment 1 (its own
   // weights and rows: the draft pass runs the mask rows' diffusion
   // projection and the anchor rows' frozen one in one launch)
-  const bool seg1 = (int)blockIdx.y >= a.gy0;
+  const bool seg1 = by >= a.gy0;
   const u32x4_t* const Wt = seg1 ? a.W2 : a.W;
   const int Mr = seg1 ? a.M2 : a.M;
   const int row0 = seg1 ? a.row02 : a.row0;
-  const int m0 = (seg1 ? blockIdx.y - a.gy0 : blockIdx.y) * 64;   // first row of this workgroup
+  const int m0 = (seg1 ? by - a.gy0 : by) * RPW;    // first row of this workgroup
   const int kb_lo = SPLIT ? s_first * KSB : 0;
   const int nkb = SPLIT ? KSB : KB;           // k-blocks of this workgroup
   const int nbk = ng * WV + wave;             // this wave's 16-column tile
   const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(Wt + ((size_t)nbk * KB + kb_lo) * 64), (short)0, nkb * 1024, BUF_FLAGS);
 
-  // stage st: k-blocks [st*SKB, st*SKB + SKB) of this workgroup's range; the
+  // stage st: k-blocks [st*SK, st*SK + SK) of this workgroup's range; the
   // lane of fragment (mt, j) holds row mt*16 + lr, k = 32 j + 8 lq .. + 7.
   // Activations and weights are read with buffer loads whose descriptors
   // cover exactly the valid rows / this wave's k-range: out-of-range loads
   // return zero without touching memory, so every load is issued
   // unconditionally, the number of loads between a ring load and its use
   // never depends on the data, and the memory-counter waits stay exact.
-  const int vrows = Mr - m0 < 64 ? Mr - m0 : 64;           // valid rows of this workgroup
+  const int vrows = Mr - m0 < RPW ? Mr - m0 : RPW;         // valid rows of this workgroup
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + (size_t)(row0 + m0) * a.ldx), (short)0, vrows * a.ldx * 2, BUF_FLAGS);
   const int a_vo = lr * a.ldx * 2 + lq * 16;                  // lane part of the offset
@@ -130,7 +146,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
       const int fr = (wave + f * WV) % NFR;
-      const int mt = fr / SKB, kbl = st * SKB + fr % SKB;
+      const int mt = fr / SK, kbl = st * SK + fr % SK;
       // k-blocks past this workgroup's range are pushed out of the
       // descriptor (range checks apply to the VGPR offset)
       const int so = kbl < nkb ? (mt * 16 * a.ldx + (kb_lo + kbl) * 32) * 2 : OOR;
@@ -144,14 +160,14 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       if (fr < NFR) *(u32x4_t*)(sX + ((size_t)fr * 64 + lane) * 8) = sr[f];
     }
   };
-  const int nst = (nkb + SKB - 1) / SKB;      // activation stages
+  const int nst = (nkb + SK - 1) / SK;      // activation stages
   load_stage(0);
-  // weight ring: slot i holds k-block st*SKB + i of the stage being computed;
+  // weight ring: slot i holds k-block st*SK + i of the stage being computed;
   // loads past this wave's k-range fall outside the descriptor (zero, no
   // memory access)
-  u32x4_t w[SKB];
+  u32x4_t w[SK];
 #pragma unroll
-  for (int i = 0; i < SKB; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + i * 1024, 0, BUF_NT);
+  for (int i = 0; i < SK; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + i * 1024, 0, BUF_NT);
 
   write_stage();
   __syncthreads();
@@ -162,7 +178,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     tot[mt] = cur[mt];
   }
-  // Per stage: switch the LDS stage, prefetch the next one, then SKB MFMA
+  // Per stage: switch the LDS stage, prefetch the next one, then SK MFMA
   // steps, each refilling its ring slot with the k-block one stage ahead.
   // The loads are the same on every path.  Past the end of a partial last
   // stage both operands are zero, so the extra MFMAs add exact zeros.
@@ -174,15 +190,15 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     }
     load_stage(st + 1);
 #pragma unroll
-    for (int i = 0; i < SKB; ++i) {
-      const int kk = st * SKB + i;
+    for (int i = 0; i < SK; ++i) {
+      const int kk = st * SK + i;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SKB + i) * 64 + lane) * 8);
+        const u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SK + i) * 64 + lane) * 8);
         cur[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[i]), as_bf16x8(xv),
                                                           cur[mt], 0, 0, 0);
       }
-      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + (kk + SKB) * 1024, 0, BUF_NT);
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + (kk + SK) * 1024, 0, BUF_NT);
       if (!SPLIT && kk < nkb && (kk + 1) % KSB == 0) {   // slice done: add in slice order
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -218,8 +234,8 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     // partial layout [slice][m-group][col group][mt][wave][lane][4]: one
     // 16-byte device-scope store / load per lane and row tile (a wave moves
     // 1 KB contiguous)
-    const size_t pstride = (size_t)gridDim.y * ngroups * MT * WV * 256;
-    float* pbase = a.part + ((size_t)blockIdx.y * ngroups + ng) * MT * WV * 256;
+    const size_t pstride = (size_t)a.gyt * ngroups * MT * WV * 256;
+    float* pbase = a.part + ((size_t)by * ngroups + ng) * MT * WV * 256;
     const __amdgpu_buffer_rsrc_t rPt =
         __builtin_amdgcn_make_buffer_rsrc((void*)pbase, (short)0, 0x7fffffff, BUF_FLAGS);
     auto poff = [&](int s, int mt) {
@@ -232,7 +248,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      unsigned* cp = a.cnt + blockIdx.y * ngroups + ng;
+      unsigned* cp = a.cnt + by * ngroups + ng;
       unsigned old = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       sLast = old == NSL - 1;
       if (old == NSL - 1)          // every slice has arrived: reset for the next launch
@@ -313,13 +329,13 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       amax_comb(bv, bi, v2, i2);
       v2 = __shfl_xor(bv, 32, 64); i2 = __shfl_xor(bi, 32, 64);
       amax_comb(bv, bi, v2, i2);
-      if (lq == 0) { sRed[wave * 64 + mt * 16 + lr] = bv; sIdx[wave * 64 + mt * 16 + lr] = bi; }
+      if (lq == 0) { sRed[wave * RPW + mt * 16 + lr] = bv; sIdx[wave * RPW + mt * 16 + lr] = bi; }
     }
     __syncthreads();
     if (tid < MT * 16 && m0 + tid < Mr) {
       float bv = sRed[tid];
       int bi = sIdx[tid];
-      for (int w = 1; w < WV; ++w) amax_comb(bv, bi, sRed[w * 64 + tid], sIdx[w * 64 + tid]);
+      for (int w = 1; w < WV; ++w) amax_comb(bv, bi, sRed[w * RPW + tid], sIdx[w * RPW + tid]);
       float2* ap = a.amax + (size_t)(row0 + m0 + tid) * ngroups + ng;
       st_agent(&ap->x, bv);
       st_agent(&ap->y, __int_as_float(bi));
@@ -328,9 +344,9 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0) {
-      unsigned* cp = a.cnt + gridDim.y * ngroups;
+      unsigned* cp = a.cnt + a.gyt * ngroups;
       unsigned old = __hip_atomic_fetch_add(cp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      unsigned total = (unsigned)ngroups * gridDim.y;   // one survivor per column group
+      unsigned total = (unsigned)ngroups * a.gyt;   // one workgroup per (column group, row block)
       sLast = old == total - 1;
       if (old == total - 1) __hip_atomic_store(cp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -435,11 +451,30 @@ static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
     case 1: hipLaunchKernelGGL((k_gemm_bf16<1, EP, WV, SPLIT>), grid, block, 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, WV, SPLIT>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<8, EP, WV, SPLIT>), grid, block, 0, s, a); break;
   }
 }
 
 int gemm_bf16_groups(int N) { return N / 128; }
+
+// rows per workgroup and workgroup rows of a launch (both segments)
+static int gemm_rows_per_wg(int M, int M2) {
+  const int Mx = M > M2 ? M : M2;
+  return Mx > 128 ? 128 : 64;
+}
+
+// Split K over workgroups only when the column groups times the row groups
+// of the launch are too few to fill the chip without it: fewer than 128,
+// or fewer than 256 for EP_RESID, whose split form only writes partials (no
+// in-kernel fixup).  0 or the number of K slices: for EP_RESID the residual
+// + RMSNorm kernel that follows must add that many slice partials.
+int gemm_bf16_split_slices(int M, int M2, int N, int ep) {
+  if (M2 < 0) M2 = 0;
+  const int rpw = gemm_rows_per_wg(M, M2);
+  const int gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
+  return (N / 128) * gy >= (ep == EP_RESID ? 256 : 128) ? 0 : NSL;
+}
 
 // Shape rules: N a multiple of 128, K a multiple of 256 (8 slices of whole
 // k-blocks).  A second segment (W2, M2, row02: same N, K and input buffer)
@@ -449,10 +484,13 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   if (!a.W2 || a.M2 <= 0) { a.W2 = nullptr; a.M2 = 0; }
   if (a.M <= 0 && a.M2 <= 0) return;
   const int Mx = a.M > a.M2 ? a.M : a.M2;
-  const int MT = Mx >= 64 ? 4 : (Mx + 15) / 16;
-  a.gy0 = (a.M + 63) / 64;
-  const dim3 gy(1, a.gy0 + (a.M2 + 63) / 64);
-  const bool wide = a.N / 128 >= 128;      // enough workgroups without splitting K
+  const int MT = Mx > 128 ? 8 : (Mx >= 64 ? 4 : (Mx + 15) / 16);
+  const int rpw = gemm_rows_per_wg(a.M, a.M2);   // = max(64, 16 MT)
+  a.gy0 = (a.M + rpw - 1) / rpw;
+  const dim3 gy(1, a.gy0 + (a.M2 + rpw - 1) / rpw);
+  a.gyt = gy.y;
+  a.flat = 0;
+  const bool wide = gemm_bf16_split_slices(a.M, a.M2, a.N, a.ep) == 0;
   if (!wide) {
     const dim3 grid(a.N / 128 * NSL, gy.y);
     switch (a.ep) {
@@ -463,16 +501,27 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     }
     return;
   }
+  // several row blocks with a column-group count divisible by 8: 1-D grid
+  // with each column group's row blocks on one XCD (see the kernel)
+  auto grid_of = [&](int ngroups) {
+    a.flat = gy.y > 1 && ngroups % 8 == 0;
+    return a.flat ? dim3(ngroups * gy.y, 1) : dim3(ngroups, gy.y);
+  };
   switch (a.ep) {
     case EP_SWIGLU:
       // 96-column workgroups when they divide N: the Qwen3-8B gate/up GEMM
       // (N = 24576) then has exactly one workgroup per compute unit
-      if ((a.N / 16) % 6 == 0 && MT <= 3) dispatch_mt<EP_SWIGLU, 6, false>(MT, dim3(a.N / 96, gy.y), a, s);
-      else dispatch_mt<EP_SWIGLU, 8, false>(MT, dim3(a.N / 128, gy.y), a, s);
+      if ((a.N / 16) % 6 == 0 && MT <= 3) {
+        const dim3 g = grid_of(a.N / 96);
+        dispatch_mt<EP_SWIGLU, 6, false>(MT, g, a, s);
+      } else {
+        const dim3 g = grid_of(a.N / 128);
+        dispatch_mt<EP_SWIGLU, 8, false>(MT, g, a, s);
+      }
       break;
-    case EP_RESID: dispatch_mt<EP_RESID, 8, false>(MT, dim3(a.N / 128, gy.y), a, s); break;
-    case EP_QKV: dispatch_mt<EP_QKV, 8, false>(MT, dim3(a.N / 128, gy.y), a, s); break;
-    default: dispatch_mt<EP_ARGMAX, 8, false>(MT, dim3(a.N / 128, gy.y), a, s); break;
+    case EP_RESID: { const dim3 g = grid_of(a.N / 128); dispatch_mt<EP_RESID, 8, false>(MT, g, a, s); break; }
+    case EP_QKV: { const dim3 g = grid_of(a.N / 128); dispatch_mt<EP_QKV, 8, false>(MT, g, a, s); break; }
+    default: { const dim3 g = grid_of(a.N / 128); dispatch_mt<EP_ARGMAX, 8, false>(MT, g, a, s); break; }
   }
 }
 

@@ -9,15 +9,13 @@ import torch
 from . import _lib as C
 
 
-def attn_chunk_for(max_ctx: int) -> int:
-    """Attention key-chunk size for a context of max_ctx slots: the smallest
-    power of two from 64 up to 2048 that cuts max_ctx into at most 64 chunks.
-    Two contexts give bit-identical attention rows only with the same chunk
-    size, so a context and its greedy (K = 0) twin should share this value."""
-    chunk = 64
-    while chunk < 2048 and chunk * 64 < max_ctx:
-        chunk *= 2
-    return chunk
+def attn_chunk_for(max_ctx: int, max_batch: int = 1) -> int:
+    """The library's default attention key chunk for a context of max_batch
+    sequences x max_ctx slots.  Two contexts give bit-identical attention
+    rows only with the same chunk size, so a context and its greedy (K = 0)
+    twin, or a batch and one of its sequences alone, should share one value
+    (pass it explicitly as attn_chunk)."""
+    return C.orthrus_default_attn_chunk(max_batch, max_ctx)
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
