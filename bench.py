@@ -227,7 +227,7 @@ def main():
     t0 = time.time()
     # both contexts fold attention over the same key chunks, so their rows are
     # bit-identical (the lossless check below compares them token for token)
-    chunk = attn_chunk_for(max_ctx, B)
+    chunk = attn_chunk_for(max_ctx, B, sh["hkv"])
     cfg = C.OrthrusConfig.make(sh["L"], sh["d"], sh["hq"], sh["hkv"], sh["hd"], sh["F"], V, K,
                                True, B, max_ctx, attn_chunk=chunk)
     lay, total = C.weight_layout(cfg)

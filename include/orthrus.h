@@ -94,7 +94,8 @@ typedef struct orthrus_config {
   int32_t max_batch;      /* sequences per call, 1..256 */
   int32_t max_ctx;        /* KV slots per sequence (cache capacity) */
   int32_t attn_chunk;     /* keys per attention chunk: 0 = orthrus_default_attn_chunk(
-                             max_batch, max_ctx), else a power of two in [64, 4096].
+                             max_batch, max_ctx, n_kv_heads), else a power of two in
+                             [64, 4096].
                              Attention partials are folded per chunk of absolute cache
                              positions, so two contexts give bit-identical rows (e.g. a
                              block_k = 32 context and its block_k = 0 greedy twin, or a batch
@@ -236,13 +237,16 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len);
 
-/* The attention key chunk a context gets for attn_chunk = 0: the smallest
- * power of two in [64, 4096] that cuts max_ctx (rounded up to 64) into at
- * most 64 chunks and max_batch x chunks to at most 160 (the chunk partials,
- * 64 KB per chunk and KV head, are written and read back once per pass).
- * Kernel (a) alone (orthrus_block_attention) uses the same rule with
- * (batch, ctx_len).  Errors: EINVAL (returned as a negative value). */
-int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx);
+/* The attention key chunk a context gets for attn_chunk = 0.  Every (chunk,
+ * KV head, sequence) is one workgroup that writes a 64 KB partial, read back
+ * once per pass.  The rule (measured on the decode workloads and on kernel
+ * (a) alone): the smallest power of two in [64, 4096] that gives at most 64
+ * chunks per sequence and at most 1280 (chunk, KV head, sequence)
+ * workgroups, and at least 1024 whenever 1024-key chunks still give 512 of
+ * them (cap = max_ctx rounded up to 64 keys per sequence).  Kernel (a) alone
+ * (orthrus_block_attention) uses the same rule with (batch, ctx_len,
+ * n_kv_heads).  Errors: EINVAL (returned as a negative value). */
+int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n_kv_heads);
 
 const char* orthrus_strerror(int code);
 int orthrus_last_hip_error(void);

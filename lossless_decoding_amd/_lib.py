@@ -87,7 +87,7 @@ def lib():
                                               i32, vp, vp, u64, vp]
         L.orthrus_attention_workspace.argtypes = [i32, i32, i32, i32, i32]
         L.orthrus_attention_workspace.restype = u64
-        L.orthrus_default_attn_chunk.argtypes = [i32, i32]
+        L.orthrus_default_attn_chunk.argtypes = [i32, i32, i32]
         L.orthrus_default_attn_chunk.restype = i32
         L.orthrus_strerror.argtypes = [ctypes.c_int]
         L.orthrus_strerror.restype = ctypes.c_char_p
@@ -189,8 +189,8 @@ def orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len) -> int:
     return lib().orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len)
 
 
-def orthrus_default_attn_chunk(max_batch, max_ctx) -> int:
-    r = lib().orthrus_default_attn_chunk(max_batch, max_ctx)
+def orthrus_default_attn_chunk(max_batch, max_ctx, n_kv_heads) -> int:
+    r = lib().orthrus_default_attn_chunk(max_batch, max_ctx, n_kv_heads)
     _check("orthrus_default_attn_chunk", min(r, 0))
     return r
 

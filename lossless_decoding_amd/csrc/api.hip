@@ -63,16 +63,21 @@ struct Layout {
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
 };
 
-// Default attention key chunk: the smallest power of two in [64, 4096] that
-// cuts a sequence of `slots` keys into at most 64 chunks and the batch into
-// at most 160 (batch x chunks), so the chunk partials (64 KB per chunk and
-// KV head) stay small next to the keys they summarise while short contexts
-// still spread over the chip.
-static int default_attn_chunk(int batch, int slots) {
+// Default attention key chunk for `batch` sequences of `slots` keys over
+// `kv_heads` KV heads.  Each (chunk, KV head, sequence) is a workgroup that
+// writes a 64 KB partial (fp32, 128 rows), which is 1/8 of the keys' bytes
+// at 1024-key chunks and 1/2 at 256.  The rule (a power of two in [64,
+// 4096], measured on the decode workloads and on kernel (a) alone): the
+// smallest one with at most 64 chunks per sequence and at most 1280
+// workgroups, and at least 1024 keys whenever 1024-key chunks still give
+// 512 workgroups (two per compute unit).
+static int default_attn_chunk(int batch, int slots, int kv_heads) {
+  const long pairs = (long)batch * (kv_heads > 0 ? kv_heads : 1);
+  const bool long_ok = pairs * ((slots + 1023) / 1024) >= 512;
   int sc = 64;
   while (sc < 4096) {
     const long nch = (slots + sc - 1) / sc;
-    if (nch <= 64 && (long)batch * nch <= 160) break;
+    if (nch <= 64 && pairs * nch <= 1280 && !(long_ok && sc < 1024)) break;
     sc *= 2;
   }
   return sc;
@@ -121,7 +126,7 @@ void make_layout(const orthrus_config& c, Layout& y) {
   // attention key chunk: fixed per context so that a row's result does not
   // depend on which pass computes it
   int sc = c.attn_chunk;
-  if (sc == 0) sc = default_attn_chunk(c.max_batch, y.cap);
+  if (sc == 0) sc = default_attn_chunk(c.max_batch, y.cap, c.n_kv_heads);
   y.sc = sc;
   y.nc = (y.cap + sc - 1) / sc;
   y.qr_max = y.tmax * y.G;
@@ -785,7 +790,7 @@ int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len) {
   if (batch < 1 || rows < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || ctx_len < 0) return 0;
-  int sc = default_attn_chunk(batch, ctx_len);
+  int sc = default_attn_chunk(batch, ctx_len, n_kv_heads);
   int nc = (ctx_len + sc - 1) / sc;
   uint64_t qr = (uint64_t)rows * (n_q_heads / n_kv_heads);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * qr;
@@ -808,7 +813,7 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
     return ORTHRUS_EINVAL;
   uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
   if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
-  int sc = default_attn_chunk(batch, ctx_len);
+  int sc = default_attn_chunk(batch, ctx_len, n_kv_heads);
   int nc = (ctx_len + sc - 1) / sc;
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
   AttnArgs a{};
@@ -824,9 +829,9 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   return check_launch();
 }
 
-int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx) {
-  if (max_batch < 1 || max_ctx < 1) return ORTHRUS_EINVAL;
-  return default_attn_chunk(max_batch, round_up(max_ctx, 64));
+int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n_kv_heads) {
+  if (max_batch < 1 || max_ctx < 1 || n_kv_heads < 1) return ORTHRUS_EINVAL;
+  return default_attn_chunk(max_batch, round_up(max_ctx, 64), n_kv_heads);
 }
 
 const char* orthrus_strerror(int code) {

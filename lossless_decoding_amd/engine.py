@@ -9,13 +9,13 @@ import torch
 from . import _lib as C
 
 
-def attn_chunk_for(max_ctx: int, max_batch: int = 1) -> int:
+def attn_chunk_for(max_ctx: int, max_batch: int = 1, n_kv_heads: int = 8) -> int:
     """The library's default attention key chunk for a context of max_batch
-    sequences x max_ctx slots.  Two contexts give bit-identical attention
-    rows only with the same chunk size, so a context and its greedy (K = 0)
-    twin, or a batch and one of its sequences alone, should share one value
-    (pass it explicitly as attn_chunk)."""
-    return C.orthrus_default_attn_chunk(max_batch, max_ctx)
+    sequences x max_ctx slots over n_kv_heads KV heads.  Two contexts give
+    bit-identical attention rows only with the same chunk size, so a context
+    and its greedy (K = 0) twin, or a batch and one of its sequences alone,
+    should share one value (pass it explicitly as attn_chunk)."""
+    return C.orthrus_default_attn_chunk(max_batch, max_ctx, n_kv_heads)
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:

@@ -72,7 +72,7 @@ def test_full_size_lossless_and_batch_invariant(name, weights8b_full):
     a = workloads.plant_lengths(STEPS, B, K, wl["plant"])
     need = 1 + int((a + 1).sum(0).max()) + K + 2
     max_ctx = P + STEPS * (K + 1) + 64
-    chunk = attn_chunk_for(max_ctx, B)
+    chunk = attn_chunk_for(max_ctx, B, sh["hkv"])
     prompts = workloads.prompts(B, P, V)
 
     # greedy trajectory from the K = 0 twin (same chunk size: same attention rows)
