@@ -364,6 +364,15 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   uint16_t* q = S<uint16_t>(c, y.w_q);
   uint16_t* act = S<uint16_t>(c, y.w_act);
   const int pb = pass_base(P.kind);
+  // host-side upper bound on the cache slots a sequence of the pass reaches
+  // (a launch-shape hint for attention; no result depends on it)
+  int reach = 0;
+  if (P.kind == PASS_PREFILL) {
+    reach = P.p0 + P.Kx;
+  } else {
+    for (int b = 0; b < P.B; ++b) reach = c->bound[b] + P.Kx + 1 > reach ? c->bound[b] + P.Kx + 1 : reach;
+  }
+  const int active_chunks = (reach + y.sc - 1) / y.sc;
   {
     Tick t(c, pb + R_SMALL, s);
     launch_embed(P, anchor_tok, block_tok, block_ld, c->packed + y.p_embed,
@@ -428,6 +437,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     a.kpad = y.kpad; a.hq = y.hq; a.hkv = y.hkv; a.hd = y.hd; a.sc = y.sc; a.nc = y.nc;
     a.qr_max = y.qr_max; a.opart = S<float>(c, y.w_opart); a.ml = S<float>(c, y.w_ml);
     a.out = x; a.fixed_ctx = -1; a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
+    a.active_chunks = active_chunks;
     if (c->dbg_attn && rows <= c->dbg_rows) {
       a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * 2;
       a.tap_rows = rows;
@@ -825,6 +835,7 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   a.opart = (float*)workspace;
   a.ml = (float*)((char*)workspace + al(pr * 128 * 4));
   a.out = out; a.fixed_ctx = ctx_len; a.block_len = block_len;
+  a.active_chunks = nc;
   launch_attention_bf16(a, (hipStream_t)stream);
   return check_launch();
 }

@@ -170,6 +170,8 @@ struct AttnArgs {
   void* tap; int tap_rows;   // optional attention-output tap for this layer
   int fixed_ctx;    // >= 0: microbenchmark mode, every row sees cache [0, fixed_ctx)
   int block_len;    // keys in the block scratch
+  int active_chunks;  // upper bound on the cache chunks a sequence of the pass reaches
+  int tpw;          // query tiles per wave, 1 or 2 (set by the launcher)
 };
 void launch_attention_bf16(const AttnArgs& a, hipStream_t s);
 void launch_attention_f32(const AttnArgs& a, hipStream_t s);

@@ -71,9 +71,11 @@ __device__ __forceinline__ void token_view(const AttnArgs& a, const SeqLimits& L
   limit = P.kind == PASS_VERIFY ? L.n + 1 + t : P.p0 + t;
 }
 
-// number of query row groups of a pass: a workgroup's four waves own two
+// number of query row groups of a pass: a workgroup's four waves own tpw
 // 16-row query tiles each
-__host__ __device__ inline int attn_row_groups(int qr) { return ((qr + 15) / 16 + 7) / 8; }
+__host__ __device__ inline int attn_row_groups(int qr, int tpw) {
+  return ((qr + 15) / 16 + 4 * tpw - 1) / (4 * tpw);
+}
 
 // A row's softmax reference m (base 2) is raised only when a tile holds a
 // score above m + REF_SLACK; otherwise the tile's weights 2^(s - m) stay
@@ -88,6 +90,7 @@ template <int N> struct IntC { static constexpr int value = N; };
 #define ATT_STAGES 2
 #endif
 
+template <int TPW>
 __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
   // ATT_STAGES stages of (K tile, V^T tile), 16 KB each
   __shared__ __attribute__((aligned(16))) uint16_t sK0[64 * 128];
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
   const int G = a.hq / a.hkv;
   const int QR = T * G;
   const int NRT = (QR + 15) >> 4;
-  const int NRG = attn_row_groups(QR);
+  const int NRG = attn_row_groups(QR, TPW);
   // 1-D grid: every (cache chunk, KV head, sequence x row group) first, then
   // the short block-chunk workgroups, which fill the tail
   int c, g, zz;
@@ -155,11 +158,12 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     k_end = a.block_len;
   }
 
-  // This wave's query tiles rt0 and rt0 + 1 (B operands of S^T = K.Q^T);
-  // lane row qr = rt*16 + lr.  A padding row (qr >= QR) gets a zero query
-  // that sees every key: it computes harmless values that are never stored.
-  const int rt0 = rg * 8 + wave * 2;
-  const int nt = rt0 >= NRT ? 0 : (rt0 + 1 < NRT ? 2 : 1);     // uniform per wave
+  // This wave's query tiles rt0 .. rt0 + tpw - 1 (B operands of
+  // S^T = K.Q^T); lane row qr = rt*16 + lr.  A padding row (qr >= QR) gets a
+  // zero query that sees every key: it computes harmless values that are
+  // never stored.  Which wave computes a row changes none of its arithmetic.
+  const int rt0 = (rg * 4 + wave) * TPW;
+  const int nt = rt0 >= NRT ? 0 : (TPW == 2 && rt0 + 1 < NRT ? 2 : 1);   // uniform per wave
   bf16x8_t qf[2][4];
   int lim[2], seesb[2];
   floatx4_t oacc[2][8];
@@ -445,7 +449,7 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     __builtin_amdgcn_s_waitcnt(0x0f70);                       // vmcnt(0)
   };
 #endif
-  if (nt == 2) run(IntC<2>{});
+  if (TPW == 2 && nt == 2) run(IntC<TPW == 2 ? 2 : 1>{});
   else if (nt == 1) run(IntC<1>{});
   else run(IntC<0>{});
 
@@ -555,11 +559,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   if (a.tap && r < a.tap_rows) *(uint32_t*)((uint16_t*)a.tap + ob) = y;
 }
 
-void launch_attention_bf16(const AttnArgs& a, hipStream_t s) {
+void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {
+  AttnArgs a = a0;
   const int B = a.P.B;
   const int T = a.fixed_ctx >= 0 ? a.P.Kx : a.P.tokens_per_seq();
-  const int nrg = attn_row_groups(T * (a.hq / a.hkv));
-  hipLaunchKernelGGL(k_attn_bf16, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+  const int QR = T * (a.hq / a.hkv);
+  // two query tiles per wave halve the K/V fragment reads per score; one
+  // tile per wave gives a latency-bound launch (fewer workgroups than two
+  // per compute unit) twice the workgroups with half the work each
+  const int act = a.active_chunks > 0 && a.active_chunks < a.nc ? a.active_chunks : a.nc;
+  a.tpw = (long)B * a.hkv * (act + 1) * attn_row_groups(QR, 2) < 512 ? 1 : 2;
+  const int nrg = attn_row_groups(QR, a.tpw);
+  if (a.tpw == 1)
+    hipLaunchKernelGGL(k_attn_bf16<1>, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_attn_bf16<2>, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
   const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
   const int npairs = rows * a.hq;
   hipLaunchKernelGGL(k_attn_merge, dim3((npairs + 3) / 4), dim3(256), 0, s, a, npairs);
