@@ -192,7 +192,7 @@ void make_layout(const orthrus_config& c, Layout& y) {
     y.w_part = take(8 * rgroups * 64 * nmax * 4);
     y.part_bytes = 8 * rgroups * 64 * nmax * 4;      // addressed with 32-bit offsets
     // slice partials of the residual GEMMs (O, down): [8][rows][d]
-    y.w_rpart = take(8 * (uint64_t)y.rmax * y.d * 4);
+    y.w_rpart = take(8 * (uint64_t)y.rmax * (y.d > y.nqkv ? y.d : y.nqkv) * 4);
     // completion counters of the split-K GEMM column groups (+1 grid counter)
     y.cnt_bytes = (rgroups * y.ngroups_max + 1) * 4;
     y.w_cnt = take(y.cnt_bytes);
@@ -388,7 +388,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   // split K; otherwise they added into h themselves) and the RMSNorm that
   // produces the next GEMM's bf16 input
   float* rpart = S<float>(c, y.w_rpart);
-  const size_t rps = (size_t)y.rmax * y.d;
+  const size_t rps = (size_t)y.rmax * (y.d > y.nqkv ? y.d : y.nqkv);   // slice stride
   auto rnorm = [&](int nsl, uint64_t gain_off) {
     Tick t(c, pb + R_SMALL, s);
     launch_resid_norm_bf16(P, h, y.d, rpart, rps, nsl, (const uint16_t*)(c->packed + gain_off),

@@ -136,7 +136,7 @@ struct GemmArgs {
   float* part; unsigned* cnt;
   int ep;
   float* y; int ldy;                                  // EP_RESID (wide: y += result)
-  float* rpart; size_t rps;     // EP_RESID split-K: slice partials [8][rows][N] (slice stride rps)
+  float* rpart; size_t rps;     // EP_RESID / EP_QKV split-K: slice partials [8][rows][N] (slice stride rps)
   uint16_t* act; int ldact;                            // EP_SWIGLU
   PassInfo P; int hq, hkv; float eps;                  // EP_QKV (and EP_ARGMAX row mapping)
   const uint16_t* qn; const uint16_t* kn; const uint16_t* dqn; const uint16_t* dkn;

@@ -25,8 +25,10 @@
 //  * Epilogues: QK-norm + RoPE + KV placement (QKV projection; a column
 //    group is one head), SwiGLU (gate/up), per-row
 //    argmax with lowest-index ties (LM head; the grid's last workgroup
-//    turns the partials into tokens).  The O and down projections write
-//    their 8 slice partials; the next kernel adds them to the residual.
+//    turns the partials into tokens).  Split O and down projections write
+//    their 8 slice partials and the next kernel adds them to the residual;
+//    a split QKV projection writes them too and a finish kernel adds them
+//    and runs its epilogue.
 //
 // fp32 path: one thread per output with a sequential k loop (check models).
 #include "internal.h"
@@ -71,6 +73,60 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 // (value, index) argmax combine: larger value wins, lowest index on ties.
 __device__ __forceinline__ void amax_comb(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+
+// QK-norm + RoPE + placement of one row's 128 outputs of column group ng
+// (one head: q heads, then k heads, then v heads); lane holds columns lane
+// and lane + 64.  Q goes to q_out; the K/V of mask rows to the block
+// scratch, of every other row to its cache slot.
+__device__ __forceinline__ void qkv_row(const GemmArgs& a, int ng, int prow, float x1, float x2,
+                                        int lane) {
+  const PassInfo& P = a.P;
+  const int hd = 128, half = 64;
+  const bool isq = ng < a.hq, isk = !isq && ng < a.hq + a.hkv;
+  const int head = isq ? ng : (isk ? ng - a.hq : ng - a.hq - a.hkv);
+  const RowInfo ri = row_info(P, prow);
+  if (ri.pad || ri.pos >= a.cap) return;
+  float o1 = x1, o2 = x2;
+  if (isq || isk) {
+    const uint16_t* g = isq ? (ri.is_mask ? a.dqn : a.qn) : (ri.is_mask ? a.dkn : a.kn);
+    float ss = wsum(x1 * x1 + x2 * x2);
+    float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
+    float y1 = x1 * inv * bf2f(g[lane]), y2 = x2 * inv * bf2f(g[lane + half]);
+    float2 cs = a.rope[(size_t)ri.pos * half + lane];
+    o1 = y1 * cs.x - y2 * cs.y;
+    o2 = y2 * cs.x + y1 * cs.y;
+  }
+  const int b = ri.b;
+  if (isq) {
+    uint16_t* qp = a.q_out + (size_t)prow * a.hq * hd + head * hd;
+    qp[lane] = f2bf(o1);
+    qp[lane + half] = f2bf(o2);
+  } else if (ri.is_mask) {
+    const int i = ri.t - P.A;
+    if (isk) {
+      uint16_t* kp = a.ks + (((size_t)b * a.hkv + head) * a.kpad + i) * hd;
+      kp[lane] = f2bf(o1);
+      kp[lane + half] = f2bf(o2);
+    } else {
+      uint16_t* vp = a.vs + ((size_t)b * a.hkv + head) * hd * a.kpad;
+      const int col = vt_col(i);
+      vp[(size_t)lane * a.kpad + col] = f2bf(o1);
+      vp[(size_t)(lane + half) * a.kpad + col] = f2bf(o2);
+    }
+  } else {
+    const int p = ri.pos;
+    if (isk) {
+      uint16_t* kp = a.kc + (((size_t)b * a.hkv + head) * a.cap + p) * hd;
+      kp[lane] = f2bf(o1);
+      kp[lane + half] = f2bf(o2);
+    } else {
+      uint16_t* vp = a.vc + (((size_t)b * a.hkv + head) * (a.cap / 64) + p / 64) * (size_t)hd * 64;
+      const int col = vt_col(p & 63);
+      vp[(size_t)lane * 64 + col] = f2bf(o1);
+      vp[(size_t)(lane + half) * 64 + col] = f2bf(o2);
+    }
+  }
 }
 
 template <int MT, int EP, int WV, bool SPLIT>
@@ -213,10 +269,11 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     for (int mt = 0; mt < MT; ++mt) cur[mt] = tot[mt];
   }
 
-  // ---- split-K residual GEMMs (O and down projections): the slice partial
-  // goes to [slice][row][N]; the residual + RMSNorm kernel that follows adds
-  // the 8 partials in slice order, so no workgroup waits for another here.
-  if (SPLIT && EP == EP_RESID) {
+  // ---- split-K residual and QKV GEMMs: the slice partial goes to
+  // [slice][row][N]; the kernel that follows (residual + RMSNorm, or the QKV
+  // finish) adds the 8 partials in slice order, so no workgroup waits for
+  // another here.
+  if (SPLIT && (EP == EP_RESID || EP == EP_QKV)) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = m0 + mt * 16 + lr;
@@ -388,60 +445,29 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     for (int mt = 0; mt < MT; ++mt)
       *(floatx4_t*)(tile + ((mt * 16 + lr) * COLS) + wave * 16 + lq * 4) = cur[mt];
     __syncthreads();
-    const PassInfo& P = a.P;
-    const int hd = 128, half = 64;
-    const bool isq = ng < a.hq, isk = !isq && ng < a.hq + a.hkv;
-    const int head = isq ? ng : (isk ? ng - a.hq : ng - a.hq - a.hkv);
     for (int rl = wave; rl < MT * 16; rl += WV) {
       const int r = m0 + rl;
       if (r >= Mr) break;
-      const int prow = row0 + r;
-      const RowInfo ri = row_info(P, prow);
-      if (ri.pad || ri.pos >= a.cap) continue;
-      float x1 = tile[rl * COLS + lane], x2 = tile[rl * COLS + lane + half];
-      float o1 = x1, o2 = x2;
-      if (isq || isk) {
-        const uint16_t* g = isq ? (ri.is_mask ? a.dqn : a.qn) : (ri.is_mask ? a.dkn : a.kn);
-        float ss = wsum(x1 * x1 + x2 * x2);
-        float inv = 1.0f / sqrtf(ss / (float)hd + a.eps);
-        float y1 = x1 * inv * bf2f(g[lane]), y2 = x2 * inv * bf2f(g[lane + half]);
-        float2 cs = a.rope[(size_t)ri.pos * half + lane];
-        o1 = y1 * cs.x - y2 * cs.y;
-        o2 = y2 * cs.x + y1 * cs.y;
-      }
-      const int b = ri.b;
-      if (isq) {
-        uint16_t* qp = a.q_out + (size_t)prow * a.hq * hd + head * hd;
-        qp[lane] = f2bf(o1);
-        qp[lane + half] = f2bf(o2);
-      } else if (ri.is_mask) {
-        const int i = ri.t - P.A;
-        if (isk) {
-          uint16_t* kp = a.ks + (((size_t)b * a.hkv + head) * a.kpad + i) * hd;
-          kp[lane] = f2bf(o1);
-          kp[lane + half] = f2bf(o2);
-        } else {
-          uint16_t* vp = a.vs + ((size_t)b * a.hkv + head) * hd * a.kpad;
-          const int col = vt_col(i);
-          vp[(size_t)lane * a.kpad + col] = f2bf(o1);
-          vp[(size_t)(lane + half) * a.kpad + col] = f2bf(o2);
-        }
-      } else {
-        const int p = ri.pos;
-        if (isk) {
-          uint16_t* kp = a.kc + (((size_t)b * a.hkv + head) * a.cap + p) * hd;
-          kp[lane] = f2bf(o1);
-          kp[lane + half] = f2bf(o2);
-        } else {
-          uint16_t* vp = a.vc + (((size_t)b * a.hkv + head) * (a.cap / 64) + p / 64) * (size_t)hd * 64;
-          const int col = vt_col(p & 63);
-          vp[(size_t)lane * 64 + col] = f2bf(o1);
-          vp[(size_t)(lane + half) * 64 + col] = f2bf(o2);
-        }
-      }
+      qkv_row(a, ng, row0 + r, tile[rl * COLS + lane], tile[rl * COLS + lane + 64], lane);
     }
     return;
   }
+}
+
+// Split QKV projection, second half: one wave per (row, head) adds the 8
+// slice partials in slice order and runs the QK-norm / RoPE / placement
+// epilogue.  Rows [0, M) are segment 0 (from row0), [M, M + M2) segment 1.
+__global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
+  const int r = blockIdx.x, ng = blockIdx.y, lane = threadIdx.x;
+  const int prow = r < a.M ? a.row0 + r : a.row02 + (r - a.M);
+  const float* p = a.rpart + (size_t)prow * a.N + ng * 128 + lane;
+  float x1 = p[0], x2 = p[64];
+#pragma unroll
+  for (int sl = 1; sl < NSL; ++sl) {
+    x1 += p[(size_t)sl * a.rps];
+    x2 += p[(size_t)sl * a.rps + 64];
+  }
+  qkv_row(a, ng, prow, x1, x2, lane);
 }
 
 template <int EP, int WV, bool SPLIT>
@@ -496,7 +522,10 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     switch (a.ep) {
       case EP_RESID: dispatch_mt<EP_RESID, 8, true>(MT, grid, a, s); break;
       case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
-      case EP_QKV: dispatch_mt<EP_QKV, 8, true>(MT, grid, a, s); break;
+      case EP_QKV:
+        dispatch_mt<EP_QKV, 8, true>(MT, grid, a, s);
+        hipLaunchKernelGGL(k_qkv_finish_bf16, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+        break;
       default: dispatch_mt<EP_ARGMAX, 8, true>(MT, grid, a, s); break;
     }
     return;
