@@ -197,6 +197,8 @@ def main():
     ap.add_argument("--breakdown-steps", type=int, default=8)
     ap.add_argument("--no-kernel-a", action="store_true",
                     help="skip the block-attention kernel measurement")
+    ap.add_argument("--attn-chunk", type=int, default=0,
+                    help="attention key chunk of both contexts (default: the library's rule)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run plain 1 GiB device copies (PMC byte-counter calibration)")
     args = ap.parse_args()
@@ -227,7 +229,7 @@ def main():
     t0 = time.time()
     # both contexts fold attention over the same key chunks, so their rows are
     # bit-identical (the lossless check below compares them token for token)
-    chunk = attn_chunk_for(max_ctx, B, sh["hkv"])
+    chunk = args.attn_chunk or attn_chunk_for(max_ctx, B, sh["hkv"])
     cfg = C.OrthrusConfig.make(sh["L"], sh["d"], sh["hq"], sh["hkv"], sh["hd"], sh["F"], V, K,
                                True, B, max_ctx, attn_chunk=chunk)
     lay, total = C.weight_layout(cfg)
@@ -367,6 +369,7 @@ def main():
         "data": "synthetic (seeded random-init weights and prompts, planted drafts)",
         "config": {"workload": workload_desc(args.workload, wl, sh), "batch": B,
                    "prompt_len": P, "block_k": K, "parallelism": "none (1 GPU)"},
+        "attn_chunk": chunk,
         "steps_per_s": round(S / (ms / 1e3), 3),
         "tokens_per_step": round(tokens / S, 4),
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
