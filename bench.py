@@ -69,6 +69,33 @@ def step_gemm_flops(sh, B, K):
     return 2 * (draft + verify)
 
 
+def hbm_read_probe(dev, nbytes=4 << 30, reps=10):
+    """The box's achievable HBM read rate: a 4 GiB buffer read once per launch
+    by the library's read probe (16-byte loads, one XOR fold per workgroup),
+    best over two grid sizes."""
+    import torch
+    from lossless_decoding_amd import _lib as C
+    buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.zeros(4096, dtype=torch.int32, device=dev)
+    st = torch.cuda.current_stream().cuda_stream
+    best = (0.0, 0)
+    for nwg in (1024, 2048, 4096):
+        for _ in range(2):
+            C.orthrus_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), nwg, st)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            C.orthrus_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), nwg, st)
+        e1.record()
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (e0.elapsed_time(e1) / 1e3) / 1e9
+        best = max(best, (gbps, nwg))
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"GBps": round(best[0], 1), "frac_of_8TBps": round(best[0] / 8000, 4), "bytes": nbytes,
+            "workgroups": best[1]}
+
+
 def kernel_a_bench(dev, points=((4, 16384), (16, 4096)), rows=32, hq=32, hkv=8, kb=32, reps=20):
     """Kernel (a) alone (orthrus_block_attention) at the configurations with
     at least 256 MB of cache K/V: `rows` mask rows per sequence see Lk cache
@@ -196,7 +223,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown-steps", type=int, default=8)
     ap.add_argument("--no-kernel-a", action="store_true",
-                    help="skip the block-attention kernel measurement")
+                    help="skip the block-attention kernel and HBM read-rate measurements")
     ap.add_argument("--attn-chunk", type=int, default=0,
                     help="attention key chunk of both contexts (default: the library's rule)")
     ap.add_argument("--calibrate", action="store_true",
@@ -353,6 +380,7 @@ def main():
     step_roof_ms = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
     gemm_flops = step_gemm_flops(sh, B, K) * S
     kernel_a = kernel_a_bench(dev) if not args.no_kernel_a else None
+    read_probe = hbm_read_probe(dev) if not args.no_kernel_a else None
 
     out = {
         "metric": "verified tokens/s (and draft+verify steps/s) on 1 GPU; % of HBM roofline",
@@ -396,6 +424,7 @@ def main():
         },
         "ms_per_step_by_class": breakdown,
         "kernel_a": kernel_a,
+        "hbm_read_achievable": read_probe,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(sh, wl, tokens / S / B)

@@ -248,6 +248,14 @@ uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_he
  * n_kv_heads).  Errors: EINVAL (returned as a negative value). */
 int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n_kv_heads);
 
+/* Measurement aid (not part of the decode step): n_workgroups workgroups
+ * read the device buffer buf (bytes, a multiple of 16, 256-byte aligned)
+ * once with 16-byte loads and write one XOR fold per workgroup to the device
+ * array out[n_workgroups].  Timing it gives the box's achievable HBM read
+ * rate for comparison with the published peak.  Errors: EINVAL, EHIP. */
+int orthrus_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int32_t n_workgroups,
+                        void* stream);
+
 const char* orthrus_strerror(int code);
 int orthrus_last_hip_error(void);
 

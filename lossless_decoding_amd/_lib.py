@@ -18,7 +18,7 @@ EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_verify_accept", "orthrus_commit_kv",
     "orthrus_set_debug", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_attention_workspace",
-    "orthrus_default_attn_chunk",
+    "orthrus_default_attn_chunk", "orthrus_stream_read",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
 
@@ -88,6 +88,7 @@ def lib():
         L.orthrus_attention_workspace.argtypes = [i32, i32, i32, i32, i32]
         L.orthrus_attention_workspace.restype = u64
         L.orthrus_default_attn_chunk.argtypes = [i32, i32, i32]
+        L.orthrus_stream_read.argtypes = [vp, u64, vp, i32, vp]
         L.orthrus_default_attn_chunk.restype = i32
         L.orthrus_strerror.argtypes = [ctypes.c_int]
         L.orthrus_strerror.restype = ctypes.c_char_p
@@ -187,6 +188,10 @@ def orthrus_timing_read(ctx):
 
 def orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len) -> int:
     return lib().orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len)
+
+
+def orthrus_stream_read(buf, nbytes, out, n_workgroups, stream):
+    _check("orthrus_stream_read", lib().orthrus_stream_read(buf, nbytes, out, n_workgroups, stream))
 
 
 def orthrus_default_attn_chunk(max_batch, max_ctx, n_kv_heads) -> int:

@@ -840,6 +840,14 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   return check_launch();
 }
 
+int orthrus_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int32_t n_workgroups,
+                        void* stream) {
+  if (!buf || !out || bytes == 0 || bytes % 16 || n_workgroups < 1 || !aligned(buf))
+    return ORTHRUS_EINVAL;
+  launch_stream_read(buf, bytes, out, n_workgroups, (hipStream_t)stream);
+  return check_launch();
+}
+
 int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n_kv_heads) {
   if (max_batch < 1 || max_ctx < 1 || n_kv_heads < 1) return ORTHRUS_EINVAL;
   return default_attn_chunk(max_batch, round_up(max_ctx, 64), n_kv_heads);

@@ -87,6 +87,7 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // common kernels
 void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, int nb_stride,
                       hipStream_t s);
+void launch_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int nwg, hipStream_t s);
 void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* block_tok,
                   int block_ld, const void* embed, const void* mask_emb, int V, int d, bool bf16,
                   float* h, hipStream_t s);

@@ -507,6 +507,14 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   const int ntot = nrow + ((sees && has_blk) ? 1 : 0);   // partials this row folds
   const size_t sbase = (size_t)(b * a.hkv + g) * (a.nc + 1);
   auto pidx = [&](int j) { return (sbase + (j < nrow ? j : a.nc)) * a.qr_max + qr; };
+  // The output partials of the first PRE chunks do not depend on the
+  // maxima: they are requested together with the chunk references, so a row
+  // with up to PRE partials costs one memory round trip.
+  constexpr int PRE = 16;
+  float2 vp[PRE];
+#pragma unroll
+  for (int u = 0; u < PRE; ++u)
+    vp[u] = u < ntot ? *(const float2*)(a.opart + pidx(u) * hd + lane * 2) : make_float2(0.f, 0.f);
   // phase 1: maxima (64 partials per pass over the lanes)
   float M = -INFINITY;
   for (int j0 = 0; j0 < ntot; j0 += 64) {
@@ -534,8 +542,21 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
     lws[0] = lw;
     for (int k = 0; k < n; ++k) l += __shfl(lws[0], k, 64);
     __builtin_amdgcn_wave_barrier();
-    // o: lane owns dimensions 2 lane, 2 lane + 1; loads in batches of 8
-    for (int k0 = 0; k0 < n; k0 += 8) {
+    // o: lane owns dimensions 2 lane, 2 lane + 1; the first PRE chunks from
+    // the registers, the rest loaded in batches of 8
+    int k0 = 0;
+    if (j0 == 0) {
+#pragma unroll
+      for (int u = 0; u < PRE; ++u) {
+        if (u < n) {
+          const float wu = sw[wave][u];
+          o0 += vp[u].x * wu;
+          o1 += vp[u].y * wu;
+        }
+      }
+      k0 = PRE;
+    }
+    for (; k0 < n; k0 += 8) {
       float2 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u)

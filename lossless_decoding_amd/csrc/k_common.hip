@@ -432,3 +432,36 @@ __global__ void k_len_add(int B, int32_t* seq_len, int add) {
 void launch_len_add(int B, int32_t* seq_len, int add, hipStream_t s) {
   hipLaunchKernelGGL(k_len_add, dim3((B + 63) / 64), dim3(64), 0, s, B, seq_len, add);
 }
+
+// Read-bandwidth probe (measurement aid, not part of the decode step): every
+// workgroup streams a contiguous share of the buffer with 16-byte loads, 8
+// per lane in flight, and folds the words with XOR into one value per
+// workgroup, so no load is dead.
+__global__ __launch_bounds__(256) void k_stream_read(const u32x4_t* __restrict__ p, uint64_t n16,
+                                                     uint32_t* __restrict__ out) {
+  __shared__ uint32_t red[4];
+  const uint64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const uint64_t lo = (uint64_t)blockIdx.x * per;
+  const uint64_t hi = lo + per < n16 ? lo + per : n16;
+  uint32_t acc = 0;
+  for (uint64_t i = lo + threadIdx.x; i < hi; i += 256 * 8) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t j = i + (uint64_t)u * 256;
+      v[u] = j < hi ? __builtin_nontemporal_load(p + j) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+void launch_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int nwg, hipStream_t s) {
+  hipLaunchKernelGGL(k_stream_read, dim3(nwg), dim3(256), 0, s, (const u32x4_t*)buf, bytes / 16, out);
+}
+
