@@ -75,6 +75,13 @@ __device__ __forceinline__ void amax_comb(float& v, int& i, float v2, int i2) {
   if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
 
+// largest divisor of n that is <= cap (at least 1)
+constexpr int largest_divisor_le(int n, int cap) {
+  int d = cap < n ? cap : n;
+  while (d > 1 && n % d != 0) --d;
+  return d < 1 ? 1 : d;
+}
+
 // QK-norm + RoPE + placement of one row's 128 outputs of column group ng
 // (one head: q heads, then k heads, then v heads); lane holds columns lane
 // and lane + 64.  Q goes to q_out; the K/V of mask rows to the block
@@ -133,12 +140,15 @@ template <int MT, int EP, int WV, bool SPLIT>
 __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf16(GemmArgs a) {
   constexpr int COLS = WV * 16;
   constexpr int RPW = MT * 16 > 64 ? MT * 16 : 64;     // rows per workgroup
-  constexpr int SK = MT <= 4 ? SKB : SKB / 2;          // k-blocks per stage (64 KB of LDS at MT 8)
+  // k-blocks per activation stage: 16, or fewer for tall tiles (LDS stays
+  // at 48-64 KB); a divisor of the 16 k-blocks of a slice
+  constexpr int SK = MT <= 4 ? SKB : (MT <= 8 ? SKB / 2 : SKB / 4);
   constexpr int NFR = MT * SK;                // activation fragments per stage
   constexpr int NF = (NFR + WV - 1) / WV;     // ... per wave
-  // LDS: one activation stage in fragment order [mt][k-block][lane][8]; it
-  // also holds the fp32 output tile (MT*16 x COLS) in the epilogue.
-  static_assert(MT * 16 * COLS * 4 <= MT * 16 * SK * 32 * 2, "epilogue tile exceeds the stage");
+  // LDS: one activation stage in fragment order [mt][k-block][lane][8]; in
+  // the epilogue it holds fp32 output tiles (16 x COLS each), MTE at a time
+  constexpr int MTE = largest_divisor_le(MT, (MT * SK * 32 * 2) / (COLS * 4));
+  static_assert(MTE >= 1 && MT % MTE == 0, "epilogue row chunks must tile MT");
   __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * SK * 32];
   __shared__ float sRed[WV * RPW];
   __shared__ int sIdx[WV * RPW];
@@ -348,26 +358,32 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     return;
   }
   if (EP == EP_SWIGLU) {
-    // odd waves hold the up block of the even wave before them
-    if (wave & 1) {
+    // odd waves hold the up block of the even wave before them; MTE row
+    // tiles at a time through the LDS tile
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        *(floatx4_t*)(tile + ((mt * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4) = cur[mt];
-    }
-    __syncthreads();
-    if (!(wave & 1)) {
+    for (int mc = 0; mc < MT; mc += MTE) {
+      if (mc > 0) __syncthreads();       // the previous chunk's tile is read
+      if (wave & 1) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        int r = m0 + mt * 16 + lr;
-        if (r >= Mr) continue;
-        floatx4_t u = *(const floatx4_t*)(tile + ((mt * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4);
-        int j = (ng * (WV / 2) + (wave >> 1)) * 16 + lq * 4;
-        uint16_t o[4];
+        for (int e = 0; e < MTE; ++e)
+          *(floatx4_t*)(tile + ((e * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4) = cur[mc + e];
+      }
+      __syncthreads();
+      if (!(wave & 1)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[mt][i]) * u[i]);
-        uint2 pk;
-        __builtin_memcpy(&pk, o, 8);
-        *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
+        for (int e = 0; e < MTE; ++e) {
+          const int mt = mc + e;
+          int r = m0 + mt * 16 + lr;
+          if (r >= Mr) continue;
+          floatx4_t u = *(const floatx4_t*)(tile + ((e * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4);
+          int j = (ng * (WV / 2) + (wave >> 1)) * 16 + lq * 4;
+          uint16_t o[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[mt][i]) * u[i]);
+          uint2 pk;
+          __builtin_memcpy(&pk, o, 8);
+          *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
+        }
       }
     }
     return;
@@ -440,15 +456,20 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     return;
   }
   if (EP == EP_QKV) {
-    // column group ng is one head: q heads, then k heads, then v heads
+    // column group ng is one head: q heads, then k heads, then v heads; MTE
+    // row tiles at a time through the LDS tile
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      *(floatx4_t*)(tile + ((mt * 16 + lr) * COLS) + wave * 16 + lq * 4) = cur[mt];
-    __syncthreads();
-    for (int rl = wave; rl < MT * 16; rl += WV) {
-      const int r = m0 + rl;
-      if (r >= Mr) break;
-      qkv_row(a, ng, row0 + r, tile[rl * COLS + lane], tile[rl * COLS + lane + 64], lane);
+    for (int mc = 0; mc < MT; mc += MTE) {
+      if (mc > 0) __syncthreads();       // the previous chunk's rows are done
+#pragma unroll
+      for (int e = 0; e < MTE; ++e)
+        *(floatx4_t*)(tile + ((e * 16 + lr) * COLS) + wave * 16 + lq * 4) = cur[mc + e];
+      __syncthreads();
+      for (int rl = wave; rl < MTE * 16; rl += WV) {
+        const int r = m0 + mc * 16 + rl;
+        if (r >= Mr) break;
+        qkv_row(a, ng, row0 + r, tile[rl * COLS + lane], tile[rl * COLS + lane + 64], lane);
+      }
     }
     return;
   }
@@ -478,16 +499,43 @@ static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
     case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, WV, SPLIT>), grid, block, 0, s, a); break;
     case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, WV, SPLIT>), grid, block, 0, s, a); break;
     case 4: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<8, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_gemm_bf16<8, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    case 12: hipLaunchKernelGGL((k_gemm_bf16<12, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<16, EP, WV, SPLIT>), grid, block, 0, s, a); break;
   }
 }
 
 int gemm_bf16_groups(int N) { return N / 128; }
 
-// rows per workgroup and workgroup rows of a launch (both segments)
-static int gemm_rows_per_wg(int M, int M2) {
+// Row tiles (16 rows) per workgroup: the rows rounded up to tiles up to 64
+// rows, 4 (64 rows) up to 128, 8 (128 rows) beyond.  This sets the row
+// groups that decide whether K is split.
+static int gemm_mt(int M, int M2) {
   const int Mx = M > M2 ? M : M2;
-  return Mx > 128 ? 128 : 64;
+  return Mx > 128 ? 8 : (Mx >= 64 ? 4 : (Mx + 15) / 16);
+}
+
+// rows per workgroup of a launch (both segments) under gemm_mt
+static int gemm_rows_per_wg(int M, int M2) {
+  const int MT = gemm_mt(M, M2);
+  return MT > 4 ? MT * 16 : 64;
+}
+
+// An unsplit single-segment launch of more than 128 rows may take taller
+// row tiles (MT 12 or 16: 192 or 256 rows), which read the weights fewer
+// times through the caches.  The MFMA operand reads from LDS per row do not
+// change, so what decides is padding: the tile with the fewest padded rows
+// (the smaller on ties) among those that keep at least 512 workgroups.
+static int gemm_mt_tall(int M, int M2, int ngroups) {
+  if (M2 > 0 || M <= 128) return gemm_mt(M, M2);
+  int best = 8;
+  long best_rows = (long)((M + 127) / 128) * 128;
+  for (int MT = 12; MT <= 16; MT += 4) {
+    const int g = (M + MT * 16 - 1) / (MT * 16);
+    const long rows = (long)g * MT * 16;
+    if ((long)ngroups * g >= 512 && rows < best_rows) { best = MT; best_rows = rows; }
+  }
+  return best;
 }
 
 // Split K over workgroups only when the column groups times the row groups
@@ -509,14 +557,14 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   if (!a.W2 || a.M2 <= 0) { a.W2 = nullptr; a.M2 = 0; }
   if (a.M <= 0 && a.M2 <= 0) return;
-  const int Mx = a.M > a.M2 ? a.M : a.M2;
-  const int MT = Mx > 128 ? 8 : (Mx >= 64 ? 4 : (Mx + 15) / 16);
-  const int rpw = gemm_rows_per_wg(a.M, a.M2);   // = max(64, 16 MT)
+  const bool wide = gemm_bf16_split_slices(a.M, a.M2, a.N, a.ep) == 0;
+  const int wv = (a.ep == EP_SWIGLU && (a.N / 16) % 6 == 0 && gemm_mt(a.M, a.M2) <= 3) ? 6 : 8;
+  const int MT = wide ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
+  const int rpw = MT > 4 ? MT * 16 : 64;         // rows per workgroup
   a.gy0 = (a.M + rpw - 1) / rpw;
   const dim3 gy(1, a.gy0 + (a.M2 + rpw - 1) / rpw);
   a.gyt = gy.y;
   a.flat = 0;
-  const bool wide = gemm_bf16_split_slices(a.M, a.M2, a.N, a.ep) == 0;
   if (!wide) {
     const dim3 grid(a.N / 128 * NSL, gy.y);
     switch (a.ep) {
@@ -540,7 +588,7 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     case EP_SWIGLU:
       // 96-column workgroups when they divide N: the Qwen3-8B gate/up GEMM
       // (N = 24576) then has exactly one workgroup per compute unit
-      if ((a.N / 16) % 6 == 0 && MT <= 3) {
+      if (wv == 6) {
         const dim3 g = grid_of(a.N / 96);
         dispatch_mt<EP_SWIGLU, 6, false>(MT, g, a, s);
       } else {
