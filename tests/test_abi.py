@@ -102,3 +102,38 @@ def test_call_order_errors_on_null_context_args():
     with pytest.raises(C.OrthrusError) as e:
         C.orthrus_block_attention(1, 200, 32, 8, 8, 8, 8, 64, 64, 8, 8, 32, 8, 8, 1 << 20, None)
     assert e.value.code == C.ORTHRUS_EINVAL
+
+
+@pytest.mark.parametrize("batch,ctx,kvh,want", [
+    (1, 4668, 8, 128),      # B = 1 decode: at most 64 chunks per sequence
+    (16, 8619, 8, 1024),    # 16 x 8192 decode: <= 1280 workgroups, >= 1024 keys
+    (8, 33096, 8, 2048),    # 8 x 32768 decode
+    (4, 16384, 8, 1024),    # kernel (a), 256 MB points
+    (16, 4096, 8, 1024),
+    (16, 32768, 8, 4096),   # capped at 4096
+    (1, 64, 2, 64),         # floor
+])
+def test_default_attention_chunk_rule(batch, ctx, kvh, want):
+    """The chunk rule the header documents: the smallest power of two in
+    [64, 4096] with <= 64 chunks per sequence and <= 1280 (chunk, KV head,
+    sequence) workgroups, at least 1024 when 1024-key chunks still give 512
+    workgroups (slots rounded up to 64)."""
+    got = C.orthrus_default_attn_chunk(batch, ctx, kvh)
+    assert got == want
+    slots = (ctx + 63) // 64 * 64
+    nch = -(-slots // got)
+    assert got & (got - 1) == 0 and 64 <= got <= 4096
+    if got < 4096:
+        assert nch <= 64 and batch * kvh * nch <= 1280
+    if got > 64:      # the next smaller size breaks a condition
+        half = got // 2
+        n2 = -(-slots // half)
+        long_ok = batch * kvh * (-(-slots // 1024)) >= 512
+        assert n2 > 64 or batch * kvh * n2 > 1280 or (long_ok and half < 1024)
+
+
+def test_default_attention_chunk_rejects_bad_args():
+    with pytest.raises(C.OrthrusError):
+        C.orthrus_default_attn_chunk(0, 1024, 8)
+    with pytest.raises(C.OrthrusError):
+        C.orthrus_default_attn_chunk(1, 1024, 0)
