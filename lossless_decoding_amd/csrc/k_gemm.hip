@@ -136,13 +136,17 @@ __device__ __forceinline__ void qkv_row(const GemmArgs& a, int ng, int prow, flo
   }
 }
 
-template <int MT, int EP, int WV, bool SPLIT>
+// CT: 16-column tiles per wave.  With CT = 2 every activation fragment read
+// from LDS feeds two MFMAs (tall row tiles, unsplit launches only).
+template <int MT, int EP, int WV, bool SPLIT, int CT>
 __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf16(GemmArgs a) {
-  constexpr int COLS = WV * 16;
+  static_assert(CT == 1 || !SPLIT, "two column tiles per wave only without split K");
+  constexpr int COLS = WV * 16 * CT;
   constexpr int RPW = MT * 16 > 64 ? MT * 16 : 64;     // rows per workgroup
   // k-blocks per activation stage: 16, or fewer for tall tiles (LDS stays
-  // at 48-64 KB); a divisor of the 16 k-blocks of a slice
-  constexpr int SK = MT <= 4 ? SKB : (MT <= 8 ? SKB / 2 : SKB / 4);
+  // at 32-64 KB, the weight ring short); a divisor of the 16 k-blocks of a
+  // slice
+  constexpr int SK = MT <= 4 ? SKB : ((MT <= 8 && CT == 1) ? SKB / 2 : SKB / 4);
   constexpr int NFR = MT * SK;                // activation fragments per stage
   constexpr int NF = (NFR + WV - 1) / WV;     // ... per wave
   // LDS: one activation stage in fragment order [mt][k-block][lane][8]; in
@@ -192,9 +196,13 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   const int m0 = (seg1 ? by - a.gy0 : by) * RPW;    // first row of this workgroup
   const int kb_lo = SPLIT ? s_first * KSB : 0;
   const int nkb = SPLIT ? KSB : KB;           // k-blocks of this workgroup
-  const int nbk = ng * WV + wave;             // this wave's 16-column tile
-  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Wt + ((size_t)nbk * KB + kb_lo) * 64), (short)0, nkb * 1024, BUF_FLAGS);
+  const int nbk0 = (ng * WV + wave) * CT;    // this wave's first 16-column tile
+  const int nbk = nbk0;                       // (CT = 1: its only tile)
+  __amdgpu_buffer_rsrc_t rW[CT];
+#pragma unroll
+  for (int c = 0; c < CT; ++c)
+    rW[c] = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(Wt + ((size_t)(nbk0 + c) * KB + kb_lo) * 64), (short)0, nkb * 1024, BUF_FLAGS);
 
   // stage st: k-blocks [st*SK, st*SK + SK) of this workgroup's range; the
   // lane of fragment (mt, j) holds row mt*16 + lr, k = 32 j + 8 lq .. + 7.
@@ -231,19 +239,24 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   // weight ring: slot i holds k-block st*SK + i of the stage being computed;
   // loads past this wave's k-range fall outside the descriptor (zero, no
   // memory access)
-  u32x4_t w[SK];
+  u32x4_t w[CT][SK];
 #pragma unroll
-  for (int i = 0; i < SK; ++i) w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + i * 1024, 0, BUF_NT);
+  for (int i = 0; i < SK; ++i)
+#pragma unroll
+    for (int c = 0; c < CT; ++c)
+      w[c][i] = __builtin_amdgcn_raw_buffer_load_b128(rW[c], lane * 16 + i * 1024, 0, BUF_NT);
 
   write_stage();
   __syncthreads();
 
-  floatx4_t cur[MT], tot[MT];
+  floatx4_t cur[CT][MT], tot[CT][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    tot[mt] = cur[mt];
-  }
+  for (int c = 0; c < CT; ++c)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      cur[c][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      tot[c][mt] = cur[c][mt];
+    }
   // Per stage: switch the LDS stage, prefetch the next one, then SK MFMA
   // steps, each refilling its ring slot with the k-block one stage ahead.
   // The loads are the same on every path.  Past the end of a partial last
@@ -261,23 +274,32 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SK + i) * 64 + lane) * 8);
-        cur[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[i]), as_bf16x8(xv),
-                                                          cur[mt], 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+          cur[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[c][i]), as_bf16x8(xv),
+                                                               cur[c][mt], 0, 0, 0);
       }
-      w[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, lane * 16 + (kk + SK) * 1024, 0, BUF_NT);
+#pragma unroll
+      for (int c = 0; c < CT; ++c)
+        w[c][i] = __builtin_amdgcn_raw_buffer_load_b128(rW[c], lane * 16 + (kk + SK) * 1024, 0, BUF_NT);
       if (!SPLIT && kk < nkb && (kk + 1) % KSB == 0) {   // slice done: add in slice order
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          tot[mt] = kk + 1 == KSB ? cur[mt] : add4(tot[mt], cur[mt]);
-          cur[mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        }
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            tot[c][mt] = kk + 1 == KSB ? cur[c][mt] : add4(tot[c][mt], cur[c][mt]);
+            cur[c][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+          }
       }
     }
   }
   if (!SPLIT) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) cur[mt] = tot[mt];
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) cur[c][mt] = tot[c][mt];
   }
+  floatx4_t (&cs)[MT] = cur[0];               // the only tile when CT = 1
 
   // ---- split-K residual and QKV GEMMs: the slice partial goes to
   // [slice][row][N]; the kernel that follows (residual + RMSNorm, or the QKV
@@ -289,7 +311,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       const int r = m0 + mt * 16 + lr;
       if (r < Mr)
         *(floatx4_t*)(a.rpart + (size_t)s_first * a.rps + (size_t)(row0 + r) * a.N + nbk * 16 + lq * 4) =
-            cur[mt];
+            cs[mt];
     }
     return;
   }
@@ -310,7 +332,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     };
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[mt]), rPt,
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cs[mt]), rPt,
                                              poff(s_first, mt), 0, BUF_SC1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -328,14 +350,14 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       floatx4_t p[NSL];
 #pragma unroll
       for (int s = 0; s < NSL; ++s) {
-        if (s == s_first) p[s] = cur[mt];
+        if (s == s_first) p[s] = cs[mt];
         else p[s] = __builtin_bit_cast(floatx4_t,
                                        __builtin_amdgcn_raw_buffer_load_b128(rPt, poff(s, mt), 0, BUF_SC1));
       }
       floatx4_t t = p[0];
 #pragma unroll
       for (int s = 1; s < NSL; ++s) t = add4(t, p[s]);
-      cur[mt] = t;
+      cs[mt] = t;
     }
   }
 
@@ -346,14 +368,33 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   if (EP == EP_RESID) {
     // h += y
 #pragma unroll
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = m0 + mt * 16 + lr;
+        if (r < Mr) {
+          float* yp = a.y + (size_t)(row0 + r) * a.ldy + (nbk0 + c) * 16 + lq * 4;
+          float4 o = *(float4*)yp;
+          o.x += cur[c][mt][0]; o.y += cur[c][mt][1]; o.z += cur[c][mt][2]; o.w += cur[c][mt][3];
+          *(float4*)yp = o;
+        }
+      }
+    return;
+  }
+  if (EP == EP_SWIGLU && CT == 2) {
+    // gate (even tile) and up (odd tile) of one 16-column act block are this
+    // wave's two tiles
+    const int j = (nbk0 >> 1) * 16 + lq * 4;
+#pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int r = m0 + mt * 16 + lr;
-      if (r < Mr) {
-        float* yp = a.y + (size_t)(row0 + r) * a.ldy + nbk * 16 + lq * 4;
-        float4 o = *(float4*)yp;
-        o.x += cur[mt][0]; o.y += cur[mt][1]; o.z += cur[mt][2]; o.w += cur[mt][3];
-        *(float4*)yp = o;
-      }
+      if (r >= Mr) continue;
+      uint16_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[0][mt][i]) * cur[CT - 1][mt][i]);
+      uint2 pk;
+      __builtin_memcpy(&pk, o, 8);
+      *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
     }
     return;
   }
@@ -366,7 +407,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       if (wave & 1) {
 #pragma unroll
         for (int e = 0; e < MTE; ++e)
-          *(floatx4_t*)(tile + ((e * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4) = cur[mc + e];
+          *(floatx4_t*)(tile + ((e * 16 + lr) * COLS) + (wave >> 1) * 16 + lq * 4) = cs[mc + e];
       }
       __syncthreads();
       if (!(wave & 1)) {
@@ -379,7 +420,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
           int j = (ng * (WV / 2) + (wave >> 1)) * 16 + lq * 4;
           uint16_t o[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[mt][i]) * u[i]);
+          for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cs[mt][i]) * u[i]);
           uint2 pk;
           __builtin_memcpy(&pk, o, 8);
           *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
@@ -392,12 +433,18 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       int r = m0 + mt * 16 + lr;
-      float bv = cur[mt][0];
-      int bi = nbk * 16 + lq * 4;
+      float bv = cur[0][mt][0];
+      int bi = nbk0 * 16 + lq * 4;
 #pragma unroll
-      for (int i = 1; i < 4; ++i) amax_comb(bv, bi, cur[mt][i], nbk * 16 + lq * 4 + i);
-      if (a.logits && r < Mr)
-        *(floatx4_t*)(a.logits + (size_t)(row0 + r) * a.ldl + nbk * 16 + lq * 4) = cur[mt];
+      for (int c = 0; c < CT; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (c > 0 || i > 0) amax_comb(bv, bi, cur[c][mt][i], (nbk0 + c) * 16 + lq * 4 + i);
+      if (a.logits && r < Mr) {
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+          *(floatx4_t*)(a.logits + (size_t)(row0 + r) * a.ldl + (nbk0 + c) * 16 + lq * 4) = cur[c][mt];
+      }
       float v2 = __shfl_xor(bv, 16, 64); int i2 = __shfl_xor(bi, 16, 64);
       amax_comb(bv, bi, v2, i2);
       v2 = __shfl_xor(bv, 32, 64); i2 = __shfl_xor(bi, 32, 64);
@@ -463,7 +510,9 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       if (mc > 0) __syncthreads();       // the previous chunk's rows are done
 #pragma unroll
       for (int e = 0; e < MTE; ++e)
-        *(floatx4_t*)(tile + ((e * 16 + lr) * COLS) + wave * 16 + lq * 4) = cur[mc + e];
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+          *(floatx4_t*)(tile + ((e * 16 + lr) * COLS) + (wave * CT + c) * 16 + lq * 4) = cur[c][mc + e];
       __syncthreads();
       for (int rl = wave; rl < MTE * 16; rl += WV) {
         const int r = m0 + mc * 16 + rl;
@@ -491,18 +540,28 @@ __global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
   qkv_row(a, ng, prow, x1, x2, lane);
 }
 
-template <int EP, int WV, bool SPLIT>
+template <int EP, int WV, bool SPLIT, int CT = 1>
 static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
   const dim3 block(WV * 64);
   switch (MT) {
-    case 1: hipLaunchKernelGGL((k_gemm_bf16<1, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_gemm_bf16<8, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    case 12: hipLaunchKernelGGL((k_gemm_bf16<12, EP, WV, SPLIT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<16, EP, WV, SPLIT>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_gemm_bf16<1, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_gemm_bf16<8, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    case 12: hipLaunchKernelGGL((k_gemm_bf16<12, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    default: hipLaunchKernelGGL((k_gemm_bf16<16, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
   }
+}
+
+// unsplit gate/up launches of 128-row tiles: four waves of two column tiles
+// (128 columns: gate and up in one wave).  Measured: faster for gate/up at
+// 256-512 rows; slower for QKV and the LM head, whose grids keep fewer loads
+// in flight with four waves per workgroup.  Taller tiles would not fit two
+// tiles' accumulators.
+template <int EP>
+static void dispatch_ct2(dim3 grid, const GemmArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((k_gemm_bf16<8, EP, 4, false, 2>), grid, dim3(256), 0, s, a);
 }
 
 int gemm_bf16_groups(int N) { return N / 128; }
@@ -559,7 +618,9 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   if (a.M <= 0 && a.M2 <= 0) return;
   const bool wide = gemm_bf16_split_slices(a.M, a.M2, a.N, a.ep) == 0;
   const int wv = (a.ep == EP_SWIGLU && (a.N / 16) % 6 == 0 && gemm_mt(a.M, a.M2) <= 3) ? 6 : 8;
-  const int MT = wide ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
+  // tall row tiles for unsplit launches other than gate/up (which takes two
+  // column tiles per wave at 128 rows instead: measured faster)
+  const int MT = wide && a.ep != EP_SWIGLU ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
   const int rpw = MT > 4 ? MT * 16 : 64;         // rows per workgroup
   a.gy0 = (a.M + rpw - 1) / rpw;
   const dim3 gy(1, a.gy0 + (a.M2 + rpw - 1) / rpw);
@@ -584,6 +645,11 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     a.flat = gy.y > 1 && ngroups % 8 == 0;
     return a.flat ? dim3(ngroups * gy.y, 1) : dim3(ngroups, gy.y);
   };
+  if (MT == 8 && a.ep == EP_SWIGLU) {        // 128-row tiles: two column tiles per wave
+    const dim3 g = grid_of(a.N / 128);
+    dispatch_ct2<EP_SWIGLU>(g, a, s);
+    return;
+  }
   switch (a.ep) {
     case EP_SWIGLU:
       // 96-column workgroups when they divide N: the Qwen3-8B gate/up GEMM
