@@ -140,7 +140,8 @@ __device__ __forceinline__ void qkv_row(const GemmArgs& a, int ng, int prow, flo
 // from LDS feeds two MFMAs (tall row tiles, unsplit launches only).
 template <int MT, int EP, int WV, bool SPLIT, int CT>
 __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf16(GemmArgs a) {
-  static_assert(CT == 1 || !SPLIT, "two column tiles per wave only without split K");
+  static_assert(CT == 1 || !SPLIT || EP == EP_RESID,
+                "two column tiles per wave: unsplit, or split with partials only");
   constexpr int COLS = WV * 16 * CT;
   constexpr int RPW = MT * 16 > 64 ? MT * 16 : 64;     // rows per workgroup
   // k-blocks per activation stage: 16, or fewer for tall tiles (LDS stays
@@ -197,7 +198,6 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   const int kb_lo = SPLIT ? s_first * KSB : 0;
   const int nkb = SPLIT ? KSB : KB;           // k-blocks of this workgroup
   const int nbk0 = (ng * WV + wave) * CT;    // this wave's first 16-column tile
-  const int nbk = nbk0;                       // (CT = 1: its only tile)
   __amdgpu_buffer_rsrc_t rW[CT];
 #pragma unroll
   for (int c = 0; c < CT; ++c)
@@ -307,12 +307,14 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   // another here.
   if (SPLIT && (EP == EP_RESID || EP == EP_QKV)) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int r = m0 + mt * 16 + lr;
-      if (r < Mr)
-        *(floatx4_t*)(a.rpart + (size_t)s_first * a.rps + (size_t)(row0 + r) * a.N + nbk * 16 + lq * 4) =
-            cs[mt];
-    }
+    for (int c = 0; c < CT; ++c)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = m0 + mt * 16 + lr;
+        if (r < Mr)
+          *(floatx4_t*)(a.rpart + (size_t)s_first * a.rps + (size_t)(row0 + r) * a.N + (nbk0 + c) * 16 +
+                        lq * 4) = cur[c][mt];
+      }
     return;
   }
   // ---- split-K: write the slice partial; the last slice workgroup adds all 8.
@@ -362,7 +364,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   }
 
   // ============================ epilogues
-  // lane (lr, lq) of wave w holds rows m0 + mt*16 + lr, columns nbk*16 + lq*4 + i
+  // lane (lr, lq) of wave w holds rows m0 + mt*16 + lr, columns (nbk0 + c)*16 + lq*4 + i
   float* tile = (float*)sX;                  // [MT*16][COLS] fp32 scratch
   __syncthreads();
   if (EP == EP_RESID) {
@@ -629,7 +631,11 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   if (!wide) {
     const dim3 grid(a.N / 128 * NSL, gy.y);
     switch (a.ep) {
-      case EP_RESID: dispatch_mt<EP_RESID, 8, true>(MT, grid, a, s); break;
+      case EP_RESID:
+        // 128-row tiles: two column tiles per wave
+        if (MT == 8) hipLaunchKernelGGL((k_gemm_bf16<8, EP_RESID, 4, true, 2>), grid, dim3(256), 0, s, a);
+        else dispatch_mt<EP_RESID, 8, true>(MT, grid, a, s);
+        break;
       case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
       case EP_QKV:
         dispatch_mt<EP_QKV, 8, true>(MT, grid, a, s);
