@@ -409,7 +409,7 @@ def main():
                           "gemm_tflops_per_s": round(gemm_flops / (ms / 1e3) / 1e12, 2),
                           "mfma_frac_bf16": round(gemm_flops / (ms / 1e3) / MFMA_PEAK_BF16, 4)},
         "roofline": {
-            "kernel": f"k_gemm_bf16<{gu_mt}, EP_SWIGLU, {gu_wv}, false> (draft-pass gate/up "
+            "kernel": f"k_gemm_bf16<{gu_mt}, EP_SWIGLU, {gu_wv}, false, 1> (draft-pass gate/up "
                       f"SwiGLU GEMM, M={M1}, N={2 * sh['F']}, K={sh['d']})",
             "bound": "hbm",
             "achieved": round(achieved, 1),
