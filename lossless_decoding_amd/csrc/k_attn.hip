@@ -38,6 +38,16 @@ __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   return r;
 }
 
+// x, as a value the compiler cannot see through (no instruction): keeps it
+// from precomputing and holding values derived from x across a loop.  The
+// register constraint exists only in the device pass.
+__device__ __forceinline__ int opaque(int x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#endif
+  return x;
+}
+
 // key index (0..63) stored at column c of a V^T tile (inverse of vt_col)
 __device__ __forceinline__ int vt_key(int c) {
   int g = c >> 5, k = c & 31;
@@ -83,34 +93,41 @@ __host__ __device__ inline int attn_row_groups(int qr, int tpw) {
 // taken per row from that row's own scores, so the arithmetic a row sees is
 // still a function of its keys alone.
 #define REF_SLACK 8.0f
+// a lane's eight keys of a half tile drop the low P term when their weights
+// sum to at most this share of the lane's running sum
+#define LO_SKIP 0.125f
 
 template <int N> struct IntC { static constexpr int value = N; };
 
-#ifndef ATT_STAGES
-#define ATT_STAGES 2
-#endif
+// LDS ring of ATT_SLOTS 16 KB slots.  A 64-key tile is two units, its K
+// (64 key rows of 256 bytes) and its V^T (128 dimension rows of 128 bytes);
+// unit u (K of tile i = 2i, V^T = 2i + 1) lives in slot u % ATT_SLOTS.  With
+// five slots three units are in flight while a tile is computed, and two
+// workgroups (80 KB each) share a compute unit's 160 KB.
+#define ATT_SLOTS 5
 
+// The kernel body, for TPW query tiles per wave (four waves per workgroup,
+// two workgroups per compute unit).  It is a device template behind plain
+// kernels, so only the device pass instantiates it.
 template <int TPW>
-__global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
-  // ATT_STAGES stages of (K tile, V^T tile), 16 KB each
-  __shared__ __attribute__((aligned(16))) uint16_t sK0[64 * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t sV0[128 * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sK1[64 * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t sV1[128 * 64];
-#if ATT_STAGES > 2
-  __shared__ __attribute__((aligned(16))) uint16_t sK2[64 * 128];
-  __shared__ __attribute__((aligned(16))) uint16_t sV2[128 * 64];
-#else
-  uint16_t* const sK2 = sK0;
-  uint16_t* const sV2 = sV0;
-#endif
-  auto kst = [&](auto stc) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int S = decltype(stc)::value;
-    if constexpr (S == 0) return sK0; else if constexpr (S == 1) return sK1; else return sK2;
-  };
-  auto vst = [&](auto stc) __attribute__((always_inline)) -> uint16_t* {
-    constexpr int S = decltype(stc)::value;
-    if constexpr (S == 0) return sV0; else if constexpr (S == 1) return sV1; else return sV2;
+__device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
+  constexpr int NW = 4;
+  // each 16 KB unit is 16 one-kilobyte loads, LPU of them per wave
+  constexpr int LPU = 16 / NW;
+  // one array per slot, so the compiler sees that loads into one slot and
+  // reads of another do not alias (no wait for in-flight loads)
+  __shared__ __attribute__((aligned(16))) uint16_t sR0[8192];
+  __shared__ __attribute__((aligned(16))) uint16_t sR1[8192];
+  __shared__ __attribute__((aligned(16))) uint16_t sR2[8192];
+  __shared__ __attribute__((aligned(16))) uint16_t sR3[8192];
+  __shared__ __attribute__((aligned(16))) uint16_t sR4[8192];
+  auto slot = [&](auto sc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(sc)::value % ATT_SLOTS;
+    if constexpr (S == 0) return sR0;
+    else if constexpr (S == 1) return sR1;
+    else if constexpr (S == 2) return sR2;
+    else if constexpr (S == 3) return sR3;
+    else return sR4;
   };
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
   const PassInfo& P = a.P;
@@ -162,7 +179,7 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
   // S^T = K.Q^T); lane row qr = rt*16 + lr.  A padding row (qr >= QR) gets a
   // zero query that sees every key: it computes harmless values that are
   // never stored.  Which wave computes a row changes none of its arithmetic.
-  const int rt0 = (rg * 4 + wave) * TPW;
+  const int rt0 = (rg * NW + wave) * TPW;
   const int nt = rt0 >= NRT ? 0 : (TPW == 2 && rt0 + 1 < NRT ? 2 : 1);   // uniform per wave
   bf16x8_t qf[2][4];
   int lim[2], seesb[2];
@@ -210,38 +227,41 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
   // hold whatever the cache holds there; they are zeroed in LDS.
   const int kv_hi = blk ? a.block_len : k_end;                 // keys [0, kv_hi) exist
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  int koff[4], voff[4];
+  int koff[LPU], voff[LPU];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int key = wv * 16 + j * 4 + (lane >> 4);
+  for (int j = 0; j < LPU; ++j) {
+    const int key = (wv * LPU + j) * 4 + (lane >> 4);
     koff[j] = key * 256 + (((lane & 15) ^ (key & 15)) << 4);   // unit (lane & 15) ^ (key & 15) of the key
-    const int d = wv * 32 + j * 8 + (lane >> 3);
+    const int d = (wv * LPU + j) * 8 + (lane >> 3);
     const int ku = (lane & 7) ^ (d & 7);
     voff[j] = blk ? (d * a.kpad + ku * 8) * 2 : d * 128 + ku * 16;
   }
-  auto issue = [&](auto s1c, int kt) __attribute__((always_inline)) {
-    uint16_t* dK = kst(s1c);
-    uint16_t* dV = vst(s1c);
-    const bool live = kt < k_end;                              // uniform
-    const int nk = live ? min(64, kv_hi - kt) : 0;
-    const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+  // K unit / V^T unit of the tile at key kt into LDS slot dst (kt past the
+  // end: size-0 descriptor, zeros, no memory access)
+  auto issue_k = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
+    const int nk = kt < k_end ? min(64, kv_hi - kt) : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(kbase + (size_t)kt * hd), (short)0, nk * hd * 2, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rV = __builtin_amdgcn_make_buffer_rsrc(
+#pragma unroll
+    for (int j = 0; j < LPU; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16, koff[j], 0, 0, 0);
+  };
+  auto issue_v = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
+    const bool live = kt < k_end;                              // uniform
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(blk ? vbase : vbase + (size_t)(kt >> 6) * 64 * hd), (short)0,
         live ? (blk ? hd * a.kpad * 2 : 64 * hd * 2) : 0, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < LPU; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rK, (__attribute__((address_space(3))) void*)(dK + (wv * 4 + j) * 512), 16, koff[j], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rV, (__attribute__((address_space(3))) void*)(dV + (wv * 4 + j) * 512), 16, voff[j], 0, 0, 0);
-    }
+          r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16, voff[j], 0, 0, 0);
   };
   // zero the V^T columns of keys >= nvalid (the last, partial tile)
   auto zero_v = [&](uint16_t* V, int nvalid) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int u = tid + m * 256;                             // 16-byte unit of the tile
+    for (int m = 0; m < 16 / NW; ++m) {
+      const int u = opaque(tid + m * NW * 64);                 // 16-byte unit of the tile (rare path)
       const int d = u >> 3, ku = (u & 7) ^ (d & 7);
       uint4 v = *(uint4*)(V + u * 8);
       uint16_t e[8];
@@ -263,10 +283,19 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
 
   // The tile's work for the wave's NT query tiles.  Every K and V^T
   // fragment read from LDS feeds one MFMA per query tile.
-  auto compute = [&](auto s1c, auto ntc, int kt, int nvalid) __attribute__((always_inline)) {
+  auto compute = [&](const uint16_t* sK, const uint16_t* sV, auto ntc, int kt, int nvalid)
+      __attribute__((always_inline)) {
     constexpr int NT = decltype(ntc)::value;
-    const char* sKb = (const char*)kst(s1c);
-    const char* sVb = (const char*)vst(s1c);
+    const char* sKb = (const char*)sK;
+    const char* sVb = (const char*)sV;
+    // fresh copies of the lane's fragment offsets each step, so the slot
+    // addresses are formed here (one add each) rather than kept in
+    // registers for all five slots
+    int ko[4], vo[2];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) ko[ds] = opaque(kfo[ds]);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) vo[ks] = opaque(vfo[ks]);
     // S^T for 4 blocks of 16 keys
     floatx4_t s[NT][4];
 #pragma unroll
@@ -278,7 +307,7 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     for (int ds = 0; ds < 4; ++ds)
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8_t kf = ld_bf16x8((const uint16_t*)(sKb + kb * 4096 + kfo[ds]));
+        const bf16x8_t kf = ld_bf16x8((const uint16_t*)(sKb + kb * 4096 + ko[ds]));
 #pragma unroll
         for (int t = 0; t < NT; ++t)
           s[t][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][ds], s[t][kb], 0, 0, 0);
@@ -288,13 +317,14 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     // invisible keys get the score -inf.
     const bool all_vis = !blk && nvalid == 64 && __all(kt + 63 <= lmin);
     if (!all_vis) {
+      const int lq4 = opaque(lq * 4);                          // (keeps no per-key constants live)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int kl = kb * 16 + lq * 4 + i;
+            const int kl = kb * 16 + lq4 + i;
             const bool ok = kl < nvalid && (blk ? seesb[t] != 0 : (kt + kl) <= lim[t]);
             s[t][kb][i] = ok ? s[t][kb][i] : -INFINITY;
           }
@@ -344,111 +374,140 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     // Weights p = 2^(s * scale - m), one fused multiply-add and v_exp_f32
     // each (arguments <= REF_SLACK; results below 2^-126 are negligible
     // weights and flush to 0).  A row whose m is still -inf has only -inf
-    // scores so far, so its p are 0.  l is summed per lane (the lane's keys
-    // in a fixed order) and across the row's lanes once, at the end.
-    // P enters the P.V product as two bf16 terms, hi = bf16(p) and
-    // lo = bf16(p - hi) (p - hi is exact in fp32), so the product carries
-    // about 16 significant bits of p instead of 8.
+    // scores so far, so its p are 0.  l is summed per lane, eight keys at a
+    // time in a fixed tree, and across the row's lanes once, at the end.
+    // P enters the P.V product as hi = bf16(p) and, where it matters,
+    // lo = bf16(p - hi) (p - hi is exact in fp32): about 16 significant bits
+    // of p instead of 8.  lo is dropped for a lane's eight keys of a half
+    // tile when their weights sum to at most LO_SKIP of the lane's running
+    // sum l; hi alone then carries them (relative error <= 2^-9 on a small
+    // share of the total).  The decision depends only on the row's own keys
+    // and position-aligned tiles, and a dropped lo is an exact zero in the
+    // product, so the lo MFMAs are issued only when some lane keeps lo.
     // Done in two halves of 32 keys (kb 0-1, then kb 2-3), so only half of
-    // P is live at a time; each accumulator still sums its terms in the
-    // same order (keys 0-31 hi, lo, then keys 32-63 hi, lo).
+    // P is live at a time; each accumulator sums its terms in the same order
+    // (keys 0-31 hi, lo, then keys 32-63 hi, lo).
     float mr[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) mr[t] = mref[t] == -INFINITY ? 0.f : mref[t];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t pf[NT], pl[NT];
+      float pv[NT][8];
+      bool keep[NT];
+      bool any_keep = false;
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kb = ks * 2 + kh;
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][kb][i], sl2, -mr[t]));
-            lsum[t] += p;
-            const __bf16 hi = (__bf16)p;
-            pf[t][kh * 4 + i] = hi;
-            pl[t][kh * 4 + i] = (__bf16)(p - (float)hi);
-          }
+          for (int i = 0; i < 4; ++i)
+            pv[t][kh * 4 + i] =
+                __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][ks * 2 + kh][i], sl2, -mr[t]));
+        const float ts = ((pv[t][0] + pv[t][1]) + (pv[t][2] + pv[t][3])) +
+                         ((pv[t][4] + pv[t][5]) + (pv[t][6] + pv[t][7]));
+        keep[t] = ts > lsum[t] * LO_SKIP;
+        lsum[t] += ts;
+        any_keep = any_keep || keep[t];
+      }
+      bf16x8_t pf[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) pf[t][j] = (__bf16)pv[t][j];
       // two dimension blocks at a time, hi terms before lo terms, so an
       // MFMA never waits on the one just issued (same per-accumulator order)
-#pragma unroll
-      for (int db = 0; db < 8; db += 2) {
-        const bf16x8_t vf0 = ld_bf16x8((const uint16_t*)(sVb + db * 2048 + vfo[ks]));
-        const bf16x8_t vf1 = ld_bf16x8((const uint16_t*)(sVb + (db + 1) * 2048 + vfo[ks]));
+      if (__any(any_keep)) {
+        bf16x8_t pl[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pf[t], oacc[t][db], 0, 0, 0);
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pf[t], oacc[t][db + 1], 0, 0, 0);
+          for (int j = 0; j < 8; ++j)
+            pl[t][j] = keep[t] ? (__bf16)(pv[t][j] - (float)pf[t][j]) : (__bf16)0.f;
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pl[t], oacc[t][db], 0, 0, 0);
+        for (int db = 0; db < 8; db += 2) {
+          const bf16x8_t vf0 = ld_bf16x8((const uint16_t*)(sVb + db * 2048 + vo[ks]));
+          const bf16x8_t vf1 = ld_bf16x8((const uint16_t*)(sVb + (db + 1) * 2048 + vo[ks]));
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-          oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pl[t], oacc[t][db + 1], 0, 0, 0);
+          for (int t = 0; t < NT; ++t)
+            oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pf[t], oacc[t][db], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pf[t], oacc[t][db + 1], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pl[t], oacc[t][db], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pl[t], oacc[t][db + 1], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int db = 0; db < 8; db += 2) {
+          const bf16x8_t vf0 = ld_bf16x8((const uint16_t*)(sVb + db * 2048 + vo[ks]));
+          const bf16x8_t vf1 = ld_bf16x8((const uint16_t*)(sVb + (db + 1) * 2048 + vo[ks]));
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            oacc[t][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf0, pf[t], oacc[t][db], 0, 0, 0);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            oacc[t][db + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf1, pf[t], oacc[t][db + 1], 0, 0, 0);
+        }
       }
     }
   };
 
-  // One tile step: wait until the tile is in LDS (own loads, then the
-  // barrier for everyone's; the barrier also ends every wave's reads of the
-  // other stage), start the next tile's loads into the other stage, compute.
-  // Every wave runs the same steps, with the number of query tiles it owns.
-  // No load is issued past the chunk's last tile, so none is in flight when
-  // the loop ends.
-#if ATT_STAGES == 2
+  // One tile step: wait until the tile's two units are in LDS (own loads:
+  // only the next tile's K, issued one step earlier, may still be in
+  // flight; then the barrier for everyone's, which also ends every wave's
+  // reads of the previous tile's slots), zero V^T columns past the end,
+  // start V^T of the next tile and K of the one after into the two freed
+  // slots, compute.  Every wave runs the same steps with the number of query
+  // tiles it owns.  Units past the end are size-0 loads (zeros, no memory
+  // access); all loads have landed before the workgroup ends.
+  // The step barrier is the hardware barrier alone.  A workgroup fence
+  // (__syncthreads) would also wait for every load still filling a later
+  // slot; the explicit wait before it covers exactly this tile's units.
+  // The empty asm statements keep the compiler from moving LDS accesses
+  // across it (they emit nothing); the wait before it also takes lgkmcnt to
+  // 0, so no wave still has a read of the previous tile's slots in flight
+  // when another wave starts loads into them.
+  auto step_barrier = []() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
   auto run = [&](auto ntc) __attribute__((always_inline)) {
-    auto step = [&](auto s1c, int kt) __attribute__((always_inline)) {
-      constexpr int S1 = decltype(s1c)::value;
+    // tile i: K in slot (2i) % 5 = S0, V^T in S0 + 1; the freed slots of
+    // tile i - 1 are S0 + 3 and S0 + 4 (mod 5)
+    auto step = [&](auto s0c, int kt) __attribute__((always_inline)) {
+      constexpr int S0 = decltype(s0c)::value;
       const int nvalid = min(64, k_end - kt);
-      __builtin_amdgcn_s_waitcnt(0x0f70);                     // vmcnt(0)
-      __syncthreads();
-      if (nvalid > 0 && nvalid < 64) {
-        zero_v(vst(s1c), nvalid);
+      __builtin_amdgcn_s_waitcnt(0x0070 | LPU);                // vmcnt(LPU) lgkmcnt(0)
+      step_barrier();
+      if (nvalid < 64) {
+        zero_v(slot(IntC<S0 + 1>{}), nvalid);
         __syncthreads();
       }
-      if (kt + 64 < k_end) issue(IntC<1 - S1>{}, kt + 64);
+      issue_v(slot(IntC<S0 + 3>{}), kt + 64);
+      issue_k(slot(IntC<S0 + 4>{}), kt + 128);
       if constexpr (decltype(ntc)::value > 0)
-        if (nvalid > 0) compute(s1c, ntc, kt, nvalid);
+        compute(slot(IntC<S0>{}), slot(IntC<S0 + 1>{}), ntc, kt, nvalid);
     };
-    issue(IntC<0>{}, k_begin);
-    for (int kt = k_begin; kt < k_end; kt += 128) {
+    issue_k(slot(IntC<0>{}), k_begin);
+    issue_v(slot(IntC<1>{}), k_begin);
+    issue_k(slot(IntC<2>{}), k_begin + 64);
+    // five tiles per round bring the slots back to the start; every step
+    // issues exactly eight loads per wave after its wait, so at a step's
+    // wait the last four are the next tile's K
+    for (int kt = k_begin; kt < k_end; kt += 320) {
       step(IntC<0>{}, kt);
-      step(IntC<1>{}, kt + 64);
+      if (kt + 64 < k_end) step(IntC<2>{}, kt + 64);
+      if (kt + 128 < k_end) step(IntC<4>{}, kt + 128);
+      if (kt + 192 < k_end) step(IntC<1>{}, kt + 192);
+      if (kt + 256 < k_end) step(IntC<3>{}, kt + 256);
     }
+    __builtin_amdgcn_s_waitcnt(0x0f70);                        // vmcnt(0)
   };
-#else
-  // Three stages: two tiles in flight while one is computed.  Every step
-  // issues the tile two ahead (past the end: no memory access, zeros), so
-  // exactly one later tile's 8 loads per wave are outstanding when a step
-  // waits for its own; the loop drains the rest before the partials.
-  auto run = [&](auto ntc) __attribute__((always_inline)) {
-    auto step = [&](auto sc_, int kt) __attribute__((always_inline)) {
-      constexpr int S = decltype(sc_)::value;
-      const int nvalid = min(64, k_end - kt);
-      __builtin_amdgcn_s_waitcnt(0x0f78);                     // vmcnt(8)
-      __syncthreads();
-      if (nvalid > 0 && nvalid < 64) {
-        zero_v(vst(sc_), nvalid);
-        __syncthreads();
-      }
-      issue(IntC<(S + 2) % 3>{}, kt + 128);
-      if constexpr (decltype(ntc)::value > 0)
-        if (nvalid > 0) compute(sc_, ntc, kt, nvalid);
-    };
-    issue(IntC<0>{}, k_begin);
-    issue(IntC<1>{}, k_begin + 64);
-    for (int kt = k_begin; kt < k_end; kt += 192) {
-      step(IntC<0>{}, kt);
-      step(IntC<1>{}, kt + 64);
-      step(IntC<2>{}, kt + 128);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0f70);                       // vmcnt(0)
-  };
-#endif
   if (TPW == 2 && nt == 2) run(IntC<TPW == 2 ? 2 : 1>{});
   else if (nt == 1) run(IntC<1>{});
   else run(IntC<0>{});
@@ -475,6 +534,10 @@ __global__ __launch_bounds__(256, ATT_STAGES == 2 ? 2 : 1) void k_attn_bf16(Attn
     }
   }
 }
+
+// one query tile per wave (launches with few workgroups), two per wave
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_t1(AttnArgs a) { attn_bf16_body<1>(a); }
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_t2(AttnArgs a) { attn_bf16_body<2>(a); }
 
 // Combine the chunk partials of one (row, query head); one wave each, four
 // per block.  Phase 1: the maximum M of the chunk maxima the row sees (its
@@ -592,9 +655,9 @@ void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {
   a.tpw = (long)B * a.hkv * (act + 1) * attn_row_groups(QR, 2) < 512 ? 1 : 2;
   const int nrg = attn_row_groups(QR, a.tpw);
   if (a.tpw == 1)
-    hipLaunchKernelGGL(k_attn_bf16<1>, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16_t1, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16<2>, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16_t2, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
   const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
   const int npairs = rows * a.hq;
   hipLaunchKernelGGL(k_attn_merge, dim3((npairs + 3) / 4), dim3(256), 0, s, a, npairs);
