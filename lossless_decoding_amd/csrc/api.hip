@@ -797,11 +797,18 @@ int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len
   return ORTHRUS_OK;
 }
 
+// kernel (a) alone: chunks of the cache keys, at least one (the draft block
+// is streamed by the last chunk, chunk 0 when there are no cache keys)
+static int block_attn_chunks(int ctx_len, int sc) {
+  const int nc = (ctx_len + sc - 1) / sc;
+  return nc > 0 ? nc : 1;
+}
+
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len) {
   if (batch < 1 || rows < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || ctx_len < 0) return 0;
   int sc = default_attn_chunk(batch, ctx_len, n_kv_heads);
-  int nc = (ctx_len + sc - 1) / sc;
+  int nc = block_attn_chunks(ctx_len, sc);
   uint64_t qr = (uint64_t)rows * (n_q_heads / n_kv_heads);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * qr;
   return al(pr * 128 * 4) + al(pr * 2 * 4);
@@ -824,7 +831,7 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
   if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
   int sc = default_attn_chunk(batch, ctx_len, n_kv_heads);
-  int nc = (ctx_len + sc - 1) / sc;
+  int nc = block_attn_chunks(ctx_len, sc);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
   AttnArgs a{};
   a.P.kind = PASS_DRAFT; a.P.B = batch; a.P.A = 0; a.P.Kx = rows; a.P.p0 = 0; a.P.len = nullptr;

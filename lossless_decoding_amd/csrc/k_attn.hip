@@ -2,22 +2,23 @@
 // rows, the verify pass's causal rows, prefill rows).
 //
 // bf16 path.  A workgroup handles (key chunk, KV head, sequence, group of
-// eight 16-row query tiles); the query rows of a sequence are its tokens x
+// 16-row query tiles); the query rows of a sequence are its tokens x
 // the G query heads of the KV head, so each 64-key K/V tile staged in LDS
-// serves the whole GQA group.  A wave owns two query tiles.
+// serves the whole GQA group.  A wave owns one or two query tiles.
 // MFMA: S^T = K . Q^T (keys x rows) and O^T = V^T . P^T (dims x rows), so a
 // lane always holds one query row and the softmax statistics stay in-lane.
 // Softmax in fp32 with a base-2 exponent against a per-row reference that is
 // raised only when a tile's scores exceed it by more than 2^8.  K/V tiles go
-// from memory straight into a two-stage LDS ring while the other stage is
-// computed.  Chunks are SC keys aligned to absolute cache positions; each
-// writes its partial (reference, sum, unnormalised output) and the merge
-// kernel combines a row's partials in increasing chunk order, the draft
-// block's keys last.  A row's result therefore depends only on which keys
-// it sees, never on the other rows of the pass: fully masked tiles and
-// chunks are exact no-ops, masked keys are removed by selection (never by
-// multiplying stale values), and keys past the pass's last written slot are
-// zeroed when staged.
+// from memory straight into a five-slot LDS ring, three tile halves ahead of
+// the one computed.  Chunks are SC keys aligned to absolute cache positions;
+// the sequence's last chunk also streams the draft block's keys, after its
+// cache keys.  Each chunk writes its partial (reference, sum, unnormalised
+// output) and the merge kernel combines a row's partials in increasing chunk
+// order.  A row's result therefore depends only on which keys it sees, never
+// on the other rows of the pass: fully masked tiles and chunks are exact
+// no-ops, masked keys are removed by selection (never by multiplying stale
+// values), and keys past the pass's last written slot are zeroed when
+// staged.
 //
 // fp32 path: one wave per (row, query head), keys in order (check models).
 #include "internal.h"
@@ -136,44 +137,28 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   const int QR = T * G;
   const int NRT = (QR + 15) >> 4;
   const int NRG = attn_row_groups(QR, TPW);
-  // 1-D grid: every (cache chunk, KV head, sequence x row group) first, then
-  // the short block-chunk workgroups, which fill the tail
-  int c, g, zz;
-  {
-    const int ncache = a.nc * a.hkv * P.B * NRG;
-    int id = blockIdx.x;
-    if (id < ncache) {
-      c = id % a.nc;
-      const int r = id / a.nc;
-      g = r % a.hkv;
-      zz = r / a.hkv;
-    } else {
-      id -= ncache;
-      c = a.nc;
-      g = id % a.hkv;
-      zz = id / a.hkv;
-    }
-  }
+  // 1-D grid over (chunk, KV head, sequence x row group), chunk fastest
+  const int c = blockIdx.x % a.nc;
+  const int g = (blockIdx.x / a.nc) % a.hkv;
+  const int zz = blockIdx.x / (a.nc * a.hkv);
   const int b = zz / NRG, rg = zz - b * NRG;
-  const bool blk = (c == a.nc);
   const int hd = 128;
   const int H = a.hq * hd;
 
-  // which chunks take part: every chunk up to the sequence's last visible
-  // slot, plus the block chunk when the pass has a draft block
+  // Which chunks take part: every chunk up to the sequence's last visible
+  // slot.  The draft block's keys (at most one tile) are streamed by the
+  // sequence's last chunk after its cache keys (by chunk 0 when there are
+  // no cache keys): one partial per chunk, no separate block workgroups.
   const bool has_blk = a.block_len > 0 && (a.fixed_ctx >= 0 || (P.kind == PASS_DRAFT && P.Kx > 0));
   const SeqLimits L = seq_limits(a, b);
   const int lastk = L.maxlim < a.cap - 1 ? L.maxlim : a.cap - 1;
   const int nch = lastk >= 0 ? lastk / a.sc + 1 : 0;
-  if (blk ? !has_blk : c >= nch) return;
-  int k_begin, k_end;
-  if (!blk) {
-    k_begin = c * a.sc;
-    k_end = min(k_begin + a.sc, lastk + 1);
-  } else {
-    k_begin = 0;
-    k_end = a.block_len;
-  }
+  const int c_last = nch > 0 ? nch - 1 : 0;
+  if (c > c_last || (nch == 0 && !has_blk)) return;
+  const int k_begin = c * a.sc;
+  const int k_end = nch > 0 ? min(k_begin + a.sc, lastk + 1) : k_begin;   // cache keys [k_begin, k_end)
+  const int nct = (k_end - k_begin + 63) >> 6;                             // cache tiles
+  const int ntot = nct + ((has_blk && c == c_last) ? 1 : 0);               // + the block tile
 
   // This wave's query tiles rt0 .. rt0 + tpw - 1 (B operands of
   // S^T = K.Q^T); lane row qr = rt*16 + lr.  A padding row (qr >= QR) gets a
@@ -206,26 +191,22 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   }
   const int lmin = nt == 2 ? min(lim[0], lim[1]) : lim[0];
 
-  const uint16_t* kbase;
-  const uint16_t* vbase;
-  if (!blk) {
-    kbase = (const uint16_t*)a.kc + ((size_t)b * a.hkv + g) * a.cap * hd;
-    vbase = (const uint16_t*)a.vc + ((size_t)b * a.hkv + g) * a.cap * hd;   // tiles of 64*hd
-  } else {
-    kbase = (const uint16_t*)a.ks + ((size_t)b * a.hkv + g) * a.kpad * hd;
-    vbase = (const uint16_t*)a.vs + ((size_t)b * a.hkv + g) * hd * a.kpad;
-  }
+  const uint16_t* kbase = (const uint16_t*)a.kc + ((size_t)b * a.hkv + g) * a.cap * hd;
+  const uint16_t* vbase = (const uint16_t*)a.vc + ((size_t)b * a.hkv + g) * a.cap * hd;   // tiles of 64*hd
+  const uint16_t* kblk = (const uint16_t*)a.ks + ((size_t)b * a.hkv + g) * a.kpad * hd;
+  const uint16_t* vblk = (const uint16_t*)a.vs + ((size_t)b * a.hkv + g) * hd * a.kpad;
   const float sl2 = 1.4426950408889634f / sqrtf((float)hd);
 
   // Tiles go from memory straight into LDS (buffer loads with an LDS
   // destination): per tile each wave moves 4 KB of K and 4 KB of V^T, one
   // kilobyte per instruction (64 lanes x 16 bytes, in lane order), each lane
   // fetching the piece that the XOR permutation puts at its position.  The
-  // descriptors cover one tile: K pieces past the chunk's last key, V^T pieces
-  // past the tile and every piece of a tile past the end read as zero without
-  // touching memory.  V^T columns of keys past the end within the last tile
-  // hold whatever the cache holds there; they are zeroed in LDS.
-  const int kv_hi = blk ? a.block_len : k_end;                 // keys [0, kv_hi) exist
+  // descriptors cover one tile: K pieces past the last key, V^T pieces past
+  // the tile and every piece of a tile past the last read as zero without
+  // touching memory.  V^T columns of keys past the end within a partial tile
+  // hold whatever memory holds there; they are zeroed in LDS.  Tile i < nct
+  // is the cache tile at key k_begin + 64 i; tile nct is the draft block
+  // (K rows [kpad][128], V^T [128][kpad] in the same column order).
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   int koff[LPU], voff[LPU];
 #pragma unroll
@@ -233,29 +214,44 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
     const int key = (wv * LPU + j) * 4 + (lane >> 4);
     koff[j] = key * 256 + (((lane & 15) ^ (key & 15)) << 4);   // unit (lane & 15) ^ (key & 15) of the key
     const int d = (wv * LPU + j) * 8 + (lane >> 3);
-    const int ku = (lane & 7) ^ (d & 7);
-    voff[j] = blk ? (d * a.kpad + ku * 8) * 2 : d * 128 + ku * 16;
+    voff[j] = d * 128 + (((lane & 7) ^ (d & 7)) << 4);         // unit (lane & 7) ^ (d & 7) of the row
   }
-  // K unit / V^T unit of the tile at key kt into LDS slot dst (kt past the
-  // end: size-0 descriptor, zeros, no memory access)
-  auto issue_k = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
-    const int nk = kt < k_end ? min(64, kv_hi - kt) : 0;
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(kbase + (size_t)kt * hd), (short)0, nk * hd * 2, 0x00020000);
+  auto issue_k = [&](uint16_t* dst, int i) __attribute__((always_inline)) {
+    const uint16_t* src = kbase;
+    int nk = 0;
+    if (i < nct) {
+      const int kt = k_begin + i * 64;
+      src = kbase + (size_t)kt * hd;
+      nk = min(64, k_end - kt);
+    } else if (i < ntot) {
+      src = kblk;
+      nk = a.block_len;
+    }
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nk * hd * 2, 0x00020000);
 #pragma unroll
     for (int j = 0; j < LPU; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16, koff[j], 0, 0, 0);
   };
-  auto issue_v = [&](uint16_t* dst, int kt) __attribute__((always_inline)) {
-    const bool live = kt < k_end;                              // uniform
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(blk ? vbase : vbase + (size_t)(kt >> 6) * 64 * hd), (short)0,
-        live ? (blk ? hd * a.kpad * 2 : 64 * hd * 2) : 0, 0x00020000);
+  // V^T: a cache tile is 128 rows of 64 keys; the block's rows are kpad
+  // keys long (pieces past kpad belong to the next row; they are zeroed in
+  // LDS with the keys past block_len).  One load sequence for both, so the
+  // compiler tracks each slot's loads as one group.
+  auto issue_v = [&](uint16_t* dst, int i) __attribute__((always_inline)) {
+    const bool bt = i >= nct && i < ntot;                      // uniform
+    const uint16_t* src = bt ? vblk : vbase + (size_t)((k_begin >> 6) + (i < nct ? i : 0)) * 64 * hd;
+    const int bytes = i >= ntot ? 0 : (bt ? hd * a.kpad * 2 : 64 * hd * 2);
+    const int row_extra = bt ? a.kpad * 2 - 128 : 0;         // row length - 128 bytes
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, bytes, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < LPU; ++j)
+    for (int j = 0; j < LPU; ++j) {
+      const int d = (wv * LPU + j) * 8 + (lane >> 3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16, voff[j], 0, 0, 0);
+          r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16,
+          voff[j] + d * row_extra, 0, 0, 0);
+    }
   };
   // zero the V^T columns of keys >= nvalid (the last, partial tile)
   auto zero_v = [&](uint16_t* V, int nvalid) __attribute__((always_inline)) {
@@ -283,7 +279,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
 
   // The tile's work for the wave's NT query tiles.  Every K and V^T
   // fragment read from LDS feeds one MFMA per query tile.
-  auto compute = [&](const uint16_t* sK, const uint16_t* sV, auto ntc, int kt, int nvalid)
+  auto compute = [&](const uint16_t* sK, const uint16_t* sV, auto ntc, int kt, int nvalid, bool bt)
       __attribute__((always_inline)) {
     constexpr int NT = decltype(ntc)::value;
     const char* sKb = (const char*)sK;
@@ -315,7 +311,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
     // Visibility: when every key of the tile is visible to every row of the
     // wave (the common case at long context) nothing is masked; otherwise
     // invisible keys get the score -inf.
-    const bool all_vis = !blk && nvalid == 64 && __all(kt + 63 <= lmin);
+    const bool all_vis = !bt && nvalid == 64 && __all(kt + 63 <= lmin);
     if (!all_vis) {
       const int lq4 = opaque(lq * 4);                          // (keeps no per-key constants live)
 #pragma unroll
@@ -325,7 +321,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int kl = kb * 16 + lq4 + i;
-            const bool ok = kl < nvalid && (blk ? seesb[t] != 0 : (kt + kl) <= lim[t]);
+            const bool ok = kl < nvalid && (bt ? seesb[t] != 0 : (kt + kl) <= lim[t]);
             s[t][kb][i] = ok ? s[t][kb][i] : -INFINITY;
           }
     }
@@ -479,32 +475,34 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   auto run = [&](auto ntc) __attribute__((always_inline)) {
     // tile i: K in slot (2i) % 5 = S0, V^T in S0 + 1; the freed slots of
     // tile i - 1 are S0 + 3 and S0 + 4 (mod 5)
-    auto step = [&](auto s0c, int kt) __attribute__((always_inline)) {
+    auto step = [&](auto s0c, int i) __attribute__((always_inline)) {
       constexpr int S0 = decltype(s0c)::value;
-      const int nvalid = min(64, k_end - kt);
+      const bool bt = i >= nct;                                // the block tile
+      const int kt = bt ? 0 : k_begin + i * 64;
+      const int nvalid = bt ? a.block_len : min(64, k_end - kt);
       __builtin_amdgcn_s_waitcnt(0x0070 | LPU);                // vmcnt(LPU) lgkmcnt(0)
       step_barrier();
       if (nvalid < 64) {
         zero_v(slot(IntC<S0 + 1>{}), nvalid);
         __syncthreads();
       }
-      issue_v(slot(IntC<S0 + 3>{}), kt + 64);
-      issue_k(slot(IntC<S0 + 4>{}), kt + 128);
+      issue_v(slot(IntC<S0 + 3>{}), i + 1);
+      issue_k(slot(IntC<S0 + 4>{}), i + 2);
       if constexpr (decltype(ntc)::value > 0)
-        compute(slot(IntC<S0>{}), slot(IntC<S0 + 1>{}), ntc, kt, nvalid);
+        compute(slot(IntC<S0>{}), slot(IntC<S0 + 1>{}), ntc, kt, nvalid, bt);
     };
-    issue_k(slot(IntC<0>{}), k_begin);
-    issue_v(slot(IntC<1>{}), k_begin);
-    issue_k(slot(IntC<2>{}), k_begin + 64);
+    issue_k(slot(IntC<0>{}), 0);
+    issue_v(slot(IntC<1>{}), 0);
+    issue_k(slot(IntC<2>{}), 1);
     // five tiles per round bring the slots back to the start; every step
-    // issues exactly eight loads per wave after its wait, so at a step's
-    // wait the last four are the next tile's K
-    for (int kt = k_begin; kt < k_end; kt += 320) {
-      step(IntC<0>{}, kt);
-      if (kt + 64 < k_end) step(IntC<2>{}, kt + 64);
-      if (kt + 128 < k_end) step(IntC<4>{}, kt + 128);
-      if (kt + 192 < k_end) step(IntC<1>{}, kt + 192);
-      if (kt + 256 < k_end) step(IntC<3>{}, kt + 256);
+    // issues exactly 2 LPU loads per wave after its wait, so at a step's
+    // wait the last LPU are the next tile's K
+    for (int i = 0; i < ntot; i += 5) {
+      step(IntC<0>{}, i);
+      if (i + 1 < ntot) step(IntC<2>{}, i + 1);
+      if (i + 2 < ntot) step(IntC<4>{}, i + 2);
+      if (i + 3 < ntot) step(IntC<1>{}, i + 3);
+      if (i + 4 < ntot) step(IntC<3>{}, i + 4);
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);                        // vmcnt(0)
   };
@@ -540,10 +538,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16_t1(AttnArgs a) { attn_bf16
 __global__ __launch_bounds__(256, 2) void k_attn_bf16_t2(AttnArgs a) { attn_bf16_body<2>(a); }
 
 // Combine the chunk partials of one (row, query head); one wave each, four
-// per block.  Phase 1: the maximum M of the chunk maxima the row sees (its
-// cache chunks, then the block chunk).  Phase 2: l = sum_c l_c 2^(m_c - M)
-// and o = sum_c o_c 2^(m_c - M), summed in increasing chunk order (block
-// last).  All loads of a phase are independent, so the merge costs two
+// per block.  Phase 1: the maximum M of the chunk maxima the row sees.
+// Phase 2: l = sum_c l_c 2^(m_c - M) and o = sum_c o_c 2^(m_c - M), summed
+// in increasing chunk order.  All loads of a phase are independent, so the merge costs two
 // memory round trips; the result depends only on the row's own partials.
 __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   __shared__ float sw[4][64];
@@ -566,10 +563,12 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   const bool has_blk = a.block_len > 0 && (a.fixed_ctx >= 0 || (P.kind == PASS_DRAFT && P.Kx > 0));
   const int qr = t * G + (h - g * G);
   if (limit >= a.cap) limit = a.cap - 1;
+  // the row folds the partials of the chunks it sees; the draft block's
+  // keys are inside the sequence's last chunk (chunk 0 without cache keys)
   const int nrow = limit >= 0 ? limit / a.sc + 1 : 0;
-  const int ntot = nrow + ((sees && has_blk) ? 1 : 0);   // partials this row folds
+  const int ntot = nrow > 0 ? nrow : ((sees && has_blk) ? 1 : 0);
   const size_t sbase = (size_t)(b * a.hkv + g) * (a.nc + 1);
-  auto pidx = [&](int j) { return (sbase + (j < nrow ? j : a.nc)) * a.qr_max + qr; };
+  auto pidx = [&](int j) { return (sbase + j) * a.qr_max + qr; };
   // The output partials of the first PRE chunks do not depend on the
   // maxima: they are requested together with the chunk references, so a row
   // with up to PRE partials costs one memory round trip.
@@ -652,12 +651,12 @@ void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {
   // tile per wave gives a latency-bound launch (fewer workgroups than two
   // per compute unit) twice the workgroups with half the work each
   const int act = a.active_chunks > 0 && a.active_chunks < a.nc ? a.active_chunks : a.nc;
-  a.tpw = (long)B * a.hkv * (act + 1) * attn_row_groups(QR, 2) < 512 ? 1 : 2;
+  a.tpw = (long)B * a.hkv * act * attn_row_groups(QR, 2) < 512 ? 1 : 2;
   const int nrg = attn_row_groups(QR, a.tpw);
   if (a.tpw == 1)
-    hipLaunchKernelGGL(k_attn_bf16_t1, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16_t1, dim3(a.nc * a.hkv * B * nrg), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16_t2, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16_t2, dim3(a.nc * a.hkv * B * nrg), dim3(256), 0, s, a);
   const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
   const int npairs = rows * a.hq;
   hipLaunchKernelGGL(k_attn_merge, dim3((npairs + 3) / 4), dim3(256), 0, s, a, npairs);
