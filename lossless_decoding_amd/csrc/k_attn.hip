@@ -137,28 +137,35 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   const int QR = T * G;
   const int NRT = (QR + 15) >> 4;
   const int NRG = attn_row_groups(QR, TPW);
-  // 1-D grid over (chunk, KV head, sequence x row group), chunk fastest
-  const int c = blockIdx.x % a.nc;
-  const int g = (blockIdx.x / a.nc) % a.hkv;
-  const int zz = blockIdx.x / (a.nc * a.hkv);
+  // 1-D grid over (chunk, KV head, sequence x row group), chunk fastest.
+  // The draft block's keys (at most one tile) are streamed by the
+  // sequence's last chunk after its cache keys (chunk 0 when there are no
+  // cache keys) when the launch has two query tiles per wave (many
+  // workgroups: one partial fewer per row, no short block workgroups in a
+  // second round); with one tile per wave (a launch that fits in one round)
+  // by a block workgroup of their own, chunk index nc, in parallel.
+  constexpr bool FOLD = TPW == 2;
+  const int ncol = FOLD ? a.nc : a.nc + 1;
+  const int c = blockIdx.x % ncol;
+  const int g = (blockIdx.x / ncol) % a.hkv;
+  const int zz = blockIdx.x / (ncol * a.hkv);
   const int b = zz / NRG, rg = zz - b * NRG;
   const int hd = 128;
   const int H = a.hq * hd;
 
-  // Which chunks take part: every chunk up to the sequence's last visible
-  // slot.  The draft block's keys (at most one tile) are streamed by the
-  // sequence's last chunk after its cache keys (by chunk 0 when there are
-  // no cache keys): one partial per chunk, no separate block workgroups.
+  // which chunks take part: every chunk up to the sequence's last visible
+  // slot, and the block
   const bool has_blk = a.block_len > 0 && (a.fixed_ctx >= 0 || (P.kind == PASS_DRAFT && P.Kx > 0));
   const SeqLimits L = seq_limits(a, b);
   const int lastk = L.maxlim < a.cap - 1 ? L.maxlim : a.cap - 1;
   const int nch = lastk >= 0 ? lastk / a.sc + 1 : 0;
   const int c_last = nch > 0 ? nch - 1 : 0;
-  if (c > c_last || (nch == 0 && !has_blk)) return;
-  const int k_begin = c * a.sc;
-  const int k_end = nch > 0 ? min(k_begin + a.sc, lastk + 1) : k_begin;   // cache keys [k_begin, k_end)
+  const bool blk_wg = !FOLD && c == a.nc;                                  // block keys only
+  if (blk_wg ? !has_blk : (c > c_last || (nch == 0 && !(FOLD && has_blk)))) return;
+  const int k_begin = blk_wg ? 0 : c * a.sc;
+  const int k_end = (blk_wg || nch == 0) ? k_begin : min(k_begin + a.sc, lastk + 1);   // cache keys
   const int nct = (k_end - k_begin + 63) >> 6;                             // cache tiles
-  const int ntot = nct + ((has_blk && c == c_last) ? 1 : 0);               // + the block tile
+  const int ntot = nct + ((has_blk && (blk_wg || (FOLD && c == c_last))) ? 1 : 0);   // + block tile
 
   // This wave's query tiles rt0 .. rt0 + tpw - 1 (B operands of
   // S^T = K.Q^T); lane row qr = rt*16 + lr.  A padding row (qr >= QR) gets a
@@ -472,7 +479,42 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  // Launches with few workgroups (one query tile per wave; B = 1 decode)
+  // have chunks of one or two tiles: there a plain two-stage schedule
+  // (slots 0-1 and 2-3) loads whole tiles, waits for all loads, and loads
+  // no tile past the end.
+  auto run2 = [&](auto ntc) __attribute__((always_inline)) {
+    auto step = [&](auto s1c, int i) __attribute__((always_inline)) {
+      constexpr int S1 = decltype(s1c)::value;
+      const bool bt = i >= nct;                                // the block tile
+      const int kt = bt ? 0 : k_begin + i * 64;
+      const int nvalid = bt ? a.block_len : min(64, k_end - kt);
+      __builtin_amdgcn_s_waitcnt(0x0f70);                      // vmcnt(0)
+      __syncthreads();
+      if (nvalid < 64) {
+        zero_v(slot(IntC<2 * S1 + 1>{}), nvalid);
+        __syncthreads();
+      }
+      if (i + 1 < ntot) {
+        issue_k(slot(IntC<2 - 2 * S1>{}), i + 1);
+        issue_v(slot(IntC<3 - 2 * S1>{}), i + 1);
+      }
+      if constexpr (decltype(ntc)::value > 0)
+        compute(slot(IntC<2 * S1>{}), slot(IntC<2 * S1 + 1>{}), ntc, kt, nvalid, bt);
+    };
+    issue_k(slot(IntC<0>{}), 0);
+    issue_v(slot(IntC<1>{}), 0);
+    for (int i = 0; i < ntot; i += 2) {
+      step(IntC<0>{}, i);
+      if (i + 1 < ntot) step(IntC<1>{}, i + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);                        // vmcnt(0)
+  };
   auto run = [&](auto ntc) __attribute__((always_inline)) {
+    if constexpr (TPW == 1) {
+      run2(ntc);
+      return;
+    }
     // tile i: K in slot (2i) % 5 = S0, V^T in S0 + 1; the freed slots of
     // tile i - 1 are S0 + 3 and S0 + 4 (mod 5)
     auto step = [&](auto s0c, int i) __attribute__((always_inline)) {
@@ -565,10 +607,13 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   if (limit >= a.cap) limit = a.cap - 1;
   // the row folds the partials of the chunks it sees; the draft block's
   // keys are inside the sequence's last chunk (chunk 0 without cache keys)
+  // after a two-tile launch, in partial nc (folded last) after a one-tile one
   const int nrow = limit >= 0 ? limit / a.sc + 1 : 0;
-  const int ntot = nrow > 0 ? nrow : ((sees && has_blk) ? 1 : 0);
+  const bool blocked = sees && has_blk;
+  const bool folded = a.tpw == 2;
+  const int ntot = folded ? (nrow > 0 ? nrow : (blocked ? 1 : 0)) : nrow + (blocked ? 1 : 0);
   const size_t sbase = (size_t)(b * a.hkv + g) * (a.nc + 1);
-  auto pidx = [&](int j) { return (sbase + j) * a.qr_max + qr; };
+  auto pidx = [&](int j) { return (sbase + (folded || j < nrow ? j : a.nc)) * a.qr_max + qr; };
   // The output partials of the first PRE chunks do not depend on the
   // maxima: they are requested together with the chunk references, so a row
   // with up to PRE partials costs one memory round trip.
@@ -654,7 +699,7 @@ void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {
   a.tpw = (long)B * a.hkv * act * attn_row_groups(QR, 2) < 512 ? 1 : 2;
   const int nrg = attn_row_groups(QR, a.tpw);
   if (a.tpw == 1)
-    hipLaunchKernelGGL(k_attn_bf16_t1, dim3(a.nc * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_attn_bf16_t1, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(k_attn_bf16_t2, dim3(a.nc * a.hkv * B * nrg), dim3(256), 0, s, a);
   const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
