@@ -67,17 +67,32 @@ struct Layout {
 // `kv_heads` KV heads.  Each (chunk, KV head, sequence) is a workgroup that
 // writes a 64 KB partial (fp32, 128 rows), which is 1/8 of the keys' bytes
 // at 1024-key chunks and 1/2 at 256.  The rule (a power of two in [64,
-// 4096], measured on the decode workloads and on kernel (a) alone): the
-// smallest one with at most 64 chunks per sequence and at most 1280
-// workgroups, and at least 1024 keys whenever 1024-key chunks still give
-// 512 workgroups (two per compute unit).
+// 4096], measured on the decode workloads): the smallest one with at most
+// 64 chunks per sequence and at most 1100 workgroups, and at least 1024 keys
+// whenever 1024-key chunks still give 512 workgroups (two per compute unit).
 static int default_attn_chunk(int batch, int slots, int kv_heads) {
   const long pairs = (long)batch * (kv_heads > 0 ? kv_heads : 1);
   const bool long_ok = pairs * ((slots + 1023) / 1024) >= 512;
   int sc = 64;
   while (sc < 4096) {
     const long nch = (slots + sc - 1) / sc;
-    if (nch <= 64 && pairs * nch <= 1280 && !(long_ok && sc < 1024)) break;
+    if (nch <= 64 && pairs * nch <= 1100 && !(long_ok && sc < 1024)) break;
+    sc *= 2;
+  }
+  return sc;
+}
+
+// Kernel (a) alone (one pass, every row sees every key): the smallest power
+// of two in [64, 16384] with at most 64 chunks per sequence and at most 512
+// (chunk, KV head, sequence) workgroups, i.e. one round of two per compute
+// unit (measured: 1024 at 4 x 16384 and 16 x 4096 keys, 8192 at 16 x 32768,
+// 4096 at 8 x 32768).
+static int block_attn_chunk(int batch, int ctx, int kv_heads) {
+  const long pairs = (long)batch * kv_heads;
+  int sc = 64;
+  while (sc < 16384) {
+    const long nch = (ctx + sc - 1) / sc;
+    if (nch <= 64 && pairs * nch <= 512) break;
     sc *= 2;
   }
   return sc;
@@ -799,7 +814,7 @@ int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len
 
 // kernel (a) alone: chunks of the cache keys, at least one (the draft block
 // is streamed by the last chunk, chunk 0 when there are no cache keys)
-static int block_attn_chunks(int ctx_len, int sc) {
+static int block_attn_nchunks(int ctx_len, int sc) {
   const int nc = (ctx_len + sc - 1) / sc;
   return nc > 0 ? nc : 1;
 }
@@ -807,8 +822,8 @@ static int block_attn_chunks(int ctx_len, int sc) {
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len) {
   if (batch < 1 || rows < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads || ctx_len < 0) return 0;
-  int sc = default_attn_chunk(batch, ctx_len, n_kv_heads);
-  int nc = block_attn_chunks(ctx_len, sc);
+  int sc = block_attn_chunk(batch, ctx_len, n_kv_heads);
+  int nc = block_attn_nchunks(ctx_len, sc);
   uint64_t qr = (uint64_t)rows * (n_q_heads / n_kv_heads);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * qr;
   return al(pr * 128 * 4) + al(pr * 2 * 4);
@@ -830,8 +845,8 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
     return ORTHRUS_EINVAL;
   uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
   if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
-  int sc = default_attn_chunk(batch, ctx_len, n_kv_heads);
-  int nc = block_attn_chunks(ctx_len, sc);
+  int sc = block_attn_chunk(batch, ctx_len, n_kv_heads);
+  int nc = block_attn_nchunks(ctx_len, sc);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
   AttnArgs a{};
   a.P.kind = PASS_DRAFT; a.P.B = batch; a.P.A = 0; a.P.Kx = rows; a.P.p0 = 0; a.P.len = nullptr;

@@ -106,16 +106,16 @@ def test_call_order_errors_on_null_context_args():
 
 @pytest.mark.parametrize("batch,ctx,kvh,want", [
     (1, 4668, 8, 128),      # B = 1 decode: at most 64 chunks per sequence
-    (16, 8619, 8, 1024),    # 16 x 8192 decode: <= 1280 workgroups, >= 1024 keys
+    (16, 8619, 8, 2048),    # 16 x 8192 decode: <= 1100 workgroups, >= 1024 keys
     (8, 33096, 8, 2048),    # 8 x 32768 decode
-    (4, 16384, 8, 1024),    # kernel (a), 256 MB points
+    (4, 16384, 8, 1024),
     (16, 4096, 8, 1024),
     (16, 32768, 8, 4096),   # capped at 4096
     (1, 64, 2, 64),         # floor
 ])
 def test_default_attention_chunk_rule(batch, ctx, kvh, want):
     """The chunk rule the header documents: the smallest power of two in
-    [64, 4096] with <= 64 chunks per sequence and <= 1280 (chunk, KV head,
+    [64, 4096] with <= 64 chunks per sequence and <= 1100 (chunk, KV head,
     sequence) workgroups, at least 1024 when 1024-key chunks still give 512
     workgroups (slots rounded up to 64)."""
     got = C.orthrus_default_attn_chunk(batch, ctx, kvh)
@@ -124,12 +124,35 @@ def test_default_attention_chunk_rule(batch, ctx, kvh, want):
     nch = -(-slots // got)
     assert got & (got - 1) == 0 and 64 <= got <= 4096
     if got < 4096:
-        assert nch <= 64 and batch * kvh * nch <= 1280
+        assert nch <= 64 and batch * kvh * nch <= 1100
     if got > 64:      # the next smaller size breaks a condition
         half = got // 2
         n2 = -(-slots // half)
         long_ok = batch * kvh * (-(-slots // 1024)) >= 512
-        assert n2 > 64 or batch * kvh * n2 > 1280 or (long_ok and half < 1024)
+        assert n2 > 64 or batch * kvh * n2 > 1100 or (long_ok and half < 1024)
+
+
+@pytest.mark.parametrize("batch,ctx,kvh,chunk", [
+    (4, 16384, 8, 1024),    # the 256 MB kernel (a) points
+    (16, 4096, 8, 1024),
+    (16, 32768, 8, 8192),
+    (8, 32768, 8, 4096),
+    (1, 4096, 8, 64),
+    (1, 0, 8, 64),          # block keys only: one chunk
+])
+def test_block_attention_chunk_rule(batch, ctx, kvh, chunk):
+    """Kernel (a) alone sizes its workspace for its own chunk rule (the
+    smallest power of two in [64, 16384] with <= 64 chunks and <= 512
+    workgroups): partials for max(1, chunks) + 1 chunks of rows x G rows,
+    each 128 fp32 plus (m, l), each array 256-byte aligned."""
+    rows, hq = 32, 32
+    nch = max(1, -(-ctx // chunk))
+    pr = batch * kvh * (nch + 1) * rows * (hq // kvh)
+    al = lambda n: (n + 255) // 256 * 256
+    assert C.orthrus_attention_workspace(batch, rows, hq, kvh, ctx) == al(pr * 512) + al(pr * 8)
+    if chunk > 64:    # the next smaller size breaks a condition
+        n2 = -(-ctx // (chunk // 2))
+        assert n2 > 64 or batch * kvh * n2 > 512
 
 
 def test_default_attention_chunk_rejects_bad_args():
