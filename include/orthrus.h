@@ -196,8 +196,11 @@ int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len
  * 0 draft, 1 verify, 2 prefill and role 0 QKV GEMM, 1 attention (+ merge),
  * 2 O GEMM, 3 gate/up SwiGLU GEMM, 4 down GEMM, 5 LM head + argmax, 6 the
  * small kernels (embed, RMSNorm, QK-norm/RoPE/KV write), 7 accept and
- * commit (pass 1 only).  class_mask bit k selects class k; capacity = event
- * pairs kept (launches past it are not timed).  class_mask 0 turns timing
+ * commit (pass 1 only).  The gate/up GEMM is one kernel; its pair is
+ * recorded by the kernel's dispatch (hipExtLaunchKernel), so it spans the
+ * kernel alone; the other classes' pairs are recorded around their launches.
+ * class_mask bit k selects class k; capacity = event pairs kept (launches
+ * past it are not timed).  class_mask 0 turns timing
  * off.  orthrus_timing_read synchronizes on the recorded events, adds each
  * pair's elapsed time to ms[class] (milliseconds) and counts launches[class]
  * (both arrays ORTHRUS_TIMING_CLASSES long), then starts a new record;

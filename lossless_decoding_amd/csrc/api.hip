@@ -261,15 +261,28 @@ int check_launch() { return hip_ok(hipGetLastError()); }
 enum { R_QKV = 0, R_ATTN = 1, R_O = 2, R_GU = 3, R_DOWN = 4, R_LM = 5, R_SMALL = 6, R_ACC = 7 };
 inline int pass_base(int kind) { return kind * 8; }
 
+// Times the launches in its scope with a pair of events on the stream.  The
+// gate/up role is one GEMM kernel: there the kernel's dispatch records the
+// pair itself (no gap from event records around it), as profiler traces do.
 struct Tick {
-  orthrus_ctx* c; int i; hipStream_t s;
-  Tick(orthrus_ctx* c_, int cls, hipStream_t s_) : c(c_), i(-1), s(s_) {
+  orthrus_ctx* c; int i; hipStream_t s; bool ext;
+  Tick(orthrus_ctx* c_, int cls, hipStream_t s_) : c(c_), i(-1), s(s_), ext(false) {
     if (!(c->tmask >> cls & 1u) || c->ev_used * 2 >= (int)c->ev.size()) return;
     i = c->ev_used++;
     c->ev_cls[i] = cls;
-    (void)hipEventRecord(c->ev[2 * i], s);
+    ext = cls % 8 == R_GU;
+    if (ext) gemm_time_next_launch(c->ev[2 * i], c->ev[2 * i + 1]);
+    else (void)hipEventRecord(c->ev[2 * i], s);
   }
-  ~Tick() { if (i >= 0) (void)hipEventRecord(c->ev[2 * i + 1], s); }
+  ~Tick() {
+    if (i < 0) return;
+    if (!ext) { (void)hipEventRecord(c->ev[2 * i + 1], s); return; }
+    if (gemm_time_pending()) {        // no GEMM launched: an empty interval
+      gemm_time_next_launch(nullptr, nullptr);
+      (void)hipEventRecord(c->ev[2 * i], s);
+      (void)hipEventRecord(c->ev[2 * i + 1], s);
+    }
+  }
 };
 
 template <typename T> T* W(orthrus_ctx* c, uint64_t off) { return (T*)(c->packed + off); }

@@ -147,6 +147,10 @@ struct GemmArgs {
   int32_t* drafts; int32_t* ar; int32_t* pending;
 };
 void launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// Profiling: the next bf16 GEMM kernel launched from this host thread
+// records start / stop itself (hipExtLaunchKernel); pending until taken.
+void gemm_time_next_launch(hipEvent_t start, hipEvent_t stop);
+bool gemm_time_pending();
 int gemm_bf16_groups(int N);
 // 0, or the K slices whose partials an EP_RESID launch of these rows leaves
 // for the residual + RMSNorm kernel

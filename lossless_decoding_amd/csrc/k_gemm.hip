@@ -33,6 +33,32 @@
 // fp32 path: one thread per output with a sequential k loop (check models).
 #include "internal.h"
 
+#include <hip/hip_ext.h>
+
+// A GEMM launch that profiling asked to time: the dispatch itself records
+// the event pair at the kernel's start and end (no gap from separate event
+// records).  One pending pair per host thread, taken by the next GEMM
+// kernel launched from that thread.
+static thread_local hipEvent_t t_ev_start = nullptr, t_ev_stop = nullptr;
+
+void gemm_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+  t_ev_start = start;
+  t_ev_stop = stop;
+}
+
+bool gemm_time_pending() { return t_ev_start != nullptr; }
+
+template <typename K>
+static void gemm_launch(K kernel, dim3 grid, dim3 block, hipStream_t s, const GemmArgs& a) {
+  if (t_ev_start) {
+    hipEvent_t e0 = t_ev_start, e1 = t_ev_stop;
+    t_ev_start = t_ev_stop = nullptr;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, e0, e1, 0, a);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, a);
+  }
+}
+
 
 #define NSL 8                 // K slices
 #define SKB 16                // k-blocks of 32 per activation stage
@@ -546,13 +572,13 @@ template <int EP, int WV, bool SPLIT, int CT = 1>
 static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
   const dim3 block(WV * 64);
   switch (MT) {
-    case 1: hipLaunchKernelGGL((k_gemm_bf16<1, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_bf16<2, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_bf16<3, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_gemm_bf16<4, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_gemm_bf16<8, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
-    case 12: hipLaunchKernelGGL((k_gemm_bf16<12, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
-    default: hipLaunchKernelGGL((k_gemm_bf16<16, EP, WV, SPLIT, CT>), grid, block, 0, s, a); break;
+    case 1: gemm_launch(k_gemm_bf16<1, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    case 2: gemm_launch(k_gemm_bf16<2, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    case 3: gemm_launch(k_gemm_bf16<3, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    case 4: gemm_launch(k_gemm_bf16<4, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    case 8: gemm_launch(k_gemm_bf16<8, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    case 12: gemm_launch(k_gemm_bf16<12, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    default: gemm_launch(k_gemm_bf16<16, EP, WV, SPLIT, CT>, grid, block, s, a); break;
   }
 }
 
@@ -563,7 +589,7 @@ static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
 // tiles' accumulators.
 template <int EP>
 static void dispatch_ct2(dim3 grid, const GemmArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((k_gemm_bf16<8, EP, 4, false, 2>), grid, dim3(256), 0, s, a);
+  gemm_launch(k_gemm_bf16<8, EP, 4, false, 2>, grid, dim3(256), s, a);
 }
 
 int gemm_bf16_groups(int N) { return N / 128; }
@@ -633,7 +659,7 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     switch (a.ep) {
       case EP_RESID:
         // 128-row tiles: two column tiles per wave
-        if (MT == 8) hipLaunchKernelGGL((k_gemm_bf16<8, EP_RESID, 4, true, 2>), grid, dim3(256), 0, s, a);
+        if (MT == 8) gemm_launch(k_gemm_bf16<8, EP_RESID, 4, true, 2>, grid, dim3(256), s, a);
         else dispatch_mt<EP_RESID, 8, true>(MT, grid, a, s);
         break;
       case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
