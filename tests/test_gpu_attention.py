@@ -101,3 +101,26 @@ def test_block_attention_full_size_sampled(B, rows, lk):
         want = oracle.attention(q[b, r, h].float().cpu().numpy().astype(np.float64), keys, vals)
         got = out[b, r, h].float().cpu().numpy()
         assert np.abs(got - want).max() < TOL, (b, r, h)
+
+
+@pytest.mark.parametrize("lk,kb", [(4000, 17), (4096, 1)])
+def test_block_attention_two_tile_launch_ragged(lk, kb):
+    """A launch of 512 workgroups (16 sequences x 8 KV heads x 4 chunks)
+    runs two query tiles per wave and streams the draft block after the
+    last chunk's cache keys: a partial last cache tile (4000 keys: 32 keys
+    in the last tile) and a ragged block (17 keys), or a whole last tile and
+    a one-key block.  Sampled (sequence, row, head) outputs against the
+    oracle."""
+    B, rows, hq, hkv = 16, 32, 32, 8
+    G = hq // hkv
+    q, kc, vc, kbk, vbk, cap = make(B, rows, hq, hkv, lk, kb, 7)
+    out = run(B, rows, hq, hkv, lk, kb, q, kc, vc, kbk, vbk, cap)
+    rng = np.random.default_rng(lk + kb)
+    for _ in range(16):
+        b, r, h = int(rng.integers(B)), int(rng.integers(rows)), int(rng.integers(hq))
+        g = h // G
+        keys = torch.cat([kc[b, g, :lk], kbk[b, g, :kb]]).float().cpu().numpy().astype(np.float64)
+        vals = torch.cat([vc[b, g, :lk], vbk[b, g, :kb]]).float().cpu().numpy().astype(np.float64)
+        want = oracle.attention(q[b, r, h].float().cpu().numpy().astype(np.float64), keys, vals)
+        got = out[b, r, h].float().cpu().numpy()
+        assert np.abs(got - want).max() < TOL, (b, r, h)
