@@ -243,7 +243,7 @@ uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_he
 /* The attention key chunk a context gets for attn_chunk = 0.  Every (chunk,
  * KV head, sequence) is one workgroup that writes a 64 KB partial, read back
  * once per pass.  The rule (measured on the decode workloads): the smallest
- * power of two in [64, 4096] that gives at most 64 chunks per sequence and
+ * power of two in [128, 4096] that gives at most 64 chunks per sequence and
  * at most 1100 (chunk, KV head, sequence) workgroups, and at least 1024
  * whenever 1024-key chunks still give 512 of them (cap = max_ctx rounded up
  * to 64 keys per sequence).  Kernel (a) alone (orthrus_block_attention)

@@ -66,14 +66,14 @@ struct Layout {
 // Default attention key chunk for `batch` sequences of `slots` keys over
 // `kv_heads` KV heads.  Each (chunk, KV head, sequence) is a workgroup that
 // writes a 64 KB partial (fp32, 128 rows), which is 1/8 of the keys' bytes
-// at 1024-key chunks and 1/2 at 256.  The rule (a power of two in [64,
+// at 1024-key chunks and 1/2 at 256.  The rule (a power of two in [128,
 // 4096], measured on the decode workloads): the smallest one with at most
 // 64 chunks per sequence and at most 1100 workgroups, and at least 1024 keys
 // whenever 1024-key chunks still give 512 workgroups (two per compute unit).
 static int default_attn_chunk(int batch, int slots, int kv_heads) {
   const long pairs = (long)batch * (kv_heads > 0 ? kv_heads : 1);
   const bool long_ok = pairs * ((slots + 1023) / 1024) >= 512;
-  int sc = 64;
+  int sc = 128;
   while (sc < 4096) {
     const long nch = (slots + sc - 1) / sc;
     if (nch <= 64 && pairs * nch <= 1100 && !(long_ok && sc < 1024)) break;

@@ -111,21 +111,22 @@ def test_call_order_errors_on_null_context_args():
     (4, 16384, 8, 1024),
     (16, 4096, 8, 1024),
     (16, 32768, 8, 4096),   # capped at 4096
-    (1, 64, 2, 64),         # floor
+    (1, 1600, 8, 128),      # B = 1 decode at a short context: the floor
+    (1, 64, 2, 128),
 ])
 def test_default_attention_chunk_rule(batch, ctx, kvh, want):
     """The chunk rule the header documents: the smallest power of two in
-    [64, 4096] with <= 64 chunks per sequence and <= 1100 (chunk, KV head,
+    [128, 4096] with <= 64 chunks per sequence and <= 1100 (chunk, KV head,
     sequence) workgroups, at least 1024 when 1024-key chunks still give 512
     workgroups (slots rounded up to 64)."""
     got = C.orthrus_default_attn_chunk(batch, ctx, kvh)
     assert got == want
     slots = (ctx + 63) // 64 * 64
     nch = -(-slots // got)
-    assert got & (got - 1) == 0 and 64 <= got <= 4096
+    assert got & (got - 1) == 0 and 128 <= got <= 4096
     if got < 4096:
         assert nch <= 64 and batch * kvh * nch <= 1100
-    if got > 64:      # the next smaller size breaks a condition
+    if got > 128:     # the next smaller size breaks a condition
         half = got // 2
         n2 = -(-slots // half)
         long_ok = batch * kvh * (-(-slots // 1024)) >= 512
