@@ -82,31 +82,30 @@ void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* b
                      embed, mask_emb, V, d, (int)bf16, h);
 }
 
-// Residual add of the split-K partials + RMSNorm -> bf16 rows.  One
-// 512-thread block per row; the row is cut into 256-element chunks, wave w
-// takes chunks w, w + 8, ..., lane l holds elements 4l .. 4l + 3.  All loads
-// are issued before use.  The partial sum runs in slice order and is then
-// added to h (the same arithmetic as a fused residual epilogue).  The sum
-// of squares is canonical: per chunk, the lane's four squares in order and
-// a fixed butterfly, then the chunk sums in chunk order (the GEMM prelude
-// computes the same value).
-template <int NCW>
-__global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __restrict__ h, int d,
-                                                         const float* __restrict__ part, size_t ps,
-                                                         int nslices,
-                                                         const uint16_t* __restrict__ gain,
-                                                         float eps, uint16_t* __restrict__ out) {
+// Residual add of the split-K partials + RMSNorm -> bf16 rows.  One block
+// of NW waves per row; the row is cut into 256-element chunks, wave w takes
+// chunks w, w + NW, ..., lane l holds elements 4l .. 4l + 3.  All loads are
+// issued before use.  The partial sum runs in slice order and is then added
+// to h (the same arithmetic as a fused residual epilogue).  The sum of
+// squares is canonical: per chunk, the lane's four squares in order and a
+// fixed butterfly, then the chunk sums in chunk order, whatever NW is.
+template <int NCW, int NW>
+__global__ __launch_bounds__(NW * 64) void k_resid_norm_bf16(PassInfo P, float* __restrict__ h, int d,
+                                                             const float* __restrict__ part, size_t ps,
+                                                             int nslices,
+                                                             const uint16_t* __restrict__ gain,
+                                                             float eps, uint16_t* __restrict__ out) {
   __shared__ float red[32];
   const int r = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63, nch = d >> 8;
   if (P.kind == PASS_DRAFT && row_info(P, r).pad) {     // keep padding rows' input at zero
-    for (int i = t * 4; i < d; i += 2048) *(uint2*)(out + (size_t)r * d + i) = make_uint2(0u, 0u);
+    for (int i = t * 4; i < d; i += NW * 256) *(uint2*)(out + (size_t)r * d + i) = make_uint2(0u, 0u);
     return;
   }
   float* x = h + (size_t)r * d;
   float4 v[NCW];
 #pragma unroll
   for (int j = 0; j < NCW; ++j) {
-    const int c = wave + j * 8;
+    const int c = wave + j * NW;
     v[j] = c < nch ? *(const float4*)(x + c * 256 + lane * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   if (nslices == 8) {
@@ -115,7 +114,7 @@ __global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __re
     for (int sl = 0; sl < 8; ++sl)
 #pragma unroll
       for (int j = 0; j < NCW; ++j) {
-        const int c = wave + j * 8;
+        const int c = wave + j * NW;
         p[sl][j] = c < nch ? *(const float4*)(part + sl * ps + (size_t)r * d + c * 256 + lane * 4)
                            : make_float4(0.f, 0.f, 0.f, 0.f);
       }
@@ -127,13 +126,13 @@ __global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __re
         s4.x += p[sl][j].x; s4.y += p[sl][j].y; s4.z += p[sl][j].z; s4.w += p[sl][j].w;
       }
       v[j].x += s4.x; v[j].y += s4.y; v[j].z += s4.z; v[j].w += s4.w;
-      const int c = wave + j * 8;
+      const int c = wave + j * NW;
       if (c < nch) *(float4*)(x + c * 256 + lane * 4) = v[j];
     }
   }
 #pragma unroll
   for (int j = 0; j < NCW; ++j) {
-    const int c = wave + j * 8;
+    const int c = wave + j * NW;
     float sq = v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
@@ -145,7 +144,7 @@ __global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __re
   const float inv = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
   for (int j = 0; j < NCW; ++j) {
-    const int c = wave + j * 8, i = c * 256 + lane * 4;
+    const int c = wave + j * NW, i = c * 256 + lane * 4;
     if (c < nch) {
       const uint2 g = *(const uint2*)(gain + i);
       const float g0 = __uint_as_float(g.x << 16), g1 = __uint_as_float(g.x & 0xffff0000u);
@@ -158,19 +157,17 @@ __global__ __launch_bounds__(512) void k_resid_norm_bf16(PassInfo P, float* __re
   }
 }
 
-// d a multiple of 256, at most 8192
+// d a multiple of 256, at most 8192: one 256-element chunk per wave up to
+// d = 4096 (16 waves), else 16 waves with two chunks each
 void launch_resid_norm_bf16(const PassInfo& P, float* h, int d, const float* part, size_t ps,
                             int nslices, const uint16_t* gain, float eps, uint16_t* out,
                             hipStream_t s) {
   const int rows = P.rows();
   if (rows <= 0) return;
-  const int ncw = ((d >> 8) + 7) / 8;          // chunks per wave
-  if (ncw <= 1)
-    hipLaunchKernelGGL(k_resid_norm_bf16<1>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
-  else if (ncw <= 2)
-    hipLaunchKernelGGL(k_resid_norm_bf16<2>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
+  if ((d >> 8) <= 16)
+    hipLaunchKernelGGL((k_resid_norm_bf16<1, 16>), dim3(rows), dim3(1024), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
   else
-    hipLaunchKernelGGL(k_resid_norm_bf16<4>, dim3(rows), dim3(512), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
+    hipLaunchKernelGGL((k_resid_norm_bf16<2, 16>), dim3(rows), dim3(1024), 0, s, P, h, d, part, ps, nslices, gain, eps, out);
 }
 
 // -------------------------------------------------------------- RMSNorm
