@@ -246,6 +246,7 @@ struct orthrus_ctx {
   std::vector<hipEvent_t> ev;     // 2 per pair
   std::vector<int> ev_cls;
   int ev_used;
+  bool ev_dropped;           // a selected launch found the event pairs full
 };
 
 namespace {
@@ -267,7 +268,8 @@ inline int pass_base(int kind) { return kind * 8; }
 struct Tick {
   orthrus_ctx* c; int i; hipStream_t s; bool ext;
   Tick(orthrus_ctx* c_, int cls, hipStream_t s_) : c(c_), i(-1), s(s_), ext(false) {
-    if (!(c->tmask >> cls & 1u) || c->ev_used * 2 >= (int)c->ev.size()) return;
+    if (!(c->tmask >> cls & 1u)) return;
+    if (c->ev_used * 2 >= (int)c->ev.size()) { c->ev_dropped = true; return; }
     i = c->ev_used++;
     c->ev_cls[i] = cls;
     ext = cls % 8 == R_GU;
@@ -573,7 +575,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
   c->state = ST_IDLE; c->step_batch = 0;
   c->bound.assign(cfg->max_batch, 0);
   c->dbg_logits = nullptr; c->dbg_attn = nullptr; c->dbg_rows = 0;
-  c->tmask = 0; c->ev_used = 0;
+  c->tmask = 0; c->ev_used = 0; c->ev_dropped = false;
   const Layout& y = c->y;
   const uint64_t E = y.esz;
   const char* w = (const char*)weights;
@@ -787,7 +789,7 @@ int orthrus_timing_enable(orthrus_ctx* ctx, uint32_t class_mask, int32_t capacit
   if (!ctx || capacity < 0) return ORTHRUS_EINVAL;
   if (class_mask && capacity == 0) return ORTHRUS_EINVAL;
   for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
-  ctx->ev.clear(); ctx->ev_cls.clear(); ctx->ev_used = 0; ctx->tmask = 0;
+  ctx->ev.clear(); ctx->ev_cls.clear(); ctx->ev_used = 0; ctx->ev_dropped = false; ctx->tmask = 0;
   if (!class_mask) return ORTHRUS_OK;
   ctx->ev.resize((size_t)2 * capacity);
   ctx->ev_cls.resize(capacity);
@@ -811,8 +813,9 @@ int orthrus_timing_read(orthrus_ctx* ctx, double* ms, int64_t* launches) {
     ms[ctx->ev_cls[i]] += t;
     launches[ctx->ev_cls[i]] += 1;
   }
-  int dropped = ctx->ev_used * 2 >= (int)ctx->ev.size() ? 1 : 0;
+  const bool dropped = ctx->ev_dropped;
   ctx->ev_used = 0;
+  ctx->ev_dropped = false;
   return dropped ? ORTHRUS_ECAPACITY : ORTHRUS_OK;
 }
 

@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+from lossless_decoding_amd import _lib as C
 from synth import workloads
 from tests import gpu_util as U
 
@@ -164,3 +165,41 @@ def test_small_repeated_passes_are_bitwise_identical():
             assert torch.isfinite(d).all() and torch.isfinite(v).all()
         else:
             assert torch.equal(d, ref[0]) and torch.equal(v, ref[1]), it
+
+
+def test_launch_timing_classes_and_capacity():
+    """orthrus_timing_enable / orthrus_timing_read: the gate/up GEMM (timed
+    by its own dispatch) and the attention class (events around the launch)
+    report one launch per layer and pass with positive time (the prefill
+    ends with an anchor-row pass, a draft pass); launches past the capacity
+    are not timed and the read says so; timing off records nothing; the
+    tokens are those of an untimed context."""
+    sh = workloads.SHAPES["small"]
+    L = sh["L"]
+    prompt = workloads.prompts(1, 40, sh["V"], seed=17)
+    ref = U.engine("small", max_ctx=512)
+    want, _ = ref.generate(prompt, 24)
+    eng = U.engine("small", max_ctx=512)
+    gu_d, gu_v = C.timing_class("draft", "gate_up"), C.timing_class("verify", "gate_up")
+    at_v = C.timing_class("verify", "attention")
+    C.orthrus_timing_enable(eng.ctx, (1 << gu_d) | (1 << gu_v) | (1 << at_v), 1000)
+    got, _ = eng.generate(prompt, 24)
+    tim, dropped = C.orthrus_timing_read(eng.ctx)
+    assert np.array_equal(got, want)
+    steps = tim[("verify", "gate_up")][1] // L
+    assert steps >= 1 and not dropped
+    for key, passes in ((("draft", "gate_up"), steps + 1), (("verify", "gate_up"), steps),
+                        (("verify", "attention"), steps)):
+        ms, n = tim[key]
+        assert n == passes * L and ms > 0.0, (key, ms, n)
+    assert set(tim) == {("draft", "gate_up"), ("verify", "gate_up"), ("verify", "attention")}
+    # capacity: only the first L draft gate/up launches are timed
+    C.orthrus_timing_enable(eng.ctx, 1 << gu_d, L)
+    eng.draft(); eng.verify(); eng.commit()
+    eng.draft(); eng.verify(); eng.commit()
+    tim, dropped = C.orthrus_timing_read(eng.ctx)
+    assert dropped and tim[("draft", "gate_up")][1] == L
+    C.orthrus_timing_enable(eng.ctx, 0, 0)
+    eng.draft(); eng.verify(); eng.commit()
+    tim, dropped = C.orthrus_timing_read(eng.ctx)
+    assert tim == {} and not dropped
