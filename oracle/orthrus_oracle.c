@@ -34,11 +34,13 @@
  * order (oc_weight_layout); each tensor starts at a multiple of 256
  * elements; matrices are row-major [out][in].
  *
- * The functions that have no pin other than GPU agreement -- the diffusion
- * view's actual values (mask-row logits, hence the drafts) -- are marked
- * "parity unpinned" below: the pages print no worked example for them.  Their
- * structure is pinned (block bidirectionality, no cache writes, reduction to
- * the AR view under tied weights and a causal block).
+ * The diffusion view's values (mask-row logits, hence the drafts) have no
+ * printed worked example on the pages, so no pin by value: they are marked
+ * "parity unpinned" below.  Their structure is pinned (block
+ * bidirectionality, no cache writes, reduction to the AR view under tied
+ * weights and a causal block), and so is their wiring at one layer (a
+ * composition of the pinned primitives with numpy matmuls, gains away
+ * from 1).
  */
 #include <math.h>
 #include <stdint.h>

@@ -247,3 +247,69 @@ def test_one_layer_wiring_fp32():
     z = np.stack([oracle.rmsnorm(r, T(2), shp.eps) for r in h])
     want = z @ T(1).reshape(shp.V, d).T
     assert np.allclose(lg, want, rtol=0, atol=1e-10)
+
+
+def test_one_layer_diffusion_wiring_fp32():
+    """The mask rows of one fp32 layer composed from the pinned primitives
+    and numpy matmuls: the mask embedding as input, the diffusion Q/K/V/O and
+    QK-norm gains, RoPE at positions n+1..n+K, attention over the cache slots
+    [0, n] (prompt plus the staged anchor) and every block key, and the
+    shared norms, FFN and LM head.  Every gain is drawn away from 1, so a
+    frozen gain or matrix used in place of a diffusion one changes the
+    logits."""
+    shp = H.shape("tiny", L=1)
+    w = H.weights(shp).copy()
+    lay, _ = oracle.weight_layout(shp)
+    rng = np.random.default_rng(12)
+    for t, off, n, gain in lay:
+        if gain:
+            w[off:off + n] = 1.0 + 0.25 * rng.standard_normal(n).astype(np.float32)
+    m = oracle.Model(shp, w)
+    K = 4
+    prompt = workloads.prompts(1, 3, shp.V, seed=13)[0]
+    seq = m.seq(16)
+    pending = seq.prefill(prompt)
+    n = seq.len
+    seq.ar_rows(np.array([pending], np.int32), n)           # anchor at slot n
+    lg, am = seq.draft_rows(n, K)
+
+    T = lambda t: H.as_f64(shp, H.tensor(shp, w, t))
+    Lt = lambda s: H.as_f64(shp, H.layer_tensor(shp, w, 0, s))
+    d, hd, hq, hkv, grp = shp.d, shp.hd, shp.hq, shp.hkv, shp.hq // shp.hkv
+
+    def qkv(h, pos, sq, sk, sv, sqn, skn):
+        R = len(pos)
+        u = np.stack([oracle.rmsnorm(r, Lt(0), shp.eps) for r in h])
+        q = (u @ Lt(sq).reshape(hq * hd, d).T).reshape(R, hq, hd)
+        k = (u @ Lt(sk).reshape(hkv * hd, d).T).reshape(R, hkv, hd)
+        v = (u @ Lt(sv).reshape(hkv * hd, d).T).reshape(R, hkv, hd)
+        for r, p in enumerate(pos):
+            for i in range(hq):
+                q[r, i] = oracle.rope(oracle.rmsnorm(q[r, i], Lt(sqn), shp.eps), p)
+            for g in range(hkv):
+                k[r, g] = oracle.rope(oracle.rmsnorm(k[r, g], Lt(skn), shp.eps), p)
+        return q, k, v
+
+    def tail(h, o, so):
+        h = h + o.reshape(len(h), -1) @ Lt(so).reshape(d, hq * hd).T
+        u = np.stack([oracle.rmsnorm(r, Lt(1), shp.eps) for r in h])
+        gate = u @ Lt(14).reshape(shp.F, d).T
+        up = u @ Lt(15).reshape(shp.F, d).T
+        h = h + (gate / (1 + np.exp(-gate)) * up) @ Lt(16).reshape(d, shp.F).T
+        z = np.stack([oracle.rmsnorm(r, T(2), shp.eps) for r in h])
+        return z @ T(1).reshape(shp.V, d).T
+
+    # the cache slots 0..n: frozen view over the prompt and the anchor token
+    toks = np.append(prompt, pending)
+    _, kc, vc = qkv(T(0).reshape(shp.V, d)[toks], range(n + 1), 2, 3, 4, 6, 7)
+    # the block: K copies of the mask embedding at positions n+1..n+K
+    hb = np.tile(T(3), (K, 1))
+    qb, kb, vb = qkv(hb, range(n + 1, n + 1 + K), 8, 9, 10, 12, 13)
+    keys, vals = np.concatenate([kc, kb]), np.concatenate([vc, vb])
+    o = np.zeros((K, hq, hd))
+    for r in range(K):
+        for i in range(hq):
+            o[r, i] = oracle.attention(qb[r, i], keys[:, i // grp], vals[:, i // grp])
+    want = tail(hb, o, 11)
+    assert np.allclose(lg, want, rtol=0, atol=1e-10)
+    assert np.array_equal(am, want.argmax(1))
