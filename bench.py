@@ -234,8 +234,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sequences shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -307,18 +307,20 @@ def main():
     n_rs = max(1, min(args.roofline_steps, S))
     C.orthrus_timing_enable(eng.ctx, 1 << cls, n_rs * sh["L"])
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event per step boundary (the first and last bracket the timed region)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(S + 1)]
     t_wall = time.perf_counter()
-    e0.record()
+    ev[0].record()
     for s in range(W, W + S):
         eng.draft()
         eng.drafts[:B].copy_(planted[s])
         eng.verify()
         eng.commit()
-    e1.record()
+        ev[s - W + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1)
+    ms = ev[0].elapsed_time(ev[S])
+    step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(S)])
     tim, _ = C.orthrus_timing_read(eng.ctx)
     C.orthrus_timing_enable(eng.ctx, 0, 0)
 
@@ -331,8 +333,9 @@ def main():
     e_end = 1 + (a + 1).sum(0)
     lossless = bool((seq_len == want_len).all() and
                     all(pend[b] == traj[b, e_end[b] - 1] for b in range(B)))
+    step_pct = {f"p{q}": round(float(np.percentile(step_ms, q)), 4) for q in (10, 50, 90)}
     log(f"[timed] {S} steps in {ms:.1f} ms ({ms_step:.3f} ms/step, wall {wall * 1e3:.1f} ms), "
-        f"{tokens} tokens, lossless={lossless}")
+        f"{tokens} tokens, lossless={lossless}, step ms {step_pct}")
 
     # dominant kernel: the draft pass's gate/up SwiGLU GEMM (M = B*(K+1) rows)
     gu_ms, gu_n = tim.get(("draft", "gate_up"), (0.0, 0))
@@ -405,6 +408,7 @@ def main():
                    "prompt_len": P, "block_k": K, "parallelism": "none (1 GPU)"},
         "attn_chunk": chunk,
         "steps_per_s": round(S / (ms / 1e3), 3),
+        "step_ms_percentiles": step_pct,
         "tokens_per_step": round(tokens / S, 4),
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
         "lossless_vs_greedy": lossless,
