@@ -588,8 +588,9 @@ static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
 // in flight with four waves per workgroup.  Taller tiles would not fit two
 // tiles' accumulators.
 template <int EP>
-static void dispatch_ct2(dim3 grid, const GemmArgs& a, hipStream_t s) {
-  gemm_launch(k_gemm_bf16<8, EP, 4, false, 2>, grid, dim3(256), s, a);
+static void dispatch_ct2(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
+  if (MT == 9) gemm_launch(k_gemm_bf16<9, EP, 4, false, 2>, grid, dim3(256), s, a);
+  else gemm_launch(k_gemm_bf16<8, EP, 4, false, 2>, grid, dim3(256), s, a);
 }
 
 int gemm_bf16_groups(int N) { return N / 128; }
@@ -648,7 +649,12 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   const int wv = (a.ep == EP_SWIGLU && (a.N / 16) % 6 == 0 && gemm_mt(a.M, a.M2) <= 3) ? 6 : 8;
   // tall row tiles for unsplit launches other than gate/up (which takes two
   // column tiles per wave at 128 rows instead: measured faster)
-  const int MT = wide && a.ep != EP_SWIGLU ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
+  int MT = wide && a.ep != EP_SWIGLU ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
+  // gate/up at 128-row tiles (two column tiles per wave): 144-row tiles
+  // where they pad fewer rows (528 rows: 4 x 144 instead of 5 x 128)
+  if (wide && a.ep == EP_SWIGLU && MT == 8 && a.M2 == 0 &&
+      (a.M + 143) / 144 * 144 < (a.M + 127) / 128 * 128)
+    MT = 9;
   const int rpw = MT > 4 ? MT * 16 : 64;         // rows per workgroup
   a.gy0 = (a.M + rpw - 1) / rpw;
   const dim3 gy(1, a.gy0 + (a.M2 + rpw - 1) / rpw);
@@ -677,9 +683,9 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     a.flat = gy.y > 1 && ngroups % 8 == 0;
     return a.flat ? dim3(ngroups * gy.y, 1) : dim3(ngroups, gy.y);
   };
-  if (MT == 8 && a.ep == EP_SWIGLU) {        // 128-row tiles: two column tiles per wave
+  if ((MT == 8 || MT == 9) && a.ep == EP_SWIGLU) {   // 128 / 144-row tiles: two column tiles per wave
     const dim3 g = grid_of(a.N / 128);
-    dispatch_ct2<EP_SWIGLU>(g, a, s);
+    dispatch_ct2<EP_SWIGLU>(MT, g, a, s);
     return;
   }
   switch (a.ep) {
