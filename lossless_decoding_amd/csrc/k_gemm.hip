@@ -577,16 +577,19 @@ static void dispatch_mt(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
     case 3: gemm_launch(k_gemm_bf16<3, EP, WV, SPLIT, CT>, grid, block, s, a); break;
     case 4: gemm_launch(k_gemm_bf16<4, EP, WV, SPLIT, CT>, grid, block, s, a); break;
     case 8: gemm_launch(k_gemm_bf16<8, EP, WV, SPLIT, CT>, grid, block, s, a); break;
+    case 9:   // unsplit launches only (tall-tile rule)
+      if constexpr (!SPLIT) gemm_launch(k_gemm_bf16<9, EP, WV, SPLIT, CT>, grid, block, s, a);
+      break;
     case 12: gemm_launch(k_gemm_bf16<12, EP, WV, SPLIT, CT>, grid, block, s, a); break;
     default: gemm_launch(k_gemm_bf16<16, EP, WV, SPLIT, CT>, grid, block, s, a); break;
   }
 }
 
-// unsplit gate/up launches of 128-row tiles: four waves of two column tiles
-// (128 columns: gate and up in one wave).  Measured: faster for gate/up at
-// 256-512 rows; slower for QKV and the LM head, whose grids keep fewer loads
-// in flight with four waves per workgroup.  Taller tiles would not fit two
-// tiles' accumulators.
+// unsplit gate/up launches of 128- or 144-row tiles: four waves of two
+// column tiles (128 columns: gate and up in one wave).  Measured: faster for
+// gate/up at 256-512 rows; slower for QKV and the LM head, whose grids keep
+// fewer loads in flight with four waves per workgroup.  Taller tiles would
+// not fit two tiles' accumulators.
 template <int EP>
 static void dispatch_ct2(int MT, dim3 grid, const GemmArgs& a, hipStream_t s) {
   if (MT == 9) gemm_launch(k_gemm_bf16<9, EP, 4, false, 2>, grid, dim3(256), s, a);
@@ -613,7 +616,8 @@ static int gemm_rows_per_wg(int M, int M2) {
 // row tiles (MT 12 or 16: 192 or 256 rows), which read the weights fewer
 // times through the caches.  The MFMA operand reads from LDS per row do not
 // change, so what decides is padding: the tile with the fewest padded rows
-// (the smaller on ties) among those that keep at least 512 workgroups.
+// (the smaller on ties) among those that keep at least 512 workgroups, then
+// 144-row tiles (MT 9) if they pad fewer still (264 rows: 2 x 144).
 static int gemm_mt_tall(int M, int M2, int ngroups) {
   if (M2 > 0 || M <= 128) return gemm_mt(M, M2);
   int best = 8;
@@ -623,8 +627,13 @@ static int gemm_mt_tall(int M, int M2, int ngroups) {
     const long rows = (long)g * MT * 16;
     if ((long)ngroups * g >= 512 && rows < best_rows) { best = MT; best_rows = rows; }
   }
+  const int g9 = (M + 143) / 144;
+  if ((long)ngroups * g9 >= 512 && (long)g9 * 144 < best_rows) best = 9;
   return best;
 }
+
+// 144-row tiles pad fewer rows than 128-row ones (528 rows: 576 against 640)
+static bool rows144_pad_less(int M) { return (M + 143) / 144 * 144 < (M + 127) / 128 * 128; }
 
 // Split K over workgroups only when the column groups times the row groups
 // of the launch are too few to fill the chip without it: fewer than 128,
@@ -650,10 +659,10 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   // tall row tiles for unsplit launches other than gate/up (which takes two
   // column tiles per wave at 128 rows instead: measured faster)
   int MT = wide && a.ep != EP_SWIGLU ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
-  // gate/up at 128-row tiles (two column tiles per wave): 144-row tiles
-  // where they pad fewer rows (528 rows: 4 x 144 instead of 5 x 128)
-  if (wide && a.ep == EP_SWIGLU && MT == 8 && a.M2 == 0 &&
-      (a.M + 143) / 144 * 144 < (a.M + 127) / 128 * 128)
+  // gate/up, and split O / down launches, at 128-row tiles (two column
+  // tiles per wave): 144-row tiles where they pad fewer rows (528 rows:
+  // 4 x 144 instead of 5 x 128)
+  if ((wide ? a.ep == EP_SWIGLU : a.ep == EP_RESID) && MT == 8 && a.M2 == 0 && rows144_pad_less(a.M))
     MT = 9;
   const int rpw = MT > 4 ? MT * 16 : 64;         // rows per workgroup
   a.gy0 = (a.M + rpw - 1) / rpw;
@@ -664,8 +673,9 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
     const dim3 grid(a.N / 128 * NSL, gy.y);
     switch (a.ep) {
       case EP_RESID:
-        // 128-row tiles: two column tiles per wave
+        // 128- and 144-row tiles: two column tiles per wave
         if (MT == 8) gemm_launch(k_gemm_bf16<8, EP_RESID, 4, true, 2>, grid, dim3(256), s, a);
+        else if (MT == 9) gemm_launch(k_gemm_bf16<9, EP_RESID, 4, true, 2>, grid, dim3(256), s, a);
         else dispatch_mt<EP_RESID, 8, true>(MT, grid, a, s);
         break;
       case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
