@@ -664,6 +664,13 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   // 4 x 144 instead of 5 x 128)
   if ((wide ? a.ep == EP_SWIGLU : a.ep == EP_RESID) && MT == 8 && a.M2 == 0 && rows144_pad_less(a.M))
     MT = 9;
+  // QKV (48 column groups at Qwen3-8B width) with 128-row tiles: 64-row
+  // tiles when 128 would leave fewer than 192 workgroups.  Measured: 264 + 8
+  // draft rows 144 -> 240 workgroups, 2.81 -> 2.02 ms per step; 512 + 16
+  // rows (240 workgroups) slower with 64-row tiles, 2.89 -> 3.65 ms.
+  if (wide && a.ep == EP_QKV && MT == 8 &&
+      (a.N / 128) * ((a.M + 127) / 128 + (a.M2 + 127) / 128) < 192)
+    MT = 4;
   const int rpw = MT > 4 ? MT * 16 : 64;         // rows per workgroup
   a.gy0 = (a.M + rpw - 1) / rpw;
   const dim3 gy(1, a.gy0 + (a.M2 + rpw - 1) / rpw);
