@@ -642,8 +642,14 @@ static bool rows144_pad_less(int M) { return (M + 143) / 144 * 144 < (M + 127) /
 // + RMSNorm kernel that follows must add that many slice partials.
 int gemm_bf16_split_slices(int M, int M2, int N, int ep) {
   if (M2 < 0) M2 = 0;
-  const int rpw = gemm_rows_per_wg(M, M2);
-  const int gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
+  int rpw = gemm_rows_per_wg(M, M2);
+  int gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
+  // QKV takes 64-row tiles where 128-row tiles give fewer than 192
+  // workgroups (the launch below makes the same choice)
+  if (ep == EP_QKV && rpw == 128 && (N / 128) * gy < 192) {
+    rpw = 64;
+    gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
+  }
   return (N / 128) * gy >= (ep == EP_RESID ? 256 : 128) ? 0 : NSL;
 }
 
