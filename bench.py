@@ -298,7 +298,15 @@ def main():
     planted = torch.from_numpy(workloads.plant_drafts(traj, 1, a, K, V)).to(dev)
 
     # ---------------------------------------------------------------- timed
+    # prefill (the prompts through the AR view into the cache), timed on its
+    # own and reported beside the step loop
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
     eng.prefill(prompts)
+    p1.record()
+    torch.cuda.synchronize()
+    prefill_ms = p0.elapsed_time(p1)
+    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms")
     for s in range(W):
         eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
     cls = C.timing_class("draft", "gate_up")
@@ -411,6 +419,8 @@ def main():
         "step_ms_percentiles": step_pct,
         "tokens_per_step": round(tokens / S, 4),
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
+        "prefill_ms": round(prefill_ms, 3),
+        "prefill_tokens_per_s": round(B * P / (prefill_ms / 1e3), 1),
         "lossless_vs_greedy": lossless,
         "plain_decoding_tokens_per_s": round(plain_tps, 3),
         "speedup_vs_plain_decoding": round(tokens / (ms / 1e3) / plain_tps, 4),
