@@ -211,7 +211,32 @@ def cpu_baseline(sh, wl, mean_tokens_per_step):
                    f"fp64 oracle after a {P0}-token prefill, {step_s:.1f} s; tokens/s = the "
                    f"workload's mean tokens per step ({mean_tokens_per_step:.3f}) / step time"),
         "step_seconds": step_s,
+        "host": host_info(),
     }
+
+
+def host_info():
+    """The host the oracle ran on: CPU model, sockets, logical CPUs visible to
+    this process, memory."""
+    model, sockets = "", set()
+    try:
+        for line in open("/proc/cpuinfo"):
+            k, _, v = line.partition(":")
+            if k.strip() == "model name" and not model:
+                model = v.strip()
+            elif k.strip() == "physical id":
+                sockets.add(v.strip())
+    except OSError:
+        pass
+    mem_gib = None
+    try:
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal:"):
+                mem_gib = round(int(line.split()[1]) / (1 << 20), 1)
+    except OSError:
+        pass
+    return {"cpu": model, "sockets": len(sockets) or None, "logical_cpus": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "mem_gib": mem_gib}
 
 
 def main():
