@@ -29,13 +29,15 @@ DEPTH_TOL_MAX = 0.15
 DEPTH_TOL_MEAN = 0.03
 
 
-def one_step(cfg, w, prompt, K, V):
-    """Prefill + one draft/verify/commit step; returns everything the oracle
-    comparison needs."""
+def one_step(cfg, w, prompt, K, V, B=1):
+    """Prefill + one draft/verify/commit step of B sequences; returns
+    everything the oracle comparison needs, for sequence 0 (its mask and
+    verify rows come first in every pass, its anchor after the padded mask
+    rows, its prefill logits in row 0)."""
     eng = Engine(cfg, w)
-    RA = U.anchor_row(K)
-    lg = torch.zeros(RA + 1, V, device="cuda")
-    eng.set_debug(lg, None, RA + 1)
+    RA = U.anchor_row(K, B)
+    lg = torch.zeros(RA + B, V, device="cuda")
+    eng.set_debug(lg, None, RA + B)
     eng.prefill(prompt)
     torch.cuda.synchronize()
     out = dict(pre=lg[0].cpu().numpy().astype(np.float64), pending=int(eng.pending[0]))
@@ -126,3 +128,22 @@ def test_qwen3_8b_orthrus_equals_gpu_greedy(weights8b):
     want, _ = ar.generate(prompt, 48)
     ar.close()
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("B", [8, 16])
+def test_qwen3_8b_single_layer_batch_against_oracle(B):
+    """One layer at full width in the batch launch shapes of the large
+    workloads: the draft pass has B x 33 rows (264 or 528: 144-row gate/up,
+    down and LM-head tiles; 64-row QKV tiles at B = 8), the verify pass
+    B x 32 (unsplit 64-row QKV at B = 8).  Sequence 0's prefill, draft,
+    anchor and verify logits against the oracle within 2e-2 (the oracle runs
+    sequence 0 alone: sequences are independent)."""
+    sh = workloads.SHAPES["qwen3_8b"]
+    K, V = sh["K"], sh["V"]
+    cfg = U.cfg_of("qwen3_8b", max_batch=B, max_ctx=128, n_layers=1)
+    lay, total = C.weight_layout(cfg)
+    w = fill_weights_device(lay, total, True)
+    prompt = workloads.prompts(B, 5, V, seed=21)
+    g = one_step(cfg, w, prompt, K, V, B)
+    del w
+    compare_step(H.shape("qwen3_8b", L=1), g, prompt[:1], K, 2e-2, 5e-3)
