@@ -215,6 +215,37 @@ def cpu_baseline(sh, wl, mean_tokens_per_step):
     }
 
 
+def gemm_class_rates(breakdown, sh, B, K):
+    """Per GEMM class and pass, from the per-class times: weight bytes
+    streamed (bf16, every layer; the draft pass's QKV and O read both the
+    frozen and the diffusion matrices) against 8 TB/s, and GEMM flops
+    (2 x rows x parameters) against the dense bf16 MFMA peak.  The class
+    times come from event pairs around every launch (a few microseconds of
+    record overhead each) and the QKV class includes its finish kernel when
+    split, so these are lower bounds of the kernels' own rates."""
+    L, d, F, V = sh["L"], sh["d"], sh["F"], sh["V"]
+    qkv = d * (sh["hq"] + 2 * sh["hkv"]) * sh["hd"]
+    o = sh["hq"] * sh["hd"] * d
+    params = {"qkv": (qkv, L), "o_proj": (o, L), "gate_up": (2 * F * d, L), "down": (F * d, L),
+              "lm_head": (V * d, 1)}
+    rows = {"draft": B * (K + 1), "verify": B * K}
+    out = {}
+    for key, ms in breakdown.items():
+        pas, _, cls = key.partition(".")
+        if cls not in params or pas not in rows or ms <= 0:
+            continue
+        n, per = params[cls]
+        sets = 2 if pas == "draft" and cls in ("qkv", "o_proj") else 1
+        wbytes = sets * n * 2 * per
+        flops = 2 * rows[pas] * n * per
+        s_ = ms / 1e3
+        out[key] = {"ms": ms, "weight_GBps": round(wbytes / s_ / 1e9, 1),
+                    "hbm_frac": round(wbytes / s_ / 8e12, 4),
+                    "tflops": round(flops / s_ / 1e12, 2),
+                    "mfma_frac": round(flops / s_ / 2.5e15, 4)}
+    return out
+
+
 def host_info():
     """The host the oracle ran on: CPU model, sockets, logical CPUs visible to
     this process, memory."""
@@ -403,6 +434,7 @@ def main():
         if extra > 0:
             breakdown = {f"{p}.{r}": round(v[0] / extra, 4) for (p, r), v in sorted(tb.items())}
         log(f"[breakdown] ms per step by class over {extra} steps: {breakdown}")
+    gemm_classes = gemm_class_rates(breakdown, sh, B, K)
 
     if args.calibrate:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -468,6 +500,7 @@ def main():
             "timed_steps": n_rs,
         },
         "ms_per_step_by_class": breakdown,
+        "gemm_classes": gemm_classes,
         "kernel_a": kernel_a,
         "hbm_read_achievable": read_probe,
     }
