@@ -51,6 +51,7 @@ struct Layout {
   // element size, dims
   int esz, L, d, hq, hkv, hd, F, V, K, G, qd, kd, nqkv;
   int cap, kpad, tmax, rmax, sc, nc, qr_max, ngroups_max;
+  int draft_tpw;   // query tiles per wave of every draft-pass attention launch
   bool bf16;
   // packed offsets (bytes)
   uint64_t p_embed, p_lm, p_fnorm, p_mask;
@@ -145,6 +146,13 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.sc = sc;
   y.nc = (y.cap + sc - 1) / sc;
   y.qr_max = y.tmax * y.G;
+  // Mask rows fold the draft block into their last chunk with two query
+  // tiles per wave and keep it as a separate last partial with one, which
+  // changes their low bits.  The draft pass therefore takes its tile count
+  // from create-time quantities only (the full cache at max_batch), so a
+  // context computes every draft row the same way whatever the call's batch
+  // or the host's length bound.
+  y.draft_tpw = (long)c.max_batch * y.hkv * y.nc * attn_row_groups((y.K + 1) * y.G, 2) < 512 ? 1 : 2;
   {
     int ns[4] = {y.nqkv, y.d, 2 * y.F, y.V};
     y.ngroups_max = 0;
@@ -394,8 +402,10 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   uint16_t* q = S<uint16_t>(c, y.w_q);
   uint16_t* act = S<uint16_t>(c, y.w_act);
   const int pb = pass_base(P.kind);
-  // host-side upper bound on the cache slots a sequence of the pass reaches
-  // (a launch-shape hint for attention; no result depends on it)
+  // host-side upper bound on the cache slots a sequence of the pass reaches:
+  // a launch-shape hint for the attention of AR rows (prefill, anchor,
+  // verify), whose results do not depend on it; draft passes take their
+  // launch shape from the context instead (see draft_tpw)
   int reach = 0;
   if (P.kind == PASS_PREFILL) {
     reach = P.p0 + P.Kx;
@@ -468,6 +478,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     a.qr_max = y.qr_max; a.opart = S<float>(c, y.w_opart); a.ml = S<float>(c, y.w_ml);
     a.out = x; a.fixed_ctx = -1; a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
     a.active_chunks = active_chunks;
+    if (P.kind == PASS_DRAFT && P.Kx > 0) a.tpw = y.draft_tpw;
     if (c->dbg_attn && rows <= c->dbg_rows) {
       a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * 2;
       a.tap_rows = rows;

@@ -176,7 +176,12 @@ struct AttnArgs {
   int fixed_ctx;    // >= 0: microbenchmark mode, every row sees cache [0, fixed_ctx)
   int block_len;    // keys in the block scratch
   int active_chunks;  // upper bound on the cache chunks a sequence of the pass reaches
-  int tpw;          // query tiles per wave, 1 or 2 (set by the launcher)
+  int tpw;          // query tiles per wave, 1 or 2 (0: the launcher chooses from the grid size)
 };
 void launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+// number of query row groups of a pass: a workgroup's four waves own tpw
+// 16-row query tiles each
+__host__ __device__ inline int attn_row_groups(int qr, int tpw) {
+  return ((qr + 15) / 16 + 4 * tpw - 1) / (4 * tpw);
+}
 void launch_attention_f32(const AttnArgs& a, hipStream_t s);

@@ -14,11 +14,14 @@
 // the sequence's last chunk also streams the draft block's keys, after its
 // cache keys.  Each chunk writes its partial (reference, sum, unnormalised
 // output) and the merge kernel combines a row's partials in increasing chunk
-// order.  A row's result therefore depends only on which keys it sees, never
-// on the other rows of the pass: fully masked tiles and chunks are exact
-// no-ops, masked keys are removed by selection (never by multiplying stale
-// values), and keys past the pass's last written slot are zeroed when
-// staged.
+// order.  An AR row's result therefore depends only on which keys it sees,
+// never on the other rows of the pass or the launch shape: fully masked
+// tiles and chunks are exact no-ops, masked keys are removed by selection
+// (never by multiplying stale values), and keys past the pass's last written
+// slot are zeroed when staged.  A mask row also depends on the launch's
+// query tiles per wave: with two the draft block's keys are folded into the
+// last chunk's partial, with one they form a partial of their own (the
+// library fixes that choice per context for draft passes).
 //
 // fp32 path: one wave per (row, query head), keys in order (check models).
 #include "internal.h"
@@ -80,12 +83,6 @@ __device__ __forceinline__ void token_view(const AttnArgs& a, const SeqLimits& L
   if (P.kind == PASS_DRAFT) { limit = L.n; sees_block = t >= P.A; return; }
   sees_block = 0;
   limit = P.kind == PASS_VERIFY ? L.n + 1 + t : P.p0 + t;
-}
-
-// number of query row groups of a pass: a workgroup's four waves own tpw
-// 16-row query tiles each
-__host__ __device__ inline int attn_row_groups(int qr, int tpw) {
-  return ((qr + 15) / 16 + 4 * tpw - 1) / (4 * tpw);
 }
 
 // A row's softmax reference m (base 2) is raised only when a tile holds a
@@ -696,7 +693,7 @@ void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {
   // tile per wave gives a latency-bound launch (fewer workgroups than two
   // per compute unit) twice the workgroups with half the work each
   const int act = a.active_chunks > 0 && a.active_chunks < a.nc ? a.active_chunks : a.nc;
-  a.tpw = (long)B * a.hkv * act * attn_row_groups(QR, 2) < 512 ? 1 : 2;
+  if (a.tpw != 1 && a.tpw != 2) a.tpw = (long)B * a.hkv * act * attn_row_groups(QR, 2) < 512 ? 1 : 2;
   const int nrg = attn_row_groups(QR, a.tpw);
   if (a.tpw == 1)
     hipLaunchKernelGGL(k_attn_bf16_t1, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);

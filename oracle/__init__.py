@@ -6,6 +6,7 @@ header for what is computed and which passages of the pages it follows.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -62,40 +63,63 @@ I32P = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
 F64P = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 
 
+def _configure(L):
+    """Argument and result types of the oracle's C entry points."""
+    vp, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    L.oc_num_tensors.argtypes = [ctypes.POINTER(_Cfg)]
+    L.oc_weight_layout.argtypes = [ctypes.POINTER(_Cfg), i32, sz, sz]
+    L.oc_round_bf16.argtypes = [dbl]; L.oc_round_bf16.restype = dbl
+    L.oc_rmsnorm.argtypes = [F64P, vp, i32, dbl, F64P]
+    L.oc_rope.argtypes = [F64P, i32, ctypes.c_long, dbl]
+    L.oc_attention_dense.argtypes = [F64P, F64P, F64P, i32, i32, F64P]
+    L.oc_silu.argtypes = [dbl]; L.oc_silu.restype = dbl
+    L.oc_argmax.argtypes = [F64P, i32]
+    L.oc_accept.argtypes = [I32P, I32P, i32]
+    L.oc_model_new.argtypes = [ctypes.POINTER(_Cfg), vp]; L.oc_model_new.restype = vp
+    L.oc_model_free.argtypes = [vp]
+    L.oc_model_set_attn_tap.argtypes = [vp, vp, i32]
+    L.oc_seq_new.argtypes = [vp, i32]; L.oc_seq_new.restype = vp
+    L.oc_seq_free.argtypes = [vp]
+    L.oc_seq_len.argtypes = [vp]
+    L.oc_seq_set_len.argtypes = [vp, i32]
+    L.oc_seq_checksum.argtypes = [vp, i32]; L.oc_seq_checksum.restype = dbl
+    L.oc_ar_rows.argtypes = [vp, vp, I32P, i32, i32, vp, vp]
+    L.oc_draft_rows.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
+    L.oc_prefill.argtypes = [vp, vp, I32P, i32, vp]
+    L.oc_step.argtypes = [vp, vp, ctypes.c_int32, i32, vp, vp, I32P, vp, vp, vp, I32P,
+                          ctypes.POINTER(ctypes.c_int32)]
+    L.oc_ar_generate.argtypes = [vp, I32P, i32, i32, I32P]
+    L.oc_generate.argtypes = [vp, I32P, i32, i32, i32, vp, i32, I32P, vp, vp]
+    L.oc_attention_many.argtypes = [F64P, F64P, F64P, i32, i32, i32, F64P]
+    L.oc_seq_load_kv.argtypes = [vp, i32, F64P, F64P, i32]
+    L.oc_seq_read_kv.argtypes = [vp, i32, F64P, F64P, i32]
+    L.oc_ar_layer.argtypes = [vp, vp, i32, F64P, i32, i32, vp]
+    L.oc_draft_layer.argtypes = [vp, vp, i32, F64P, i32, i32, i32, vp]
+    L.oc_final.argtypes = [vp, F64P, i32, vp, vp]
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             build()
-        L = ctypes.CDLL(LIB_PATH)
-        vp, i32, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_double
-        sz = ctypes.POINTER(ctypes.c_size_t)
-        L.oc_num_tensors.argtypes = [ctypes.POINTER(_Cfg)]
-        L.oc_weight_layout.argtypes = [ctypes.POINTER(_Cfg), i32, sz, sz]
-        L.oc_round_bf16.argtypes = [dbl]; L.oc_round_bf16.restype = dbl
-        L.oc_rmsnorm.argtypes = [F64P, vp, i32, dbl, F64P]
-        L.oc_rope.argtypes = [F64P, i32, ctypes.c_long, dbl]
-        L.oc_attention_dense.argtypes = [F64P, F64P, F64P, i32, i32, F64P]
-        L.oc_silu.argtypes = [dbl]; L.oc_silu.restype = dbl
-        L.oc_argmax.argtypes = [F64P, i32]
-        L.oc_accept.argtypes = [I32P, I32P, i32]
-        L.oc_model_new.argtypes = [ctypes.POINTER(_Cfg), vp]; L.oc_model_new.restype = vp
-        L.oc_model_free.argtypes = [vp]
-        L.oc_model_set_attn_tap.argtypes = [vp, vp, i32]
-        L.oc_seq_new.argtypes = [vp, i32]; L.oc_seq_new.restype = vp
-        L.oc_seq_free.argtypes = [vp]
-        L.oc_seq_len.argtypes = [vp]
-        L.oc_seq_set_len.argtypes = [vp, i32]
-        L.oc_seq_checksum.argtypes = [vp, i32]; L.oc_seq_checksum.restype = dbl
-        L.oc_ar_rows.argtypes = [vp, vp, I32P, i32, i32, vp, vp]
-        L.oc_draft_rows.argtypes = [vp, vp, i32, i32, vp, i32, vp, vp]
-        L.oc_prefill.argtypes = [vp, vp, I32P, i32, vp]
-        L.oc_step.argtypes = [vp, vp, ctypes.c_int32, i32, vp, vp, I32P, vp, vp, vp, I32P,
-                              ctypes.POINTER(ctypes.c_int32)]
-        L.oc_ar_generate.argtypes = [vp, I32P, i32, i32, I32P]
-        L.oc_generate.argtypes = [vp, I32P, i32, i32, i32, vp, i32, I32P, vp, vp]
-        _lib = L
+        _lib = _configure(ctypes.CDLL(LIB_PATH))
     return _lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Run the oracle from another build of its source (the mutation tests
+    compile copies with one step removed and check that a pin fails)."""
+    global _lib
+    saved = _lib
+    _lib = _configure(ctypes.CDLL(path))
+    try:
+        yield _lib
+    finally:
+        _lib = saved
 
 
 def _ptr(a):
@@ -154,6 +178,16 @@ def attention(q, K, V):
     return out
 
 
+def attention_many(q, K, V):
+    """attention() of every row of q [nq, hd] over the same keys."""
+    q = np.ascontiguousarray(q, np.float64)
+    K = np.ascontiguousarray(K, np.float64)
+    V = np.ascontiguousarray(V, np.float64)
+    out = np.empty_like(q)
+    lib().oc_attention_many(q, K, V, q.shape[0], K.shape[0], q.shape[1], out)
+    return out
+
+
 def silu(x):
     return lib().oc_silu(float(x))
 
@@ -198,6 +232,15 @@ class Model:
 
     def seq(self, cap: int) -> "Seq":
         return Seq(self, cap)
+
+    def final(self, h):
+        """Final RMSNorm + LM head of rows h [R, d]: (logits [R, V], argmax [R])."""
+        h = np.ascontiguousarray(h, np.float64)
+        R = h.shape[0]
+        lg = np.zeros((R, self.shape.V), np.float64)
+        am = np.zeros(R, np.int32)
+        lib().oc_final(self.h, h, R, lg.ctypes.data, am.ctypes.data)
+        return lg, am
 
     def ar_generate(self, prompt, n_new: int) -> np.ndarray:
         prompt = np.ascontiguousarray(prompt, np.int32)
@@ -259,6 +302,45 @@ class Seq:
         rc = lib().oc_ar_rows(self.m.h, self.h, tokens, R, pos0, lg.ctypes.data, am.ctypes.data)
         assert rc == 0, rc
         return lg, am
+
+    def load_kv(self, layer: int, k, v):
+        """Cache slots [0, n) of one layer from K, V [hkv, n, hd]."""
+        k = np.ascontiguousarray(k, np.float64)
+        v = np.ascontiguousarray(v, np.float64)
+        assert k.shape == v.shape and k.shape[0] == self.m.shape.hkv
+        rc = lib().oc_seq_load_kv(self.h, layer, k, v, k.shape[1])
+        assert rc == 0, rc
+
+    def read_kv(self, layer: int, n: int):
+        """Cache slots [0, n) of one layer as K, V [hkv, n, hd]."""
+        s = self.m.shape
+        k = np.zeros((s.hkv, n, s.hd), np.float64)
+        v = np.zeros_like(k)
+        rc = lib().oc_seq_read_kv(self.h, layer, k, v, n)
+        assert rc == 0, rc
+        return k, v
+
+    def ar_layer(self, layer: int, h, pos0: int):
+        """One frozen-view layer for rows at pos0.. from inputs h [R, d]:
+        (layer outputs [R, d], attention output before rounding [R, hq*hd]);
+        writes the rows' K/V into this layer's cache slots."""
+        h = np.array(h, np.float64, order="C")
+        s = self.m.shape
+        o = np.zeros((h.shape[0], s.hq * s.hd), np.float64)
+        rc = lib().oc_ar_layer(self.m.h, self.h, layer, h, h.shape[0], pos0, o.ctypes.data)
+        assert rc == 0, rc
+        return h, o
+
+    def draft_layer(self, layer: int, h, n: int, causal=False):
+        """One diffusion-view layer for the mask rows at n+1.. from inputs
+        h [K, d] (keys: cache [0, n] plus the block)."""
+        h = np.array(h, np.float64, order="C")
+        s = self.m.shape
+        o = np.zeros((h.shape[0], s.hq * s.hd), np.float64)
+        rc = lib().oc_draft_layer(self.m.h, self.h, layer, h, n, h.shape[0], int(causal),
+                                  o.ctypes.data)
+        assert rc == 0, rc
+        return h, o
 
     def draft_rows(self, n: int, K: int, in_tokens=None, causal=False):
         V = self.m.shape.V

@@ -34,13 +34,21 @@
  * order (oc_weight_layout); each tensor starts at a multiple of 256
  * elements; matrices are row-major [out][in].
  *
+ * The bf16 rounding points are pinned by numpy compositions of one and two
+ * bf16 layers (frozen rows and mask rows) that agree to 1e-9, and by
+ * mutation: removing any one rounding statement makes a composition fail.
+ *
  * The diffusion view's values (mask-row logits, hence the drafts) have no
  * printed worked example on the pages, so no pin by value: they are marked
  * "parity unpinned" below.  Their structure is pinned (block
  * bidirectionality, no cache writes, reduction to the AR view under tied
- * weights and a causal block), and so is their wiring at one layer (a
- * composition of the pinned primitives with numpy matmuls, gains away
- * from 1).
+ * weights and a causal block), and so is their wiring (compositions of the
+ * pinned primitives with numpy matmuls, gains away from 1, fp32 and bf16).
+ *
+ * Per-layer entry points (oc_ar_layer, oc_draft_layer, oc_final,
+ * oc_seq_load_kv) run the same arithmetic one layer at a time from given
+ * inputs, so a test can hold another implementation to the oracle layer by
+ * layer from that implementation's own layer inputs and cache.
  */
 #include <math.h>
 #include <stdint.h>
@@ -159,6 +167,18 @@ void oc_attention_dense(const double* q, const double* K, const double* V, int n
   const double** vp = (const double**)malloc(sizeof(void*) * (n > 0 ? n : 1));
   for (int j = 0; j < n; ++j) { kp[j] = K + (size_t)j * hd; vp[j] = V + (size_t)j * hd; }
   oc_attention(q, kp, vp, n, hd, out);
+  free(kp); free(vp);
+}
+
+/* oc_attention of nq queries over the same n keys (one call per query,
+ * queries in parallel; each result is exactly the single-query one). */
+void oc_attention_many(const double* q, const double* K, const double* V, int nq, int n, int hd,
+                       double* out) {
+  const double** kp = (const double**)malloc(sizeof(void*) * (n > 0 ? n : 1));
+  const double** vp = (const double**)malloc(sizeof(void*) * (n > 0 ? n : 1));
+  for (int j = 0; j < n; ++j) { kp[j] = K + (size_t)j * hd; vp[j] = V + (size_t)j * hd; }
+#pragma omp parallel for schedule(dynamic)
+  for (int i = 0; i < nq; ++i) oc_attention(q + (size_t)i * hd, kp, vp, n, hd, out + (size_t)i * hd);
   free(kp); free(vp);
 }
 
@@ -365,112 +385,170 @@ static void final_logits(const oc_model* m, const double* h, int R, double* logi
   free(g); free(z);
 }
 
-/* Frozen AR view over R consecutive tokens at positions pos0..pos0+R-1.
- * Row r attends causally to cache slots [0, pos0+r]; its own K/V (and those
- * of the rows before it) are written to the cache at pos0+r before the
- * attention of each layer.  This single routine is prefill (R = prompt),
- * plain greedy decoding (R = 1), the draft pass's anchor row (R = 1 at
- * position len) and the verify pass (R = K at len+1).  Logits [R][V]
- * (optional) and argmax tokens [R] are returned.  The sequence length is
- * not changed (callers commit). */
-int oc_ar_rows(const oc_model* m, oc_seq* s, const int32_t* tokens, int R, int pos0,
-               double* logits, int32_t* amax) {
+/* Cache slots [0, n) of layer l from K and V rows laid out [hkv][n][hd]
+ * (test infrastructure: lets a test hold the oracle to another
+ * implementation's cache state, layer by layer). */
+int oc_seq_load_kv(oc_seq* s, int l, const double* k, const double* v, int n) {
+  const oc_cfg* c = &s->m->c;
+  if (l < 0 || l >= c->L || n < 0 || n > s->cap) return -2;
+  for (int g = 0; g < c->hkv; ++g)
+    for (int p = 0; p < n; ++p) {
+      memcpy(kslot(s, l, g, p), k + ((size_t)g * n + p) * c->hd, sizeof(double) * c->hd);
+      memcpy(vslot(s, l, g, p), v + ((size_t)g * n + p) * c->hd, sizeof(double) * c->hd);
+    }
+  return 0;
+}
+
+/* The inverse of oc_seq_load_kv: cache slots [0, n) of layer l into K and V
+ * rows [hkv][n][hd]. */
+int oc_seq_read_kv(const oc_seq* s, int l, double* k, double* v, int n) {
+  const oc_cfg* c = &s->m->c;
+  if (l < 0 || l >= c->L || n < 0 || n > s->cap) return -2;
+  for (int g = 0; g < c->hkv; ++g)
+    for (int p = 0; p < n; ++p) {
+      memcpy(k + ((size_t)g * n + p) * c->hd, kslot(s, l, g, p), sizeof(double) * c->hd);
+      memcpy(v + ((size_t)g * n + p) * c->hd, vslot(s, l, g, p), sizeof(double) * c->hd);
+    }
+  return 0;
+}
+
+/* One layer of the frozen AR view for R consecutive rows at positions
+ * pos0..pos0+R-1 whose layer inputs are h[R][d] (overwritten with the layer
+ * outputs).  Row r's K/V are written to cache slot pos0+r of layer l, then
+ * row r attends causally to slots [0, pos0+r].  o_raw (optional, [R][hq*hd])
+ * receives the attention output before its bf16 rounding. */
+int oc_ar_layer(const oc_model* m, oc_seq* s, int l, double* h, int R, int pos0, double* o_raw) {
   const oc_cfg* c = &m->c;
-  if (pos0 < 0 || pos0 + R > s->cap) return -2;
-  int d = c->d, hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd, grp = c->hq / c->hkv;
-  for (int r = 0; r < R; ++r)
-    if (tokens[r] < 0 || tokens[r] >= c->V) return -1;
-  double* h = (double*)malloc(sizeof(double) * (size_t)R * d);
-  for (int r = 0; r < R; ++r)
-    for (int i = 0; i < d; ++i) h[(size_t)r * d + i] = wget(m, T_EMBED, (size_t)tokens[r] * d + i);
+  if (l < 0 || l >= c->L || pos0 < 0 || pos0 + R > s->cap) return -2;
+  int hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd, grp = c->hq / c->hkv;
   long* pos = (long*)malloc(sizeof(long) * R);
   for (int r = 0; r < R; ++r) pos[r] = pos0 + r;
   double* q = (double*)malloc(sizeof(double) * (size_t)R * qd);
   double* k = (double*)malloc(sizeof(double) * (size_t)R * kd);
   double* v = (double*)malloc(sizeof(double) * (size_t)R * kd);
   double* o = (double*)malloc(sizeof(double) * (size_t)R * qd);
-  for (int l = 0; l < c->L; ++l) {
-    qkv_proj(m, l, lt(l, T_WQ), lt(l, T_WK), lt(l, T_WV), lt(l, T_QN), lt(l, T_KN), h, R, pos, q,
-             k, v);
-    for (int r = 0; r < R; ++r)
-      for (int g = 0; g < c->hkv; ++g) {
-        memcpy(kslot(s, l, g, pos0 + r), k + (size_t)r * kd + (size_t)g * hd, sizeof(double) * hd);
-        memcpy(vslot(s, l, g, pos0 + r), v + (size_t)r * kd + (size_t)g * hd, sizeof(double) * hd);
-      }
-#pragma omp parallel for collapse(2) schedule(static)
-    for (int r = 0; r < R; ++r)
-      for (int hh = 0; hh < c->hq; ++hh) {
-        int g = hh / grp, n = pos0 + r + 1;
-        const double** kp = (const double**)malloc(sizeof(void*) * n);
-        const double** vp = (const double**)malloc(sizeof(void*) * n);
-        for (int j = 0; j < n; ++j) { kp[j] = kslot(s, l, g, j); vp[j] = vslot(s, l, g, j); }
-        oc_attention(q + (size_t)r * qd + (size_t)hh * hd, kp, vp, n, hd,
-                     o + (size_t)r * qd + (size_t)hh * hd);
-        free(kp); free(vp);
-      }
-    if (m->attn_tap && R <= m->attn_tap_rows) {
-      double* tap = m->attn_tap + (size_t)l * m->attn_tap_rows * qd;
-      memcpy(tap, o, sizeof(double) * (size_t)R * qd);
-      store_round(m, tap, (size_t)R * qd);
+  qkv_proj(m, l, lt(l, T_WQ), lt(l, T_WK), lt(l, T_WV), lt(l, T_QN), lt(l, T_KN), h, R, pos, q, k,
+           v);
+  for (int r = 0; r < R; ++r)
+    for (int g = 0; g < c->hkv; ++g) {
+      memcpy(kslot(s, l, g, pos0 + r), k + (size_t)r * kd + (size_t)g * hd, sizeof(double) * hd);
+      memcpy(vslot(s, l, g, pos0 + r), v + (size_t)r * kd + (size_t)g * hd, sizeof(double) * hd);
     }
-    layer_tail(m, l, lt(l, T_WO), h, o, R);
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int r = 0; r < R; ++r)
+    for (int hh = 0; hh < c->hq; ++hh) {
+      int g = hh / grp, n = pos0 + r + 1;
+      const double** kp = (const double**)malloc(sizeof(void*) * n);
+      const double** vp = (const double**)malloc(sizeof(void*) * n);
+      for (int j = 0; j < n; ++j) { kp[j] = kslot(s, l, g, j); vp[j] = vslot(s, l, g, j); }
+      oc_attention(q + (size_t)r * qd + (size_t)hh * hd, kp, vp, n, hd,
+                   o + (size_t)r * qd + (size_t)hh * hd);
+      free(kp); free(vp);
+    }
+  if (o_raw) memcpy(o_raw, o, sizeof(double) * (size_t)R * qd);
+  if (m->attn_tap && R <= m->attn_tap_rows) {
+    double* tap = m->attn_tap + (size_t)l * m->attn_tap_rows * qd;
+    memcpy(tap, o, sizeof(double) * (size_t)R * qd);
+    store_round(m, tap, (size_t)R * qd);
   }
-  final_logits(m, h, R, logits, amax);
-  free(h); free(pos); free(q); free(k); free(v); free(o);
+  layer_tail(m, l, lt(l, T_WO), h, o, R);
+  free(pos); free(q); free(k); free(v); free(o);
   return 0;
 }
 
-/* Diffusion view over the block of K mask positions n+1..n+K (n = len), in
- * one forward pass.  Every row starts from the mask embedding (or, for the
- * structural test only, from the embeddings of given tokens), goes through
- * the diffusion Q/K/V/O projections and QK-norm gains and the shared
- * norms/FFN/LM head, and attends to the cache slots [0, n] plus all K block
- * rows (bidirectional; causal = 1 restricts row i to block rows 0..i, for
- * the structural test).  Block K/V stay in local scratch: nothing is written
- * to the cache.  Parity unpinned (values): see the file header. */
-int oc_draft_rows(const oc_model* m, const oc_seq* s, int n, int K, const int32_t* in_tokens,
-                  int causal, double* logits, int32_t* amax) {
+/* Final RMSNorm and LM head of R rows: logits [R][V] and argmax tokens [R]
+ * (each optional). */
+void oc_final(const oc_model* m, const double* h, int R, double* logits, int32_t* amax) {
+  final_logits(m, h, R, logits, amax);
+}
+
+/* Frozen AR view over R consecutive tokens at positions pos0..pos0+R-1:
+ * the embeddings, then every layer (oc_ar_layer), then the final norm and LM
+ * head.  This single routine is prefill (R = prompt), plain greedy decoding
+ * (R = 1), the draft pass's anchor row (R = 1 at position len) and the
+ * verify pass (R = K at len+1).  Logits [R][V] (optional) and argmax tokens
+ * [R] are returned.  The sequence length is not changed (callers commit). */
+int oc_ar_rows(const oc_model* m, oc_seq* s, const int32_t* tokens, int R, int pos0,
+               double* logits, int32_t* amax) {
   const oc_cfg* c = &m->c;
-  if (n < 0 || n >= s->cap || K <= 0) return -2;
-  int d = c->d, hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd, grp = c->hq / c->hkv;
-  double* h = (double*)malloc(sizeof(double) * (size_t)K * d);
-  for (int r = 0; r < K; ++r)
-    for (int i = 0; i < d; ++i)
-      h[(size_t)r * d + i] = in_tokens ? wget(m, T_EMBED, (size_t)in_tokens[r] * d + i)
-                                       : wget(m, T_MASK, (size_t)i);
+  if (pos0 < 0 || pos0 + R > s->cap) return -2;
+  int d = c->d;
+  for (int r = 0; r < R; ++r)
+    if (tokens[r] < 0 || tokens[r] >= c->V) return -1;
+  double* h = (double*)malloc(sizeof(double) * (size_t)R * d);
+  for (int r = 0; r < R; ++r)
+    for (int i = 0; i < d; ++i) h[(size_t)r * d + i] = wget(m, T_EMBED, (size_t)tokens[r] * d + i);
+  for (int l = 0; l < c->L; ++l) oc_ar_layer(m, s, l, h, R, pos0, NULL);
+  final_logits(m, h, R, logits, amax);
+  free(h);
+  return 0;
+}
+
+/* One layer of the diffusion view for the block of K mask positions
+ * n+1..n+K (n = len) whose layer inputs are h[K][d] (overwritten with the
+ * layer outputs): the diffusion Q/K/V/O projections and QK-norm gains, the
+ * shared norms and FFN; every row attends to the cache slots [0, n] plus
+ * all K block rows of this layer (bidirectional; causal = 1 restricts row i
+ * to block rows 0..i, for the structural test).  Block K/V stay in local
+ * scratch: nothing is written to the cache.  o_raw (optional, [K][hq*hd])
+ * receives the attention output before its bf16 rounding. */
+int oc_draft_layer(const oc_model* m, const oc_seq* s, int l, double* h, int n, int K, int causal,
+                   double* o_raw) {
+  const oc_cfg* c = &m->c;
+  if (l < 0 || l >= c->L || n < 0 || n >= s->cap || K <= 0) return -2;
+  int hd = c->hd, qd = c->hq * hd, kd = c->hkv * hd, grp = c->hq / c->hkv;
   long* pos = (long*)malloc(sizeof(long) * K);
   for (int r = 0; r < K; ++r) pos[r] = n + 1 + r;
   double* q = (double*)malloc(sizeof(double) * (size_t)K * qd);
   double* bk = (double*)malloc(sizeof(double) * (size_t)K * kd);
   double* bv = (double*)malloc(sizeof(double) * (size_t)K * kd);
   double* o = (double*)malloc(sizeof(double) * (size_t)K * qd);
-  for (int l = 0; l < c->L; ++l) {
-    qkv_proj(m, l, lt(l, T_DQ), lt(l, T_DK), lt(l, T_DV), lt(l, T_DQN), lt(l, T_DKN), h, K, pos, q,
-             bk, bv);
+  qkv_proj(m, l, lt(l, T_DQ), lt(l, T_DK), lt(l, T_DV), lt(l, T_DQN), lt(l, T_DKN), h, K, pos, q,
+           bk, bv);
 #pragma omp parallel for collapse(2) schedule(static)
-    for (int r = 0; r < K; ++r)
-      for (int hh = 0; hh < c->hq; ++hh) {
-        int g = hh / grp, nb = causal ? r + 1 : K, nk = n + 1 + nb;
-        const double** kp = (const double**)malloc(sizeof(void*) * nk);
-        const double** vp = (const double**)malloc(sizeof(void*) * nk);
-        for (int j = 0; j <= n; ++j) { kp[j] = kslot(s, l, g, j); vp[j] = vslot(s, l, g, j); }
-        for (int j = 0; j < nb; ++j) {
-          kp[n + 1 + j] = bk + (size_t)j * kd + (size_t)g * hd;
-          vp[n + 1 + j] = bv + (size_t)j * kd + (size_t)g * hd;
-        }
-        oc_attention(q + (size_t)r * qd + (size_t)hh * hd, kp, vp, nk, hd,
-                     o + (size_t)r * qd + (size_t)hh * hd);
-        free(kp); free(vp);
+  for (int r = 0; r < K; ++r)
+    for (int hh = 0; hh < c->hq; ++hh) {
+      int g = hh / grp, nb = causal ? r + 1 : K, nk = n + 1 + nb;
+      const double** kp = (const double**)malloc(sizeof(void*) * nk);
+      const double** vp = (const double**)malloc(sizeof(void*) * nk);
+      for (int j = 0; j <= n; ++j) { kp[j] = kslot(s, l, g, j); vp[j] = vslot(s, l, g, j); }
+      for (int j = 0; j < nb; ++j) {
+        kp[n + 1 + j] = bk + (size_t)j * kd + (size_t)g * hd;
+        vp[n + 1 + j] = bv + (size_t)j * kd + (size_t)g * hd;
       }
-    if (m->attn_tap && K <= m->attn_tap_rows) {
-      double* tap = m->attn_tap + (size_t)l * m->attn_tap_rows * qd;
-      memcpy(tap, o, sizeof(double) * (size_t)K * qd);
-      store_round(m, tap, (size_t)K * qd);
+      oc_attention(q + (size_t)r * qd + (size_t)hh * hd, kp, vp, nk, hd,
+                   o + (size_t)r * qd + (size_t)hh * hd);
+      free(kp); free(vp);
     }
-    layer_tail(m, l, lt(l, T_DO), h, o, K);
+  if (o_raw) memcpy(o_raw, o, sizeof(double) * (size_t)K * qd);
+  if (m->attn_tap && K <= m->attn_tap_rows) {
+    double* tap = m->attn_tap + (size_t)l * m->attn_tap_rows * qd;
+    memcpy(tap, o, sizeof(double) * (size_t)K * qd);
+    store_round(m, tap, (size_t)K * qd);
   }
+  layer_tail(m, l, lt(l, T_DO), h, o, K);
+  free(pos); free(q); free(bk); free(bv); free(o);
+  return 0;
+}
+
+/* Diffusion view over the block of K mask positions n+1..n+K in one
+ * forward pass: every row starts from the mask embedding (or, for the
+ * structural test only, from the embeddings of given tokens), then every
+ * layer (oc_draft_layer), then the shared final norm and LM head.  Parity
+ * unpinned (values): see the file header. */
+int oc_draft_rows(const oc_model* m, const oc_seq* s, int n, int K, const int32_t* in_tokens,
+                  int causal, double* logits, int32_t* amax) {
+  const oc_cfg* c = &m->c;
+  if (n < 0 || n >= s->cap || K <= 0) return -2;
+  int d = c->d;
+  double* h = (double*)malloc(sizeof(double) * (size_t)K * d);
+  for (int r = 0; r < K; ++r)
+    for (int i = 0; i < d; ++i)
+      h[(size_t)r * d + i] = in_tokens ? wget(m, T_EMBED, (size_t)in_tokens[r] * d + i)
+                                       : wget(m, T_MASK, (size_t)i);
+  for (int l = 0; l < c->L; ++l) oc_draft_layer(m, s, l, h, n, K, causal, NULL);
   final_logits(m, h, K, logits, amax);
-  free(h); free(pos); free(q); free(bk); free(bv); free(o);
+  free(h);
   return 0;
 }
 

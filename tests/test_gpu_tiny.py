@@ -5,6 +5,8 @@ import numpy as np
 import pytest
 import torch
 
+from lossless_decoding_amd.layout import vt_cols
+
 from synth import workloads
 from tests import gpu_util as U
 
@@ -89,10 +91,19 @@ def test_tiny_draft_leaves_committed_cache_untouched():
     cap = (256 + 63) // 64 * 64
     hd, hkv, L = sh["hd"], sh["hkv"], sh["L"]
     kv = eng.kv.view(torch.float32).view(2, L, 1, hkv, cap * hd)
-    before = kv[..., :n * hd].clone()
+    # committed slots [0, n): K rows; V^T tiles of 64 keys (whole tiles
+    # below n // 64, then the columns of keys j < n % 64 of the partial tile)
+    vt = kv[1].view(L, 1, hkv, cap // 64, hd, 64)
+    cols = torch.as_tensor(vt_cols()[:n % 64], device=kv.device)
+
+    def committed():
+        return (kv[0, ..., :n * hd].clone(), vt[..., :n // 64, :, :].clone(),
+                vt[..., n // 64, :, :][..., cols].clone())
+
+    before = committed()
     eng.draft()
     torch.cuda.synchronize()
-    assert torch.equal(kv[0, ..., :n * hd], before[0])
+    assert all(torch.equal(a, b) for a, b in zip(committed(), before))
     eng.verify(); eng.commit()
     torch.cuda.synchronize()
-    assert torch.equal(kv[0, ..., :n * hd], before[0])
+    assert all(torch.equal(a, b) for a, b in zip(committed(), before))

@@ -313,3 +313,39 @@ def test_one_layer_diffusion_wiring_fp32():
     want = tail(hb, o, 11)
     assert np.allclose(lg, want, rtol=0, atol=1e-10)
     assert np.array_equal(am, want.argmax(1))
+
+
+@pytest.mark.parametrize("model", ["tiny", "small"])
+def test_layer_entry_points_compose_to_the_step(request, model):
+    """The per-layer entry points, chained from the embeddings with a cache
+    loaded slot by slot from another sequence, give exactly the logits of the
+    whole-pass routines (anchor, mask and verify rows of one step)."""
+    shp, w, m = request.getfixturevalue(model)
+    K = 5
+    prompt = workloads.prompts(1, 9, shp.V, seed=14)[0]
+    a = m.seq(32)
+    pending = a.prefill(prompt)
+    n = a.len
+    b = m.seq(32)
+    for l in range(shp.L):
+        k, v = a.read_kv(l, n)
+        b.load_kv(l, k, v)
+    b.len = n
+    r = a.step(pending, K)
+    E = H.as_f64(shp, H.tensor(shp, w, 0)).reshape(shp.V, shp.d)
+    # anchor row at n, then the mask rows over [0, n] + block, then verify
+    h = E[[pending]]
+    for l in range(shp.L):
+        h, _ = b.ar_layer(l, h, n)
+    lg, am = m.final(h)
+    assert np.array_equal(lg[0], r["logits_anchor"]) and am[0] == r["ar"][0]
+    hm = np.tile(H.as_f64(shp, H.tensor(shp, w, 3)), (K, 1))
+    for l in range(shp.L):
+        hm, _ = b.draft_layer(l, hm, n)
+    lg, am = m.final(hm)
+    assert np.array_equal(lg, r["logits_draft"]) and np.array_equal(am, r["drafts"])
+    hv = E[r["drafts"]]
+    for l in range(shp.L):
+        hv, _ = b.ar_layer(l, hv, n + 1)
+    lg, am = m.final(hv)
+    assert np.array_equal(lg, r["logits_verify"]) and np.array_equal(am, r["ar"][1:])
