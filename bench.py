@@ -1,19 +1,26 @@
 #!/usr/bin/env python3
 """Throughput of the Orthrus draft -> verify -> accept -> commit step on one
-MI355X, on a random-init Qwen3-8B-shaped model (synthetic, seeded).
+MI355X, on random-init Qwen3-8B-shaped models (synthetic, seeded).
 
 A step is one pass of the whole hot path for every sequence of the batch:
 pass 1 (anchor + K mask rows through all layers, LM-head argmax), the
 planted-draft copy, pass 2 (K verify rows), acceptance and commit.  Drafts
 are planted from the model's own greedy trajectory so that each step
-accepts a seeded number of tokens (the random model's own drafts would
-almost never be accepted); the timed loop does all the work of a real step.
+accepts a seeded number of tokens (a random model's own drafts would almost
+never be accepted); the timed loop does all the work of a real step.
+
+The headline workload is the largest single-GPU one: 8 sequences with a
+32768-token context each (38.65 GB of KV cache), K = 32, planted accept
+length uniform on {0..32}.  The batch-1 / 512-token and 16 x 8192 workloads
+are run after it and reported as extra keys.
 
 Prints ONE JSON line (everything else goes to stderr):
   value          verified tokens/s = sum over steps and sequences of (m+1) / time
-  roofline       the dominant kernel (the draft pass's gate/up SwiGLU GEMM):
-                 algorithmic bytes per launch / its average duration, timed
-                 with HIP events around its launches inside the timed region
+  roofline       the dominant kernel of the headline workload, the draft
+                 pass's block attention (kernel (a): the attention kernel and
+                 its chunk merge): algorithmic bytes per launch / its average
+                 duration, from HIP events on the launch stream around its
+                 launches inside the timed region
   cpu_baseline   the CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -30,7 +37,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-PROFILE_PMC = os.path.join(ROOT, "profiles", "gemm_gateup_draft_pmc.txt")
+MFMA_PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, published
+PROFILES = os.path.join(ROOT, "profiles")
+HEADLINE = "qwen3_8b_b8_c32768"
+# (steps, warmup) of each workload when it is not the headline
+SECONDARY = {"qwen3_8b_b1_p512": (60, 4), "qwen3_8b_b16_c8192": (10, 2),
+             "qwen3_8b_b8_c32768": (10, 2)}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def tpf_from_accept(mean_accept: float) -> float:
@@ -38,41 +54,65 @@ def tpf_from_accept(mean_accept: float) -> float:
     return (mean_accept + 1.0) / 2.0
 
 
-MFMA_PEAK_BF16 = 2.5e15         # MI355X dense bf16 MFMA, published
-
-
-def KV_BYTES_PER_TOKEN(sh):
+def kv_bytes_per_token(sh):
     """K and V of one token, all layers, bf16."""
     return sh["L"] * 2 * sh["hkv"] * sh["hd"] * 2
 
 
-def step_weight_bytes(sh):
-    """Weight bytes one draft + verify step streams (bf16): pass 1 reads the
-    frozen and the diffusion Q/K/V/O, the FFN and the LM head; pass 2 the
-    frozen Q/K/V/O, the FFN and the LM head."""
-    d, qd, kd, F, V, L = sh["d"], sh["hq"] * sh["hd"], sh["hkv"] * sh["hd"], sh["F"], sh["V"], sh["L"]
-    qkvo = d * qd + 2 * d * kd + qd * d
-    ffn = 3 * d * F
-    return 2 * (L * (2 * qkvo + ffn) + d * V) + 2 * (L * (qkvo + ffn) + d * V)
+def gemm_classes_of(sh):
+    """Per GEMM class: (parameters per layer, layers)."""
+    L, d, F, V = sh["L"], sh["d"], sh["F"], sh["V"]
+    qkv = d * (sh["hq"] + 2 * sh["hkv"]) * sh["hd"]
+    o = sh["hq"] * sh["hd"] * d
+    return {"qkv": (qkv, L), "o_proj": (o, L), "gate_up": (2 * F * d, L), "down": (F * d, L),
+            "lm_head": (V * d, 1)}
 
 
-def step_gemm_flops(sh, B, K):
-    """GEMM flops of one step: pass 1 has B anchor rows on the frozen
-    projections and B*K mask rows on the diffusion ones, all B*(K+1) rows
-    through the FFN and LM head; pass 2 has B*K rows through the frozen
-    model."""
-    d, qd, kd, F, V, L = sh["d"], sh["hq"] * sh["hd"], sh["hkv"] * sh["hd"], sh["F"], sh["V"], sh["L"]
-    qkvo = d * qd + 2 * d * kd + qd * d
-    ffn = 3 * d * F
-    draft = B * (K + 1) * (L * (qkvo + ffn) + d * V)
-    verify = B * K * (L * (qkvo + ffn) + d * V)
-    return 2 * (draft + verify)
+def step_roofline(sh, B, K, n0):
+    """Roofline time of one step whose sequences start at lengths n0 [B]:
+    the sum over kernel classes of max(bytes / 8 TB/s, flops / 2.5 PFLOP/s).
+    GEMM classes: weight bytes (bf16; the draft pass's QKV and O read both
+    the frozen and the diffusion matrices) against 2 x rows x parameters.
+    Attention: the cache K/V each pass must read (draft: slots [0, n] plus
+    the block; verify: [0, n + K]), which is HBM-bound.  Returns (seconds,
+    bytes, gemm flops)."""
+    t = 0.0
+    byts = 0.0
+    flops = 0.0
+    rows = {"draft": B * (K + 1), "verify": B * K}
+    for cls, (n, per) in gemm_classes_of(sh).items():
+        for pas, r in rows.items():
+            sets = 2 if pas == "draft" and cls in ("qkv", "o_proj") else 1
+            wb = sets * n * 2 * per
+            fl = 2 * r * n * per
+            t += max(wb / (HBM_PEAK_GBS * 1e9), fl / MFMA_PEAK_BF16)
+            byts += wb
+            flops += fl
+    kvt = kv_bytes_per_token(sh)
+    kv = float(((n0 + 1 + K) * kvt).sum() + ((n0 + 1 + K) * kvt).sum())
+    t += kv / (HBM_PEAK_GBS * 1e9)
+    return t, byts + kv, flops
+
+
+def attn_launch_bytes(sh, B, K, n0, kind):
+    """Algorithmic bytes of one layer's attention launch: every visible cache
+    key's K and V once (draft: slots [0, n] incl. the staged anchor, plus the
+    K block keys; verify: [0, n + K]), the queries read and the outputs
+    written (bf16)."""
+    hkv, hd, hq = sh["hkv"], sh["hd"], sh["hq"]
+    if kind == "draft":
+        keys = (n0 + 1 + K).sum()
+        rows = B * (K + 1)
+    else:
+        keys = (n0 + 1 + K).sum()
+        rows = B * K
+    return float(keys * hkv * hd * 2 * 2 + 2 * rows * hq * hd * 2)
 
 
 def hbm_read_probe(dev, nbytes=4 << 30, reps=10):
     """The box's achievable HBM read rate: a 4 GiB buffer read once per launch
     by the library's read probe (16-byte loads, one XOR fold per workgroup),
-    best over two grid sizes."""
+    best over three grid sizes."""
     import torch
     from lossless_decoding_amd import _lib as C
     buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
@@ -96,13 +136,15 @@ def hbm_read_probe(dev, nbytes=4 << 30, reps=10):
             "workgroups": best[1]}
 
 
-def kernel_a_bench(dev, points=((4, 16384), (16, 4096)), rows=32, hq=32, hkv=8, kb=32, reps=20):
-    """Kernel (a) alone (orthrus_block_attention) at the configurations with
-    at least 256 MB of cache K/V: `rows` mask rows per sequence see Lk cache
-    keys and kb block keys.  Seeded N(0, 1) bf16 inputs; four independent
-    buffer sets are rotated so that the 256 MB Infinity Cache does not hold
-    the keys between launches.  Algorithmic bytes = cache K/V + block K/V +
-    Q + output."""
+def kernel_a_bench(dev, rows=32, hq=32, hkv=8, kb=32, reps=20):
+    """Kernel (a) alone (orthrus_block_attention) at all twelve points of the
+    block-attention microbenchmark: `rows` mask rows per sequence see Lk cache
+    keys and kb block keys, Lk in {1024, 4096, 16384, 32768} x batch
+    {1, 4, 16}.  Seeded N(0, 1) bf16 inputs; enough independent buffer sets
+    are rotated (at least 4, at least 1 GB in all) that the 256 MB Infinity
+    Cache does not hold the keys between launches.  Algorithmic bytes = cache
+    K/V + block K/V + Q + output; points under 20 us at 8 TB/s are
+    launch- or latency-bound and flagged so."""
     import torch
 
     import synth
@@ -112,9 +154,11 @@ def kernel_a_bench(dev, points=((4, 16384), (16, 4096)), rows=32, hq=32, hkv=8, 
     from synth.device import fill_normal_device
 
     res = []
-    for B, lk in points:
+    for lk, B in workloads.ATTN_GRID:
+        alg = B * hkv * (lk + kb) * 128 * 2 * 2 + 2 * B * rows * hq * 128 * 2
+        nsets = max(4, -(-(1 << 30) // alg))
         sets = []
-        for i in range(4):
+        for i in range(nsets):
             st = workloads.attn_inputs_stream(B, lk) + 100 * i
             q = torch.empty(B, rows, hq, 128, dtype=torch.bfloat16, device=dev)
             fill_normal_device(q, workloads.ATTN_SEED, st, 1.0, synth.P_ATTN)
@@ -135,11 +179,11 @@ def kernel_a_bench(dev, points=((4, 16384), (16, 4096)), rows=32, hq=32, hkv=8, 
         stream = torch.cuda.current_stream().cuda_stream
 
         def go(i):
-            q, kc, vt, kbk, vbt = sets[i % 4]
+            q, kc, vt, kbk, vbt = sets[i % nsets]
             C.orthrus_block_attention(B, rows, hq, hkv, q.data_ptr(), kc.data_ptr(), vt.data_ptr(), lk,
                                       lk, kbk.data_ptr(), vbt.data_ptr(), kb, out.data_ptr(),
                                       ws.data_ptr(), wsb, stream)
-        for i in range(4):
+        for i in range(nsets):
             go(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -148,25 +192,37 @@ def kernel_a_bench(dev, points=((4, 16384), (16, 4096)), rows=32, hq=32, hkv=8, 
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
-        alg = B * hkv * (lk + kb) * 128 * 2 * 2 + 2 * B * rows * hq * 128 * 2
+        roof_us = alg / (HBM_PEAK_GBS * 1e3)
         res.append({"batch": B, "cache_keys": lk, "block_keys": kb, "rows": rows, "us": round(us, 2),
                     "algorithmic_bytes": alg, "achieved_GBps": round(alg / us / 1e3, 1),
-                    "frac_of_8TBps": round(alg / us / 1e3 / HBM_PEAK_GBS, 4)})
-        log(f"[kernel a] B={B} Lk={lk}: {us:.1f} us, {alg / us / 1e3:.0f} GB/s")
+                    "frac_of_8TBps": round(alg / us / 1e3 / HBM_PEAK_GBS, 4),
+                    "roofline_us": round(roof_us, 2), "latency_bound": roof_us < 20.0})
+        log(f"[kernel a] B={B} Lk={lk}: {us:.1f} us, {alg / us / 1e3:.0f} GB/s"
+            f"{' (latency-bound point)' if roof_us < 20.0 else ''}")
         del sets, out, ws
         torch.cuda.empty_cache()
     return res
 
 
-def log(*a):
-    print(*a, file=sys.stderr, flush=True)
-
-
-def kernel_source_hash() -> str:
+def source_hash(*names) -> str:
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "lossless_decoding_amd", "csrc", "k_gemm.hip"), "rb") as f:
-        h.update(f.read())
+    for n in names:
+        with open(os.path.join(ROOT, "lossless_decoding_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def pmc_traffic(fname, workload, src_hash):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
+    taken on this workload with the current kernel source."""
+    path = os.path.join(PROFILES, fname)
+    if not os.path.exists(path):
+        return None
+    pm = dict(l.split(": ", 1) for l in open(path).read().splitlines()
+              if l and not l.startswith("#") and ": " in l)
+    if pm.get("kernel_source_hash") == src_hash and pm.get("workload") == workload:
+        return int(pm["hbm_bytes_per_launch"])
+    return None
 
 
 def workload_desc(name, wl, sh):
@@ -177,44 +233,6 @@ def workload_desc(name, wl, sh):
             f"bf16), batch {wl['B']}, prompt {wl['P']} uniform-random tokens, K={sh['K']}, {law}")
 
 
-def cpu_baseline(sh, wl, mean_tokens_per_step):
-    """Oracle (plain fp64 C, as it stands) on one full draft+verify step of
-    one sequence at the full model shape after a short prefill."""
-    import numpy as np
-
-    import oracle
-    from synth import workloads
-
-    t0 = time.time()
-    shp = oracle.ModelShape(**sh)
-    lay, total = oracle.weight_layout(shp)
-    w = workloads.fill_weights(lay, total, True)
-    log(f"[cpu] weights generated in {time.time() - t0:.1f}s")
-    m = oracle.Model(shp, w)
-    P0 = 4
-    prompt = workloads.prompts(1, P0, sh["V"])[0]
-    seq = m.seq(P0 + sh["K"] + 4)
-    t1 = time.time()
-    pending = seq.prefill(prompt)
-    t2 = time.time()
-    r = seq.step(pending, sh["K"])
-    t3 = time.time()
-    step_s = t3 - t2
-    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
-    log(f"[cpu] prefill {P0} rows {t2 - t1:.1f}s, one step {step_s:.1f}s, m={r['m']}")
-    return {
-        "value": mean_tokens_per_step / step_s,
-        "unit": "tokens/s",
-        "cores": cores,
-        "kind": "oracle",
-        "sample": (f"one draft+verify step (2 passes, 36 layers, K={sh['K']}, 1 sequence) of the "
-                   f"fp64 oracle after a {P0}-token prefill, {step_s:.1f} s; tokens/s = the "
-                   f"workload's mean tokens per step ({mean_tokens_per_step:.3f}) / step time"),
-        "step_seconds": step_s,
-        "host": host_info(),
-    }
-
-
 def gemm_class_rates(breakdown, sh, B, K):
     """Per GEMM class and pass, from the per-class times: weight bytes
     streamed (bf16, every layer; the draft pass's QKV and O read both the
@@ -223,11 +241,7 @@ def gemm_class_rates(breakdown, sh, B, K):
     times come from event pairs around every launch (a few microseconds of
     record overhead each) and the QKV class includes its finish kernel when
     split, so these are lower bounds of the kernels' own rates."""
-    L, d, F, V = sh["L"], sh["d"], sh["F"], sh["V"]
-    qkv = d * (sh["hq"] + 2 * sh["hkv"]) * sh["hd"]
-    o = sh["hq"] * sh["hd"] * d
-    params = {"qkv": (qkv, L), "o_proj": (o, L), "gate_up": (2 * F * d, L), "down": (F * d, L),
-              "lm_head": (V * d, 1)}
+    params = gemm_classes_of(sh)
     rows = {"draft": B * (K + 1), "verify": B * K}
     out = {}
     for key, ms in breakdown.items():
@@ -242,7 +256,9 @@ def gemm_class_rates(breakdown, sh, B, K):
         out[key] = {"ms": ms, "weight_GBps": round(wbytes / s_ / 1e9, 1),
                     "hbm_frac": round(wbytes / s_ / 8e12, 4),
                     "tflops": round(flops / s_ / 1e12, 2),
-                    "mfma_frac": round(flops / s_ / 2.5e15, 4)}
+                    "mfma_frac": round(flops / s_ / 2.5e15, 4),
+                    "bound": "mfma" if flops / MFMA_PEAK_BF16 > wbytes / (HBM_PEAK_GBS * 1e9)
+                    else "hbm"}
     return out
 
 
@@ -270,30 +286,68 @@ def host_info():
             "affinity_cpus": len(os.sched_getaffinity(0)), "mem_gib": mem_gib}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=120)
-    ap.add_argument("--warmup", type=int, default=4)
-    ap.add_argument("--roofline-steps", type=int, default=4,
-                    help="timed steps whose gate/up launches carry HIP events for the roofline "
-                         "(the first ones of the timed region; each event pair adds a few us)")
-    ap.add_argument("--workload", default="qwen3_8b_b1_p512")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown-steps", type=int, default=8)
-    ap.add_argument("--no-kernel-a", action="store_true",
-                    help="skip the block-attention kernel and HBM read-rate measurements")
-    ap.add_argument("--attn-chunk", type=int, default=0,
-                    help="attention key chunk of both contexts (default: the library's rule)")
-    ap.add_argument("--calibrate", action="store_true",
-                    help="also run plain 1 GiB device copies (PMC byte-counter calibration)")
-    args = ap.parse_args()
+def cpu_baseline(sh, wl, mean_tokens_per_step):
+    """The oracle (plain fp64 C, as it stands) on a bounded sample of one
+    sequence's step at the workload's context: layer 0 of the step (the
+    anchor row, the K mask rows and the K verify rows) over a cache of
+    P + 1 slots holding synthetic N(0, 1) keys and values, timed and scaled
+    by the number of layers, plus the final norm and LM head of the 2K + 1
+    rows.  Layer 0's weights, the embeddings and the LM head are the model's
+    own (the weight generator draws each tensor from its own stream)."""
+    import numpy as np
 
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this library has no multi-GPU path "
-              "(sequences shard across GPUs with no exchange)", file=sys.stderr)
-        sys.exit(2)
+    import oracle
+    import synth
+    from synth import workloads
 
+    P, K, L = wl["P"], sh["K"], sh["L"]
+    t0 = time.time()
+    shp1 = oracle.ModelShape(**dict(sh, L=1))
+    lay, total = oracle.weight_layout(shp1)
+    w = workloads.fill_weights(lay, total, True)
+    m = oracle.Model(shp1, w)
+    seq = m.seq(P + K + 2)
+    kc = np.zeros((sh["hkv"], P, sh["hd"]), np.uint16)
+    vc = np.zeros_like(kc)
+    synth.host_fill_normal(kc, workloads.ATTN_SEED, 900, 1.0, synth.P_ATTN)
+    synth.host_fill_normal(vc, workloads.ATTN_SEED, 901, 1.0, synth.P_ATTN)
+    f64 = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    seq.load_kv(0, f64(kc), f64(vc))
+    del kc, vc
+    seq.len = P
+    log(f"[cpu] one-layer model and a {P}-slot synthetic cache in {time.time() - t0:.1f}s")
+    E = f64(w[lay[0][1]:lay[0][1] + lay[0][2]]).reshape(sh["V"], sh["d"])
+    toks = workloads.prompts(1, K + 1, sh["V"], seed=77)[0]
+    e_mask = f64(w[lay[3][1]:lay[3][1] + lay[3][2]])
+    t1 = time.time()
+    ha, _ = seq.ar_layer(0, E[toks[:1]], P)                 # anchor at slot P
+    hm, _ = seq.draft_layer(0, np.tile(e_mask, (K, 1)), P)  # masks over [0, P] + block
+    hv, _ = seq.ar_layer(0, E[toks[1:]], P + 1)             # verify rows at P+1..P+K
+    t2 = time.time()
+    m.final(np.concatenate([ha, hm, hv]))
+    t3 = time.time()
+    layer_s, head_s = t2 - t1, t3 - t2
+    step_s = L * layer_s + head_s
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    log(f"[cpu] one layer of the step {layer_s:.2f}s, final norm + LM head {head_s:.2f}s, "
+        f"estimated step {step_s:.1f}s")
+    return {
+        "value": mean_tokens_per_step / step_s,
+        "unit": "tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"one sequence's draft+verify step at the workload's {P}-token context "
+                   f"(K={K}): layer 0 of both passes (anchor, {K} mask rows, {K} verify rows; "
+                   f"cache of synthetic N(0,1) K/V) took {layer_s:.2f} s and the final norm + "
+                   f"LM head of the {2 * K + 1} rows {head_s:.2f} s on the fp64 oracle; step "
+                   f"= {L} x layer + head = {step_s:.1f} s; tokens/s = the workload's mean "
+                   f"tokens per step per sequence ({mean_tokens_per_step:.3f}) / step time"),
+        "step_seconds": round(step_s, 3),
+        "host": host_info(),
+    }
+
+
+def run_workload(name, S, W, args, headline):
     import numpy as np
     import torch
 
@@ -302,12 +356,11 @@ def main():
     from synth import workloads
     from synth.device import fill_weights_device
 
-    wl = workloads.WORKLOADS[args.workload]
+    wl = workloads.WORKLOADS[name]
     sh = workloads.SHAPES[wl["shape"]]
     B, P, K, V = wl["B"], wl["P"], sh["K"], sh["V"]
-    W, S = args.warmup, args.steps
-    torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+    log(f"==== {name} ({'headline' if headline else 'summary'}: {S} timed steps, {W} warmup)")
 
     a = workloads.plant_lengths(W + S, B, K, wl["plant"])
     need = 1 + int((a + 1).sum(0).max()) + K + 2          # trajectory tokens per sequence
@@ -335,8 +388,6 @@ def main():
     ar.prefill(prompts)
     traj = torch.zeros(need, B, dtype=torch.int32, device=dev)
     traj[0] = ar.pending[:B]
-    # the same kernels in plain greedy decoding (K = 0): one token per
-    # sequence per step, timed for the speedup figure
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a0.record()
     for j in range(1, need):
@@ -346,16 +397,15 @@ def main():
     torch.cuda.synchronize()
     plain_tps = B * (need - 1) / (a0.elapsed_time(a1) / 1e3)
     traj = traj.t().contiguous().cpu().numpy()
-    ar_s = time.time() - t0
-    log(f"[setup] greedy trajectory of {need} tokens x {B} in {ar_s:.1f}s "
+    log(f"[setup] greedy trajectory of {need} tokens x {B} in {time.time() - t0:.1f}s "
         f"(plain decoding {plain_tps:.1f} tokens/s)")
     ar.close()
     del ar
+    torch.cuda.empty_cache()
     planted = torch.from_numpy(workloads.plant_drafts(traj, 1, a, K, V)).to(dev)
 
-    # ---------------------------------------------------------------- timed
     # prefill (the prompts through the AR view into the cache), timed on its
-    # own and reported beside the step loop
+    # own and reported beside the step loop: the time to first token
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record()
     eng.prefill(prompts)
@@ -365,13 +415,21 @@ def main():
     log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms")
     for s in range(W):
         eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
-    cls = C.timing_class("draft", "gate_up")
-    # events around the draft gate/up launches of the first roofline-steps
-    # timed steps (the library stops recording at the capacity)
+
+    # events around the dominant kernel's launches in the first roofline
+    # steps of the timed region (the library stops recording at the capacity)
     n_rs = max(1, min(args.roofline_steps, S))
-    C.orthrus_timing_enable(eng.ctx, 1 << cls, n_rs * sh["L"])
+    rcls = [("draft", "attention"), ("draft", "gate_up")]
+    mask = sum(1 << C.timing_class(p, r) for p, r in rcls)
+    C.orthrus_timing_enable(eng.ctx, mask, n_rs * sh["L"] * len(rcls))
     torch.cuda.synchronize()
-    # one event per step boundary (the first and last bracket the timed region)
+    marker = None
+    if args.markers:
+        # a tiny read-probe launch before and after the timed region marks it
+        # in a profiler's kernel trace
+        marker = torch.zeros(4096, dtype=torch.uint8, device=dev)
+        mout = torch.zeros(1, dtype=torch.int32, device=dev)
+        C.orthrus_stream_read(marker.data_ptr(), 4096, mout.data_ptr(), 1, eng.s)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(S + 1)]
     t_wall = time.perf_counter()
     ev[0].record()
@@ -381,6 +439,8 @@ def main():
         eng.verify()
         eng.commit()
         ev[s - W + 1].record()
+    if marker is not None:
+        C.orthrus_stream_read(marker.data_ptr(), 4096, mout.data_ptr(), 1, eng.s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = ev[0].elapsed_time(ev[S])
@@ -390,7 +450,6 @@ def main():
 
     tokens = int((a[W:W + S] + 1).sum())
     ms_step = ms / S
-    # correctness of the timed run: lengths and the emitted stream match greedy decoding
     seq_len = eng.seq_len[:B].cpu().numpy()
     want_len = P + (a + 1).sum(0)
     pend = eng.pending[:B].cpu().numpy()
@@ -401,30 +460,43 @@ def main():
     log(f"[timed] {S} steps in {ms:.1f} ms ({ms_step:.3f} ms/step, wall {wall * 1e3:.1f} ms), "
         f"{tokens} tokens, lossless={lossless}, step ms {step_pct}")
 
-    # dominant kernel: the draft pass's gate/up SwiGLU GEMM (M = B*(K+1) rows)
+    # sequence lengths at the start of every step
+    n_all = P + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(a + 1, axis=0)])
+    n_timed = n_all[W:W + S]
+    roof_s, step_bytes, gemm_flops = 0.0, 0.0, 0.0
+    for s in range(S):
+        t_, b_, f_ = step_roofline(sh, B, K, n_timed[s])
+        roof_s += t_; step_bytes += b_; gemm_flops += f_
+
+    # the dominant kernel: the draft pass's block attention
+    at_ms, at_n = tim.get(("draft", "attention"), (0.0, 0))
+    at_steps = at_n // sh["L"]
+    at_bytes = (sum(attn_launch_bytes(sh, B, K, n_timed[s], "draft") for s in range(at_steps))
+                / max(at_steps, 1))
+    at_avg_s = at_ms / max(at_n, 1) / 1e3
+    # the attention kernel the draft pass launches: one query tile per wave
+    # when the context's full cache at this batch gives under 512 workgroups
+    G = sh["hq"] // sh["hkv"]
+    nc = -(-((max_ctx + 63) // 64 * 64) // chunk)
+    rg = -(-(-(-((K + 1) * G) // 16)) // 8)
+    at_kernel = "k_attn_bf16_t%d + k_attn_merge" % (1 if B * sh["hkv"] * nc * rg < 512 else 2)
+    at_ach = at_bytes / at_avg_s / 1e9 if at_n else 0.0
+    # the draft pass's gate/up SwiGLU GEMM, with the launch shape the library picks
+    M1 = B * K + ((-(B * K)) % 16) + B if K > 0 else B
+    gu_plan = C.orthrus_gemm_plan(M1, 0, 2 * sh["F"], sh["d"], C.EP_SWIGLU)
     gu_ms, gu_n = tim.get(("draft", "gate_up"), (0.0, 0))
-    M1 = B * (K + 1)
-    gu_bytes = 2 * sh["F"] * sh["d"] * 2 + M1 * sh["d"] * 2 + M1 * sh["F"] * 2
+    M1a = B * (K + 1)
+    gu_bytes = 2 * sh["F"] * sh["d"] * 2 + M1a * sh["d"] * 2 + M1a * sh["F"] * 2
     gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
-    # the instantiation the library launches for it (row tiles, waves per workgroup)
-    gu_mt = min(4, (M1 + 15) // 16)
-    gu_wv = 6 if (2 * sh["F"] // 16) % 6 == 0 and gu_mt <= 3 else 8
-    achieved = gu_bytes / gu_avg_s / 1e9 if gu_n else 0.0
-    traffic = None
-    if os.path.exists(PROFILE_PMC):
-        pm = dict(l.split(": ", 1) for l in open(PROFILE_PMC).read().splitlines()
-                  if l and not l.startswith("#"))
-        if pm.get("kernel_source_hash") == kernel_source_hash() and \
-                pm.get("workload") == args.workload:
-            traffic = int(pm["hbm_bytes_per_launch"])
+    gu_ach = gu_bytes / gu_avg_s / 1e9 if gu_n else 0.0
+    gu_flops = 2 * M1a * 2 * sh["F"] * sh["d"]
 
     # per-class breakdown over a few more steps (all classes timed)
     breakdown = {}
     if args.breakdown_steps > 0:
-        # a few more steps with every class timed (acceptance differs: the
-        # planted rows no longer line up with the trajectory; cost does not)
         C.orthrus_sync_lengths(eng.ctx, B, seq_len)
-        extra = min(args.breakdown_steps, (max_ctx - int(seq_len.max()) - 64) // (K + 1))
+        extra = min(args.breakdown_steps, (max_ctx - int(seq_len.max()) - 64) // (K + 1),
+                    planted.shape[0] - W)
         C.orthrus_timing_enable(eng.ctx, (1 << 24) - 1, max(extra, 1) * 800 + 64)
         for j in range(extra):
             eng.draft(); eng.drafts[:B].copy_(planted[W + j]); eng.verify(); eng.commit()
@@ -434,44 +506,16 @@ def main():
         if extra > 0:
             breakdown = {f"{p}.{r}": round(v[0] / extra, 4) for (p, r), v in sorted(tb.items())}
         log(f"[breakdown] ms per step by class over {extra} steps: {breakdown}")
-    gemm_classes = gemm_class_rates(breakdown, sh, B, K)
+    eng.close()
+    del eng, planted
+    torch.cuda.empty_cache()
 
-    if args.calibrate:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log("[calibrate] 3 plain copies of 1 GiB")
-
-    # whole-step roofline: algorithmic bytes of the timed steps (weights of
-    # both passes + the cache keys each pass must read) at 8 TB/s
-    wb = step_weight_bytes(sh)
-    n0 = P + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(a + 1, axis=0)])[W:W + S]
-    kv_b = float(((2 * n0 + K + 2) * KV_BYTES_PER_TOKEN(sh)).sum())
-    step_bytes = S * wb + kv_b
-    step_roof_ms = step_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
-    gemm_flops = step_gemm_flops(sh, B, K) * S
-    kernel_a = kernel_a_bench(dev) if not args.no_kernel_a else None
-    read_probe = hbm_read_probe(dev) if not args.no_kernel_a else None
-
-    out = {
-        "metric": "verified tokens/s (and draft+verify steps/s) on 1 GPU; % of HBM roofline",
-        "value": round(tokens / (ms / 1e3), 3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": S,
-        "warmup": W,
+    res = {
+        "workload": workload_desc(name, wl, sh),
+        "batch": B, "prompt_len": P, "block_k": K, "attn_chunk": chunk,
+        "tokens_per_s": round(tokens / (ms / 1e3), 3),
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded random-init weights and prompts, planted drafts)",
-        "config": {"workload": workload_desc(args.workload, wl, sh), "batch": B,
-                   "prompt_len": P, "block_k": K, "parallelism": "none (1 GPU)"},
-        "attn_chunk": chunk,
+        "steps": S, "warmup": W,
         "steps_per_s": round(S / (ms / 1e3), 3),
         "step_ms_percentiles": step_pct,
         "tokens_per_step": round(tokens / S, 4),
@@ -481,31 +525,127 @@ def main():
         "lossless_vs_greedy": lossless,
         "plain_decoding_tokens_per_s": round(plain_tps, 3),
         "speedup_vs_plain_decoding": round(tokens / (ms / 1e3) / plain_tps, 4),
-        "step_roofline": {"bytes_per_step": round(step_bytes / S), "roofline_ms": round(step_roof_ms / S, 4),
-                          "frac": round(step_roof_ms / ms, 4),
-                          "gemm_tflops_per_s": round(gemm_flops / (ms / 1e3) / 1e12, 2),
-                          "mfma_frac_bf16": round(gemm_flops / (ms / 1e3) / MFMA_PEAK_BF16, 4)},
+        "step_roofline": {
+            "method": "sum over kernel classes of max(bytes / 8 TB/s, flops / 2.5 PFLOP/s)",
+            "bytes_per_step": round(step_bytes / S), "roofline_ms": round(roof_s * 1e3 / S, 4),
+            "frac": round(roof_s * 1e3 / ms, 4),
+            "gemm_tflops_per_s": round(gemm_flops / (ms / 1e3) / 1e12, 2),
+            "mfma_frac_bf16": round(gemm_flops / (ms / 1e3) / MFMA_PEAK_BF16, 4)},
+        "attention_draft": {
+            "kernel": at_kernel,
+            "bytes_per_launch": round(at_bytes), "avg_launch_us": round(at_avg_s * 1e6, 3),
+            "launches": at_n, "achieved_GBps": round(at_ach, 1),
+            "frac": round(at_ach / HBM_PEAK_GBS, 4)},
+        "gate_up_draft": {
+            "kernel": (f"k_gemm_bf16<{gu_plan['MT']}, EP_SWIGLU, {gu_plan['WV']}, "
+                       f"{'true' if gu_plan['split'] else 'false'}, {gu_plan['CT']}> (M={M1}, "
+                       f"N={2 * sh['F']}, K={sh['d']}, {gu_plan['workgroups']} workgroups)"),
+            "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
+            "launches": gu_n, "achieved_GBps": round(gu_ach, 1),
+            "hbm_frac": round(gu_ach / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(gu_flops / max(gu_avg_s, 1e-12) / MFMA_PEAK_BF16, 4) if gu_n else 0.0},
+        "ms_per_step_by_class": breakdown,
+        "gemm_classes": gemm_class_rates(breakdown, sh, B, K),
+    }
+    return res, sh, wl
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--roofline-steps", type=int, default=4,
+                    help="timed steps whose attention and gate/up launches carry HIP events "
+                         "(the first ones of the timed region; each event pair adds a few us)")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--also", default="qwen3_8b_b1_p512,qwen3_8b_b16_c8192",
+                    help="comma-separated workloads summarised after the headline ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown-steps", type=int, default=6)
+    ap.add_argument("--no-kernel-a", action="store_true",
+                    help="skip the block-attention microbenchmark and HBM read-rate measurements")
+    ap.add_argument("--attn-chunk", type=int, default=0,
+                    help="attention key chunk of both contexts (default: the library's rule)")
+    ap.add_argument("--markers", action="store_true",
+                    help="launch a tiny read probe before and after the headline's timed region "
+                         "(marks it in a profiler's kernel trace)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run plain 1 GiB device copies (PMC byte-counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the decode step shards by sequence with no "
+              "exchange, and this build runs on a single GPU (no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    res, sh, wl = run_workload(args.workload, args.steps, args.warmup, args, True)
+    others = {}
+    for name in [x for x in args.also.split(",") if x and x != args.workload]:
+        S2, W2 = SECONDARY[name]
+        a2 = argparse.Namespace(**vars(args))
+        a2.breakdown_steps = 0
+        a2.markers = False
+        r2, _, _ = run_workload(name, S2, W2, a2, False)
+        others[name] = r2
+
+    if args.calibrate:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[calibrate] 3 plain copies of 1 GiB")
+    kernel_a = kernel_a_bench(dev) if not args.no_kernel_a else None
+    read_probe = hbm_read_probe(dev) if not args.no_kernel_a else None
+
+    at = res["attention_draft"]
+    traffic = pmc_traffic("attn_draft_%s_pmc.txt" % args.workload, args.workload,
+                          source_hash("k_attn.hip"))
+    out = {
+        "metric": "verified tokens/s (and draft+verify steps/s) on 1 GPU; % of HBM roofline",
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": res["steps"],
+        "warmup": res["warmup"],
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and prompts, planted drafts)",
+        "config": {"workload": res["workload"], "batch": res["batch"],
+                   "prompt_len": res["prompt_len"], "block_k": res["block_k"],
+                   "parallelism": "none (1 GPU)"},
         "roofline": {
-            "kernel": f"k_gemm_bf16<{gu_mt}, EP_SWIGLU, {gu_wv}, false, 1> (draft-pass gate/up "
-                      f"SwiGLU GEMM, M={M1}, N={2 * sh['F']}, K={sh['d']})",
+            "kernel": f"{at['kernel']} (draft-pass block attention, kernel (a), per layer)",
             "bound": "hbm",
-            "achieved": round(achieved, 1),
+            "achieved": at["achieved_GBps"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "frac": at["frac"],
             "traffic": traffic,
-            "bytes_per_launch": gu_bytes,
-            "avg_launch_us": round(gu_avg_s * 1e6, 3),
-            "launches": gu_n,
-            "timed_steps": n_rs,
+            "bytes_per_launch": at["bytes_per_launch"],
+            "avg_launch_us": at["avg_launch_us"],
+            "launches": at["launches"],
+            "timed_steps": max(1, min(args.roofline_steps, args.steps)),
         },
-        "ms_per_step_by_class": breakdown,
-        "gemm_classes": gemm_classes,
-        "kernel_a": kernel_a,
-        "hbm_read_achievable": read_probe,
     }
+    for k, v in res.items():
+        if k not in ("workload", "batch", "prompt_len", "block_k", "tokens_per_s", "ms_per_step",
+                     "steps", "warmup"):
+            out[k] = v
+    out["other_workloads"] = others
+    out["kernel_a"] = kernel_a
+    out["hbm_read_achievable"] = read_probe
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(sh, wl, tokens / S / B)
+        out["cpu_baseline"] = cpu_baseline(sh, wl, res["tokens_per_step"] / res["batch"])
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -221,6 +221,17 @@ int orthrus_timing_read(orthrus_ctx* ctx, double* ms, int64_t* launches);
  * earlier pass wrote).  Errors: EINVAL. */
 int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_cap);
 
+/* Per-layer parity taps (optional; NULL disables), for holding the library
+ * to a reference one layer at a time from the library's own layer inputs.
+ * resid: device fp32 [n_layers + 1][rows_cap][d_model]: entry l < n_layers
+ * receives every later pass's layer-l input residual rows, entry n_layers
+ * the final norm's input rows.  attn32: device fp32
+ * [n_layers][rows_cap][n_q_heads*head_dim]: each layer's attention output
+ * before its rounding to bf16 (bf16 models only; EINVAL otherwise).  Rows
+ * are pass rows as for orthrus_set_debug; a pass with more rows than
+ * rows_cap writes neither.  Errors: EINVAL. */
+int orthrus_set_debug_layers(orthrus_ctx* ctx, float* resid, float* attn32, int32_t rows_cap);
+
 /* Kernel (a) alone: block attention of `batch` sequences, bf16.  q: [batch]
  * [rows][n_q_heads][128]; k_cache: [batch][n_kv_heads][cap][128]; v_cache
  * in the library's tiled layout: [batch][n_kv_heads][cap/64][128][64] where
@@ -252,6 +263,16 @@ uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_he
  * workgroups (one round of two per compute unit).  Errors: EINVAL
  * (returned as a negative value). */
 int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n_kv_heads);
+
+/* Measurement aid: the launch shape the library uses for a bf16 GEMM of m
+ * rows (plus m2 rows of a second weight segment, as the draft pass's
+ * projections have), n output features and k inputs, with epilogue 1
+ * (residual), 2 (SwiGLU), 3 (LM-head argmax) or 4 (Q/K/V + QK-norm + RoPE).
+ * plan (host, 5 ints): row tiles of 16 per workgroup, waves per workgroup,
+ * 1 if K is split over workgroups (8 slices), 16-column tiles per wave,
+ * workgroups.  Host only.  Errors: EINVAL. */
+int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, int32_t epilogue,
+                      int32_t* plan);
 
 /* Measurement aid (not part of the decode step): n_workgroups workgroups
  * read the device buffer buf (bytes, a multiple of 16, 256-byte aligned)

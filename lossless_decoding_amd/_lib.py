@@ -17,8 +17,8 @@ ORTHRUS_F32, ORTHRUS_BF16 = 0, 1
 EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_verify_accept", "orthrus_commit_kv",
-    "orthrus_set_debug", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_attention_workspace",
-    "orthrus_default_attn_chunk", "orthrus_stream_read",
+    "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_attention_workspace",
+    "orthrus_default_attn_chunk", "orthrus_stream_read", "orthrus_gemm_plan",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
 
@@ -80,6 +80,7 @@ def lib():
         L.orthrus_verify_accept.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.orthrus_commit_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orthrus_set_debug.argtypes = [vp, vp, vp, i32]
+        L.orthrus_set_debug_layers.argtypes = [vp, vp, vp, i32]
         L.orthrus_sync_lengths.argtypes = [vp, i32, vp]
         L.orthrus_timing_enable.argtypes = [vp, ctypes.c_uint32, i32]
         L.orthrus_timing_read.argtypes = [vp, vp, vp]
@@ -89,6 +90,7 @@ def lib():
         L.orthrus_attention_workspace.restype = u64
         L.orthrus_default_attn_chunk.argtypes = [i32, i32, i32]
         L.orthrus_stream_read.argtypes = [vp, u64, vp, i32, vp]
+        L.orthrus_gemm_plan.argtypes = [i32, i32, i32, i32, i32, vp]
         L.orthrus_default_attn_chunk.restype = i32
         L.orthrus_strerror.argtypes = [ctypes.c_int]
         L.orthrus_strerror.restype = ctypes.c_char_p
@@ -154,6 +156,10 @@ def orthrus_set_debug(ctx, logits, attn, rows_cap):
     _check("orthrus_set_debug", lib().orthrus_set_debug(ctx, logits, attn, rows_cap))
 
 
+def orthrus_set_debug_layers(ctx, resid, attn32, rows_cap):
+    _check("orthrus_set_debug_layers", lib().orthrus_set_debug_layers(ctx, resid, attn32, rows_cap))
+
+
 def orthrus_sync_lengths(ctx, batch, seq_len_host: np.ndarray):
     sl = np.ascontiguousarray(seq_len_host, np.int32)
     _check("orthrus_sync_lengths", lib().orthrus_sync_lengths(ctx, batch, sl.ctypes.data))
@@ -192,6 +198,17 @@ def orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len) -> int:
 
 def orthrus_stream_read(buf, nbytes, out, n_workgroups, stream):
     _check("orthrus_stream_read", lib().orthrus_stream_read(buf, nbytes, out, n_workgroups, stream))
+
+
+EP_RESID, EP_SWIGLU, EP_ARGMAX, EP_QKV = 1, 2, 3, 4
+
+
+def orthrus_gemm_plan(m, m2, n, k, epilogue) -> dict:
+    """The launch shape of a bf16 GEMM (see include/orthrus.h)."""
+    plan = np.zeros(5, np.int32)
+    _check("orthrus_gemm_plan", lib().orthrus_gemm_plan(m, m2, n, k, epilogue, plan.ctypes.data))
+    return dict(MT=int(plan[0]), WV=int(plan[1]), split=bool(plan[2]), CT=int(plan[3]),
+                workgroups=int(plan[4]))
 
 
 def orthrus_default_attn_chunk(max_batch, max_ctx, n_kv_heads) -> int:

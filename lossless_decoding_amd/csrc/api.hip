@@ -249,6 +249,9 @@ struct orthrus_ctx {
   float* dbg_logits;
   void* dbg_attn;
   int dbg_rows;
+  float* dbg_resid;    // [L+1][dbg_lrows][d]: layer inputs, then the final norm's input
+  float* dbg_attn32;   // [L][dbg_lrows][qd]: attention output before rounding (bf16 models)
+  int dbg_lrows;
   // opt-in launch timing: event pairs around launches of the selected classes
   uint32_t tmask;
   std::vector<hipEvent_t> ev;     // 2 per pair
@@ -295,6 +298,15 @@ struct Tick {
   }
 };
 
+// Per-layer parity tap: residual rows of the pass (the input of layer l, or
+// of the final norm for l = L) copied out when the pass fits the tap.
+void tap_resid(orthrus_ctx* c, int l, const float* h, int rows, hipStream_t s) {
+  if (!c->dbg_resid || rows > c->dbg_lrows) return;
+  const uint64_t d = c->y.d;
+  (void)hipMemcpyAsync(c->dbg_resid + (uint64_t)l * c->dbg_lrows * d, h, rows * d * 4,
+                       hipMemcpyDeviceToDevice, s);
+}
+
 template <typename T> T* W(orthrus_ctx* c, uint64_t off) { return (T*)(c->packed + off); }
 template <typename T> T* S(orthrus_ctx* c, uint64_t off) { return (T*)(c->ws + off); }
 
@@ -335,6 +347,7 @@ void run_pass_f32(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
                  c->packed + y.p_mask, y.V, y.d, false, h, s);
   }
   for (int l = 0; l < y.L; ++l) {
+    tap_resid(c, l, h, rows, s);
     launch_rmsnorm(h, rows, y.d, c->packed + y.p_anorm[l], false, eps, x, s);
     if (P.kind == PASS_DRAFT) {
       if (BK > 0)
@@ -376,6 +389,7 @@ void run_pass_f32(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     gemm(c, y.p_gu[l], y.p_gu[l] + (uint64_t)y.F * y.d * E, x, y.d, rows, y.d, y.F, og, s);
     gemm(c, y.p_down[l], 0, act, y.F, rows, y.F, y.d, out_store(h, y.d, EP_RESID), s);
   }
+  tap_resid(c, y.L, h, rows, s);
   if (!want_tokens) return;
   launch_rmsnorm(h, rows, y.d, c->packed + y.p_fnorm, false, eps, x, s);
   GemmOut ol{};
@@ -435,6 +449,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
                            eps, x, s);
   };
   g0.rpart = rpart; g0.rps = rps;
+  tap_resid(c, 0, h, rows, s);
   rnorm(0, y.p_anorm[0]);
   auto run = [&](GemmArgs g, uint64_t w, int row0, int M, int K, int N, int ep) {
     g.W = (const u32x4_t*)(c->packed + w);
@@ -483,6 +498,10 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       a.tap = (char*)c->dbg_attn + (uint64_t)l * c->dbg_rows * y.qd * 2;
       a.tap_rows = rows;
     }
+    if (c->dbg_attn32 && rows <= c->dbg_lrows) {
+      a.tap32 = c->dbg_attn32 + (uint64_t)l * c->dbg_lrows * y.qd;
+      a.tap32_rows = rows;
+    }
     {
       Tick t(c, pb + R_ATTN, s);
       launch_attention_bf16(a, s);
@@ -516,6 +535,7 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     // residual + the next RMSNorm: the next layer's attention norm, or the
     // final norm in front of the LM head
     rnorm(gemm_bf16_split_slices(rows, 0, y.d, EP_RESID), l + 1 < y.L ? y.p_anorm[l + 1] : y.p_fnorm);
+    tap_resid(c, l + 1, h, rows, s);
   }
   if (!want_tokens) return;
   Tick tl(c, pb + R_LM, s);
@@ -586,6 +606,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
   c->state = ST_IDLE; c->step_batch = 0;
   c->bound.assign(cfg->max_batch, 0);
   c->dbg_logits = nullptr; c->dbg_attn = nullptr; c->dbg_rows = 0;
+  c->dbg_resid = nullptr; c->dbg_attn32 = nullptr; c->dbg_lrows = 0;
   c->tmask = 0; c->ev_used = 0; c->ev_dropped = false;
   const Layout& y = c->y;
   const uint64_t E = y.esz;
@@ -681,6 +702,16 @@ int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_
   ctx->dbg_logits = logits;
   ctx->dbg_attn = attn;
   ctx->dbg_rows = rows_cap;
+  return ORTHRUS_OK;
+}
+
+int orthrus_set_debug_layers(orthrus_ctx* ctx, float* resid, float* attn32, int32_t rows_cap) {
+  if (!ctx || rows_cap < 0) return ORTHRUS_EINVAL;
+  if ((resid || attn32) && rows_cap == 0) return ORTHRUS_EINVAL;
+  if (attn32 && !ctx->y.bf16) return ORTHRUS_EINVAL;
+  ctx->dbg_resid = resid;
+  ctx->dbg_attn32 = attn32;
+  ctx->dbg_lrows = rows_cap;
   return ORTHRUS_OK;
 }
 
@@ -856,22 +887,34 @@ uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_he
   return al(pr * 128 * 4) + al(pr * 2 * 4);
 }
 
-int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
-                            const void* q, const void* k_cache, const void* v_cache, int32_t cap,
-                            int32_t ctx_len, const void* k_block, const void* v_block,
-                            int32_t block_len, void* out, void* workspace,
-                            uint64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by both forms of kernel (a) alone.
+int block_attention_args(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
+                         const void* q, const void* k_cache, const void* v_cache, int32_t cap,
+                         int32_t ctx_len, const void* k_block, const void* v_block,
+                         int32_t block_len, void* out) {
   if (batch < 1 || rows < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads)
     return ORTHRUS_EINVAL;
   int G = n_q_heads / n_kv_heads;
   if (rows * G > 144 || cap % 64 || ctx_len < 0 || ctx_len > cap || block_len < 0 ||
       block_len > 64 || ctx_len + block_len < 1)
     return ORTHRUS_EINVAL;
-  if (!q || !out || !workspace || (ctx_len > 0 && (!k_cache || !v_cache)) ||
+  if (!q || !out || (ctx_len > 0 && (!k_cache || !v_cache)) ||
       (block_len > 0 && (!k_block || !v_block)))
     return ORTHRUS_EINVAL;
-  uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
-  if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
+  return ORTHRUS_OK;
+}
+
+// Kernel (a) alone with its chunk partials in `workspace` (checked by the
+// caller: at least orthrus_attention_workspace bytes, 256-byte aligned).
+int block_attention_run(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
+                        const void* q, const void* k_cache, const void* v_cache, int32_t cap,
+                        int32_t ctx_len, const void* k_block, const void* v_block,
+                        int32_t block_len, void* out, void* workspace, void* stream) {
+  int G = n_q_heads / n_kv_heads;
   int sc = block_attn_chunk(batch, ctx_len, n_kv_heads);
   int nc = block_attn_nchunks(ctx_len, sc);
   uint64_t pr = (uint64_t)batch * n_kv_heads * (nc + 1) * rows * G;
@@ -887,6 +930,25 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   a.active_chunks = nc;
   launch_attention_bf16(a, (hipStream_t)stream);
   return check_launch();
+}
+
+}  // namespace
+
+extern "C" {
+
+int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
+                            const void* q, const void* k_cache, const void* v_cache, int32_t cap,
+                            int32_t ctx_len, const void* k_block, const void* v_block,
+                            int32_t block_len, void* out, void* workspace,
+                            uint64_t workspace_bytes, void* stream) {
+  int rc = block_attention_args(batch, rows, n_q_heads, n_kv_heads, q, k_cache, v_cache, cap,
+                                ctx_len, k_block, v_block, block_len, out);
+  if (rc) return rc;
+  if (!workspace) return ORTHRUS_EINVAL;
+  uint64_t need = orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len);
+  if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
+  return block_attention_run(batch, rows, n_q_heads, n_kv_heads, q, k_cache, v_cache, cap,
+                             ctx_len, k_block, v_block, block_len, out, workspace, stream);
 }
 
 int orthrus_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int32_t n_workgroups,

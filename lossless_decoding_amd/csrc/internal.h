@@ -173,6 +173,7 @@ struct AttnArgs {
   float* ml;        // [B][hkv][nc+1][qr_max][2]
   void* out;        // [rows][hq*hd] model dtype
   void* tap; int tap_rows;   // optional attention-output tap for this layer
+  float* tap32; int tap32_rows;   // optional fp32 tap of the attention output before rounding
   int fixed_ctx;    // >= 0: microbenchmark mode, every row sees cache [0, fixed_ctx)
   int block_len;    // keys in the block scratch
   int active_chunks;  // upper bound on the cache chunks a sequence of the pass reaches

@@ -682,6 +682,7 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   const uint32_t y = (uint32_t)f2bf(o0 * inv) | ((uint32_t)f2bf(o1 * inv) << 16);
   *(uint32_t*)((uint16_t*)a.out + ob) = y;
   if (a.tap && r < a.tap_rows) *(uint32_t*)((uint16_t*)a.tap + ob) = y;
+  if (a.tap32 && r < a.tap32_rows) *(float2*)(a.tap32 + ob) = make_float2(o0 * inv, o1 * inv);
 }
 
 void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {

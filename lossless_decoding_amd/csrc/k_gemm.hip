@@ -653,6 +653,58 @@ int gemm_bf16_split_slices(int M, int M2, int N, int ep) {
   return (N / 128) * gy >= (ep == EP_RESID ? 256 : 128) ? 0 : NSL;
 }
 
+// The launch shape launch_gemm_bf16 picks for a GEMM (row tiles, waves per
+// workgroup, K split or not, column tiles per wave, workgroups).  Shared by
+// the launcher and the measurement query, so the two cannot disagree.
+struct GemmPlan { int MT, WV, split, CT, wgs; };
+
+static GemmPlan gemm_plan(int M, int M2, int N, int ep) {
+  GemmPlan p{};
+  if (M2 < 0) M2 = 0;
+  const bool wide = gemm_bf16_split_slices(M, M2, N, ep) == 0;
+  const int wv = (ep == EP_SWIGLU && (N / 16) % 6 == 0 && gemm_mt(M, M2) <= 3) ? 6 : 8;
+  // tall row tiles for unsplit launches other than gate/up (which takes two
+  // column tiles per wave at 128 rows instead: measured faster)
+  int MT = wide && ep != EP_SWIGLU ? gemm_mt_tall(M, M2, N / (16 * wv)) : gemm_mt(M, M2);
+  // gate/up, and split O / down launches, at 128-row tiles (two column
+  // tiles per wave): 144-row tiles where they pad fewer rows (528 rows:
+  // 4 x 144 instead of 5 x 128)
+  if ((wide ? ep == EP_SWIGLU : ep == EP_RESID) && MT == 8 && M2 == 0 && rows144_pad_less(M))
+    MT = 9;
+  // QKV (48 column groups at Qwen3-8B width) with 128-row tiles: 64-row
+  // tiles when 128 would leave fewer than 192 workgroups.  Measured: 264 + 8
+  // draft rows 144 -> 240 workgroups, 2.81 -> 2.02 ms per step; 512 + 16
+  // rows (240 workgroups) slower with 64-row tiles, 2.89 -> 3.65 ms.
+  if (wide && ep == EP_QKV && MT == 8 && (N / 128) * ((M + 127) / 128 + (M2 + 127) / 128) < 192)
+    MT = 4;
+  const int rpw = MT > 4 ? MT * 16 : 64;
+  const int gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
+  p.MT = MT;
+  p.split = !wide;
+  if (!wide) {
+    p.WV = (ep == EP_RESID && (MT == 8 || MT == 9)) ? 4 : 8;
+    p.CT = p.WV == 4 ? 2 : 1;
+    p.wgs = N / 128 * NSL * gy;
+  } else if ((MT == 8 || MT == 9) && ep == EP_SWIGLU) {
+    p.WV = 4; p.CT = 2; p.wgs = N / 128 * gy;
+  } else {
+    p.WV = (ep == EP_SWIGLU && wv == 6) ? 6 : 8;
+    p.CT = 1;
+    p.wgs = N / (16 * p.WV) * gy;
+  }
+  return p;
+}
+
+extern "C" int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, int32_t epilogue,
+                                 int32_t* plan) {
+  if (!plan || m < 0 || m2 < 0 || m + m2 < 1 || n < 128 || n % 128 || k < 256 || k % 256 ||
+      epilogue < EP_RESID || epilogue > EP_QKV)
+    return ORTHRUS_EINVAL;
+  const GemmPlan p = gemm_plan(m, m2, n, epilogue);
+  plan[0] = p.MT; plan[1] = p.WV; plan[2] = p.split; plan[3] = p.CT; plan[4] = p.wgs;
+  return ORTHRUS_OK;
+}
+
 // Shape rules: N a multiple of 128, K a multiple of 256 (8 slices of whole
 // k-blocks).  A second segment (W2, M2, row02: same N, K and input buffer)
 // runs in the same launch; the argmax epilogue takes one segment only.
@@ -660,23 +712,10 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   if (!a.W2 || a.M2 <= 0) { a.W2 = nullptr; a.M2 = 0; }
   if (a.M <= 0 && a.M2 <= 0) return;
-  const bool wide = gemm_bf16_split_slices(a.M, a.M2, a.N, a.ep) == 0;
-  const int wv = (a.ep == EP_SWIGLU && (a.N / 16) % 6 == 0 && gemm_mt(a.M, a.M2) <= 3) ? 6 : 8;
-  // tall row tiles for unsplit launches other than gate/up (which takes two
-  // column tiles per wave at 128 rows instead: measured faster)
-  int MT = wide && a.ep != EP_SWIGLU ? gemm_mt_tall(a.M, a.M2, a.N / (16 * wv)) : gemm_mt(a.M, a.M2);
-  // gate/up, and split O / down launches, at 128-row tiles (two column
-  // tiles per wave): 144-row tiles where they pad fewer rows (528 rows:
-  // 4 x 144 instead of 5 x 128)
-  if ((wide ? a.ep == EP_SWIGLU : a.ep == EP_RESID) && MT == 8 && a.M2 == 0 && rows144_pad_less(a.M))
-    MT = 9;
-  // QKV (48 column groups at Qwen3-8B width) with 128-row tiles: 64-row
-  // tiles when 128 would leave fewer than 192 workgroups.  Measured: 264 + 8
-  // draft rows 144 -> 240 workgroups, 2.81 -> 2.02 ms per step; 512 + 16
-  // rows (240 workgroups) slower with 64-row tiles, 2.89 -> 3.65 ms.
-  if (wide && a.ep == EP_QKV && MT == 8 &&
-      (a.N / 128) * ((a.M + 127) / 128 + (a.M2 + 127) / 128) < 192)
-    MT = 4;
+  const GemmPlan plan = gemm_plan(a.M, a.M2, a.N, a.ep);
+  const bool wide = !plan.split;
+  const int MT = plan.MT;
+  const int wv = plan.WV == 6 ? 6 : 8;
   const int rpw = MT > 4 ? MT * 16 : 64;         // rows per workgroup
   a.gy0 = (a.M + rpw - 1) / rpw;
   const dim3 gy(1, a.gy0 + (a.M2 + rpw - 1) / rpw);

@@ -76,6 +76,9 @@ class Engine:
     def set_debug(self, logits: torch.Tensor | None, attn: torch.Tensor | None, rows: int):
         C.orthrus_set_debug(self.ctx, _ptr(logits), _ptr(attn), rows)
 
+    def set_debug_layers(self, resid: torch.Tensor | None, attn32: torch.Tensor | None, rows: int):
+        C.orthrus_set_debug_layers(self.ctx, _ptr(resid), _ptr(attn32), rows)
+
     def prefill(self, prompts: np.ndarray, prompt_len=None):
         prompts = np.ascontiguousarray(prompts, np.int32)
         B, P = prompts.shape

@@ -30,3 +30,10 @@ def tile_block_v(v: torch.Tensor, kpad: int) -> torch.Tensor:
     cols = torch.as_tensor(vt_cols()[:Kb], device=v.device)
     out[..., cols] = v.transpose(-1, -2)
     return out
+
+
+def untile_v(vt: torch.Tensor) -> torch.Tensor:
+    """[..., tiles, 128, 64] tiled -> [..., tiles * 64, 128] logical (inverse of tile_v)."""
+    *lead, nt, d, _ = vt.shape
+    cols = torch.as_tensor(vt_cols(), device=vt.device)
+    return vt[..., cols].transpose(-1, -2).reshape(*lead, nt * 64, d)

@@ -97,6 +97,7 @@ def _configure(L):
     L.oc_ar_layer.argtypes = [vp, vp, i32, F64P, i32, i32, vp]
     L.oc_draft_layer.argtypes = [vp, vp, i32, F64P, i32, i32, i32, vp]
     L.oc_final.argtypes = [vp, F64P, i32, vp, vp]
+    L.oc_layer_tail.argtypes = [vp, i32, i32, F64P, F64P, i32]
     return L
 
 
@@ -232,6 +233,16 @@ class Model:
 
     def seq(self, cap: int) -> "Seq":
         return Seq(self, cap)
+
+    def layer_tail(self, layer: int, h, o, diffusion=False):
+        """Layer `layer` after attention (O projection + residual, FFN +
+        residual) for rows h [R, d] with attention outputs o [R, hq*hd]:
+        the layer outputs [R, d]."""
+        h = np.array(h, np.float64, order="C")
+        o = np.ascontiguousarray(o, np.float64)
+        rc = lib().oc_layer_tail(self.h, layer, int(diffusion), h, o, h.shape[0])
+        assert rc == 0, rc
+        return h
 
     def final(self, h):
         """Final RMSNorm + LM head of rows h [R, d]: (logits [R, V], argmax [R])."""

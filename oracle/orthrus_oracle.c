@@ -456,6 +456,22 @@ int oc_ar_layer(const oc_model* m, oc_seq* s, int l, double* h, int R, int pos0,
   return 0;
 }
 
+/* The rest of layer l after attention (O projection + residual, FFN +
+ * residual) for R rows with inputs h[R][d] (overwritten with the layer
+ * outputs) and attention outputs o[R][hq*hd] (rounded to the model's
+ * storage precision first, as in every layer): the diffusion view's O
+ * projection if diffusion != 0, else the frozen one. */
+int oc_layer_tail(const oc_model* m, int l, int diffusion, double* h, const double* o, int R) {
+  const oc_cfg* c = &m->c;
+  if (l < 0 || l >= c->L || R < 1) return -2;
+  size_t n = (size_t)R * c->hq * c->hd;
+  double* oc = (double*)malloc(sizeof(double) * n);
+  memcpy(oc, o, sizeof(double) * n);
+  layer_tail(m, l, lt(l, diffusion ? T_DO : T_WO), h, oc, R);
+  free(oc);
+  return 0;
+}
+
 /* Final RMSNorm and LM head of R rows: logits [R][V] and argmax tokens [R]
  * (each optional). */
 void oc_final(const oc_model* m, const double* h, int R, double* logits, int32_t* amax) {

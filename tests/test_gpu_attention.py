@@ -124,3 +124,48 @@ def test_block_attention_two_tile_launch_ragged(lk, kb):
         want = oracle.attention(q[b, r, h].float().cpu().numpy().astype(np.float64), keys, vals)
         got = out[b, r, h].float().cpu().numpy()
         assert np.abs(got - want).max() < TOL, (b, r, h)
+
+
+def _reference_rows(q, kc, vc, kbk, vbk, b, g, lk, kb, qrows, G):
+    """Oracle outputs of query rows qrows = [(token, head)] of sequence b,
+    all reading KV head g: every cache key and every block key."""
+    keys = torch.cat([kc[b, g, :lk], kbk[b, g, :kb]]).float().cpu().numpy().astype(np.float64)
+    vals = torch.cat([vc[b, g, :lk], vbk[b, g, :kb]]).float().cpu().numpy().astype(np.float64)
+    qs = np.stack([q[b, t, h] for t, h in qrows]).astype(np.float64)
+    return oracle.attention_many(qs, keys, vals)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("lk,B", workloads.ATTN_GRID)
+def test_block_attention_microbenchmark_grid(lk, B):
+    """Every point of the block-attention microbenchmark (32 query tokens x
+    32 query heads over 8 KV heads, 32 block keys, Lk cached keys, bf16
+    N(0, 1) inputs).  B in {1, 4}: every (sequence, token, head) output
+    against the oracle.  B = 16: for every sequence, the four heads of one
+    KV head (rotating over the KV heads) at tokens 0..31 step 3 plus the last
+    token 31, which covers all eight 16-row query tiles (every row group of
+    either launch form) of that (sequence, KV head): 16 x 12 x 4 = 768
+    outputs."""
+    rows, hq, hkv, kb = 32, 32, 8, 32
+    G = hq // hkv
+    print(f"[attention grid] B={B} lk={lk}", flush=True)
+    q, kc, vc, kbk, vbk, cap = make(B, rows, hq, hkv, lk, kb, 11)
+    out = run(B, rows, hq, hkv, lk, kb, q, kc, vc, kbk, vbk, cap)
+    err = 0.0
+    if B <= 4:
+        pairs = [(b, g, [(t, g * G + j) for t in range(rows) for j in range(G)])
+                 for b in range(B) for g in range(hkv)]
+    else:
+        toks = sorted(set(range(0, rows, 3)) | {rows - 1})
+        pairs = [(b, b % hkv, [(t, (b % hkv) * G + j) for t in toks for j in range(G)])
+                 for b in range(B)]
+    n = 0
+    qn = q.float().cpu().numpy()
+    on = out.float().cpu().numpy()
+    for b, g, qrows in pairs:
+        want = _reference_rows(qn, kc, vc, kbk, vbk, b, g, lk, kb, qrows, G)
+        got = np.stack([on[b, t, h] for t, h in qrows])
+        err = max(err, float(np.abs(got - want).max()))
+        n += len(qrows)
+    assert n >= (B * rows * hq if B <= 4 else 256)
+    assert err < TOL, err

@@ -1,7 +1,21 @@
-"""The full Qwen3-8B shape (36 layers, d 4096, vocab 151936, bf16) on the GPU:
-one draft/verify step against the oracle after a short prompt (logits
-within 2e-2, tokens exact outside near-ties), and draft/verify decoding equal
-to the GPU's own greedy decoding."""
+"""The full Qwen3-8B shape (36 layers, d 4096, vocab 151936, bf16) on the GPU.
+
+* Full depth, teacher-forced layer by layer: at every layer of every pass
+  the oracle recomputes the layer's attention from the GPU's own layer-input
+  rows and committed cache (compared before the bf16 rounding of its
+  output), and the rest of the layer from the GPU's own layer input and
+  bf16 attention output (the layer output compared); the final logits come
+  from the GPU's last residual rows.  All within 2e-2; every token must be
+  the oracle's argmax, or at an oracle near-tie (top-1 minus top-2 <= 2e-2)
+  its runner-up; accept lengths and commit indices exactly.  Forcing at both
+  points isolates each layer's arithmetic: the fp32 (GPU) and fp64 (oracle)
+  attention outputs differ by ~1e-4, which flips a few percent of their
+  bf16 roundings, and where the residual is small (layer 0: rms ~0.4) the
+  FFN's RMSNorm amplifies those flips to ~1e-2 in the layer output; a
+  free-running comparison compounds such flips over 36 layers.
+* One layer at full width (and in the batch launch shapes) free-running
+  against the oracle, with the same token rule.
+* Draft/verify decoding equal to the GPU's own greedy decoding."""
 import numpy as np
 import pytest
 import torch
@@ -9,6 +23,7 @@ import torch
 import oracle
 from lossless_decoding_amd import _lib as C
 from lossless_decoding_amd.engine import Engine
+from lossless_decoding_amd.layout import untile_v
 from synth import workloads
 from synth.device import fill_weights_device
 from tests import gpu_util as U
@@ -16,17 +31,18 @@ from tests import helpers as H
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
+TOL = 2e-2
 
-# Full depth: an fp32-accumulating bf16 pipeline and the fp64 oracle round
-# to bf16 at the same points, but a value that lands within the fp32
-# accumulation error of a bf16 rounding boundary rounds differently on the
-# two sides (one bf16 ulp).  Such flips start at the second layer and
-# propagate; measured on this model the logits drift grows from 0.0016 (one
-# layer) to 0.035 (4), 0.056 (16) and 0.071 (36 layers, mean 0.013).  The
-# depth-36 bound below is that measurement with headroom; the contract's
-# 2e-2 applies layer by layer (see the single-layer test).
-DEPTH_TOL_MAX = 0.15
-DEPTH_TOL_MEAN = 0.03
+
+def check_token(gpu_tok, oracle_row, tol=TOL):
+    """The GPU's token is the oracle's argmax, or at an oracle near-tie its
+    runner-up.  Returns 1 for a near-tie event, 0 otherwise."""
+    o = np.argsort(-np.asarray(oracle_row), kind="stable")
+    if int(gpu_tok) == int(o[0]):
+        return 0
+    assert oracle_row[o[0]] - oracle_row[o[1]] <= tol and int(gpu_tok) == int(o[1]), \
+        (int(gpu_tok), int(o[0]), int(o[1]), oracle_row[o[0]] - oracle_row[o[1]])
+    return 1
 
 
 def one_step(cfg, w, prompt, K, V, B=1):
@@ -57,7 +73,9 @@ def one_step(cfg, w, prompt, K, V, B=1):
     return out
 
 
-def compare_step(shp, g, prompt, K, tol_max, tol_mean):
+def compare_step(shp, g, prompt, K, tol=TOL, tol_mean=5e-3):
+    """Free-running comparison of one prefill + step with the oracle, which
+    follows the GPU's tokens (each checked with check_token)."""
     m = oracle.Model(shp, H.weights(shp))
     P = prompt.shape[1]
     seq = m.seq(P + K + 4)
@@ -65,25 +83,132 @@ def compare_step(shp, g, prompt, K, tol_max, tol_mean):
 
     def close(a, b):
         d = np.abs(a - b)
-        assert d.max() < tol_max and d.mean() < tol_mean, (d.max(), d.mean())
+        assert d.max() < tol and d.mean() < tol_mean, (d.max(), d.mean())
 
     close(g["pre"], lg0)
-    if g["pending"] != pend_o:
-        assert U.margin(lg0) <= tol_max        # a tie within the band: nothing more to compare
-        return
+    events = check_token(g["pending"], lg0)
+    pend = g["pending"]
     # the oracle's own diffusion pass from the same state (anchor staged first)
-    seq.ar_rows(np.array([pend_o], np.int32), P)
+    seq.ar_rows(np.array([pend], np.int32), P)
     ld, _ = seq.draft_rows(P, K)
     close(g["draft"], ld)
-    r = seq.step(pend_o, K, planted=g["drafts"])    # verify the drafts the GPU verified
+    for i in range(K):
+        events += check_token(g["drafts"][i], ld[i])
+    r = seq.step(pend, K, planted=g["drafts"])    # verify the drafts the GPU verified
     close(g["anchor"], r["logits_anchor"])
     close(g["verify"], r["logits_verify"])
     rows = [r["logits_anchor"]] + list(r["logits_verify"])
     for i in range(K + 1):
-        if g["ar"][i] != r["ar"][i]:
-            assert U.margin(rows[i]) <= tol_max, i
-            return
-    assert g["m"] == r["m"]
+        events += check_token(g["ar"][i], rows[i])
+    assert g["m"] == oracle.accept(g["drafts"], g["ar"])
+    if events == 0:
+        assert g["m"] == r["m"]
+
+
+def load_gpu_cache(eng, seq, L, hkv, hd, n):
+    """The GPU's committed cache slots [0, n) of every layer, into the oracle's
+    sequence (K rows, V from its 64-key transposed tiles)."""
+    cap = (eng.cfg.max_ctx + 63) // 64 * 64
+    kv = eng.kv.view(torch.bfloat16)[:2 * L * hkv * cap * hd].view(2, L, hkv, cap, hd)
+    for l in range(L):
+        k = kv[0, l, :, :n].float().cpu().numpy().astype(np.float64)
+        vt = kv[1, l].reshape(hkv, cap // 64, hd, 64)
+        v = untile_v(vt)[:, :n].float().cpu().numpy().astype(np.float64)
+        seq.load_kv(l, k, v)
+    seq.len = n
+
+
+def test_qwen3_8b_full_depth_teacher_forced(weights8b):
+    """All 36 layers, batch 1, K = 32 (the qwen3_8b_b1_p512 launch shapes), a
+    64-token prompt and 3 steps with planted accept lengths 7, 0 and 32."""
+    sh = workloads.SHAPES["qwen3_8b"]
+    K, V, L, d, hkv, hd = sh["K"], sh["V"], sh["L"], sh["d"], sh["hkv"], sh["hd"]
+    qd = sh["hq"] * hd
+    P = 64
+    prompt = workloads.prompts(1, P, V, seed=24)
+    a = np.array([[7], [0], [32]], np.int32)
+    twin = Engine(U.cfg_of("qwen3_8b", K=0, max_batch=1, max_ctx=256), weights8b)
+    traj, _ = twin.generate(prompt, int((a + 1).sum()) + K + 2)
+    twin.close()
+    planted = workloads.plant_drafts(traj, 1, a, K, V)[:, 0, :]
+
+    eng = Engine(U.cfg_of("qwen3_8b", max_batch=1, max_ctx=256), weights8b)
+    RA = U.anchor_row(K)                    # anchor row of the draft pass (32)
+    rows = RA + 1
+    lg = torch.zeros(rows, V, device="cuda")
+    resid = torch.zeros(L + 1, rows, d, device="cuda")
+    at32 = torch.zeros(L, rows, qd, device="cuda")
+    atb = torch.zeros(L, rows, qd, dtype=torch.bfloat16, device="cuda")
+    eng.set_debug(lg, atb, rows)
+    eng.set_debug_layers(resid, at32, rows)
+    eng.prefill(prompt)
+    torch.cuda.synchronize()
+    assert np.array_equal(int(eng.pending[0]), traj[0, 0])
+
+    shp = H.shape("qwen3_8b")
+    m = oracle.Model(shp, H.weights(shp))
+    seq = m.seq(256)
+    worst = dict(attn=0.0, h=0.0, logits=0.0)
+    events = 0
+    R = A32 = AB = None
+
+    def f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    def hold(l, o_o, sl, diffusion):
+        """Layer l for pass rows sl: the oracle's attention output (from the
+        GPU's layer input) against the GPU's before rounding; the oracle's
+        layer output from the GPU's layer input and bf16 attention output
+        against the GPU's."""
+        ea = np.abs(o_o - A32[l, sl]).max()
+        h_o = m.layer_tail(l, R[l, sl], AB[l, sl], diffusion=diffusion)
+        eh = np.abs(h_o - R[l + 1, sl]).max()
+        worst["attn"] = max(worst["attn"], ea)
+        worst["h"] = max(worst["h"], eh)
+        assert ea < TOL and eh < TOL, (l, ea, eh)
+
+    for step in range(3):
+        n = int(eng.seq_len[0])
+        load_gpu_cache(eng, seq, L, hkv, hd, n)
+        eng.draft()
+        torch.cuda.synchronize()
+        R, A32, AB = f64(resid), f64(at32), f64(atb)
+        for l in range(L):
+            _, o_a = seq.ar_layer(l, R[l, RA:RA + 1], n)            # anchor at slot n
+            hold(l, o_a, slice(RA, RA + 1), False)
+            _, o_m = seq.draft_layer(l, R[l, :K], n)                # masks over [0, n] + block
+            hold(l, o_m, slice(0, K), True)
+        lo, _ = m.final(R[L])
+        gl = f64(lg)
+        worst["logits"] = max(worst["logits"], np.abs(lo - gl).max())
+        assert np.abs(lo - gl).max() < TOL
+        drafts = eng.drafts[0].cpu().numpy()
+        ar0 = int(eng.ar[0, 0])
+        events += check_token(ar0, lo[RA]) + sum(check_token(drafts[i], lo[i]) for i in range(K))
+
+        eng.drafts[0].copy_(torch.as_tensor(planted[step], device="cuda"))
+        eng.verify()
+        torch.cuda.synchronize()
+        R, A32, AB = f64(resid), f64(at32), f64(atb)
+        for l in range(L):
+            _, o_v = seq.ar_layer(l, R[l, :K], n + 1)               # verify rows at n+1..n+K
+            hold(l, o_v, slice(0, K), False)
+        lo, _ = m.final(R[L, :K])
+        gl = f64(lg[:K])
+        worst["logits"] = max(worst["logits"], np.abs(lo - gl).max())
+        assert np.abs(lo - gl).max() < TOL
+        ar = eng.ar[0].cpu().numpy()
+        events += sum(check_token(ar[1 + i], lo[i]) for i in range(K))
+        mm = int(eng.accept[0])
+        assert mm == oracle.accept(planted[step], ar) == a[step, 0]
+        eng.commit()
+        torch.cuda.synchronize()
+        assert int(eng.commit_start[0]) == n and int(eng.seq_len[0]) == n + 1 + mm
+        assert int(eng.pending[0]) == ar[mm]
+    eng.close()
+    print(f"teacher-forced 36 layers x 3 steps: max |attention| {worst['attn']:.2e}, "
+          f"max |layer output| {worst['h']:.2e}, max |logits| {worst['logits']:.2e}, "
+          f"near-tie events {events}", flush=True)
 
 
 def test_qwen3_8b_single_layer_against_oracle():
@@ -97,7 +222,7 @@ def test_qwen3_8b_single_layer_against_oracle():
     prompt = workloads.prompts(1, 5, V, seed=21)
     g = one_step(cfg, w, prompt, K, V)
     del w
-    compare_step(H.shape("qwen3_8b", L=1), g, prompt, K, 2e-2, 5e-3)
+    compare_step(H.shape("qwen3_8b", L=1), g, prompt, K)
 
 
 @pytest.fixture(scope="module")
@@ -108,14 +233,6 @@ def weights8b():
     yield w
     del w
     torch.cuda.empty_cache()
-
-
-def test_qwen3_8b_full_depth_against_oracle(weights8b):
-    sh = workloads.SHAPES["qwen3_8b"]
-    K, V = sh["K"], sh["V"]
-    prompt = workloads.prompts(1, 4, V, seed=22)
-    g = one_step(U.cfg_of("qwen3_8b", max_batch=1, max_ctx=128), weights8b, prompt, K, V)
-    compare_step(H.shape("qwen3_8b"), g, prompt, K, DEPTH_TOL_MAX, DEPTH_TOL_MEAN)
 
 
 def test_qwen3_8b_orthrus_equals_gpu_greedy(weights8b):
@@ -146,4 +263,4 @@ def test_qwen3_8b_single_layer_batch_against_oracle(B):
     prompt = workloads.prompts(B, 5, V, seed=21)
     g = one_step(cfg, w, prompt, K, V, B)
     del w
-    compare_step(H.shape("qwen3_8b", L=1), g, prompt[:1], K, 2e-2, 5e-3)
+    compare_step(H.shape("qwen3_8b", L=1), g, prompt[:1], K)

@@ -349,3 +349,21 @@ def test_layer_entry_points_compose_to_the_step(request, model):
         hv, _ = b.ar_layer(l, hv, n + 1)
     lg, am = m.final(hv)
     assert np.array_equal(lg, r["logits_verify"]) and np.array_equal(am, r["ar"][1:])
+
+
+def test_layer_tail_entry_point_matches_the_layer(tiny):
+    """oc_layer_tail from a layer's own attention output reproduces the
+    whole layer (frozen and diffusion views)."""
+    shp, w, m = tiny
+    prompt = workloads.prompts(1, 6, shp.V, seed=15)[0]
+    seq = m.seq(32)
+    seq.prefill(prompt)
+    n = seq.len
+    E = H.as_f64(shp, H.tensor(shp, w, 0)).reshape(shp.V, shp.d)
+    h = E[[3]]
+    h1, o = seq.ar_layer(0, h, n)
+    assert np.array_equal(m.layer_tail(0, h, o), h1)
+    hm = np.tile(H.as_f64(shp, H.tensor(shp, w, 3)), (4, 1))
+    hm1, om = seq.draft_layer(0, hm, n)
+    assert np.array_equal(m.layer_tail(0, hm, om, diffusion=True), hm1)
+    assert not np.array_equal(m.layer_tail(0, hm, om, diffusion=False), hm1)
