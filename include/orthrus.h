@@ -251,6 +251,28 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
 uint64_t orthrus_attention_workspace(int32_t batch, int32_t rows, int32_t n_q_heads,
                                      int32_t n_kv_heads, int32_t ctx_len);
 
+/* Kernel (a) alone without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels and results as
+ * orthrus_block_attention, with the chunk partials in a scratch array that
+ * the library's device code object holds on every GPU it runs on, for the
+ * life of the process: ORTHRUS_NOALLOC_SCRATCH_BYTES (48 MiB; enough for
+ * every point of the 32-row, 32/8-head microbenchmark up to 16 sequences x
+ * 32768 keys).  The call allocates and frees nothing.  Calls needing more
+ * than that (orthrus_attention_workspace) fail with ECAPACITY before
+ * anything is enqueued.  All calls on one GPU share its array: calls that
+ * may overlap on one GPU (several streams or host threads) race and must be
+ * serialized by the caller.  Nothing in the array needs clearing between
+ * calls (every partial the merge reads is written by the same call).  The
+ * array's address is looked up on the first call on each device.  Arguments
+ * and layouts as orthrus_block_attention.  Errors: EINVAL, ECAPACITY, EHIP. */
+#define ORTHRUS_NOALLOC_SCRATCH_BYTES (48u << 20)
+int orthrus_block_attention_noalloc(int32_t batch, int32_t rows, int32_t n_q_heads,
+                                    int32_t n_kv_heads, const void* q, const void* k_cache,
+                                    const void* v_cache, int32_t cap, int32_t ctx_len,
+                                    const void* k_block, const void* v_block, int32_t block_len,
+                                    void* out, void* stream);
+
 /* The attention key chunk a context gets for attn_chunk = 0.  Every (chunk,
  * KV head, sequence) is one workgroup that writes a 64 KB partial, read back
  * once per pass.  The rule (measured on the decode workloads): the smallest

@@ -17,7 +17,7 @@ ORTHRUS_F32, ORTHRUS_BF16 = 0, 1
 EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_verify_accept", "orthrus_commit_kv",
-    "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_attention_workspace",
+    "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_block_attention_noalloc", "orthrus_attention_workspace",
     "orthrus_default_attn_chunk", "orthrus_stream_read", "orthrus_gemm_plan",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
@@ -86,6 +86,8 @@ def lib():
         L.orthrus_timing_read.argtypes = [vp, vp, vp]
         L.orthrus_block_attention.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp,
                                               i32, vp, vp, u64, vp]
+        L.orthrus_block_attention_noalloc.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp,
+                                                      vp, i32, vp, vp]
         L.orthrus_attention_workspace.argtypes = [i32, i32, i32, i32, i32]
         L.orthrus_attention_workspace.restype = u64
         L.orthrus_default_attn_chunk.argtypes = [i32, i32, i32]
@@ -194,6 +196,13 @@ def orthrus_timing_read(ctx):
 
 def orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len) -> int:
     return lib().orthrus_attention_workspace(batch, rows, hq, hkv, ctx_len)
+
+
+def orthrus_block_attention_noalloc(batch, rows, hq, hkv, q, k_cache, v_cache, cap, ctx_len,
+                                    k_block, v_block, block_len, out, stream):
+    _check("orthrus_block_attention_noalloc",
+           lib().orthrus_block_attention_noalloc(batch, rows, hq, hkv, q, k_cache, v_cache, cap,
+                                                 ctx_len, k_block, v_block, block_len, out, stream))
 
 
 def orthrus_stream_read(buf, nbytes, out, n_workgroups, stream):

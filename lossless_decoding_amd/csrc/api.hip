@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "internal.h"
@@ -934,6 +935,37 @@ int block_attention_run(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t 
 
 }  // namespace
 
+// The allocation-free form's scratch: one array per GPU, in the library's
+// device code object, holding the chunk partials of the last call.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in): its device address is looked up once per device with
+// hipGetSymbolAddress and kept in g_scratch_dev.
+static __device__ __align__(256) char scratch[ORTHRUS_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  int rc = hip_ok(hipGetDevice(&dev));
+  if (rc) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return ORTHRUS_EINVAL;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    rc = hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (rc) return rc;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return ORTHRUS_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
@@ -949,6 +981,24 @@ int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int3
   if (workspace_bytes < need || !aligned(workspace)) return ORTHRUS_EINVAL;
   return block_attention_run(batch, rows, n_q_heads, n_kv_heads, q, k_cache, v_cache, cap,
                              ctx_len, k_block, v_block, block_len, out, workspace, stream);
+}
+
+int orthrus_block_attention_noalloc(int32_t batch, int32_t rows, int32_t n_q_heads,
+                                    int32_t n_kv_heads, const void* q, const void* k_cache,
+                                    const void* v_cache, int32_t cap, int32_t ctx_len,
+                                    const void* k_block, const void* v_block, int32_t block_len,
+                                    void* out, void* stream) {
+  int rc = block_attention_args(batch, rows, n_q_heads, n_kv_heads, q, k_cache, v_cache, cap,
+                                ctx_len, k_block, v_block, block_len, out);
+  if (rc) return rc;
+  if (orthrus_attention_workspace(batch, rows, n_q_heads, n_kv_heads, ctx_len) >
+      ORTHRUS_NOALLOC_SCRATCH_BYTES)
+    return ORTHRUS_ECAPACITY;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(&ws);
+  if (rc) return rc;
+  return block_attention_run(batch, rows, n_q_heads, n_kv_heads, q, k_cache, v_cache, cap,
+                             ctx_len, k_block, v_block, block_len, out, ws, stream);
 }
 
 int orthrus_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int32_t n_workgroups,
