@@ -158,6 +158,35 @@ int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int3
 int orthrus_draft_block(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
                         const int32_t* pending, int32_t* drafts, int32_t* ar_tokens, void* stream);
 
+/* Pass 1 with a block of k <= block_k mask positions for this step only
+ * (dynamic K: the openai-hub.net article, "Future Directions", item 1, block
+ * size adjusted per step to the generation's certainty; the choice itself is
+ * the caller's).  drafts and ar_tokens keep their [batch][block_k] and
+ * [batch][block_k + 1] layouts; only the first k (drafts) and k + 1
+ * (ar_tokens, after verify) columns are written.  The verify_accept and
+ * commit_kv calls of the step follow this k: accept_len is in [0, k], the
+ * host bound grows by k + 1.  k = 0 is one step of plain greedy decoding.
+ * orthrus_draft_block is this call with k = block_k.  Errors: EINVAL (k out
+ * of range), ECAPACITY, ESTATE. */
+int orthrus_draft_block_k(orthrus_ctx* ctx, int32_t batch, int32_t k, const int32_t* seq_len,
+                          const int32_t* pending, int32_t* drafts, int32_t* ar_tokens,
+                          void* stream);
+
+/* One more denoising pass over the outstanding block (the 2-step iterative
+ * denoising variant the pages compare against single-step block
+ * projection: atlas.scime.ai page, "Surprising findings"; HN item page,
+ * "Results").  Taken as: the diffusion view runs again over the same k mask
+ * positions n+1..n+k, each row now starting from the embedding of its
+ * current draft instead of the mask embedding, with the same attention
+ * (cache slots [0, n], the staged anchor included, and the whole block,
+ * bidirectionally; the block K/V are rewritten in the block scratch); its
+ * argmax replaces drafts[b][0..k).  The anchor row and a_0 are not
+ * recomputed; nothing is written to the cache.  May be called more than
+ * once between draft_block and verify_accept.  drafts: [batch][block_k]
+ * (read, then written).  Errors: EINVAL, ESTATE (no outstanding draft). */
+int orthrus_draft_refine(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                         int32_t* drafts, void* stream);
+
 /* Pass 2 and acceptance.  drafts: [batch][K] (read; the caller may have
  * replaced the drafted ids since draft_block); ar_tokens: [batch][K+1]
  * (column 0 read, columns 1..K written); accept_len: [batch] (written, in

@@ -16,7 +16,7 @@ ORTHRUS_F32, ORTHRUS_BF16 = 0, 1
 
 EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
-    "orthrus_prefill", "orthrus_draft_block", "orthrus_verify_accept", "orthrus_commit_kv",
+    "orthrus_prefill", "orthrus_draft_block", "orthrus_draft_block_k", "orthrus_draft_refine", "orthrus_verify_accept", "orthrus_commit_kv",
     "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_block_attention_noalloc", "orthrus_attention_workspace",
     "orthrus_default_attn_chunk", "orthrus_stream_read", "orthrus_gemm_plan",
     "orthrus_strerror", "orthrus_last_hip_error",
@@ -77,6 +77,8 @@ def lib():
         L.orthrus_destroy.argtypes = [vp]
         L.orthrus_prefill.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp]
         L.orthrus_draft_block.argtypes = [vp, i32, vp, vp, vp, vp, vp]
+        L.orthrus_draft_block_k.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
+        L.orthrus_draft_refine.argtypes = [vp, i32, vp, vp, vp]
         L.orthrus_verify_accept.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.orthrus_commit_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orthrus_set_debug.argtypes = [vp, vp, vp, i32]
@@ -140,6 +142,15 @@ def orthrus_prefill(ctx, batch, tokens, stride, prompt_len: np.ndarray, seq_len,
 def orthrus_draft_block(ctx, batch, seq_len, pending, drafts, ar_tokens, stream):
     _check("orthrus_draft_block",
            lib().orthrus_draft_block(ctx, batch, seq_len, pending, drafts, ar_tokens, stream))
+
+
+def orthrus_draft_block_k(ctx, batch, k, seq_len, pending, drafts, ar_tokens, stream):
+    _check("orthrus_draft_block_k",
+           lib().orthrus_draft_block_k(ctx, batch, k, seq_len, pending, drafts, ar_tokens, stream))
+
+
+def orthrus_draft_refine(ctx, batch, seq_len, drafts, stream):
+    _check("orthrus_draft_refine", lib().orthrus_draft_refine(ctx, batch, seq_len, drafts, stream))
 
 
 def orthrus_verify_accept(ctx, batch, seq_len, drafts, ar_tokens, accept_len, stream):

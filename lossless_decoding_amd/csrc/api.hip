@@ -246,6 +246,7 @@ struct orthrus_ctx {
   char* ws;
   int state;
   int step_batch;
+  int step_k;          // block size of the outstanding step (<= block_k)
   std::vector<int64_t> bound;   // host upper bound of every sequence's length
   float* dbg_logits;
   void* dbg_attn;
@@ -604,7 +605,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
   if (c->y.part_bytes >= (1ull << 31)) { delete c; return ORTHRUS_EINVAL; }
   c->packed = (char*)packed; c->kv = (char*)kv_cache; c->scr = (char*)block_scratch;
   c->ws = (char*)workspace;
-  c->state = ST_IDLE; c->step_batch = 0;
+  c->state = ST_IDLE; c->step_batch = 0; c->step_k = 0;
   c->bound.assign(cfg->max_batch, 0);
   c->dbg_logits = nullptr; c->dbg_attn = nullptr; c->dbg_rows = 0;
   c->dbg_resid = nullptr; c->dbg_attn32 = nullptr; c->dbg_lrows = 0;
@@ -759,26 +760,49 @@ int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int3
   return ORTHRUS_OK;
 }
 
-int orthrus_draft_block(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
-                        const int32_t* pending, int32_t* drafts, int32_t* ar_tokens,
-                        void* stream) {
+int orthrus_draft_block_k(orthrus_ctx* ctx, int32_t batch, int32_t k, const int32_t* seq_len,
+                          const int32_t* pending, int32_t* drafts, int32_t* ar_tokens,
+                          void* stream) {
   if (!ctx || !seq_len || !pending || !ar_tokens) return ORTHRUS_EINVAL;
+  if (k < 0 || k > ctx->y.K) return ORTHRUS_EINVAL;
   if (ctx->y.K > 0 && !drafts) return ORTHRUS_EINVAL;
   if (batch < 1 || batch > ctx->cfg.max_batch) return ORTHRUS_EINVAL;
   if (ctx->state != ST_IDLE) return ORTHRUS_ESTATE;
   for (int b = 0; b < batch; ++b)
     if (ctx->bound[b] < 1) return ORTHRUS_ESTATE;          // never prefilled
   for (int b = 0; b < batch; ++b)
-    if (ctx->bound[b] + ctx->y.K + 1 > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
+    if (ctx->bound[b] + k + 1 > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
   PassInfo P{};
-  P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = ctx->y.K; P.p0 = 0; P.len = seq_len;
+  P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = k; P.p0 = 0; P.len = seq_len;
   set_rm(P);
   run_pass(ctx, P, pending, nullptr, 0, true, drafts, ar_tokens, nullptr, (hipStream_t)stream);
   int rc = check_launch();
   if (rc) return rc;
   ctx->state = ST_DRAFTED;
   ctx->step_batch = batch;
+  ctx->step_k = k;
   return ORTHRUS_OK;
+}
+
+int orthrus_draft_refine(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                         int32_t* drafts, void* stream) {
+  if (!ctx || !seq_len || !drafts) return ORTHRUS_EINVAL;
+  if (ctx->state != ST_DRAFTED) return ORTHRUS_ESTATE;
+  if (batch != ctx->step_batch) return ORTHRUS_EINVAL;
+  if (ctx->step_k == 0) return ORTHRUS_OK;                 // no block to refine
+  PassInfo P{};
+  P.kind = PASS_DRAFT; P.B = batch; P.A = 0; P.Kx = ctx->step_k; P.p0 = 0; P.len = seq_len;
+  P.refine = 1;
+  set_rm(P);
+  run_pass(ctx, P, nullptr, drafts, ctx->y.K, true, drafts, nullptr, nullptr, (hipStream_t)stream);
+  return check_launch();
+}
+
+int orthrus_draft_block(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
+                        const int32_t* pending, int32_t* drafts, int32_t* ar_tokens,
+                        void* stream) {
+  if (!ctx) return ORTHRUS_EINVAL;
+  return orthrus_draft_block_k(ctx, batch, ctx->y.K, seq_len, pending, drafts, ar_tokens, stream);
 }
 
 int orthrus_verify_accept(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len,
@@ -789,16 +813,16 @@ int orthrus_verify_accept(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_le
   if (ctx->state != ST_DRAFTED) return ORTHRUS_ESTATE;
   if (batch != ctx->step_batch) return ORTHRUS_EINVAL;
   hipStream_t s = (hipStream_t)stream;
-  const int K = ctx->y.K;
+  const int K = ctx->step_k;
   if (K > 0) {
     PassInfo P{};
     P.kind = PASS_VERIFY; P.B = batch; P.A = 0; P.Kx = K; P.p0 = 0; P.len = seq_len;
     set_rm(P);
-    run_pass(ctx, P, nullptr, drafts, K, true, nullptr, ar_tokens, nullptr, s);
+    run_pass(ctx, P, nullptr, drafts, ctx->y.K, true, nullptr, ar_tokens, nullptr, s);
   }
   {
     Tick t(ctx, pass_base(PASS_VERIFY) + R_ACC, s);
-    launch_accept(batch, K, drafts, ar_tokens, accept_len, s);
+    launch_accept(batch, K, ctx->y.K, drafts, ar_tokens, accept_len, s);
   }
   int rc = check_launch();
   if (rc) return rc;
@@ -823,7 +847,7 @@ int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len
   }
   int rc = check_launch();
   if (rc) return rc;
-  for (int b = 0; b < batch; ++b) ctx->bound[b] += ctx->y.K + 1;
+  for (int b = 0; b < batch; ++b) ctx->bound[b] += ctx->step_k + 1;
   ctx->state = ST_IDLE;
   return ORTHRUS_OK;
 }

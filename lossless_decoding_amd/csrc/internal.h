@@ -26,6 +26,8 @@ struct PassInfo {
   int p0;            // prefill: absolute position of block row 0
   int RM;            // draft: first anchor row (B*Kx rounded up to 16)
   const int32_t* len;  // device seq_len[B] (draft / verify)
+  int refine;        // draft pass without anchors whose mask rows take the
+                     // embeddings of the current drafts (iterative denoising)
   __host__ __device__ int rows() const { return kind == PASS_DRAFT ? RM + A * B : B * Kx; }
   __host__ __device__ int tokens_per_seq() const { return A + Kx; }
 };
@@ -105,9 +107,11 @@ void launch_qkv_post(const PassInfo& P, const float* qkv, int hq, int hkv, int h
                      void* ks, void* vs, int kpad, hipStream_t s);
 void launch_lm_reduce(const float2* part, int rows, int nparts, const PassInfo& P, int K,
                       int32_t* drafts, int32_t* ar_tokens, int32_t* pending, hipStream_t s);
-void launch_accept(int B, int K, const int32_t* drafts, const int32_t* ar, int32_t* accept_len,
-                   hipStream_t s);
-void launch_commit(int B, int K, const int32_t* accept_len, const int32_t* ar,
+// K drafts per sequence, stored with row stride ld (drafts [B][ld], ar [B][ld + 1])
+void launch_accept(int B, int K, int ld, const int32_t* drafts, const int32_t* ar,
+                   int32_t* accept_len, hipStream_t s);
+// ld: row stride of drafts [B][ld] and ar [B][ld + 1]
+void launch_commit(int B, int ld, const int32_t* accept_len, const int32_t* ar,
                    const int32_t* drafts, int32_t* seq_len, int32_t* pending,
                    int32_t* commit_start, int32_t* out_tokens, int32_t* out_off, hipStream_t s);
 void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev,

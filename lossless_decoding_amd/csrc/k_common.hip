@@ -36,7 +36,8 @@ void launch_pack_bf16(const uint16_t* src, int N, int K, void* dst, int nb_off, 
 }
 
 // ----------------------------------------------------------- embedding
-// h[row] = E[token] (token rows) or the mask embedding (mask rows); padding
+// h[row] = E[token] (token rows) or the mask embedding (mask rows; in a
+// refining draft pass the embedding of the row's current draft); padding
 // rows get zeros.
 __global__ __launch_bounds__(256) void k_embed(PassInfo P, const int32_t* __restrict__ anchor_tok,
                                                const int32_t* __restrict__ block_tok, int block_ld,
@@ -48,8 +49,14 @@ __global__ __launch_bounds__(256) void k_embed(PassInfo P, const int32_t* __rest
   int tok = 0;
   if (P.kind == PASS_DRAFT) {
     if (r >= P.RM) { kind = 0; tok = anchor_tok[r - P.RM]; }
-    else if (r < P.B * P.Kx) kind = 1;
-    else kind = 2;
+    else if (r < P.B * P.Kx) {
+      kind = 1;
+      if (P.refine) {                   // the mask row takes its current draft's embedding
+        const int b = r / P.Kx;
+        kind = 0;
+        tok = block_tok[(size_t)b * block_ld + (r - b * P.Kx)];
+      }
+    } else kind = 2;
   } else {
     int b = r / P.Kx, i = r - b * P.Kx;
     kind = 0;
@@ -343,25 +350,25 @@ void launch_lm_reduce(const float2* part, int rows, int nparts, const PassInfo& 
 // ------------------------------------------------------------ accept
 // One wave per sequence: lane i compares d_{i+1} with a_i; the accept length
 // is the index of the lowest lane that disagrees (K if none).
-__global__ __launch_bounds__(64) void k_accept(int K, const int32_t* __restrict__ drafts,
+__global__ __launch_bounds__(64) void k_accept(int K, int ld, const int32_t* __restrict__ drafts,
                                                const int32_t* __restrict__ ar,
                                                int32_t* __restrict__ accept_len) {
   int b = blockIdx.x, lane = threadIdx.x;
   bool ne = false;
-  if (lane < K) ne = drafts[(size_t)b * K + lane] != ar[(size_t)b * (K + 1) + lane];
+  if (lane < K) ne = drafts[(size_t)b * ld + lane] != ar[(size_t)b * (ld + 1) + lane];
   unsigned long long mask = __ballot(ne);
   if (lane == 0) accept_len[b] = mask ? (int)__ffsll((long long)mask) - 1 : K;
 }
 
-void launch_accept(int B, int K, const int32_t* drafts, const int32_t* ar, int32_t* accept_len,
-                   hipStream_t s) {
-  hipLaunchKernelGGL(k_accept, dim3(B), dim3(64), 0, s, K, drafts, ar, accept_len);
+void launch_accept(int B, int K, int ld, const int32_t* drafts, const int32_t* ar,
+                   int32_t* accept_len, hipStream_t s) {
+  hipLaunchKernelGGL(k_accept, dim3(B), dim3(64), 0, s, K, ld, drafts, ar, accept_len);
 }
 
 // ------------------------------------------------------------ commit
 // One 256-thread block; thread b handles sequence b.  Output offsets are an
 // exclusive prefix sum of (m_b + 1): a wave scan plus a scan of wave totals.
-__global__ __launch_bounds__(256) void k_commit(int B, int K, const int32_t* __restrict__ acc,
+__global__ __launch_bounds__(256) void k_commit(int B, int ld, const int32_t* __restrict__ acc,
                                                 const int32_t* __restrict__ ar,
                                                 const int32_t* __restrict__ drafts,
                                                 int32_t* __restrict__ seq_len,
@@ -388,19 +395,19 @@ __global__ __launch_bounds__(256) void k_commit(int B, int K, const int32_t* __r
     int n = seq_len[b];
     commit_start[b] = n;
     seq_len[b] = n + 1 + m;
-    int bonus = ar[(size_t)b * (K + 1) + m];
+    int bonus = ar[(size_t)b * (ld + 1) + m];
     pending[b] = bonus;
-    for (int j = 0; j < m; ++j) out_tokens[off + j] = drafts[(size_t)b * K + j];
+    for (int j = 0; j < m; ++j) out_tokens[off + j] = drafts[(size_t)b * ld + j];
     out_tokens[off + m] = bonus;
     out_off[b] = off;
     if (b == B - 1) out_off[B] = off + cnt;
   }
 }
 
-void launch_commit(int B, int K, const int32_t* accept_len, const int32_t* ar,
+void launch_commit(int B, int ld, const int32_t* accept_len, const int32_t* ar,
                    const int32_t* drafts, int32_t* seq_len, int32_t* pending,
                    int32_t* commit_start, int32_t* out_tokens, int32_t* out_off, hipStream_t s) {
-  hipLaunchKernelGGL(k_commit, dim3(1), dim3(256), 0, s, B, K, accept_len, ar, drafts, seq_len,
+  hipLaunchKernelGGL(k_commit, dim3(1), dim3(256), 0, s, B, ld, accept_len, ar, drafts, seq_len,
                      pending, commit_start, out_tokens, out_off);
 }
 

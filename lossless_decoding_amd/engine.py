@@ -89,10 +89,17 @@ class Engine:
                           self.pending.data_ptr(), self.s)
         self.B = B
 
-    def draft(self):
-        C.orthrus_draft_block(self.ctx, self.B, self.seq_len.data_ptr(), self.pending.data_ptr(),
-                              self.drafts.data_ptr() if self.K else None, self.ar.data_ptr(),
-                              self.s)
+    def draft(self, k: int | None = None):
+        """Pass 1 with a block of k <= block_k masks (default block_k)."""
+        C.orthrus_draft_block_k(self.ctx, self.B, self.K if k is None else int(k),
+                                self.seq_len.data_ptr(), self.pending.data_ptr(),
+                                self.drafts.data_ptr() if self.K else None, self.ar.data_ptr(),
+                                self.s)
+
+    def refine(self):
+        """One more denoising pass over the outstanding block (2-step variant)."""
+        C.orthrus_draft_refine(self.ctx, self.B, self.seq_len.data_ptr(), self.drafts.data_ptr(),
+                               self.s)
 
     def verify(self):
         C.orthrus_verify_accept(self.ctx, self.B, self.seq_len.data_ptr(),
@@ -112,15 +119,21 @@ class Engine:
         self.verify()
         self.commit()
 
-    def generate(self, prompts: np.ndarray, n_new: int, planted=None, record=False):
+    def generate(self, prompts: np.ndarray, n_new: int, planted=None, record=False, k_policy=None,
+                 denoise_steps: int = 1):
         """Greedy generation of n_new tokens per sequence (token 1 is the
-        prefill's).  planted: optional [steps][B][K] int32 drafts.  Returns
-        (tokens [B][n_new], per-step records)."""
+        prefill's).  planted: optional [steps][B][K] int32 drafts.  k_policy:
+        optional block size per step (dynamic K): a callable (step index,
+        accept lengths of the previous step or None) -> k <= block_k, e.g. a
+        CertaintyK.  denoise_steps: diffusion passes per block (1 = single-step
+        block projection; 2 = the 2-step iterative denoising variant).
+        Returns (tokens [B][n_new], per-step records)."""
         self.prefill(prompts)
         B = self.B
         outs = [[int(t)] for t in self.pending[:B].cpu().tolist()]
         recs = []
         s = 0
+        last_m = None
         while min(len(o) for o in outs) < n_new:
             n_before = self.seq_len[:B].clone() if record else None
             pl = None
@@ -128,23 +141,46 @@ class Engine:
                 if s >= planted.shape[0]:
                     break
                 pl = torch.as_tensor(planted[s], dtype=torch.int32, device=self.device)
-            self.draft()
+            k = self.K if k_policy is None else int(k_policy(s, last_m))
+            self.draft(k)
+            for _ in range(denoise_steps - 1):
+                self.refine()
             if record:
                 drafted = self.drafts[:B].clone()
             if pl is not None:
                 self.drafts[:B].copy_(pl)
             self.verify()
             self.commit()
+            last_m = self.accept[:B].cpu().numpy()
             off = self.out_off[:B + 1].cpu().numpy()
             C.orthrus_sync_lengths(self.ctx, B, self.seq_len[:B].cpu().numpy())
             tok = self.out_tokens[:off[-1]].cpu().numpy()
             for b in range(B):
                 outs[b].extend(tok[off[b]:off[b + 1]].tolist())
             if record:
-                recs.append(dict(n=n_before.cpu().numpy(), drafted=drafted.cpu().numpy(),
+                recs.append(dict(k=k, n=n_before.cpu().numpy(), drafted=drafted.cpu().numpy(),
                                  drafts=self.drafts[:B].cpu().numpy(),
                                  ar=self.ar[:B].cpu().numpy(), m=self.accept[:B].cpu().numpy(),
                                  commit_start=self.commit_start[:B].cpu().numpy(),
                                  len=self.seq_len[:B].cpu().numpy()))
             s += 1
         return np.array([o[:n_new] for o in outs], np.int32), recs
+
+
+class CertaintyK:
+    """A dynamic-K policy: the pages propose adjusting K to the generation's
+    certainty (openai-hub.net article, "Future Directions", item 1).  Taken
+    here as: the accept lengths of the previous step measure how predictable
+    the continuation is, so the next block holds twice the smallest accept
+    length of the batch plus a margin, clamped to [k_min, k_max]; the first
+    step uses k_max.  Any schedule is lossless (every emitted token is the
+    AR argmax); K only changes how much work a step spends on drafts."""
+
+    def __init__(self, k_max: int, k_min: int = 4, margin: int = 4):
+        self.k_max, self.k_min, self.margin = k_max, min(k_min, k_max), margin
+
+    def __call__(self, step: int, last_m) -> int:
+        if last_m is None or len(last_m) == 0:
+            return self.k_max
+        k = 2 * int(np.min(last_m)) + self.margin
+        return max(self.k_min, min(self.k_max, k))

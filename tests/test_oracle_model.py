@@ -367,3 +367,50 @@ def test_layer_tail_entry_point_matches_the_layer(tiny):
     hm1, om = seq.draft_layer(0, hm, n)
     assert np.array_equal(m.layer_tail(0, hm, om, diffusion=True), hm1)
     assert not np.array_equal(m.layer_tail(0, hm, om, diffusion=False), hm1)
+
+
+@pytest.mark.parametrize("model", ["tiny", "small"])
+def test_any_block_size_schedule_is_lossless(request, model):
+    """Dynamic K (openai-hub.net article, "Future Directions", item 1): a
+    different block size every step, 0 and the full K included, still emits
+    exactly greedy AR decoding, grows the cache by m+1 and accepts m <= k."""
+    shp, w, m = request.getfixturevalue(model)
+    sched = [shp.K, 3, 0, 5, 1, shp.K, 2, 7 % (shp.K + 1), 0, 4]
+    prompt = workloads.prompts(1, 11, shp.V, seed=16)[0]
+    n_new = 40
+    want = m.ar_generate(prompt, n_new)
+    seq = m.seq(11 + n_new + shp.K + 4)
+    pend = seq.prefill(prompt)
+    out = [pend]
+    s = 0
+    while len(out) < n_new:
+        k = sched[s % len(sched)]
+        n = seq.len
+        r = seq.step(pend, k)
+        assert 0 <= r["m"] <= k and seq.len == n + 1 + r["m"]
+        out.extend(r["emitted"].tolist())
+        pend = r["pending"]
+        s += 1
+    assert np.array_equal(np.array(out[:n_new]), want)
+
+
+def test_two_step_denoised_drafts_are_lossless(tiny):
+    """Drafts from a second diffusion pass over the first pass's argmax tokens
+    (the 2-step variant) change only how much is accepted: the output is
+    still greedy AR decoding."""
+    shp, w, m = tiny
+    K = shp.K
+    prompt = workloads.prompts(1, 10, shp.V, seed=17)[0]
+    n_new = 30
+    seq = m.seq(10 + n_new + K + 4)
+    pend = seq.prefill(prompt)
+    out = [pend]
+    while len(out) < n_new:
+        n = seq.len
+        seq.ar_rows(np.array([pend], np.int32), n)
+        _, d1 = seq.draft_rows(n, K)
+        _, d2 = seq.draft_rows(n, K, in_tokens=d1)
+        r = seq.step(pend, K, planted=d2)
+        out.extend(r["emitted"].tolist())
+        pend = r["pending"]
+    assert np.array_equal(np.array(out[:n_new]), m.ar_generate(prompt, n_new))
