@@ -43,14 +43,14 @@
  *    owned by the caller.  The library never allocates or frees device
  *    memory; the sizes of the buffers it needs come from
  *    orthrus_query_sizes().  "stream" is a hipStream_t (NULL = default
- *    stream).  Every call only enqueues work on that stream (prefill and
- *    create also do small host->device copies on it).
+ *    stream).  Every call only enqueues work on that stream (create also
+ *    does a small host->device copy on it).
  *  - Token ids are int32.  Ids outside [0, vocab) are clamped when embedded.
  *  - One context is driven by one stream at a time; calls on a context must
  *    be serialized by the caller.
  *  - Call order per step: draft_block -> verify_accept -> commit_kv
  *    (ORTHRUS_ESTATE otherwise).  The host keeps an upper bound on every
- *    sequence's length (prompt_len, plus block_k + 1 per committed step) and
+ *    sequence's length (max_prompt_len, plus k + 1 per committed step) and
  *    refuses a step that could write past max_ctx (ORTHRUS_ECAPACITY).
  */
 #ifndef ORTHRUS_H
@@ -82,8 +82,8 @@ enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1 };
  * are shared.
  * BF16 models: bf16 weights, bf16 KV cache, fp32 residual stream, fp32
  * accumulation; requires head_dim 128, d_model, n_q_heads*head_dim and
- * ffn_dim multiples of 256, d_model <= 8192, vocab a multiple of 128, and (block_k + 1) * group <= 144 and
- * 32 * group <= 144 (group = n_q_heads / n_kv_heads).
+ * ffn_dim multiples of 256, d_model <= 8192, vocab a multiple of 128, and
+ * (block_k + 1) * group <= 144 (group = n_q_heads / n_kv_heads).
  * F32 models: everything fp32 (small check models). */
 typedef struct orthrus_config {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
@@ -143,12 +143,19 @@ int orthrus_destroy(orthrus_ctx* ctx);
 
 /* AR-view prefill of `batch` prompts (the frozen view builds the cache:
  * opentrain.ai page, abstract).  tokens: device [batch][tokens_stride]
- * int32; prompt_len: HOST [batch], each in [1, tokens_stride].  Writes the
- * cache slots [0, prompt_len), sets seq_len[b] = prompt_len[b] and
- * pending[b] = argmax of the last prompt row (the first generated token).
- * Resets the call-order state.  Errors: EINVAL, ECAPACITY. */
+ * int32; prompt_len: device [batch], each in [1, max_prompt_len] (values
+ * outside are clamped); max_prompt_len: host, in [1, tokens_stride], the
+ * longest prompt.  Writes the cache slots [0, prompt_len), sets seq_len[b] =
+ * prompt_len[b] and pending[b] = argmax of the last prompt row (the first
+ * generated token).  The prompts run through the frozen view in passes of
+ * up to 2048 / max_batch rows per sequence (32 to 256), causal within and
+ * across passes, every sequence to max_prompt_len - 1 (rows past a shorter
+ * prompt land in slots that no later step reads).  Only enqueues work; the
+ * host's length bound of every sequence becomes max_prompt_len.  Resets the
+ * call-order state.  Errors: EINVAL, ECAPACITY. */
 int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int32_t tokens_stride,
-                    const int32_t* prompt_len, int32_t* seq_len, int32_t* pending, void* stream);
+                    const int32_t* prompt_len, int32_t max_prompt_len, int32_t* seq_len,
+                    int32_t* pending, void* stream);
 
 /* Pass 1 (see the top of this file).  seq_len, pending: [batch] (read);
  * drafts: [batch][K] (written); ar_tokens: [batch][K+1], only column 0
@@ -249,6 +256,35 @@ int orthrus_timing_read(orthrus_ctx* ctx, double* ms, int64_t* launches);
  * A pass with more rows than rows_cap writes neither tap (both keep what an
  * earlier pass wrote).  Errors: EINVAL. */
 int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_cap);
+
+/* Sampling at temperature T > 0 with lossless rejection sampling (the
+ * pages: greedy and rejection sampling only, the latter briefly described;
+ * HN item page and atlas.scime.ai page, "Limitations").  temperature 0
+ * (the default) is greedy decoding.  With T > 0, for every later step:
+ *   draft_block   draws each mask row's draft d_i from q_i = softmax(z_i / T)
+ *                 of the diffusion view (orthrus_draft_refine redraws from
+ *                 the refined rows);
+ *   verify_accept takes p_0 = softmax(z / T) of the anchor row and p_i of
+ *                 verify row i; accepts d_i with probability
+ *                 min(1, p_{i-1}(d_i) / q_i(d_i)) in order until the first
+ *                 rejection (accept_len = m); the step's final token is a
+ *                 sample of max(0, p_m - q_{m+1}) renormalised after a
+ *                 rejection, of p_k after k acceptances; ar_tokens[b][0..m)
+ *                 = the accepted drafts, ar_tokens[b][m] = the final token
+ *                 (other columns unspecified);
+ *   commit_kv     unchanged (emits d_1..d_m and ar_tokens[b][m]);
+ *   prefill       the first generated token is a sample of the last prompt
+ *                 row's p.
+ * Each emitted token is distributed as the frozen model's own sample at its
+ * position, whatever the diffusion view drafts (drafts a caller replaces
+ * keep this only if they are draws of q).  Random numbers: Philox4x32-10
+ * keyed by seed, counter (index, sequence, step, purpose), uniform =
+ * (x0 >> 8) * 2^-24 with x0 the first output word; step counts the
+ * committed steps since this call; purposes 1 (draft of mask row i, index
+ * i), 2 (acceptance of draft i, index i, 1-based), 3 (the final token, index
+ * 0), 4 (the prefill's first token, index 0).  Host only; not while a step is
+ * in flight (ESTATE).  Errors: EINVAL (T negative or not finite). */
+int orthrus_set_sampling(orthrus_ctx* ctx, float temperature, uint64_t seed);
 
 /* Per-layer parity taps (optional; NULL disables), for holding the library
  * to a reference one layer at a time from the library's own layer inputs.

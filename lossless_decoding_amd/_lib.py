@@ -17,7 +17,7 @@ ORTHRUS_F32, ORTHRUS_BF16 = 0, 1
 EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_draft_block_k", "orthrus_draft_refine", "orthrus_verify_accept", "orthrus_commit_kv",
-    "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_block_attention_noalloc", "orthrus_attention_workspace",
+    "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_set_sampling", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_block_attention_noalloc", "orthrus_attention_workspace",
     "orthrus_default_attn_chunk", "orthrus_stream_read", "orthrus_gemm_plan",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
@@ -75,7 +75,7 @@ def lib():
         L.orthrus_weight_tensor.argtypes = [cfgp, i32, ctypes.POINTER(u64), ctypes.POINTER(u64)]
         L.orthrus_create.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(vp)]
         L.orthrus_destroy.argtypes = [vp]
-        L.orthrus_prefill.argtypes = [vp, i32, vp, i32, vp, vp, vp, vp]
+        L.orthrus_prefill.argtypes = [vp, i32, vp, i32, vp, i32, vp, vp, vp]
         L.orthrus_draft_block.argtypes = [vp, i32, vp, vp, vp, vp, vp]
         L.orthrus_draft_block_k.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp]
         L.orthrus_draft_refine.argtypes = [vp, i32, vp, vp, vp]
@@ -83,6 +83,7 @@ def lib():
         L.orthrus_commit_kv.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.orthrus_set_debug.argtypes = [vp, vp, vp, i32]
         L.orthrus_set_debug_layers.argtypes = [vp, vp, vp, i32]
+        L.orthrus_set_sampling.argtypes = [vp, ctypes.c_float, ctypes.c_uint64]
         L.orthrus_sync_lengths.argtypes = [vp, i32, vp]
         L.orthrus_timing_enable.argtypes = [vp, ctypes.c_uint32, i32]
         L.orthrus_timing_read.argtypes = [vp, vp, vp]
@@ -133,10 +134,10 @@ def orthrus_destroy(ctx):
     _check("orthrus_destroy", lib().orthrus_destroy(ctx))
 
 
-def orthrus_prefill(ctx, batch, tokens, stride, prompt_len: np.ndarray, seq_len, pending, stream):
-    pl = np.ascontiguousarray(prompt_len, np.int32)
-    _check("orthrus_prefill", lib().orthrus_prefill(ctx, batch, tokens, stride, pl.ctypes.data,
-                                                    seq_len, pending, stream))
+def orthrus_prefill(ctx, batch, tokens, stride, prompt_len, max_prompt_len, seq_len, pending,
+                    stream):
+    _check("orthrus_prefill", lib().orthrus_prefill(ctx, batch, tokens, stride, prompt_len,
+                                                    max_prompt_len, seq_len, pending, stream))
 
 
 def orthrus_draft_block(ctx, batch, seq_len, pending, drafts, ar_tokens, stream):
@@ -167,6 +168,10 @@ def orthrus_commit_kv(ctx, batch, accept_len, ar_tokens, drafts, seq_len, pendin
 
 def orthrus_set_debug(ctx, logits, attn, rows_cap):
     _check("orthrus_set_debug", lib().orthrus_set_debug(ctx, logits, attn, rows_cap))
+
+
+def orthrus_set_sampling(ctx, temperature: float, seed: int):
+    _check("orthrus_set_sampling", lib().orthrus_set_sampling(ctx, temperature, seed))
 
 
 def orthrus_set_debug_layers(ctx, resid, attn32, rows_cap):

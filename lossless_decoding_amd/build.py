@@ -7,7 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liborthrus.so")
-SOURCES = ["api.hip", "k_common.hip", "k_gemm.hip", "k_attn.hip"]
+SOURCES = ["api.hip", "k_common.hip", "k_gemm.hip", "k_attn.hip", "k_sample.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed-fp32 VALU forms are disabled for all device code.

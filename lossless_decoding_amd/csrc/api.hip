@@ -14,7 +14,6 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-constexpr int kPrefillChunk = 32;     // prompt rows per sequence per prefill pass
 constexpr int kAlign = 256;
 
 inline uint64_t al(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -51,7 +50,7 @@ uint64_t canon_offset(const orthrus_config& c, int t) {
 struct Layout {
   // element size, dims
   int esz, L, d, hq, hkv, hd, F, V, K, G, qd, kd, nqkv;
-  int cap, kpad, tmax, rmax, sc, nc, qr_max, ngroups_max;
+  int cap, kpad, tmax, rmax, sc, nc, qr_max, ngroups_max, pchunk;
   int draft_tpw;   // query tiles per wave of every draft-pass attention launch
   bool bf16;
   // packed offsets (bytes)
@@ -60,6 +59,7 @@ struct Layout {
       p_gu, p_down;
   uint64_t packed_bytes;
   // workspace offsets (bytes)
+  uint64_t w_dlog, w_vlog, w_dst, w_vst;   // sampling: logits and row stats of both passes
   uint64_t w_h, w_x, w_qkv, w_q, w_act, w_opart, w_ml, w_parts, w_logits, w_rope, w_i32,
       w_part, w_rpart, w_cnt, cnt_bytes, w_amax, workspace_bytes, part_bytes;
   uint64_t kv_layer_elems, kv_bytes, scr_layer_elems, scratch_bytes;
@@ -120,7 +120,7 @@ int validate(const orthrus_config* c) {
       return ORTHRUS_EINVAL;
     if (c->vocab % 128) return ORTHRUS_EINVAL;
     if (c->d_model > 8192) return ORTHRUS_EINVAL;
-    if ((c->block_k + 1) * G > 144 || kPrefillChunk * G > 144) return ORTHRUS_EINVAL;
+    if ((c->block_k + 1) * G > 144) return ORTHRUS_EINVAL;
   } else if (c->dtype != ORTHRUS_F32) {
     return ORTHRUS_EINVAL;
   }
@@ -135,10 +135,15 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.qd = y.hq * y.hd; y.kd = y.hkv * y.hd; y.nqkv = y.qd + 2 * y.kd;
   y.cap = round_up(c.max_ctx, 64);
   y.kpad = y.K > 0 ? round_up(y.K, 32) : 0;
-  y.tmax = y.K + 1 > kPrefillChunk ? y.K + 1 : kPrefillChunk;
+  // prompt rows per sequence per prefill pass: about 2048 rows per pass
+  // (tall GEMMs, each attention key tile shared by the pass's rows), at
+  // least 32 and at most 256 per sequence
+  y.pchunk = 2048 / c.max_batch;
+  y.pchunk = y.pchunk < 32 ? 32 : (y.pchunk > 256 ? 256 : y.pchunk / 32 * 32);
+  y.tmax = y.K + 1 > y.pchunk ? y.K + 1 : y.pchunk;
   // physical rows: draft passes pad the mask rows to a multiple of 16
   int draft_rows = round_up(c.max_batch * y.K, 16) + c.max_batch;
-  int other_rows = c.max_batch * (y.K > kPrefillChunk ? y.K : kPrefillChunk);
+  int other_rows = c.max_batch * (y.K > y.pchunk ? y.K : y.pchunk);
   y.rmax = draft_rows > other_rows ? draft_rows : other_rows;
   // attention key chunk: fixed per context so that a row's result does not
   // depend on which pass computes it
@@ -226,6 +231,14 @@ void make_layout(const orthrus_config& c, Layout& y) {
     y.part_bytes = 0;
     y.cnt_bytes = 0;
   }
+  // sampling at T > 0: the draft pass's logits (anchor and mask rows) must
+  // outlive the verify pass, so each pass keeps its own, with (max, sum)
+  const uint64_t vrows = (uint64_t)c.max_batch * y.K;
+  const uint64_t drows = (uint64_t)draft_rows;
+  y.w_dlog = take(drows * y.V * 4);
+  y.w_vlog = take(vrows * y.V * 4);
+  y.w_dst = take(drows * 8);
+  y.w_vst = take(vrows * 8);
   y.workspace_bytes = o;
 }
 
@@ -247,6 +260,9 @@ struct orthrus_ctx {
   int state;
   int step_batch;
   int step_k;          // block size of the outstanding step (<= block_k)
+  float temp;          // sampling temperature (0: greedy)
+  uint64_t seed;       // Philox key of the sampling draws
+  uint32_t rng_step;   // Philox counter word of the current step
   std::vector<int64_t> bound;   // host upper bound of every sequence's length
   float* dbg_logits;
   void* dbg_attn;
@@ -310,6 +326,39 @@ void tap_resid(orthrus_ctx* c, int l, const float* h, int rows, hipStream_t s) {
 }
 
 template <typename T> T* W(orthrus_ctx* c, uint64_t off) { return (T*)(c->packed + off); }
+template <typename T> T* S(orthrus_ctx* c, uint64_t off);
+
+SampleArgs sample_args(orthrus_ctx* c, int B, int k) {
+  SampleArgs a{};
+  a.T = c->temp; a.seed = c->seed; a.step = c->rng_step; a.V = c->y.V;
+  a.RM = round_up(B * k, 16);
+  a.dlogits = S<float>(c, c->y.w_dlog); a.vlogits = S<float>(c, c->y.w_vlog);
+  a.dstats = S<float2>(c, c->y.w_dst); a.vstats = S<float2>(c, c->y.w_vst);
+  return a;
+}
+
+// The logits buffer of a pass's LM head when sampling (nullptr: greedy).
+float* sampling_logits(orthrus_ctx* c, const PassInfo& P) {
+  if (!(c->temp > 0.f)) return nullptr;
+  if (P.kind == PASS_DRAFT) return S<float>(c, c->y.w_dlog);
+  if (P.kind == PASS_VERIFY) return S<float>(c, c->y.w_vlog);
+  return nullptr;
+}
+
+// After a sampling pass's LM head: the debug copy of its logits, each row's
+// (max, sum), the draws of a draft pass's mask rows, and for the prefill's
+// last rows the first generated token.
+void sample_after_lm_head(orthrus_ctx* c, const PassInfo& P, const float* slog, int32_t* drafts,
+                          int32_t* pending, hipStream_t s) {
+  const Layout& y = c->y;
+  const int rows = P.rows();
+  if (c->dbg_logits && rows <= c->dbg_rows)
+    (void)hipMemcpyAsync(c->dbg_logits, slog, (uint64_t)rows * y.V * 4, hipMemcpyDeviceToDevice, s);
+  SampleArgs a = sample_args(c, P.B, P.Kx);
+  float2* st = S<float2>(c, P.kind == PASS_DRAFT ? y.w_dst : y.w_vst);
+  launch_sample_rows(a, P, slog, y.V, st, P.kind == PASS_DRAFT ? drafts : nullptr, y.K, s);
+  if (pending) launch_sample_first(a, P.B, P.RM, slog, st, pending, s);
+}
 template <typename T> T* S(orthrus_ctx* c, uint64_t off) { return (T*)(c->ws + off); }
 
 // fp32 GEMM on canonical row-major weights (check models)
@@ -397,11 +446,13 @@ void run_pass_f32(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   GemmOut ol{};
   ol.ep = EP_ARGMAX;
   ol.part = S<float2>(c, y.w_parts);
-  ol.y = S<float>(c, y.w_logits);
+  float* slog = sampling_logits(c, P);
+  ol.y = slog ? slog : S<float>(c, y.w_logits);
   ol.ldy = y.V;
-  if (c->dbg_logits && rows <= c->dbg_rows) { ol.logits = c->dbg_logits; ol.ldl = y.V; }
+  if (!slog && c->dbg_logits && rows <= c->dbg_rows) { ol.logits = c->dbg_logits; ol.ldl = y.V; }
   gemm(c, y.p_lm, 0, x, y.d, rows, y.d, y.V, ol, s);
   launch_lm_reduce(ol.part, rows, 1, P, y.K, drafts, ar, pending, s);
+  if (slog) sample_after_lm_head(c, P, slog, drafts, pending, s);
 }
 
 void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
@@ -545,8 +596,11 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
   g.X = x; g.ldx = y.d;
   g.amax = S<float2>(c, y.w_amax);
   g.Kb = y.K; g.drafts = drafts; g.ar = ar; g.pending = pending;
-  if (c->dbg_logits && rows <= c->dbg_rows) { g.logits = c->dbg_logits; g.ldl = y.V; }
+  float* slog = sampling_logits(c, P);
+  if (slog) { g.logits = slog; g.ldl = y.V; }
+  else if (c->dbg_logits && rows <= c->dbg_rows) { g.logits = c->dbg_logits; g.ldl = y.V; }
   run(g, y.p_lm, 0, rows, y.d, y.V, EP_ARGMAX);
+  if (slog) sample_after_lm_head(c, P, slog, drafts, pending, s);
 }
 
 void run_pass(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
@@ -606,6 +660,7 @@ int orthrus_create(const orthrus_config* cfg, const void* weights, void* packed,
   c->packed = (char*)packed; c->kv = (char*)kv_cache; c->scr = (char*)block_scratch;
   c->ws = (char*)workspace;
   c->state = ST_IDLE; c->step_batch = 0; c->step_k = 0;
+  c->temp = 0.f; c->seed = 0; c->rng_step = 0;
   c->bound.assign(cfg->max_batch, 0);
   c->dbg_logits = nullptr; c->dbg_attn = nullptr; c->dbg_rows = 0;
   c->dbg_resid = nullptr; c->dbg_attn32 = nullptr; c->dbg_lrows = 0;
@@ -707,6 +762,15 @@ int orthrus_set_debug(orthrus_ctx* ctx, float* logits, void* attn, int32_t rows_
   return ORTHRUS_OK;
 }
 
+int orthrus_set_sampling(orthrus_ctx* ctx, float temperature, uint64_t seed) {
+  if (!ctx || !(temperature >= 0.f) || !(temperature <= 1e4f)) return ORTHRUS_EINVAL;
+  if (ctx->state != ST_IDLE) return ORTHRUS_ESTATE;
+  ctx->temp = temperature;
+  ctx->seed = seed;
+  ctx->rng_step = 0;
+  return ORTHRUS_OK;
+}
+
 int orthrus_set_debug_layers(orthrus_ctx* ctx, float* resid, float* attn32, int32_t rows_cap) {
   if (!ctx || rows_cap < 0) return ORTHRUS_EINVAL;
   if ((resid || attn32) && rows_cap == 0) return ORTHRUS_EINVAL;
@@ -718,44 +782,35 @@ int orthrus_set_debug_layers(orthrus_ctx* ctx, float* resid, float* attn32, int3
 }
 
 int orthrus_prefill(orthrus_ctx* ctx, int32_t batch, const int32_t* tokens, int32_t tokens_stride,
-                    const int32_t* prompt_len, int32_t* seq_len, int32_t* pending, void* stream) {
+                    const int32_t* prompt_len, int32_t max_prompt_len, int32_t* seq_len,
+                    int32_t* pending, void* stream) {
   if (!ctx || !tokens || !prompt_len || !seq_len || !pending) return ORTHRUS_EINVAL;
   if (batch < 1 || batch > ctx->cfg.max_batch || tokens_stride < 1) return ORTHRUS_EINVAL;
-  int pmax = 0;
-  for (int b = 0; b < batch; ++b) {
-    if (prompt_len[b] < 1 || prompt_len[b] > tokens_stride) return ORTHRUS_EINVAL;
-    if (prompt_len[b] > pmax) pmax = prompt_len[b];
-  }
+  const int pmax = max_prompt_len;
+  if (pmax < 1 || pmax > tokens_stride) return ORTHRUS_EINVAL;
   // prefill rows of every sequence run to pmax-1 (rows past a sequence's own
   // prompt compute values that land in slots no later step reads)
   if (pmax + 1 > ctx->y.cap || pmax > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
   hipStream_t s = (hipStream_t)stream;
   const Layout& y = ctx->y;
-  int32_t* i32 = S<int32_t>(ctx, y.w_i32);
-  int32_t* plen_dev = i32;
-  int32_t* last_tok = i32 + ctx->cfg.max_batch;
-  int rc = hip_ok(hipMemcpyAsync(plen_dev, prompt_len, sizeof(int32_t) * batch,
-                                 hipMemcpyHostToDevice, s));
-  if (rc) return rc;
-  rc = hip_ok(hipStreamSynchronize(s));
-  if (rc) return rc;
-  for (int p0 = 0; p0 < pmax - 1; p0 += kPrefillChunk) {
+  int32_t* last_tok = S<int32_t>(ctx, y.w_i32) + ctx->cfg.max_batch;
+  for (int p0 = 0; p0 < pmax - 1; p0 += y.pchunk) {
     PassInfo P{};
     P.kind = PASS_PREFILL; P.B = batch; P.A = 0;
-    P.Kx = (pmax - 1 - p0) < kPrefillChunk ? (pmax - 1 - p0) : kPrefillChunk;
+    P.Kx = (pmax - 1 - p0) < y.pchunk ? (pmax - 1 - p0) : y.pchunk;
     P.p0 = p0; P.len = nullptr;
     set_rm(P);
     run_pass(ctx, P, nullptr, tokens, tokens_stride, false, nullptr, nullptr, nullptr, s);
   }
-  launch_prefill_tail(batch, tokens, tokens_stride, plen_dev, seq_len, last_tok, s);
+  launch_prefill_tail(batch, tokens, tokens_stride, prompt_len, pmax, seq_len, last_tok, s);
   PassInfo P{};
   P.kind = PASS_DRAFT; P.B = batch; P.A = 1; P.Kx = 0; P.p0 = 0; P.len = seq_len;
   set_rm(P);
   run_pass(ctx, P, last_tok, nullptr, 0, true, nullptr, nullptr, pending, s);
   launch_len_add(batch, seq_len, 1, s);
-  rc = check_launch();
+  int rc = check_launch();
   if (rc) return rc;
-  for (int b = 0; b < ctx->cfg.max_batch; ++b) ctx->bound[b] = b < batch ? prompt_len[b] : 0;
+  for (int b = 0; b < ctx->cfg.max_batch; ++b) ctx->bound[b] = b < batch ? pmax : 0;
   ctx->state = ST_IDLE;
   return ORTHRUS_OK;
 }
@@ -822,7 +877,11 @@ int orthrus_verify_accept(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_le
   }
   {
     Tick t(ctx, pass_base(PASS_VERIFY) + R_ACC, s);
-    launch_accept(batch, K, ctx->y.K, drafts, ar_tokens, accept_len, s);
+    if (ctx->temp > 0.f)
+      launch_spec_accept(sample_args(ctx, batch, K), batch, K, ctx->y.K, drafts, ar_tokens,
+                         accept_len, s);
+    else
+      launch_accept(batch, K, ctx->y.K, drafts, ar_tokens, accept_len, s);
   }
   int rc = check_launch();
   if (rc) return rc;
@@ -848,6 +907,7 @@ int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len
   int rc = check_launch();
   if (rc) return rc;
   for (int b = 0; b < batch; ++b) ctx->bound[b] += ctx->step_k + 1;
+  ctx->rng_step += 1;
   ctx->state = ST_IDLE;
   return ORTHRUS_OK;
 }

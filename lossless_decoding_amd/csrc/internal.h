@@ -114,7 +114,9 @@ void launch_accept(int B, int K, int ld, const int32_t* drafts, const int32_t* a
 void launch_commit(int B, int ld, const int32_t* accept_len, const int32_t* ar,
                    const int32_t* drafts, int32_t* seq_len, int32_t* pending,
                    int32_t* commit_start, int32_t* out_tokens, int32_t* out_off, hipStream_t s);
-void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev,
+// seq_len[b] = prompt length - 1 (the length clamped to [1, pmax]) and
+// last_tok[b] = the prompt's last token
+void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev, int pmax,
                          int32_t* seq_len, int32_t* last_tok, hipStream_t s);
 void launch_len_add(int B, int32_t* seq_len, int add, hipStream_t s);
 
@@ -184,6 +186,30 @@ struct AttnArgs {
   int tpw;          // query tiles per wave, 1 or 2 (0: the launcher chooses from the grid size)
 };
 void launch_attention_bf16(const AttnArgs& a, hipStream_t s);
+
+// Sampling at T > 0 (k_sample.hip).  dlogits / dstats: the draft pass's
+// logits [rows][V] and per-row (max, weight sum); vlogits / vstats: the
+// verify pass's; RM: the draft pass's first anchor row.
+struct SampleArgs {
+  float T;
+  uint64_t seed;
+  uint32_t step;
+  int V, RM;
+  const float* dlogits; const float* vlogits;
+  const float2* dstats; const float2* vstats;
+};
+// per row of pass P: (max, weight sum) into stats; the mask rows of a draft
+// pass also draw their drafts (drafts [B][Kb])
+void launch_sample_rows(const SampleArgs& s, const PassInfo& P, const float* logits, int ld,
+                        float2* stats, int32_t* drafts, int Kb, hipStream_t st);
+// the first generated token after a prefill: a sample of each sequence's
+// anchor row RM + b (its stats already computed)
+void launch_sample_first(const SampleArgs& s, int B, int RM, const float* logits,
+                         const float2* stats, int32_t* pending, hipStream_t st);
+// acceptance of the K drafts and the final token, per sequence: accept_len,
+// ar[b][0..m) = the accepted drafts, ar[b][m] = the final token
+void launch_spec_accept(const SampleArgs& s, int B, int K, int ld_tok, const int32_t* drafts,
+                        int32_t* ar, int32_t* accept_len, hipStream_t st);
 // number of query row groups of a pass: a workgroup's four waves own tpw
 // 16-row query tiles each
 __host__ __device__ inline int attn_row_groups(int qr, int tpw) {

@@ -413,19 +413,20 @@ void launch_commit(int B, int ld, const int32_t* accept_len, const int32_t* ar,
 
 // ----------------------------------------------------- prefill helpers
 __global__ void k_prefill_tail(int B, const int32_t* __restrict__ tokens, int ld,
-                               const int32_t* __restrict__ plen, int32_t* __restrict__ seq_len,
-                               int32_t* __restrict__ last_tok) {
+                               const int32_t* __restrict__ plen, int pmax,
+                               int32_t* __restrict__ seq_len, int32_t* __restrict__ last_tok) {
   int b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= B) return;
   int p = plen[b];
+  p = p < 1 ? 1 : (p > pmax ? pmax : p);
   seq_len[b] = p - 1;
   last_tok[b] = tokens[(size_t)b * ld + p - 1];
 }
 
-void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev,
+void launch_prefill_tail(int B, const int32_t* tokens, int ld, const int32_t* plen_dev, int pmax,
                          int32_t* seq_len, int32_t* last_tok, hipStream_t s) {
   hipLaunchKernelGGL(k_prefill_tail, dim3((B + 63) / 64), dim3(64), 0, s, B, tokens, ld, plen_dev,
-                     seq_len, last_tok);
+                     pmax, seq_len, last_tok);
 }
 
 __global__ void k_len_add(int B, int32_t* seq_len, int add) {

@@ -76,6 +76,10 @@ class Engine:
     def set_debug(self, logits: torch.Tensor | None, attn: torch.Tensor | None, rows: int):
         C.orthrus_set_debug(self.ctx, _ptr(logits), _ptr(attn), rows)
 
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """T > 0: sampling with lossless rejection sampling; 0: greedy."""
+        C.orthrus_set_sampling(self.ctx, float(temperature), int(seed))
+
     def set_debug_layers(self, resid: torch.Tensor | None, attn32: torch.Tensor | None, rows: int):
         C.orthrus_set_debug_layers(self.ctx, _ptr(resid), _ptr(attn32), rows)
 
@@ -84,9 +88,10 @@ class Engine:
         B, P = prompts.shape
         plen = np.full(B, P, np.int32) if prompt_len is None else np.asarray(prompt_len, np.int32)
         tok = torch.from_numpy(prompts).to(self.device)
-        self._prompt_dev = tok
-        C.orthrus_prefill(self.ctx, B, tok.data_ptr(), P, plen, self.seq_len.data_ptr(),
-                          self.pending.data_ptr(), self.s)
+        pl = torch.from_numpy(np.ascontiguousarray(plen)).to(self.device)
+        self._prompt_dev = (tok, pl)
+        C.orthrus_prefill(self.ctx, B, tok.data_ptr(), P, pl.data_ptr(), int(plen.max()),
+                          self.seq_len.data_ptr(), self.pending.data_ptr(), self.s)
         self.B = B
 
     def draft(self, k: int | None = None):

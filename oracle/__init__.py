@@ -98,6 +98,15 @@ def _configure(L):
     L.oc_draft_layer.argtypes = [vp, vp, i32, F64P, i32, i32, i32, vp]
     L.oc_final.argtypes = [vp, F64P, i32, vp, vp]
     L.oc_layer_tail.argtypes = [vp, i32, i32, F64P, F64P, i32]
+    U32P = np.ctypeslib.ndpointer(dtype=np.uint32, flags="C_CONTIGUOUS")
+    L.oc_philox4x32_10.argtypes = [U32P, U32P, U32P]
+    L.oc_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
+                             ctypes.c_uint32]
+    L.oc_uniform.restype = dbl
+    L.oc_draw.argtypes = [F64P, i32, dbl]
+    L.oc_sample_logits.argtypes = [F64P, i32, dbl, dbl]
+    L.oc_spec_accept.argtypes = [F64P, F64P, I32P, i32, i32, dbl, F64P, dbl,
+                                 ctypes.POINTER(ctypes.c_int32)]
     return L
 
 
@@ -187,6 +196,40 @@ def attention_many(q, K, V):
     out = np.empty_like(q)
     lib().oc_attention_many(q, K, V, q.shape[0], K.shape[0], q.shape[1], out)
     return out
+
+
+def philox4x32_10(ctr, key):
+    c = np.ascontiguousarray(ctr, np.uint32)
+    k = np.ascontiguousarray(key, np.uint32)
+    out = np.zeros(4, np.uint32)
+    lib().oc_philox4x32_10(c, k, out)
+    return out
+
+
+def uniform(seed: int, step: int, purpose: int, index: int, seq: int) -> float:
+    return lib().oc_uniform(seed, step, purpose, index, seq)
+
+
+def draw(w, u: float) -> int:
+    w = np.ascontiguousarray(w, np.float64)
+    return lib().oc_draw(w, w.size, u)
+
+
+def sample_logits(z, T: float, u: float) -> int:
+    z = np.ascontiguousarray(z, np.float64)
+    return lib().oc_sample_logits(z, z.size, T, u)
+
+
+def spec_accept(pz, qz, d, T: float, ua, uf: float):
+    """(m, final token) of one sequence: pz [K+1, V], qz [K, V], drafts d [K]."""
+    pz = np.ascontiguousarray(pz, np.float64)
+    qz = np.ascontiguousarray(qz, np.float64)
+    d = np.ascontiguousarray(d, np.int32)
+    ua = np.ascontiguousarray(ua, np.float64)
+    K, V = qz.shape
+    tok = ctypes.c_int32()
+    m = lib().oc_spec_accept(pz, qz, d, K, V, T, ua, uf, ctypes.byref(tok))
+    return m, tok.value
 
 
 def silu(x):

@@ -678,3 +678,100 @@ int oc_generate(const oc_model* m, const int32_t* prompt, int P, int n_new, int 
   oc_seq_free(s);
   return steps;
 }
+
+/* ------------------------------------------------------ sampling at T > 0
+ * The pages say only that T > 0 relies on rejection sampling (HN item page
+ * and atlas.scime.ai page, "Limitations").  The rule followed is the
+ * standard speculative-sampling one: drafts are draws of the draft
+ * distribution q; draft i is accepted with probability
+ * min(1, p_{i-1}(d_i) / q_i(d_i)); at the first rejection the final token is
+ * a draw of max(0, p - q) renormalised, after K acceptances a draw of p_K.
+ * Distributions are softmax(z / T) of the logits. */
+
+/* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+ * easy as 1, 2, 3", SC'11): ten rounds on the 128-bit counter, the key
+ * bumped by the Weyl constants between rounds. */
+void oc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    k0 += 0x9E3779B9u; k1 += 0xBB67AE85u;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The uniform in [0, 1) a draw of (purpose, index) of sequence seq at step
+ * uses: counter (index, seq, step, purpose) under key seed; 24 bits of the
+ * first output word. */
+double oc_uniform(uint64_t seed, uint32_t step, uint32_t purpose, uint32_t index, uint32_t seq) {
+  uint32_t ctr[4] = {index, seq, step, purpose}, key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  oc_philox4x32_10(ctr, key, out);
+  return (double)(out[0] >> 8) / 16777216.0;
+}
+
+/* softmax(z / T) of n logits into prob (float64, index-order sum). */
+void oc_softmax_t(const double* z, int n, double T, double* prob) {
+  double m = -INFINITY, s = 0.0;
+  for (int j = 0; j < n; ++j) if (z[j] > m) m = z[j];
+  for (int j = 0; j < n; ++j) { prob[j] = exp((z[j] - m) / T); s += prob[j]; }
+  for (int j = 0; j < n; ++j) prob[j] /= s;
+}
+
+/* A draw of the (unnormalised) weights w[0..n) with uniform u: the first j
+ * whose running sum in index order exceeds u * sum(w); -1 if all are 0. */
+int oc_draw(const double* w, int n, double u) {
+  double s = 0.0;
+  for (int j = 0; j < n; ++j) s += w[j];
+  if (!(s > 0.0)) return -1;
+  double t = u * s, acc = 0.0;
+  int last = -1;
+  for (int j = 0; j < n; ++j) {
+    if (!(w[j] > 0.0)) continue;
+    last = j;
+    acc += w[j];
+    if (acc > t) return j;
+  }
+  return last;
+}
+
+/* A draw of softmax(z / T) with uniform u. */
+int oc_sample_logits(const double* z, int n, double T, double u) {
+  double* p = (double*)malloc(sizeof(double) * n);
+  oc_softmax_t(z, n, T, p);
+  int j = oc_draw(p, n, u);
+  free(p);
+  return j;
+}
+
+/* Acceptance of one sequence's K drafts and its final token.  pz: the AR
+ * logits [K+1][V] (p_0 from the anchor row, p_i from verify row i); qz:
+ * the draft logits [K][V] (q_1..q_K); d: the drafts; ua[i]: the uniform of
+ * draft i+1's test; uf: the final token's.  Returns m; *tok = the final
+ * token. */
+int oc_spec_accept(const double* pz, const double* qz, const int32_t* d, int K, int V, double T,
+                   const double* ua, double uf, int32_t* tok) {
+  double* p = (double*)malloc(sizeof(double) * V);
+  double* q = (double*)malloc(sizeof(double) * V);
+  int m = 0;
+  for (; m < K; ++m) {
+    if (d[m] < 0 || d[m] >= V) break;
+    oc_softmax_t(pz + (size_t)m * V, V, T, p);
+    oc_softmax_t(qz + (size_t)m * V, V, T, q);
+    if (!(ua[m] < p[d[m]] / q[d[m]])) break;
+  }
+  oc_softmax_t(pz + (size_t)m * V, V, T, p);
+  if (m < K) {
+    oc_softmax_t(qz + (size_t)m * V, V, T, q);
+    for (int j = 0; j < V; ++j) q[j] = p[j] > q[j] ? p[j] - q[j] : 0.0;
+    int j = oc_draw(q, V, uf);
+    *tok = j >= 0 ? j : oc_draw(p, V, uf);
+  } else {
+    *tok = oc_draw(p, V, uf);
+  }
+  free(p); free(q);
+  return m;
+}

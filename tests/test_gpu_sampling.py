@@ -1,0 +1,194 @@
+"""Sampling at T > 0 with lossless rejection sampling (HN item page and
+atlas.scime.ai page, "Limitations"; orthrus_set_sampling).
+
+* Parity of the sampler: on the GPU's own logits (debug tap) and the same
+  Philox4x32-10 uniforms (the oracle implements the generator itself), the
+  oracle's draws and its acceptance rule give the GPU's drafts, accept
+  lengths and final tokens; a mismatch is allowed only where the uniform
+  lies within 1e-5 of a decision boundary (fp32 against fp64 sums), and is
+  counted.
+* Distribution: the first token each step emits must follow the AR
+  distribution p_0 = softmax(z_anchor / T) whatever the diffusion view
+  drafts.  256 sequences share one prompt (greedy prefill), each takes one
+  sampled step with its own counters; 40 seeds give 10240 draws, tested by
+  chi-square against p_0 (from the oracle's fp64 anchor logits) -- and,
+  to show the test can tell the two apart, against the first draft's q_1."""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+
+import oracle
+from synth import workloads
+from tests import gpu_util as U
+
+pytestmark = pytest.mark.gpu
+BOUND = 1e-5
+
+
+def probs(z, T):
+    z = np.asarray(z, np.float64)
+    p = np.exp((z - z.max()) / T)
+    return p / p.sum()
+
+
+def check_draw(gpu_tok, z, T, u):
+    """0 if the oracle's draw equals the GPU's, 1 for an allowed boundary
+    case (u within BOUND of the GPU token's CDF interval)."""
+    if oracle.sample_logits(z, T, u) == gpu_tok:
+        return 0
+    cdf = np.cumsum(probs(z, T))
+    lo = cdf[gpu_tok - 1] if gpu_tok else 0.0
+    assert lo - BOUND <= u <= cdf[gpu_tok] + BOUND, (gpu_tok, u, lo, cdf[gpu_tok])
+    return 1
+
+
+def check_accept(pz, qz, d, T, ua, uf, gm, gtok):
+    """0 if the oracle's acceptance gives the GPU's (m, final token), 1 for
+    an allowed boundary case: the first differing acceptance test has its
+    uniform within BOUND of p/q, or (same m) the final draw's uniform lies
+    within BOUND of the GPU token's CDF interval."""
+    m, tok = oracle.spec_accept(pz, qz, d, T, ua, uf)
+    if (m, tok) == (gm, gtok):
+        return 0
+    if m != gm:
+        i = min(m, gm)
+        r = probs(pz[i], T)[d[i]] / probs(qz[i], T)[d[i]]
+        assert abs(ua[i] - r) < BOUND, (m, gm, ua[i], r)
+        return 1
+    w = probs(pz[m], T)
+    if m < len(d):
+        w = np.maximum(w - probs(qz[m], T), 0.0)
+    cdf = np.cumsum(w) / w.sum()
+    lo = cdf[gtok - 1] if gtok else 0.0
+    assert lo - BOUND <= uf <= cdf[gtok] + BOUND, (tok, gtok, uf)
+    return 1
+
+
+def test_tiny_sampler_matches_oracle():
+    sh = workloads.SHAPES["tiny"]
+    K, V, B, T, seed = sh["K"], sh["V"], 2, 0.8, 1234
+    eng = U.engine("tiny", max_batch=B, max_ctx=400)
+    RA = U.anchor_row(K, B)
+    rows = RA + B
+    lg = torch.zeros(rows, V, device="cuda")
+    eng.set_debug(lg, None, rows)
+    eng.set_sampling(T, seed)
+    prompt = workloads.prompts(B, 40, V, seed=51)
+    eng.prefill(prompt)
+    torch.cuda.synchronize()
+    f64 = lambda t: t.cpu().numpy().astype(np.float64)
+    events = 0
+    pre = f64(lg[:B])                  # the prefill's last pass: one row per sequence
+    for b in range(B):
+        events += check_draw(int(eng.pending[b]), pre[b], T, oracle.uniform(seed, 0, 4, 0, b))
+    accepted = 0
+    for step in range(8):
+        n = eng.seq_len[:B].cpu().numpy().copy()
+        eng.draft()
+        torch.cuda.synchronize()
+        gd = f64(lg)
+        drafts = eng.drafts[:B].cpu().numpy()
+        for b in range(B):
+            for i in range(K):
+                u = oracle.uniform(seed, step, 1, i, b)
+                events += check_draw(int(drafts[b, i]), gd[b * K + i], T, u)
+        eng.verify()
+        torch.cuda.synchronize()
+        gv = f64(lg[:B * K])
+        ar = eng.ar[:B].cpu().numpy()
+        acc = eng.accept[:B].cpu().numpy()
+        for b in range(B):
+            pz = np.concatenate([gd[RA + b:RA + b + 1], gv[b * K:(b + 1) * K]])
+            qz = gd[b * K:(b + 1) * K]
+            ua = [oracle.uniform(seed, step, 2, i + 1, b) for i in range(K)]
+            uf = oracle.uniform(seed, step, 3, 0, b)
+            events += check_accept(pz, qz, drafts[b], T, ua, uf, int(acc[b]), int(ar[b, acc[b]]))
+            assert np.array_equal(ar[b, :acc[b]], drafts[b, :acc[b]])
+            accepted += int(acc[b])
+        eng.commit()
+        torch.cuda.synchronize()
+        assert (eng.seq_len[:B].cpu().numpy() == n + 1 + acc).all()
+        assert (eng.pending[:B].cpu().numpy() == ar[np.arange(B), acc]).all()
+    assert events <= 2, events
+    print(f"sampler parity: {8 * B} steps, {accepted} drafts accepted, {events} boundary events",
+          flush=True)
+
+
+def test_tiny_first_emitted_token_follows_p0():
+    sh = workloads.SHAPES["tiny"]
+    K, V, B, T = sh["K"], sh["V"], 256, 0.5
+    prompt = workloads.prompts(1, 24, V, seed=52)
+    m = U.oracle_model("tiny")
+    seq = m.seq(64)
+    pend = seq.prefill(prompt[0])
+    n = seq.len
+    za, _ = seq.ar_rows(np.array([pend], np.int32), n)        # anchor logits at slot n
+    zq, _ = seq.draft_rows(n, K)                              # the mask rows' logits
+    p0, q1 = probs(za[0], T), probs(zq[0], T)
+    eng = U.engine("tiny", max_batch=B, max_ctx=64)
+    counts = np.zeros(V)
+    acc_steps = 0
+    trials = 40
+    for t in range(trials):
+        eng.set_sampling(0.0, 0)
+        eng.prefill(np.repeat(prompt, B, axis=0))             # greedy prefill: one shared state
+        eng.set_sampling(T, 1000 + t)
+        eng.draft(); eng.verify(); eng.commit()
+        off = eng.out_off[:B + 1].cpu().numpy()
+        tok = eng.out_tokens[:off[-1]].cpu().numpy()
+        counts += np.bincount(tok[off[:-1]], minlength=V)
+        acc_steps += int((eng.accept[:B].cpu().numpy() > 0).sum())
+    N = counts.sum()
+    assert N == trials * B
+    assert int(eng.pending[0]) >= 0
+
+    def chi2_p(pexp):
+        e = pexp * N
+        big = e >= 5
+        obs = np.append(counts[big], counts[~big].sum())
+        exp = np.append(e[big], e[~big].sum())
+        keep = exp > 0
+        stat = ((obs[keep] - exp[keep]) ** 2 / exp[keep]).sum()
+        return stats.chi2.sf(stat, keep.sum() - 1)
+
+    p_ok, p_q = chi2_p(p0), chi2_p(q1)
+    print(f"first-token chi-square: p-value {p_ok:.3g} against p_0, {p_q:.3g} against q_1; "
+          f"{acc_steps} of {int(N)} steps accepted a draft (expected rate "
+          f"{np.minimum(p0, q1).sum():.3f})", flush=True)
+    assert p_ok > 1e-3
+    assert p_q < 1e-6
+    assert abs(acc_steps / N - np.minimum(p0, q1).sum()) < 0.03
+
+
+def test_small_bf16_sampling_steps_are_consistent():
+    """bf16 kernels with T > 0: drafts are the oracle's draws on the GPU's
+    logits, every step commits m + 1 tokens and emits the accepted drafts."""
+    sh = workloads.SHAPES["small"]
+    K, V, B, T, seed = sh["K"], sh["V"], 2, 1.0, 99
+    eng = U.engine("small", max_batch=B, max_ctx=512)
+    RA = U.anchor_row(K, B)
+    lg = torch.zeros(RA + B, V, device="cuda")
+    eng.set_debug(lg, None, RA + B)
+    eng.set_sampling(T, seed)
+    eng.prefill(workloads.prompts(B, 20, V, seed=53))
+    events = 0
+    for step in range(4):
+        n = eng.seq_len[:B].cpu().numpy().copy()
+        eng.draft()
+        torch.cuda.synchronize()
+        gd = lg.cpu().numpy().astype(np.float64)
+        drafts = eng.drafts[:B].cpu().numpy()
+        for b in range(B):
+            for i in range(K):
+                events += check_draw(int(drafts[b, i]), gd[b * K + i], T,
+                                     oracle.uniform(seed, step, 1, i, b))
+        eng.verify(); eng.commit()
+        torch.cuda.synchronize()
+        acc = eng.accept[:B].cpu().numpy()
+        assert (eng.seq_len[:B].cpu().numpy() == n + 1 + acc).all()
+        off = eng.out_off[:B + 1].cpu().numpy()
+        tok = eng.out_tokens[:off[-1]].cpu().numpy()
+        for b in range(B):
+            assert np.array_equal(tok[off[b]:off[b] + acc[b]], drafts[b, :acc[b]])
+    assert events <= 2
