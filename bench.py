@@ -347,6 +347,17 @@ def cpu_baseline(sh, wl, mean_tokens_per_step):
     }
 
 
+def gemm_label(plan, ep, M, N, K):
+    """The kernel instantiation a GEMM launch runs (from the library's plan)."""
+    sp = "true" if plan["split"] else "false"
+    if plan["form"] == 0:
+        name = f"k_gemm_bf16<{plan['MT']}, {ep}, {plan['WV']}, {sp}, {plan['CT']}>"
+    else:
+        two = "true" if plan["form"] == 2 else "false"
+        name = f"k_gemm_rows<{plan['CT']}, {ep}, {sp}, {two}>"
+    return f"{name} (M={M}, N={N}, K={K}, {plan['workgroups']} workgroups)"
+
+
 def run_workload(name, S, W, args, headline):
     import numpy as np
     import torch
@@ -537,9 +548,7 @@ def run_workload(name, S, W, args, headline):
             "launches": at_n, "achieved_GBps": round(at_ach, 1),
             "frac": round(at_ach / HBM_PEAK_GBS, 4)},
         "gate_up_draft": {
-            "kernel": (f"k_gemm_bf16<{gu_plan['MT']}, EP_SWIGLU, {gu_plan['WV']}, "
-                       f"{'true' if gu_plan['split'] else 'false'}, {gu_plan['CT']}> (M={M1}, "
-                       f"N={2 * sh['F']}, K={sh['d']}, {gu_plan['workgroups']} workgroups)"),
+            "kernel": gemm_label(gu_plan, "EP_SWIGLU", M1, 2 * sh["F"], sh["d"]),
             "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
             "launches": gu_n, "achieved_GBps": round(gu_ach, 1),
             "hbm_frac": round(gu_ach / HBM_PEAK_GBS, 4),

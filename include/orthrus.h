@@ -355,9 +355,12 @@ int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n
  * rows (plus m2 rows of a second weight segment, as the draft pass's
  * projections have), n output features and k inputs, with epilogue 1
  * (residual), 2 (SwiGLU), 3 (LM-head argmax) or 4 (Q/K/V + QK-norm + RoPE).
- * plan (host, 5 ints): row tiles of 16 per workgroup, waves per workgroup,
- * 1 if K is split over workgroups (8 slices), 16-column tiles per wave,
- * workgroups.  Host only.  Errors: EINVAL. */
+ * plan (host, 6 ints): row tiles of 16 per workgroup, waves per workgroup,
+ * 1 if K is split over workgroups (8 slices), 16-column tiles per wave
+ * (column-split form) or per workgroup (row-split form), workgroups, and
+ * the form: 0 = column-split (k_gemm_bf16: the waves of a workgroup split
+ * its columns), 1 = row-split (k_gemm_rows: the waves split its rows), 2 =
+ * row-split with two weight segments.  Host only.  Errors: EINVAL. */
 int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, int32_t epilogue,
                       int32_t* plan);
 

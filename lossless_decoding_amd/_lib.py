@@ -230,10 +230,10 @@ EP_RESID, EP_SWIGLU, EP_ARGMAX, EP_QKV = 1, 2, 3, 4
 
 def orthrus_gemm_plan(m, m2, n, k, epilogue) -> dict:
     """The launch shape of a bf16 GEMM (see include/orthrus.h)."""
-    plan = np.zeros(5, np.int32)
+    plan = np.zeros(6, np.int32)
     _check("orthrus_gemm_plan", lib().orthrus_gemm_plan(m, m2, n, k, epilogue, plan.ctypes.data))
     return dict(MT=int(plan[0]), WV=int(plan[1]), split=bool(plan[2]), CT=int(plan[3]),
-                workgroups=int(plan[4]))
+                workgroups=int(plan[4]), form=int(plan[5]))
 
 
 def orthrus_default_attn_chunk(max_batch, max_ctx, n_kv_heads) -> int:

@@ -198,10 +198,12 @@ void make_layout(const orthrus_config& c, Layout& y) {
   o = 0;
   int xw = y.d > y.qd ? y.d : y.qd;
   y.w_h = take((uint64_t)y.rmax * y.d * 4);
-  y.w_x = take((uint64_t)y.rmax * xw * E);
+  // bf16 GEMM inputs are kept in fragment order: whole 16-row tiles
+  const uint64_t rows16 = (uint64_t)(y.rmax + 15) / 16 * 16;
+  y.w_x = take(rows16 * xw * E);
   y.w_qkv = y.bf16 ? take(0) : take((uint64_t)y.rmax * y.nqkv * 4);
   y.w_q = take((uint64_t)y.rmax * y.qd * E);
-  y.w_act = take((uint64_t)y.rmax * y.F * E);
+  y.w_act = take(rows16 * y.F * E);
   uint64_t part_rows = (uint64_t)c.max_batch * y.hkv * (y.nc + 1) * y.qr_max;
   y.w_opart = y.bf16 ? take(part_rows * y.hd * 4) : take(0);
   y.w_ml = y.bf16 ? take(part_rows * 2 * 4) : take(0);
@@ -225,7 +227,9 @@ void make_layout(const orthrus_config& c, Layout& y) {
     // completion counters of the split-K GEMM column groups (+1 grid counter)
     y.cnt_bytes = (rgroups * y.ngroups_max + 1) * 4;
     y.w_cnt = take(y.cnt_bytes);
-    y.w_amax = take((uint64_t)y.rmax * (y.V / 128) * 8);
+    // per-row (value, index) partials of the LM head's column groups (at
+    // least 64 columns each)
+    y.w_amax = take((uint64_t)y.rmax * ((y.V + 63) / 64) * 8);
   } else {
     y.w_part = y.w_rpart = y.w_cnt = y.w_amax = take(0);
     y.part_bytes = 0;
@@ -544,7 +548,8 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
     a.P = P; a.q = q; a.kc = kc; a.vc = vc; a.cap = y.cap; a.ks = ks; a.vs = vs;
     a.kpad = y.kpad; a.hq = y.hq; a.hkv = y.hkv; a.hd = y.hd; a.sc = y.sc; a.nc = y.nc;
     a.qr_max = y.qr_max; a.opart = S<float>(c, y.w_opart); a.ml = S<float>(c, y.w_ml);
-    a.out = x; a.fixed_ctx = -1; a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
+    a.out = x; a.out_kb = y.qd / 32;   // the O projection's input, fragment order
+    a.fixed_ctx = -1; a.block_len = (P.kind == PASS_DRAFT) ? P.Kx : 0;
     a.active_chunks = active_chunks;
     if (P.kind == PASS_DRAFT && P.Kx > 0) a.tpw = y.draft_tpw;
     if (c->dbg_attn && rows <= c->dbg_rows) {

@@ -131,6 +131,16 @@ struct GemmOut {                // fp32 path
 };
 
 // bf16 path: one launch covers GEMM rows [0, M) = pass rows [row0, row0+M).
+// The bf16 activations that feed the GEMMs (RMSNorm output, attention
+// output, SwiGLU product) are stored in MFMA fragment order: row tiles of
+// 16 rows, k-blocks of 32 columns, and within a (tile, k-block) the 64
+// lanes' 16-byte B-operand pieces in lane order (lane = 16 * (k / 8 % 4) +
+// row % 16), so a wave loads a fragment as 1 KB of contiguous memory.  kb =
+// columns / 32.  Element offset of (row r, column k):
+__host__ __device__ __forceinline__ size_t frag_off(int r, int k, int kb) {
+  return ((size_t)(r >> 4) * kb + (k >> 5)) * 512 + (size_t)(((((k >> 3) & 3) << 4) | (r & 15)) * 8 + (k & 7));
+}
+
 struct GemmArgs {
   const u32x4_t* W;             // packed weight (16x32 MFMA fragments)
   int M, K, N, row0;
@@ -138,7 +148,7 @@ struct GemmArgs {
   int gy0;                      // row blocks of the first segment (set by the launcher)
   int gyt;                      // row blocks of both segments (set by the launcher)
   int flat;                     // 1-D grid over (column group, row block) (set by the launcher)
-  const uint16_t* X; int ldx;   // bf16 input rows
+  const uint16_t* X; int ldx;   // bf16 input, fragment order (K / 32 k-blocks; ldx = K)
   // split-K partials [8][M][N] and completion counters (zero between launches)
   float* part; unsigned* cnt;
   int ep;
@@ -151,6 +161,7 @@ struct GemmArgs {
   uint16_t* ks; uint16_t* vs; int kpad;
   float2* amax; float* logits; int ldl; int Kb;       // EP_ARGMAX
   int32_t* drafts; int32_t* ar; int32_t* pending;
+  int tnrb, ttb, tng;           // row-split launches: row blocks, row tiles per block, column groups (set by the launcher)
 };
 void launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
 // Profiling: the next bf16 GEMM kernel launched from this host thread
@@ -177,7 +188,8 @@ struct AttnArgs {
   int qr_max;       // q-rows per (sequence, kv head) capacity of the partial buffers
   float* opart;     // [B][hkv][nc+1][qr_max][hd]
   float* ml;        // [B][hkv][nc+1][qr_max][2]
-  void* out;        // [rows][hq*hd] model dtype
+  void* out;        // model dtype: [rows][hq*hd], or fragment order when out_kb > 0
+  int out_kb;       // bf16 output in fragment order with out_kb = hq*hd/32 k-blocks (0: row-major)
   void* tap; int tap_rows;   // optional attention-output tap for this layer
   float* tap32; int tap32_rows;   // optional fp32 tap of the attention output before rounding
   int fixed_ctx;    // >= 0: microbenchmark mode, every row sees cache [0, fixed_ctx)

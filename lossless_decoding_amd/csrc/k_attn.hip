@@ -680,7 +680,8 @@ __global__ __launch_bounds__(256) void k_attn_merge(AttnArgs a, int npairs) {
   const float inv = 1.0f / l;
   const size_t ob = (size_t)r * a.hq * hd + (size_t)h * hd + lane * 2;
   const uint32_t y = (uint32_t)f2bf(o0 * inv) | ((uint32_t)f2bf(o1 * inv) << 16);
-  *(uint32_t*)((uint16_t*)a.out + ob) = y;
+  const size_t oo = a.out_kb > 0 ? frag_off(r, h * hd + lane * 2, a.out_kb) : ob;
+  *(uint32_t*)((uint16_t*)a.out + oo) = y;
   if (a.tap && r < a.tap_rows) *(uint32_t*)((uint16_t*)a.tap + ob) = y;
   if (a.tap32 && r < a.tap32_rows) *(float2*)(a.tap32 + ob) = make_float2(o0 * inv, o1 * inv);
 }

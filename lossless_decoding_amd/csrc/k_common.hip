@@ -89,7 +89,8 @@ void launch_embed(const PassInfo& P, const int32_t* anchor_tok, const int32_t* b
                      embed, mask_emb, V, d, (int)bf16, h);
 }
 
-// Residual add of the split-K partials + RMSNorm -> bf16 rows.  One block
+// Residual add of the split-K partials + RMSNorm -> bf16 rows (fragment
+// order, the GEMMs' input layout).  One block
 // of NW waves per row; the row is cut into 256-element chunks, wave w takes
 // chunks w, w + NW, ..., lane l holds elements 4l .. 4l + 3.  All loads are
 // issued before use.  The partial sum runs in slice order and is then added
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(NW * 64) void k_resid_norm_bf16(PassInfo P, float* 
   __shared__ float red[32];
   const int r = blockIdx.x, t = threadIdx.x, wave = t >> 6, lane = t & 63, nch = d >> 8;
   if (P.kind == PASS_DRAFT && row_info(P, r).pad) {     // keep padding rows' input at zero
-    for (int i = t * 4; i < d; i += NW * 256) *(uint2*)(out + (size_t)r * d + i) = make_uint2(0u, 0u);
+    for (int i = t * 4; i < d; i += NW * 256) *(uint2*)(out + frag_off(r, i, d >> 5)) = make_uint2(0u, 0u);
     return;
   }
   float* x = h + (size_t)r * d;
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(NW * 64) void k_resid_norm_bf16(PassInfo P, float* 
       uint2 o;
       o.x = (uint32_t)f2bf(v[j].x * inv * g0) | ((uint32_t)f2bf(v[j].y * inv * g1) << 16);
       o.y = (uint32_t)f2bf(v[j].z * inv * g2) | ((uint32_t)f2bf(v[j].w * inv * g3) << 16);
-      *(uint2*)(out + (size_t)r * d + i) = o;
+      *(uint2*)(out + frag_off(r, i, d >> 5)) = o;
     }
   }
 }

@@ -60,6 +60,8 @@ static void gemm_launch(K kernel, dim3 grid, dim3 block, hipStream_t s, const Ge
 }
 
 
+template <int N> struct IntC { static constexpr int value = N; };
+
 #define NSL 8                 // K slices
 #define SKB 16                // k-blocks of 32 per activation stage
 #define BUF_FLAGS 0x00020000  // buffer descriptor word 3: 32-bit data format
@@ -162,6 +164,42 @@ __device__ __forceinline__ void qkv_row(const GemmArgs& a, int ng, int prow, flo
   }
 }
 
+// The LM head's last workgroup: each row's token from its per-column-group
+// (value, index) partials amax[row][ngroups] (larger value, then lower
+// index), written where the pass keeps it.  Rows row0 .. row0 + Mr - 1,
+// one wave per row at a time.
+__device__ __forceinline__ void amax_finish(const GemmArgs& a, int ngroups, int Mr, int row0,
+                                            int wave, int nwaves, int lane) {
+  for (int r = wave; r < Mr; r += nwaves) {
+    const int prow = row0 + r;
+    const float2* pp = a.amax + (size_t)prow * ngroups;
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int j = lane; j < ngroups; j += 64) {
+      float tv = ld_agent(&pp[j].x), ti = ld_agent(&pp[j].y);
+      amax_comb(bv, bi, tv, __float_as_int(ti));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      float v2 = __shfl_xor(bv, o, 64); int i2 = __shfl_xor(bi, o, 64);
+      amax_comb(bv, bi, v2, i2);
+    }
+    const PassInfo& P = a.P;
+    const RowInfo ri = row_info(P, prow);
+    if (lane == 0 && !ri.pad) {
+      if (P.kind == PASS_DRAFT) {
+        if (!ri.is_mask) {
+          if (a.pending) a.pending[ri.b] = bi; else a.ar[(size_t)ri.b * (a.Kb + 1)] = bi;
+        } else {
+          a.drafts[(size_t)ri.b * a.Kb + (ri.t - P.A)] = bi;
+        }
+      } else if (P.kind == PASS_VERIFY) {
+        a.ar[(size_t)ri.b * (a.Kb + 1) + 1 + ri.t] = bi;
+      }
+    }
+  }
+}
+
 // CT: 16-column tiles per wave.  With CT = 2 every activation fragment read
 // from LDS feeds two MFMAs (tall row tiles, unsplit launches only).
 template <int MT, int EP, int WV, bool SPLIT, int CT>
@@ -173,14 +211,23 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   // k-blocks per activation stage: 16, or fewer for tall tiles (LDS stays
   // at 32-64 KB, the weight ring short); a divisor of the 16 k-blocks of a
   // slice
-  constexpr int SK = MT <= 4 ? SKB : ((MT <= 8 && CT == 1) ? SKB / 2 : SKB / 4);
+  // Tall row tiles (MT >= 8) stage activations straight from memory into
+  // two LDS stages (no registers, no LDS writes, one barrier per stage) and
+  // keep the weight ring 8 k-blocks deep (2 or 4 stages); shorter tiles go
+  // through registers into one stage, the ring one stage deep.
+  constexpr bool DL = MT >= 8;
+  constexpr int SK = DL ? (MT >= 12 ? SKB / 8 : SKB / 4) : (MT <= 4 ? SKB : (CT == 1 ? SKB / 2 : SKB / 4));
   constexpr int NFR = MT * SK;                // activation fragments per stage
   constexpr int NF = (NFR + WV - 1) / WV;     // ... per wave
-  // LDS: one activation stage in fragment order [mt][k-block][lane][8]; in
-  // the epilogue it holds fp32 output tiles (16 x COLS each), MTE at a time
-  constexpr int MTE = largest_divisor_le(MT, (MT * SK * 32 * 2) / (COLS * 4));
+  constexpr int NSTG = DL ? 2 : 1;            // LDS activation stages
+  constexpr int RING = DL ? SKB / 2 : SK;     // weight ring depth (k-blocks)
+  constexpr int NU = RING / SK;               // stages per ring turn
+  static_assert(RING % SK == 0 && (!DL || NU == 2 || NU == 4), "ring turns hold 2 or 4 stages");
+  // LDS: the activation stages in fragment order [mt][k-block][lane][8]; in
+  // the epilogue they hold fp32 output tiles (16 x COLS each), MTE at a time
+  constexpr int MTE = largest_divisor_le(MT, (NSTG * MT * SK * 32 * 2) / (COLS * 4));
   static_assert(MTE >= 1 && MT % MTE == 0, "epilogue row chunks must tile MT");
-  __shared__ __attribute__((aligned(16))) uint16_t sX[MT * 16 * SK * 32];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[NSTG * MT * 16 * SK * 32];
   __shared__ float sRed[WV * RPW];
   __shared__ int sIdx[WV * RPW];
   __shared__ int sLast;
@@ -238,9 +285,13 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   // unconditionally, the number of loads between a ring load and its use
   // never depends on the data, and the memory-counter waits stay exact.
   const int vrows = Mr - m0 < RPW ? Mr - m0 : RPW;         // valid rows of this workgroup
+  // activations in fragment order: the row tiles of this workgroup from
+  // tile (row0 + m0) / 16, KB 1 KB fragments each; tiles past the valid rows
+  // read as zero (rows past them inside the last tile are never stored)
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.X + (size_t)(row0 + m0) * a.ldx), (short)0, vrows * a.ldx * 2, BUF_FLAGS);
-  const int a_vo = lr * a.ldx * 2 + lq * 16;                  // lane part of the offset
+      (void*)(a.X + (size_t)((row0 + m0) >> 4) * KB * 512), (short)0, ((vrows + 15) >> 4) * KB * 1024,
+      BUF_FLAGS);
+  const int a_vo = lane * 16;                                  // lane part of the offset
   u32x4_t sr[NF];
   auto load_stage = [&](int st) __attribute__((always_inline)) {
 #pragma unroll
@@ -249,7 +300,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       const int mt = fr / SK, kbl = st * SK + fr % SK;
       // k-blocks past this workgroup's range are pushed out of the
       // descriptor (range checks apply to the VGPR offset)
-      const int so = kbl < nkb ? (mt * 16 * a.ldx + (kb_lo + kbl) * 32) * 2 : OOR;
+      const int so = kbl < nkb ? (mt * KB + kb_lo + kbl) * 1024 : OOR;
       sr[f] = __builtin_amdgcn_raw_buffer_load_b128(rA, a_vo + so, 0, 0);
     }
   };
@@ -260,20 +311,39 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       if (fr < NFR) *(u32x4_t*)(sX + ((size_t)fr * 64 + lane) * 8) = sr[f];
     }
   };
-  const int nst = (nkb + SK - 1) / SK;      // activation stages
-  load_stage(0);
-  // weight ring: slot i holds k-block st*SK + i of the stage being computed;
-  // loads past this wave's k-range fall outside the descriptor (zero, no
-  // memory access)
-  u32x4_t w[CT][SK];
+  // direct form: fragment fr of stage st goes to LDS stage (st & 1) in lane
+  // order (a buffer load with an LDS destination writes lane l's 16 bytes at
+  // the stage's base + 16 l); k-blocks past the range read as zero
+  auto issue_stage = [&](int st) __attribute__((always_inline)) {
+    uint16_t* dst = sX + (size_t)(st & 1) * (MT * 16 * SK * 32);
 #pragma unroll
-  for (int i = 0; i < SK; ++i)
+    for (int f = 0; f < NF; ++f) {
+      const int fr = wave + f * WV;
+      if (fr < NFR) {
+        const int mt = fr / SK, kbl = st * SK + fr % SK;
+        const int so = kbl < nkb ? (mt * KB + kb_lo + kbl) * 1024 : OOR;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void*)(dst + (size_t)fr * 512), 16, a_vo + so, 0, 0, 0);
+      }
+    }
+  };
+  const int nst0 = (nkb + SK - 1) / SK;      // activation stages
+  const int nst = DL ? (nst0 + NU - 1) / NU * NU : nst0;   // direct form: whole ring turns (extra stages add zeros)
+  if (DL) issue_stage(0);
+  else load_stage(0);
+  // weight ring: slot j holds k-block j (mod RING) ahead of use; loads past
+  // this wave's k-range fall outside the descriptor (zero, no memory access)
+  u32x4_t w[CT][RING];
+#pragma unroll
+  for (int i = 0; i < RING; ++i)
 #pragma unroll
     for (int c = 0; c < CT; ++c)
       w[c][i] = __builtin_amdgcn_raw_buffer_load_b128(rW[c], lane * 16 + i * 1024, 0, BUF_NT);
 
-  write_stage();
-  __syncthreads();
+  if (!DL) {
+    write_stage();
+    __syncthreads();
+  }
 
   floatx4_t cur[CT][MT], tot[CT][MT];
 #pragma unroll
@@ -287,27 +357,25 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
   // steps, each refilling its ring slot with the k-block one stage ahead.
   // The loads are the same on every path.  Past the end of a partial last
   // stage both operands are zero, so the extra MFMAs add exact zeros.
-  for (int st = 0; st < nst; ++st) {
-    if (st > 0) {
-      __syncthreads();                 // every wave is done with the previous stage
-      write_stage();
-      __syncthreads();
-    }
-    load_stage(st + 1);
+  // SK MFMA steps of stage st from LDS stage `buf`, each refilling its ring
+  // slot (sub-stage u of the ring) with the k-block RING ahead
+  auto compute_stage = [&](int st, const uint16_t* buf, auto uc) __attribute__((always_inline)) {
+    constexpr int U = decltype(uc)::value;
 #pragma unroll
     for (int i = 0; i < SK; ++i) {
       const int kk = st * SK + i;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const u32x4_t xv = *(const u32x4_t*)(sX + ((size_t)(mt * SK + i) * 64 + lane) * 8);
+        const u32x4_t xv = *(const u32x4_t*)(buf + ((size_t)(mt * SK + i) * 64 + lane) * 8);
 #pragma unroll
         for (int c = 0; c < CT; ++c)
-          cur[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[c][i]), as_bf16x8(xv),
-                                                               cur[c][mt], 0, 0, 0);
+          cur[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(w[c][U * SK + i]),
+                                                               as_bf16x8(xv), cur[c][mt], 0, 0, 0);
       }
 #pragma unroll
       for (int c = 0; c < CT; ++c)
-        w[c][i] = __builtin_amdgcn_raw_buffer_load_b128(rW[c], lane * 16 + (kk + SK) * 1024, 0, BUF_NT);
+        w[c][U * SK + i] =
+            __builtin_amdgcn_raw_buffer_load_b128(rW[c], lane * 16 + (kk + RING) * 1024, 0, BUF_NT);
       if (!SPLIT && kk < nkb && (kk + 1) % KSB == 0) {   // slice done: add in slice order
 #pragma unroll
         for (int c = 0; c < CT; ++c)
@@ -317,6 +385,52 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
             cur[c][mt] = floatx4_t{0.f, 0.f, 0.f, 0.f};
           }
       }
+    }
+  };
+  if constexpr (DL) {
+    // Stage st: wait for this wave's loads of stage st (only the weight
+    // loads issued after them may still be in flight: RING loads before the
+    // first stage, SK per stage after) and for its LDS reads of the
+    // previous stage; the barrier then makes every wave's share visible and
+    // frees the other LDS stage, which takes stage st + 1.
+    constexpr int W0 = RING * CT, W1 = SK * CT;
+    static_assert(W0 < 64 && W1 < 64, "vmcnt range");
+    constexpr int E0 = (W0 & 15) | ((W0 >> 4) << 14) | (7 << 4);   // vmcnt(W0) lgkmcnt(0)
+    constexpr int E1 = (W1 & 15) | ((W1 >> 4) << 14) | (7 << 4);   // vmcnt(W1) lgkmcnt(0)
+    auto sync_stage = [&](bool first) __attribute__((always_inline)) {
+      if (first) __builtin_amdgcn_s_waitcnt(E0);
+      else __builtin_amdgcn_s_waitcnt(E1);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    for (int st0 = 0; st0 < nst; st0 += NU) {
+      // one ring turn: stage st0 + u reads LDS stage u & 1 and ring slots
+      // [u SK, u SK + SK)
+      auto one = [&](auto uc) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value;
+        const int st = st0 + U;
+        sync_stage(st == 0);
+        if (st + 1 < nst) issue_stage(st + 1);
+        compute_stage(st, sX + (U & 1) * (MT * 16 * SK * 32), uc);
+      };
+      one(IntC<0>{});
+      one(IntC<1>{});
+      if constexpr (NU == 4) {
+        one(IntC<2>{});
+        one(IntC<3>{});
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  } else {
+    for (int st = 0; st < nst; ++st) {
+      if (st > 0) {
+        __syncthreads();                 // every wave is done with the previous stage
+        write_stage();
+        __syncthreads();
+      }
+      load_stage(st + 1);
+      compute_stage(st, sX, IntC<0>{});
     }
   }
   if (!SPLIT) {
@@ -422,7 +536,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
       for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[0][mt][i]) * cur[CT - 1][mt][i]);
       uint2 pk;
       __builtin_memcpy(&pk, o, 8);
-      *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
+      *(uint2*)(a.act + frag_off(row0 + r, j, a.ldact >> 5)) = pk;
     }
     return;
   }
@@ -451,7 +565,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
           for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cs[mt][i]) * u[i]);
           uint2 pk;
           __builtin_memcpy(&pk, o, 8);
-          *(uint2*)(a.act + (size_t)(row0 + r) * a.ldact + j) = pk;
+          *(uint2*)(a.act + frag_off(row0 + r, j, a.ldact >> 5)) = pk;
         }
       }
     }
@@ -500,34 +614,7 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
     }
     __syncthreads();
     if (!sLast) return;
-    for (int r = wave; r < Mr; r += WV) {
-      const int prow = row0 + r;
-      const float2* pp = a.amax + (size_t)prow * ngroups;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      for (int j = lane; j < ngroups; j += 64) {
-        float tv = ld_agent(&pp[j].x), ti = ld_agent(&pp[j].y);
-        amax_comb(bv, bi, tv, __float_as_int(ti));
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float v2 = __shfl_xor(bv, o, 64); int i2 = __shfl_xor(bi, o, 64);
-        amax_comb(bv, bi, v2, i2);
-      }
-      const PassInfo& P = a.P;
-      const RowInfo ri = row_info(P, prow);
-      if (lane == 0 && !ri.pad) {
-        if (P.kind == PASS_DRAFT) {
-          if (!ri.is_mask) {
-            if (a.pending) a.pending[ri.b] = bi; else a.ar[(size_t)ri.b * (a.Kb + 1)] = bi;
-          } else {
-            a.drafts[(size_t)ri.b * a.Kb + (ri.t - P.A)] = bi;
-          }
-        } else if (P.kind == PASS_VERIFY) {
-          a.ar[(size_t)ri.b * (a.Kb + 1) + 1 + ri.t] = bi;
-        }
-      }
-    }
+    amax_finish(a, ngroups, Mr, row0, wave, WV, lane);
     return;
   }
   if (EP == EP_QKV) {
@@ -566,6 +653,342 @@ __global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
     x2 += p[(size_t)sl * a.rps + 64];
   }
   qkv_row(a, ng, prow, x1, x2, lane);
+}
+
+// ------------------------------------------------------------ row-split form
+// Launches of 256 rows and more (draft / verify passes of several
+// sequences, prefill passes).  A workgroup of four waves owns C column
+// tiles and one row block of up to 3 TRW + TRW0 row tiles (16 rows each),
+// which the waves split: waves 1-3 take TRW tiles each, wave 0 the rest
+// (at most TRW0) and loads the workgroup's weights.  Each weight fragment
+// is loaded once per workgroup, straight from memory into LDS (buffer loads
+// with an LDS destination, TNS stages of TS k-blocks in flight), and read
+// from LDS by all four waves.  Each wave loads its own activation fragments
+// into a register ring TDX k-blocks deep.  Memory counters complete in issue
+// order, so a wave that waits for an activation load also waits for every
+// older load; keeping the weight loads in wave 0 lets the other waves wait
+// for their activations only.  Per k-block a wave reads C weight fragments
+// from LDS and issues (tiles) x C MFMAs.
+//  * The arithmetic of every output is the slice order of the kernel above
+//    (same MFMA, same operands, same slice sums), so the two forms give
+//    identical bits for a row.
+//  * Two segments (mask rows with one weight set, anchor rows with another)
+//    may share a row block: the workgroup then stages both weight sets.
+//  * Split launches (O, down, QKV) give each K slice its own workgroup and
+//    write the slice partials for the next kernel; unsplit launches run the
+//    SwiGLU or argmax epilogue.
+#define TRW 5    // row tiles of waves 1-3
+#define TRW0 2   // row tiles of wave 0 (the weight loader)
+#define TS 2     // k-blocks per weight stage
+
+template <int C, int EP, bool SPLIT, bool TWO>
+__global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
+  static_assert(SPLIT ? (EP == EP_RESID || EP == EP_QKV) : (EP == EP_SWIGLU || EP == EP_ARGMAX),
+                "split launches write partials; unsplit ones run SwiGLU or argmax");
+  static_assert(!TWO || SPLIT, "two weight sets: split launches only");
+  static_assert(EP != EP_SWIGLU || C % 2 == 0, "SwiGLU pairs gate and up tiles");
+  constexpr int NW = TWO ? 2 * C : C;           // weight fragments per k-block
+  constexpr int LPS = NW * TS;                  // weight loads (1 KB) per stage, all by wave 0
+  constexpr int TNS = TWO ? 4 : 5;              // weight stages in LDS
+  constexpr int TDX = TWO ? 4 : 5;              // activation ring depth (k-blocks)
+  static_assert((TNS * TS) % TDX == 0, "ring slots stay compile-time over a ring turn");
+  constexpr int SU = LPS * 512;                 // one stage (uint16 elements)
+  static_assert(TNS * SU * 2 <= 160 * 1024, "LDS");
+  // one array per stage, so the compiler sees that loads into one stage and
+  // reads of another do not alias (no wait for the loads in flight)
+  __shared__ __attribute__((aligned(16))) uint16_t sW0[SU];
+  __shared__ __attribute__((aligned(16))) uint16_t sW1[SU];
+  __shared__ __attribute__((aligned(16))) uint16_t sW2[SU];
+  __shared__ __attribute__((aligned(16))) uint16_t sW3[SU];
+  __shared__ __attribute__((aligned(16))) uint16_t sW4[TNS > 4 ? SU : 8];
+  auto stage_buf = [&](auto uc) __attribute__((always_inline)) -> uint16_t* {
+    constexpr int S = decltype(uc)::value % TNS;
+    if constexpr (S == 0) return sW0;
+    else if constexpr (S == 1) return sW1;
+    else if constexpr (S == 2) return sW2;
+    else if constexpr (S == 3) return sW3;
+    else return sW4;
+  };
+
+  const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KB = a.K / 32;
+  const int KSB = KB / NSL;
+  const int nsl = SPLIT ? NSL : 1;
+  // 1-D grid; the row blocks of one (column group, slice) are consecutive
+  // workgroups of one XCD (workgroup id mod 8), so a weight fragment comes
+  // from memory once and from that XCD's L2 for the other row blocks
+  const int id = blockIdx.x, j8 = id >> 3;
+  const int gq = j8 / a.tnrb, rb = j8 - gq * a.tnrb;
+  const int grp = gq * 8 + (id & 7);
+  if (grp >= a.tng * nsl) return;
+  const int ng = SPLIT ? grp / NSL : grp;
+  const int sl = SPLIT ? grp - ng * NSL : 0;
+  const int kb_lo = sl * KSB;
+  const int nkb = SPLIT ? KSB : KB;
+  const int ntiles = a.N / 16;                  // column tiles of the matrix
+  const int ct0 = ng * C;                       // first column tile of the workgroup
+  const int nct = min(C, ntiles - ct0);         // its valid column tiles
+
+  // row tiles: segment 0 (M rows from row0) then segment 1 (M2 rows from
+  // row02); this block's nb tiles: wave 0 the first n0, then TRW per wave
+  const int T0 = (a.M + 15) >> 4;
+  const int T = T0 + ((a.M2 + 15) >> 4);
+  const int tb0 = rb * a.ttb;
+  const int nb = min(a.ttb, T - tb0);
+  const int n0 = max(0, nb - 3 * TRW);          // <= TRW0 (launcher)
+  const int my_lo = wave == 0 ? 0 : n0 + (wave - 1) * TRW;
+  const int ntw = wave == 0 ? n0 : max(0, min(TRW, nb - my_lo));   // uniform
+  __amdgpu_buffer_rsrc_t rX[TRW];
+  int rowb[TRW], vrow[TRW];
+  bool s1[TRW];
+#pragma unroll
+  for (int jj = 0; jj < TRW; ++jj) {
+    const int gt = tb0 + my_lo + jj;
+    s1[jj] = TWO && gt >= T0;
+    const int rbase = s1[jj] ? a.row02 + (gt - T0) * 16 : a.row0 + gt * 16;
+    int v = s1[jj] ? a.M2 - (gt - T0) * 16 : a.M - gt * 16;
+    v = jj < ntw ? (v < 16 ? v : 16) : 0;
+    rowb[jj] = rbase; vrow[jj] = v;
+    // fragment order: tile rbase / 16, KB fragments of 1 KB (rows past the
+    // valid ones inside the tile are never stored)
+    rX[jj] = __builtin_amdgcn_make_buffer_rsrc((void*)(a.X + (size_t)(v > 0 ? rbase >> 4 : 0) * KB * 512),
+                                               (short)0, v > 0 ? KB * 1024 : 0, BUF_FLAGS);
+  }
+  const int x_vo = lane * 16;
+  // weights: the workgroup's C column tiles are contiguous ([tile][k-block][1 KB])
+  const __amdgpu_buffer_rsrc_t rW = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + (size_t)ct0 * KB * 64), (short)0, nct * KB * 1024, BUF_FLAGS);
+  __amdgpu_buffer_rsrc_t rW2 = rW;
+  if (TWO)
+    rW2 = __builtin_amdgcn_make_buffer_rsrc((void*)(a.W2 + (size_t)ct0 * KB * 64), (short)0,
+                                            nct * KB * 1024, BUF_FLAGS);
+
+  // stage st (wave 0): the NW fragments of k-blocks st*TS .. st*TS+TS-1
+  // into LDS ([k-block][fragment] of 1 KB, lane order); k-blocks past the
+  // range read as zero
+  auto issue_w = [&](uint16_t* buf, int st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TS; ++i) {
+      const int kk = st * TS + i;
+      const int ko = kk < nkb ? (kb_lo + kk) * 1024 + lane * 16 : OOR;
+#pragma unroll
+      for (int f = 0; f < NW; ++f) {
+        const bool second = TWO && f >= C;
+        const int c = second ? f - C : f;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            second ? rW2 : rW, (__attribute__((address_space(3))) void*)(buf + (i * NW + f) * 512), 16,
+            ko == OOR ? OOR : c * KB * 1024 + ko, 0, 0, BUF_NT);
+      }
+    }
+  };
+  u32x4_t xr[TDX][TRW];
+  floatx4_t cur[TRW][C];
+  floatx4_t tot[SPLIT ? 1 : TRW][SPLIT ? 1 : C];
+#pragma unroll
+  for (int jj = 0; jj < TRW; ++jj)
+#pragma unroll
+    for (int c = 0; c < C; ++c) cur[jj][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int jj = 0; jj < TRW; ++jj)
+#pragma unroll
+      for (int c = 0; c < C; ++c) tot[jj][c] = cur[jj][c];
+  }
+  const int nst = (nkb + TS - 1) / TS;
+  int next_end = KSB;                           // k-block count at the end of the current slice
+
+  // The main loop for a wave of R row tiles (wave 0: R = TRW0, the loader).
+  auto main_loop = [&](auto rc) __attribute__((always_inline)) {
+    constexpr int R = decltype(rc)::value;
+    constexpr bool LD = R == TRW0;
+    auto issue_x = [&](int kk, u32x4_t (&dst)[TRW]) __attribute__((always_inline)) {
+      const int so = kk < nkb ? (kb_lo + kk) * 1024 : OOR;
+#pragma unroll
+      for (int jj = 0; jj < R; ++jj) dst[jj] = __builtin_amdgcn_raw_buffer_load_b128(rX[jj], x_vo + so, 0, 0);
+    };
+    if constexpr (LD) {
+#pragma unroll
+      for (int p = 0; p < TNS - 1; ++p) {
+        if (p == 0) issue_w(stage_buf(IntC<0>{}), 0);
+        else if (p == 1) issue_w(stage_buf(IntC<1>{}), 1);
+        else if (p == 2) issue_w(stage_buf(IntC<2>{}), 2);
+        else issue_w(stage_buf(IntC<3>{}), 3);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < TDX; ++d) issue_x(d, xr[d]);
+    // wave 0's waits for stage st's weights: the loads issued after them are
+    // the later prologue stages and the prologue activations (first TNS-1
+    // stages, fewer), or TNS-1 stages of activations and TNS-2 of weights
+    constexpr int N0 = (TNS - 2) * LPS + TDX * R;
+    constexpr int NA0 = (TNS - 1) * TS * R + (TNS - 2) * LPS;
+    constexpr int NA = NA0 < 63 ? NA0 : 63;
+    static_assert(!LD || N0 <= 63, "prologue wait within the counter's range");
+    constexpr int E0 = (N0 & 15) | ((N0 >> 4) << 14) | (7 << 4);   // vmcnt(N0) lgkmcnt(0)
+    constexpr int EA = (NA & 15) | ((NA >> 4) << 14) | (7 << 4);   // vmcnt(NA) lgkmcnt(0)
+    constexpr int EL = 15 | (3 << 14) | (7 << 4);                  // lgkmcnt(0)
+
+    for (int st0 = 0; st0 < nst; st0 += TNS) {
+      auto one = [&](auto uc) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value;
+        const int st = st0 + U;
+        // stage st's weights are in LDS and every wave's reads of stage
+        // st-1 are done: wave 0 waits for its loads, every wave for its
+        // LDS reads, then the barrier; stage st-1's buffer takes stage
+        // st + TNS - 1
+        if constexpr (LD) {
+          if (st < TNS - 1) __builtin_amdgcn_s_waitcnt(E0);
+          else __builtin_amdgcn_s_waitcnt(EA);
+        } else {
+          __builtin_amdgcn_s_waitcnt(EL);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if constexpr (LD) issue_w(stage_buf(IntC<U + TNS - 1>{}), st + TNS - 1);
+        const uint16_t* buf = stage_buf(IntC<U>{});
+#pragma unroll
+        for (int i = 0; i < TS; ++i) {
+          const int kk = st * TS + i;
+          u32x4_t (&xv)[TRW] = xr[(U * TS + i) % TDX];
+          u32x4_t wf[C], wf2[TWO ? C : 1];
+#pragma unroll
+          for (int c = 0; c < C; ++c) wf[c] = *(const u32x4_t*)(buf + ((i * NW + c) * 64 + lane) * 8);
+          if constexpr (TWO) {
+            bool any2 = false;
+#pragma unroll
+            for (int jj = 0; jj < R; ++jj) any2 = any2 || (jj < ntw && s1[jj]);
+            if (any2) {
+#pragma unroll
+              for (int c = 0; c < C; ++c) wf2[c] = *(const u32x4_t*)(buf + ((i * NW + C + c) * 64 + lane) * 8);
+            } else {
+#pragma unroll
+              for (int c = 0; c < C; ++c) wf2[c] = wf[c];
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < R; ++jj) {
+            if (jj >= ntw) break;
+            if (TWO && s1[jj]) {
+#pragma unroll
+              for (int c = 0; c < C; ++c)
+                cur[jj][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf2[TWO ? c : 0]),
+                                                                    as_bf16x8(xv[jj]), cur[jj][c], 0, 0, 0);
+            } else {
+#pragma unroll
+              for (int c = 0; c < C; ++c)
+                cur[jj][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(wf[c]), as_bf16x8(xv[jj]),
+                                                                    cur[jj][c], 0, 0, 0);
+            }
+          }
+          issue_x(kk + TDX, xv);
+          // slice done: add it in slice order.  tot starts at +0 and a slice
+          // sum is never -0 (its chain starts at +0), so the first addition
+          // gives the slice sum exactly.  (Unsplit launches have no k-blocks
+          // past the range: KB is a multiple of 8.)  The empty asm keeps this
+          // a branch taken 8 times, not selects at every k-block.
+          if constexpr (!SPLIT) {
+            if (kk + 1 == next_end) {
+              asm volatile("" ::: "memory");
+              next_end += KSB;
+#pragma unroll
+              for (int jj = 0; jj < R; ++jj)
+#pragma unroll
+                for (int c = 0; c < C; ++c) {
+                  tot[jj][c] = add4(tot[jj][c], cur[jj][c]);
+                  cur[jj][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+          }
+        }
+      };
+      one(IntC<0>{});
+      if (st0 + 1 < nst) one(IntC<1>{});
+      if (st0 + 2 < nst) one(IntC<2>{});
+      if (st0 + 3 < nst) one(IntC<3>{});
+      if constexpr (TNS > 4) {
+        if (st0 + 4 < nst) one(IntC<4>{});
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+  };
+  if (wave == 0) main_loop(IntC<TRW0>{});
+  else main_loop(IntC<TRW>{});
+  if constexpr (!SPLIT) {
+#pragma unroll
+    for (int jj = 0; jj < TRW; ++jj)
+#pragma unroll
+      for (int c = 0; c < C; ++c) cur[jj][c] = tot[jj][c];
+  }
+
+  // ============================ epilogues
+  // lane (lr, lq): rows rowb[jj] + lr, columns (ct0 + c)*16 + lq*4 + i
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int jj = 0; jj < TRW; ++jj) {
+      if (lr >= vrow[jj]) continue;
+      float* pp = a.rpart + (size_t)sl * a.rps + (size_t)(rowb[jj] + lr) * a.N + ct0 * 16 + lq * 4;
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        if (c < nct) *(floatx4_t*)(pp + c * 16) = cur[jj][c];
+    }
+    return;
+  }
+  if constexpr (EP == EP_SWIGLU) {
+    // gate (even tile) and up (odd tile) of one 16-column act block
+#pragma unroll
+    for (int jj = 0; jj < TRW; ++jj) {
+      if (lr >= vrow[jj]) continue;
+#pragma unroll
+      for (int c = 0; c < C; c += 2) {
+        if (c >= nct) break;
+        uint16_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = f2bf(silu_f(cur[jj][c][i]) * cur[jj][c + 1][i]);
+        uint2 pk;
+        __builtin_memcpy(&pk, o, 8);
+        *(uint2*)(a.act + frag_off(rowb[jj] + lr, ((ct0 + c) >> 1) * 16 + lq * 4, a.ldact >> 5)) = pk;
+      }
+    }
+    return;
+  }
+  if constexpr (EP == EP_ARGMAX) {
+#pragma unroll
+    for (int jj = 0; jj < TRW; ++jj) {
+      if (jj >= ntw) break;
+      float bv = cur[jj][0][0];
+      int bi = ct0 * 16 + lq * 4;
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if ((c > 0 || i > 0) && c < nct) amax_comb(bv, bi, cur[jj][c][i], (ct0 + c) * 16 + lq * 4 + i);
+      if (a.logits && lr < vrow[jj]) {
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+          if (c < nct)
+            *(floatx4_t*)(a.logits + (size_t)(rowb[jj] + lr) * a.ldl + (ct0 + c) * 16 + lq * 4) = cur[jj][c];
+      }
+      float v2 = __shfl_xor(bv, 16, 64); int i2 = __shfl_xor(bi, 16, 64);
+      amax_comb(bv, bi, v2, i2);
+      v2 = __shfl_xor(bv, 32, 64); i2 = __shfl_xor(bi, 32, 64);
+      amax_comb(bv, bi, v2, i2);
+      if (lq == 0 && lr < vrow[jj]) {
+        float2* ap = a.amax + (size_t)(rowb[jj] + lr) * a.tng + ng;
+        st_agent(&ap->x, bv);
+        st_agent(&ap->y, __int_as_float(bi));
+      }
+    }
+    // k_amax_rows, launched next, turns the per-group partials into tokens
+    return;
+  }
+}
+
+// The row-split LM head's second half: one wave per row reduces the row's
+// per-column-group (value, index) partials.
+__global__ __launch_bounds__(64) void k_amax_rows(GemmArgs a) {
+  amax_finish(a, a.tng, a.M, a.row0, blockIdx.x, gridDim.x, threadIdx.x);
 }
 
 template <int EP, int WV, bool SPLIT, int CT = 1>
@@ -640,8 +1063,36 @@ static bool rows144_pad_less(int M) { return (M + 143) / 144 * 144 < (M + 127) /
 // or fewer than 256 for EP_RESID, whose split form only writes partials (no
 // in-kernel fixup).  0 or the number of K slices: for EP_RESID the residual
 // + RMSNorm kernel that follows must add that many slice partials.
+// The row-split form (k_gemm_rows) takes launches of at least 16 row tiles
+// (256 rows) with 16-column tiles in whole pairs: SwiGLU and argmax unsplit
+// (one weight set), QKV and the residual GEMMs split into the 8 K slices.
+// Column tiles per workgroup: 6 for SwiGLU (the Qwen3-8B gate/up GEMM is
+// then one workgroup per compute unit at 272 rows), argmax and QKV, 4 for
+// the residual GEMMs (512 workgroups at Qwen3-8B width); row blocks of at
+// most 3 * TRW + TRW0 tiles, balanced.
+struct RowsPlan { int C, two, nrb, tb, ng, wgs; };
+
+static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
+  if (M2 < 0) M2 = 0;
+  const int T = (M + 15) / 16 + (M2 + 15) / 16;
+  if (T < 16 || N % 32 != 0) return false;
+  if ((ep == EP_SWIGLU || ep == EP_ARGMAX) && M2 > 0) return false;
+  if (ep != EP_SWIGLU && ep != EP_ARGMAX && ep != EP_RESID && ep != EP_QKV) return false;
+  p.C = ep == EP_RESID ? 4 : 6;
+  if (ep == EP_SWIGLU && (N / 16) % 6 != 0) p.C = 4;   // whole gate/up pairs per workgroup
+  p.two = M2 > 0;
+  p.nrb = (T + 3 * TRW + TRW0 - 1) / (3 * TRW + TRW0);
+  p.tb = (T + p.nrb - 1) / p.nrb;
+  p.ng = (N / 16 + p.C - 1) / p.C;
+  const int ngs = p.ng * ((ep == EP_RESID || ep == EP_QKV) ? NSL : 1);
+  p.wgs = (ngs + 7) / 8 * 8 * p.nrb;
+  return true;
+}
+
 int gemm_bf16_split_slices(int M, int M2, int N, int ep) {
   if (M2 < 0) M2 = 0;
+  RowsPlan rp;
+  if (rows_plan(M, M2, N, ep, rp)) return (ep == EP_RESID || ep == EP_QKV) ? NSL : 0;
   int rpw = gemm_rows_per_wg(M, M2);
   int gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
   // QKV takes 64-row tiles where 128-row tiles give fewer than 192
@@ -700,8 +1151,14 @@ extern "C" int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, in
   if (!plan || m < 0 || m2 < 0 || m + m2 < 1 || n < 128 || n % 128 || k < 256 || k % 256 ||
       epilogue < EP_RESID || epilogue > EP_QKV)
     return ORTHRUS_EINVAL;
+  RowsPlan rp;
+  if (rows_plan(m, m2, n, epilogue, rp)) {
+    plan[0] = rp.tb; plan[1] = 4; plan[2] = epilogue == EP_RESID || epilogue == EP_QKV;
+    plan[3] = rp.C; plan[4] = rp.wgs; plan[5] = 1 + rp.two;
+    return ORTHRUS_OK;
+  }
   const GemmPlan p = gemm_plan(m, m2, n, epilogue);
-  plan[0] = p.MT; plan[1] = p.WV; plan[2] = p.split; plan[3] = p.CT; plan[4] = p.wgs;
+  plan[0] = p.MT; plan[1] = p.WV; plan[2] = p.split; plan[3] = p.CT; plan[4] = p.wgs; plan[5] = 0;
   return ORTHRUS_OK;
 }
 
@@ -712,6 +1169,31 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
   GemmArgs a = a0;
   if (!a.W2 || a.M2 <= 0) { a.W2 = nullptr; a.M2 = 0; }
   if (a.M <= 0 && a.M2 <= 0) return;
+  RowsPlan rp;
+  if (rows_plan(a.M, a.M2, a.N, a.ep, rp)) {
+    a.tnrb = rp.nrb; a.ttb = rp.tb; a.tng = rp.ng;
+    const dim3 g(rp.wgs), b(256);
+    switch (a.ep) {
+      case EP_SWIGLU:
+        if (rp.C == 6) gemm_launch(k_gemm_rows<6, EP_SWIGLU, false, false>, g, b, s, a);
+        else gemm_launch(k_gemm_rows<4, EP_SWIGLU, false, false>, g, b, s, a);
+        break;
+      case EP_ARGMAX:
+        gemm_launch(k_gemm_rows<6, EP_ARGMAX, false, false>, g, b, s, a);
+        hipLaunchKernelGGL(k_amax_rows, dim3(a.M), dim3(64), 0, s, a);
+        break;
+      case EP_RESID:
+        if (rp.two) gemm_launch(k_gemm_rows<4, EP_RESID, true, true>, g, b, s, a);
+        else gemm_launch(k_gemm_rows<4, EP_RESID, true, false>, g, b, s, a);
+        break;
+      default:
+        if (rp.two) gemm_launch(k_gemm_rows<6, EP_QKV, true, true>, g, b, s, a);
+        else gemm_launch(k_gemm_rows<6, EP_QKV, true, false>, g, b, s, a);
+        hipLaunchKernelGGL(k_qkv_finish_bf16, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+        break;
+    }
+    return;
+  }
   const GemmPlan plan = gemm_plan(a.M, a.M2, a.N, a.ep);
   const bool wide = !plan.split;
   const int MT = plan.MT;
