@@ -488,7 +488,7 @@ def run_workload(name, S, W, args, headline):
     # the attention kernel the draft pass launches: one query tile per wave
     # when the context's full cache at this batch gives under 512 workgroups
     G = sh["hq"] // sh["hkv"]
-    nc = -(-((max_ctx + 63) // 64 * 64) // chunk)
+    nc = -(-int(eng.sizes.kv_slots) // chunk)
     rg = -(-(-(-((K + 1) * G) // 16)) // 8)
     at_kernel = "k_attn_bf16_t%d + k_attn_merge" % (1 if B * sh["hkv"] * nc * rg < 512 else 2)
     at_ach = at_bytes / at_avg_s / 1e9 if at_n else 0.0

@@ -109,6 +109,8 @@ typedef struct orthrus_sizes {
   uint64_t kv_bytes;         /* the shared KV cache */
   uint64_t scratch_bytes;    /* block K/V scratch: 2*L*max_batch*Hkv*K*head_dim*elt */
   uint64_t workspace_bytes;  /* activations, partial results, RoPE table */
+  uint64_t kv_slots;         /* cache slots per (sequence, KV head), "cap": max_ctx
+                                rounded up to a multiple of 64 */
 } orthrus_sizes;
 
 typedef struct orthrus_ctx orthrus_ctx;
@@ -343,8 +345,8 @@ int orthrus_block_attention_noalloc(int32_t batch, int32_t rows, int32_t n_q_hea
  * once per pass.  The rule (measured on the decode workloads): the smallest
  * power of two in [128, 4096] that gives at most 64 chunks per sequence and
  * at most 1100 (chunk, KV head, sequence) workgroups, and at least 1024
- * whenever 1024-key chunks still give 512 of them (cap = max_ctx rounded up
- * to 64 keys per sequence).  Kernel (a) alone (orthrus_block_attention)
+ * whenever 1024-key chunks still give 512 of them (cap = the context's
+ * kv_slots, see orthrus_sizes).  Kernel (a) alone (orthrus_block_attention)
  * chunks its ctx_len keys by its own rule: the smallest power of two in
  * [64, 16384] with at most 64 chunks per sequence and at most 512
  * workgroups (one round of two per compute unit).  Errors: EINVAL

@@ -19,6 +19,9 @@ constexpr int kAlign = 256;
 inline uint64_t al(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
+// KV slots per (sequence, KV head): max_ctx rounded up to whole 64-key tiles
+inline int kv_slots(int max_ctx) { return round_up(max_ctx, 64); }
+
 enum { ST_IDLE = 0, ST_DRAFTED = 1, ST_VERIFIED = 2 };
 
 // canonical tensor numel (see orthrus_weight_tensor)
@@ -133,7 +136,7 @@ void make_layout(const orthrus_config& c, Layout& y) {
   y.L = c.n_layers; y.d = c.d_model; y.hq = c.n_q_heads; y.hkv = c.n_kv_heads; y.hd = c.head_dim;
   y.F = c.ffn_dim; y.V = c.vocab; y.K = c.block_k; y.G = y.hq / y.hkv;
   y.qd = y.hq * y.hd; y.kd = y.hkv * y.hd; y.nqkv = y.qd + 2 * y.kd;
-  y.cap = round_up(c.max_ctx, 64);
+  y.cap = kv_slots(c.max_ctx);
   y.kpad = y.K > 0 ? round_up(y.K, 32) : 0;
   // prompt rows per sequence per prefill pass: about 2048 rows per pass
   // (tall GEMMs, each attention key tile shared by the pass's rows), at
@@ -632,6 +635,7 @@ int orthrus_query_sizes(const orthrus_config* cfg, orthrus_sizes* out) {
   out->kv_bytes = y.kv_bytes;
   out->scratch_bytes = y.scratch_bytes;
   out->workspace_bytes = y.workspace_bytes;
+  out->kv_slots = (uint64_t)y.cap;
   return ORTHRUS_OK;
 }
 
@@ -1100,7 +1104,7 @@ int orthrus_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int32_t 
 
 int32_t orthrus_default_attn_chunk(int32_t max_batch, int32_t max_ctx, int32_t n_kv_heads) {
   if (max_batch < 1 || max_ctx < 1 || n_kv_heads < 1) return ORTHRUS_EINVAL;
-  return default_attn_chunk(max_batch, round_up(max_ctx, 64), n_kv_heads);
+  return default_attn_chunk(max_batch, kv_slots(max_ctx), n_kv_heads);
 }
 
 const char* orthrus_strerror(int code) {

@@ -118,9 +118,10 @@ def test_default_attention_chunk_rule(batch, ctx, kvh, want):
     """The chunk rule the header documents: the smallest power of two in
     [128, 4096] with <= 64 chunks per sequence and <= 1100 (chunk, KV head,
     sequence) workgroups, at least 1024 when 1024-key chunks still give 512
-    workgroups (slots rounded up to 64)."""
+    workgroups (slots: the context's kv_slots)."""
     got = C.orthrus_default_attn_chunk(batch, ctx, kvh)
     assert got == want
+    # the context's kv_slots (include/orthrus.h, orthrus_sizes)
     slots = (ctx + 63) // 64 * 64
     nch = -(-slots // got)
     assert got & (got - 1) == 0 and 128 <= got <= 4096

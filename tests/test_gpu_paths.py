@@ -22,7 +22,7 @@ def poison(eng, bf16):
     and into the whole block scratch."""
     cfg = eng.cfg
     L, hkv, hd, maxB = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.max_batch
-    cap = (cfg.max_ctx + 63) // 64 * 64
+    cap = int(eng.sizes.kv_slots)
     dt = torch.bfloat16 if bf16 else torch.float32
     nan = float("nan")
     kv = eng.kv.view(dt)[:2 * L * maxB * hkv * cap * hd].view(2, L, maxB, hkv, cap, hd)

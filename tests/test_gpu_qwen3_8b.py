@@ -108,7 +108,7 @@ def compare_step(shp, g, prompt, K, tol=TOL, tol_mean=5e-3):
 def load_gpu_cache(eng, seq, L, hkv, hd, n):
     """The GPU's committed cache slots [0, n) of every layer, into the oracle's
     sequence (K rows, V from its 64-key transposed tiles)."""
-    cap = (eng.cfg.max_ctx + 63) // 64 * 64
+    cap = int(eng.sizes.kv_slots)
     kv = eng.kv.view(torch.bfloat16)[:2 * L * hkv * cap * hd].view(2, L, hkv, cap, hd)
     for l in range(L):
         k = kv[0, l, :, :n].float().cpu().numpy().astype(np.float64)

@@ -88,7 +88,7 @@ def test_tiny_draft_leaves_committed_cache_untouched():
         eng.step()
     torch.cuda.synchronize()
     n = int(eng.seq_len[0])
-    cap = (256 + 63) // 64 * 64
+    cap = int(eng.sizes.kv_slots)
     hd, hkv, L = sh["hd"], sh["hkv"], sh["L"]
     kv = eng.kv.view(torch.float32).view(2, L, 1, hkv, cap * hd)
     # committed slots [0, n): K rows; V^T tiles of 64 keys (whole tiles
