@@ -428,11 +428,24 @@ def run_workload(name, S, W, args, headline):
         eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
 
     # events around the dominant kernel's launches in the first roofline
-    # steps of the timed region (the library stops recording at the capacity)
+    # steps of the timed region (the library stops recording at the
+    # capacity).  With --graph the timed steps are replays of one captured
+    # step (no events inside); the per-launch times then come from the
+    # breakdown's eager steps after the timed region.
     n_rs = max(1, min(args.roofline_steps, S))
     rcls = [("draft", "attention"), ("draft", "gate_up")]
     mask = sum(1 << C.timing_class(p, r) for p, r in rcls)
-    C.orthrus_timing_enable(eng.ctx, mask, n_rs * sh["L"] * len(rcls))
+    graph = None
+    if args.graph:
+        pbuf = torch.zeros_like(planted[0])
+        try:
+            graph = eng.capture_step(pbuf)
+        except Exception as ex:          # fall back to eager calls, said in the output
+            log(f"[graph] capture failed ({ex}); timing eager calls")
+            graph = None
+            torch.cuda.synchronize()
+    if graph is None:
+        C.orthrus_timing_enable(eng.ctx, mask, n_rs * sh["L"] * len(rcls))
     torch.cuda.synchronize()
     marker = None
     if args.markers:
@@ -445,10 +458,14 @@ def run_workload(name, S, W, args, headline):
     t_wall = time.perf_counter()
     ev[0].record()
     for s in range(W, W + S):
-        eng.draft()
-        eng.drafts[:B].copy_(planted[s])
-        eng.verify()
-        eng.commit()
+        if graph is not None:
+            pbuf.copy_(planted[s])
+            eng.replay(graph)
+        else:
+            eng.draft()
+            eng.drafts[:B].copy_(planted[s])
+            eng.verify()
+            eng.commit()
         ev[s - W + 1].record()
     if marker is not None:
         C.orthrus_stream_read(marker.data_ptr(), 4096, mout.data_ptr(), 1, eng.s)
@@ -456,8 +473,10 @@ def run_workload(name, S, W, args, headline):
     wall = time.perf_counter() - t_wall
     ms = ev[0].elapsed_time(ev[S])
     step_ms = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(S)])
-    tim, _ = C.orthrus_timing_read(eng.ctx)
-    C.orthrus_timing_enable(eng.ctx, 0, 0)
+    tim = {}
+    if graph is None:
+        tim, _ = C.orthrus_timing_read(eng.ctx)
+        C.orthrus_timing_enable(eng.ctx, 0, 0)
 
     tokens = int((a[W:W + S] + 1).sum())
     ms_step = ms / S
@@ -474,6 +493,22 @@ def run_workload(name, S, W, args, headline):
     # sequence lengths at the start of every step
     n_all = P + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(a + 1, axis=0)])
     n_timed = n_all[W:W + S]
+    n_roof = n_timed          # contexts of the steps whose launches were timed
+    if graph is not None:
+        # eager steps after the timed region for the per-launch times
+        C.orthrus_sync_lengths(eng.ctx, B, seq_len)
+        nr = max(0, min(n_rs, (max_ctx - int(seq_len.max()) - 64) // (K + 1), planted.shape[0] - W))
+        C.orthrus_timing_enable(eng.ctx, mask, max(nr, 1) * sh["L"] * len(rcls))
+        lens = []
+        for j in range(nr):
+            lens.append(eng.seq_len[:B].cpu().numpy().astype(np.int64))
+            eng.draft(); eng.drafts[:B].copy_(planted[W + j]); eng.verify(); eng.commit()
+        torch.cuda.synchronize()
+        tim, _ = C.orthrus_timing_read(eng.ctx)
+        C.orthrus_timing_enable(eng.ctx, 0, 0)
+        if lens:
+            n_roof = np.array(lens)
+        seq_len = eng.seq_len[:B].cpu().numpy()
     roof_s, step_bytes, gemm_flops = 0.0, 0.0, 0.0
     for s in range(S):
         t_, b_, f_ = step_roofline(sh, B, K, n_timed[s])
@@ -482,7 +517,7 @@ def run_workload(name, S, W, args, headline):
     # the dominant kernel: the draft pass's block attention
     at_ms, at_n = tim.get(("draft", "attention"), (0.0, 0))
     at_steps = at_n // sh["L"]
-    at_bytes = (sum(attn_launch_bytes(sh, B, K, n_timed[s], "draft") for s in range(at_steps))
+    at_bytes = (sum(attn_launch_bytes(sh, B, K, n_roof[s], "draft") for s in range(at_steps))
                 / max(at_steps, 1))
     at_avg_s = at_ms / max(at_n, 1) / 1e3
     # the attention kernel the draft pass launches: one query tile per wave
@@ -522,6 +557,7 @@ def run_workload(name, S, W, args, headline):
     torch.cuda.empty_cache()
 
     res = {
+        "graph": graph is not None,
         "workload": workload_desc(name, wl, sh),
         "batch": B, "prompt_len": P, "block_k": K, "attn_chunk": chunk,
         "tokens_per_s": round(tokens / (ms / 1e3), 3),
@@ -576,6 +612,10 @@ def main():
                     help="skip the block-attention microbenchmark and HBM read-rate measurements")
     ap.add_argument("--attn-chunk", type=int, default=0,
                     help="attention key chunk of both contexts (default: the library's rule)")
+    ap.add_argument("--eager", dest="graph", action="store_false",
+                    help="time eager draft/verify/commit calls instead of replays of one "
+                         "captured step (HIP graph; per-launch times then come from eager "
+                         "steps right after the timed region)")
     ap.add_argument("--markers", action="store_true",
                     help="launch a tiny read probe before and after the headline's timed region "
                          "(marks it in a profiler's kernel trace)")
@@ -643,12 +683,15 @@ def main():
             "bytes_per_launch": at["bytes_per_launch"],
             "avg_launch_us": at["avg_launch_us"],
             "launches": at["launches"],
-            "timed_steps": max(1, min(args.roofline_steps, args.steps)),
+            "timed_steps": at["launches"] // sh["L"],
+            "timed_on": ("eager steps right after the timed region (the timed steps are graph replays)"
+                         if res["graph"] else "the first steps of the timed region"),
         },
+        "step_launch": "HIP graph replay of one captured step" if res["graph"] else "eager calls",
     }
     for k, v in res.items():
         if k not in ("workload", "batch", "prompt_len", "block_k", "tokens_per_s", "ms_per_step",
-                     "steps", "warmup"):
+                     "steps", "warmup", "graph"):
             out[k] = v
     out["other_workloads"] = others
     out["kernel_a"] = kernel_a

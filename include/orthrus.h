@@ -228,6 +228,17 @@ int orthrus_commit_kv(orthrus_ctx* ctx, int32_t batch, const int32_t* accept_len
  * Host only; must not be called while a step is in flight (ESTATE). */
 int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len_host);
 
+/* For steps that run without these calls: replays of a HIP graph that
+ * captured one draft_block(_k) -> verify_accept -> commit_kv step (every
+ * call only enqueues kernels and device-to-device work on its stream, so
+ * the three calls can be captured; greedy decoding only, since the
+ * sampling step counter is host state).  Raises the host's length bound of
+ * sequences 0..batch-1 by n_steps * (k + 1), as n_steps eager steps of
+ * block k would; call it before replaying n_steps times.  Errors: EINVAL,
+ * ESTATE (a step in flight, or never prefilled), ECAPACITY (a sequence
+ * could grow past max_ctx: nothing is reserved). */
+int orthrus_reserve_steps(orthrus_ctx* ctx, int32_t batch, int32_t k, int32_t n_steps);
+
 /* Launch timing for profiling.  When enabled, the library records a pair
  * of hipEvents (host-created; no device memory) around every launch of the
  * selected classes on the call's stream.  Class = pass*8 + role with pass

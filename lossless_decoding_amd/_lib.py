@@ -18,7 +18,7 @@ EXPORTED = [
     "orthrus_query_sizes", "orthrus_weight_tensor", "orthrus_create", "orthrus_destroy",
     "orthrus_prefill", "orthrus_draft_block", "orthrus_draft_block_k", "orthrus_draft_refine", "orthrus_verify_accept", "orthrus_commit_kv",
     "orthrus_set_debug", "orthrus_set_debug_layers", "orthrus_set_sampling", "orthrus_sync_lengths", "orthrus_timing_enable", "orthrus_timing_read", "orthrus_block_attention", "orthrus_block_attention_noalloc", "orthrus_attention_workspace",
-    "orthrus_default_attn_chunk", "orthrus_stream_read", "orthrus_gemm_plan",
+    "orthrus_default_attn_chunk", "orthrus_stream_read", "orthrus_gemm_plan", "orthrus_reserve_steps",
     "orthrus_strerror", "orthrus_last_hip_error",
 ]
 
@@ -85,6 +85,7 @@ def lib():
         L.orthrus_set_debug_layers.argtypes = [vp, vp, vp, i32]
         L.orthrus_set_sampling.argtypes = [vp, ctypes.c_float, ctypes.c_uint64]
         L.orthrus_sync_lengths.argtypes = [vp, i32, vp]
+        L.orthrus_reserve_steps.argtypes = [vp, i32, i32, i32]
         L.orthrus_timing_enable.argtypes = [vp, ctypes.c_uint32, i32]
         L.orthrus_timing_read.argtypes = [vp, vp, vp]
         L.orthrus_block_attention.argtypes = [i32, i32, i32, i32, vp, vp, vp, i32, i32, vp, vp,
@@ -176,6 +177,10 @@ def orthrus_set_sampling(ctx, temperature: float, seed: int):
 
 def orthrus_set_debug_layers(ctx, resid, attn32, rows_cap):
     _check("orthrus_set_debug_layers", lib().orthrus_set_debug_layers(ctx, resid, attn32, rows_cap))
+
+
+def orthrus_reserve_steps(ctx, batch, k, n_steps):
+    _check("orthrus_reserve_steps", lib().orthrus_reserve_steps(ctx, batch, k, n_steps))
 
 
 def orthrus_sync_lengths(ctx, batch, seq_len_host: np.ndarray):

@@ -964,6 +964,18 @@ int orthrus_sync_lengths(orthrus_ctx* ctx, int32_t batch, const int32_t* seq_len
   return ORTHRUS_OK;
 }
 
+int orthrus_reserve_steps(orthrus_ctx* ctx, int32_t batch, int32_t k, int32_t n_steps) {
+  if (!ctx || batch < 1 || batch > ctx->cfg.max_batch || k < 0 || k > ctx->y.K || n_steps < 0)
+    return ORTHRUS_EINVAL;
+  if (ctx->state != ST_IDLE) return ORTHRUS_ESTATE;
+  for (int b = 0; b < batch; ++b) {
+    if (ctx->bound[b] < 1) return ORTHRUS_ESTATE;          // never prefilled
+    if ((int64_t)ctx->bound[b] + (int64_t)n_steps * (k + 1) > ctx->cfg.max_ctx) return ORTHRUS_ECAPACITY;
+  }
+  for (int b = 0; b < batch; ++b) ctx->bound[b] += n_steps * (k + 1);
+  return ORTHRUS_OK;
+}
+
 // kernel (a) alone: chunks of the cache keys, at least one (the draft block
 // is streamed by the last chunk, chunk 0 when there are no cache keys)
 static int block_attn_nchunks(int ctx_len, int sc) {

@@ -124,6 +124,37 @@ class Engine:
         self.verify()
         self.commit()
 
+    def capture_step(self, planted: torch.Tensor | None = None) -> torch.cuda.CUDAGraph:
+        """One greedy draft -> verify -> commit step of the current batch as
+        a HIP graph (every call only enqueues work, none allocates or
+        clears memory).  planted: optional device [B][K] int32 buffer whose
+        contents replace the drafts at every replay (fill it before each
+        replay).  Replay with graph.replay() on the engine's stream.  The
+        launches are recorded as they are now: greedy decoding only (the
+        sampling step counter is host state) and the batch size fixed.
+        Replay it with replay(), which first reserves the step's capacity
+        with the library (its host length bound, as an eager step would)."""
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(self.device)
+        cap.wait_stream(self.stream)
+        prev = self.stream
+        try:
+            with torch.cuda.graph(g, stream=cap):
+                self.stream = cap
+                self.step(planted)
+        finally:
+            self.stream = prev
+        self.stream.wait_stream(cap)
+        return g
+
+    def replay(self, graph: torch.cuda.CUDAGraph, n: int = 1):
+        """n replays of a captured step (capture_step), after reserving their
+        capacity (ORTHRUS_ECAPACITY if a sequence could outgrow max_ctx)."""
+        C.orthrus_reserve_steps(self.ctx, self.B, self.K, n)
+        with torch.cuda.stream(self.stream):
+            for _ in range(n):
+                graph.replay()
+
     def generate(self, prompts: np.ndarray, n_new: int, planted=None, record=False, k_policy=None,
                  denoise_steps: int = 1):
         """Greedy generation of n_new tokens per sequence (token 1 is the
