@@ -212,16 +212,16 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def pmc_traffic(fname, workload, src_hash):
-    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was
-    taken on this workload with the current kernel source."""
+def pmc_traffic(fname, workload, src_hash, key="hbm_bytes_per_launch"):
+    """Bytes per launch (HBM by default) from a committed rocprofv3 PMC
+    summary, if it was taken on this workload with the current kernel source."""
     path = os.path.join(PROFILES, fname)
     if not os.path.exists(path):
         return None
     pm = dict(l.split(": ", 1) for l in open(path).read().splitlines()
               if l and not l.startswith("#") and ": " in l)
-    if pm.get("kernel_source_hash") == src_hash and pm.get("workload") == workload:
-        return int(pm["hbm_bytes_per_launch"])
+    if pm.get("kernel_source_hash") == src_hash and pm.get("workload") == workload and key in pm:
+        return int(pm[key])
     return None
 
 
@@ -588,7 +588,11 @@ def run_workload(name, S, W, args, headline):
             "bytes_per_launch": gu_bytes, "avg_launch_us": round(gu_avg_s * 1e6, 3),
             "launches": gu_n, "achieved_GBps": round(gu_ach, 1),
             "hbm_frac": round(gu_ach / HBM_PEAK_GBS, 4),
-            "mfma_frac": round(gu_flops / max(gu_avg_s, 1e-12) / MFMA_PEAK_BF16, 4) if gu_n else 0.0},
+            "mfma_frac": round(gu_flops / max(gu_avg_s, 1e-12) / MFMA_PEAK_BF16, 4) if gu_n else 0.0,
+            "traffic": pmc_traffic("gemm_gateup_draft_%s_pmc.txt" % name, name,
+                                   source_hash("k_gemm.hip")),
+            "l2_read_bytes": pmc_traffic("gemm_gateup_draft_%s_pmc.txt" % name, name,
+                                         source_hash("k_gemm.hip"), "l2_read_bytes_per_launch")},
         "ms_per_step_by_class": breakdown,
         "gemm_classes": gemm_class_rates(breakdown, sh, B, K),
     }
