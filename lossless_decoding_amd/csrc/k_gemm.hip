@@ -679,7 +679,6 @@ __global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
 //    SwiGLU or argmax epilogue.
 #define TRW 5    // row tiles of waves 1-3
 #define TRW0 2   // row tiles of wave 0 (the weight loader)
-#define TS 2     // k-blocks per weight stage
 
 template <int C, int EP, bool SPLIT, bool TWO>
 __global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
@@ -688,6 +687,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
   static_assert(!TWO || SPLIT, "two weight sets: split launches only");
   static_assert(EP != EP_SWIGLU || C % 2 == 0, "SwiGLU pairs gate and up tiles");
   constexpr int NW = TWO ? 2 * C : C;           // weight fragments per k-block
+  // k-blocks per weight stage: one for the widest workgroups, so that wave
+  // 0's prologue wait stays within the memory counter's range
+  constexpr int TS = (NW > 12 || C >= 12) ? 1 : 2;
   constexpr int LPS = NW * TS;                  // weight loads (1 KB) per stage, all by wave 0
   constexpr int TNS = TWO ? 4 : 5;              // weight stages in LDS
   constexpr int TDX = TWO ? 4 : 5;              // activation ring depth (k-blocks)
@@ -1078,7 +1080,9 @@ static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
   if (T < 16 || N % 32 != 0) return false;
   if ((ep == EP_SWIGLU || ep == EP_ARGMAX) && M2 > 0) return false;
   if (ep != EP_SWIGLU && ep != EP_ARGMAX && ep != EP_RESID && ep != EP_QKV) return false;
-  p.C = ep == EP_RESID ? 4 : 6;
+  // split launches keep no running sums, so they take wider column groups:
+  // fewer of them, and fewer reads of the activations (one per group)
+  p.C = ep == EP_RESID ? 8 : (ep == EP_QKV && M2 <= 0 ? 12 : 6);
   if (ep == EP_SWIGLU && (N / 16) % 6 != 0) p.C = 4;   // whole gate/up pairs per workgroup
   p.two = M2 > 0;
   p.nrb = (T + 3 * TRW + TRW0 - 1) / (3 * TRW + TRW0);
@@ -1183,12 +1187,12 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
         hipLaunchKernelGGL(k_amax_rows, dim3(a.M), dim3(64), 0, s, a);
         break;
       case EP_RESID:
-        if (rp.two) gemm_launch(k_gemm_rows<4, EP_RESID, true, true>, g, b, s, a);
-        else gemm_launch(k_gemm_rows<4, EP_RESID, true, false>, g, b, s, a);
+        if (rp.two) gemm_launch(k_gemm_rows<8, EP_RESID, true, true>, g, b, s, a);
+        else gemm_launch(k_gemm_rows<8, EP_RESID, true, false>, g, b, s, a);
         break;
       default:
         if (rp.two) gemm_launch(k_gemm_rows<6, EP_QKV, true, true>, g, b, s, a);
-        else gemm_launch(k_gemm_rows<6, EP_QKV, true, false>, g, b, s, a);
+        else gemm_launch(k_gemm_rows<12, EP_QKV, true, false>, g, b, s, a);
         hipLaunchKernelGGL(k_qkv_finish_bf16, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
         break;
     }
