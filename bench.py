@@ -375,7 +375,9 @@ def run_workload(name, S, W, args, headline):
 
     a = workloads.plant_lengths(W + S, B, K, wl["plant"])
     need = 1 + int((a + 1).sum(0).max()) + K + 2          # trajectory tokens per sequence
-    max_ctx = P + (W + S) * (K + 1) + 64                  # host bound grows K+1 per step
+    # host bound grows K+1 per step: warmup, timed steps, and the eager steps
+    # after them whose launches are timed one by one
+    max_ctx = P + (W + S + max(1, min(args.roofline_steps, S))) * (K + 1) + 64
     t0 = time.time()
     # both contexts fold attention over the same key chunks, so their rows are
     # bit-identical (the lossless check below compares them token for token)
