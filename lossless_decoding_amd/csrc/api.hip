@@ -541,7 +541,13 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       g.dqn = (const uint16_t*)(c->packed + y.p_dqn[l]);
       g.dkn = (const uint16_t*)(c->packed + y.p_dkn[l]);
       g.kc = kc; g.vc = vc; g.ks = ks; g.vs = vs;
-      if (P.kind == PASS_DRAFT) {
+      if (P.kind == PASS_DRAFT && NA > 0 && gemm_bf16_rows_form(BK, y.nqkv, EP_QKV)) {
+        // many mask rows: their own row-split launch (wider column groups than
+        // a two-segment one) and a small launch for the anchor rows; every
+        // row's arithmetic is the same in either form
+        run(g, y.p_dqkv[l], 0, BK, y.d, y.nqkv, EP_QKV);
+        run(g, y.p_qkv[l], RM, NA, y.d, y.nqkv, EP_QKV);
+      } else if (P.kind == PASS_DRAFT) {
         run2(g, y.p_dqkv[l], y.p_qkv[l], y.d, y.nqkv, EP_QKV);
       } else {
         run(g, y.p_qkv[l], 0, rows, y.d, y.nqkv, EP_QKV);

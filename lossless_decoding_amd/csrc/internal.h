@@ -172,6 +172,8 @@ int gemm_bf16_groups(int N);
 // 0, or the K slices whose partials an EP_RESID launch of these rows leaves
 // for the residual + RMSNorm kernel
 int gemm_bf16_split_slices(int M, int M2, int N, int ep);
+// whether a one-segment launch of M rows takes the row-split form
+bool gemm_bf16_rows_form(int M, int N, int ep);
 // fp32: W canonical row-major [N][K] (for SwiGLU: gate at W, up at W2).
 void launch_gemm_f32(const float* W, const float* W2, const float* X, int ldx, int M, int K,
                      int N, const GemmOut& o, hipStream_t s);

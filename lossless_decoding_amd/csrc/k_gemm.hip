@@ -1093,6 +1093,11 @@ static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
   return true;
 }
 
+bool gemm_bf16_rows_form(int M, int N, int ep) {
+  RowsPlan rp;
+  return rows_plan(M, 0, N, ep, rp);
+}
+
 int gemm_bf16_split_slices(int M, int M2, int N, int ep) {
   if (M2 < 0) M2 = 0;
   RowsPlan rp;
