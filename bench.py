@@ -631,7 +631,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the decode step shards by sequence with no "
-              "exchange, and this build runs on a single GPU (no multi-GPU path)", file=sys.stderr)
+              "exchange, and the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     import torch
