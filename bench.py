@@ -110,7 +110,7 @@ def attn_launch_bytes(sh, B, K, n0, kind):
 
 
 def hbm_read_probe(dev, nbytes=4 << 30, reps=10):
-    """The box's achievable HBM read rate: a 4 GiB buffer read once per launch
+    """The device's achievable HBM read rate: a 4 GiB buffer read once per launch
     by the library's read probe (16-byte loads, one XOR fold per workgroup),
     best over three grid sizes."""
     import torch

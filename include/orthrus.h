@@ -380,8 +380,8 @@ int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, int32_t epilo
 /* Measurement aid (not part of the decode step): n_workgroups workgroups
  * read the device buffer buf (bytes, a multiple of 16, 256-byte aligned)
  * once with 16-byte loads and write one XOR fold per workgroup to the device
- * array out[n_workgroups].  Timing it gives the box's achievable HBM read
- * rate for comparison with the published peak.  Errors: EINVAL, EHIP. */
+ * array out[n_workgroups].  Timing it gives the device's achievable HBM
+ * read rate for comparison with the published peak.  Errors: EINVAL, EHIP. */
 int orthrus_stream_read(const void* buf, uint64_t bytes, uint32_t* out, int32_t n_workgroups,
                         void* stream);
 
