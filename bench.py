@@ -54,6 +54,31 @@ def tpf_from_accept(mean_accept: float) -> float:
     return (mean_accept + 1.0) / 2.0
 
 
+def prefill_roofline(sh, B, P, rows_per_pass, prefill_ms):
+    """A lower bound for the prefill of B prompts of P tokens in passes of
+    rows_per_pass rows per sequence: per part, max(bytes / 8 TB/s, flops /
+    2.5 PFLOP/s).  GEMMs: every pass reads the frozen view's layer weights
+    once (bf16) and multiplies them with its rows, plus the LM head for the
+    last row of each sequence.  Attention: a prompt row at position t sees
+    t + 1 keys (Q.K and P.V, 4 flops per key and dimension per query head);
+    a pass reads the cache keys and values its rows can see once and writes
+    its own."""
+    L, d, hq, hkv, hd, F, V = (sh[k] for k in ("L", "d", "hq", "hkv", "hd", "F", "V"))
+    layer_params = d * (hq + 2 * hkv) * hd + hq * hd * d + 3 * F * d
+    passes = -(-P // rows_per_pass)
+    gemm_flops = 2.0 * L * layer_params * B * P + 2.0 * d * V * B
+    gemm_bytes = 2.0 * (passes * L * layer_params + d * V)
+    attn_flops = 4.0 * hd * hq * L * B * P * (P + 1) / 2
+    seen = sum(min(P, (p + 1) * rows_per_pass) for p in range(passes))
+    kv_bytes = kv_bytes_per_token(sh) * B * (seen + P)
+    g = max(gemm_bytes / (HBM_PEAK_GBS * 1e9), gemm_flops / MFMA_PEAK_BF16)
+    a = max(kv_bytes / (HBM_PEAK_GBS * 1e9), attn_flops / MFMA_PEAK_BF16)
+    return {"method": "GEMMs and attention, each max(bytes / 8 TB/s, flops / 2.5 PFLOP/s)",
+            "passes": passes, "gemm_tflop": round(gemm_flops / 1e12, 1),
+            "attention_tflop": round(attn_flops / 1e12, 1),
+            "roofline_ms": round((g + a) * 1e3, 3), "frac": round((g + a) * 1e3 / prefill_ms, 4)}
+
+
 def kv_bytes_per_token(sh):
     """K and V of one token, all layers, bf16."""
     return sh["L"] * 2 * sh["hkv"] * sh["hd"] * 2
@@ -425,7 +450,8 @@ def run_workload(name, S, W, args, headline):
     p1.record()
     torch.cuda.synchronize()
     prefill_ms = p0.elapsed_time(p1)
-    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms")
+    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms "
+        f"(roofline {prefill_roofline(sh, B, P, int(eng.sizes.prefill_rows), prefill_ms)['frac']:.3f})")
     for s in range(W):
         eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
 
@@ -571,6 +597,7 @@ def run_workload(name, S, W, args, headline):
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(B * P / (prefill_ms / 1e3), 1),
+        "prefill_roofline": prefill_roofline(sh, B, P, int(eng.sizes.prefill_rows), prefill_ms),
         "lossless_vs_greedy": lossless,
         "plain_decoding_tokens_per_s": round(plain_tps, 3),
         "speedup_vs_plain_decoding": round(tokens / (ms / 1e3) / plain_tps, 4),

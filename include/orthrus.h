@@ -111,6 +111,9 @@ typedef struct orthrus_sizes {
   uint64_t workspace_bytes;  /* activations, partial results, RoPE table */
   uint64_t kv_slots;         /* cache slots per (sequence, KV head), "cap": max_ctx
                                 rounded up to a multiple of 64 */
+  uint64_t prefill_rows;     /* prompt rows per sequence in one orthrus_prefill pass:
+                                2048 / max_batch rounded down to a multiple of 32,
+                                clamped to [32, 256] */
 } orthrus_sizes;
 
 typedef struct orthrus_ctx orthrus_ctx;

@@ -51,7 +51,8 @@ class OrthrusConfig(ctypes.Structure):
 class OrthrusSizes(ctypes.Structure):
     _fields_ = [("weights_bytes", ctypes.c_uint64), ("packed_bytes", ctypes.c_uint64),
                 ("kv_bytes", ctypes.c_uint64), ("scratch_bytes", ctypes.c_uint64),
-                ("workspace_bytes", ctypes.c_uint64), ("kv_slots", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("kv_slots", ctypes.c_uint64),
+                ("prefill_rows", ctypes.c_uint64)]
 
 
 _lib = None

@@ -642,6 +642,7 @@ int orthrus_query_sizes(const orthrus_config* cfg, orthrus_sizes* out) {
   out->scratch_bytes = y.scratch_bytes;
   out->workspace_bytes = y.workspace_bytes;
   out->kv_slots = (uint64_t)y.cap;
+  out->prefill_rows = (uint64_t)y.pchunk;
   return ORTHRUS_OK;
 }
 

@@ -162,3 +162,14 @@ def test_default_attention_chunk_rejects_bad_args():
         C.orthrus_default_attn_chunk(0, 1024, 8)
     with pytest.raises(C.OrthrusError):
         C.orthrus_default_attn_chunk(1, 1024, 0)
+
+
+@pytest.mark.parametrize("batch,want", [(1, 256), (4, 256), (8, 256), (12, 160), (16, 128), (64, 32),
+                                        (128, 32)])
+def test_sizes_report_cache_slots_and_prefill_rows(batch, want):
+    """orthrus_query_sizes: kv_slots is max_ctx rounded up to 64, and
+    prefill_rows (prompt rows per sequence in one prefill pass) is 2048 /
+    max_batch rounded down to a multiple of 32, clamped to [32, 256]."""
+    s = C.orthrus_query_sizes(cfg_of("small", max_batch=batch, max_ctx=1000))
+    assert s.kv_slots == 1024
+    assert s.prefill_rows == want
