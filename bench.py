@@ -450,8 +450,8 @@ def run_workload(name, S, W, args, headline):
     p1.record()
     torch.cuda.synchronize()
     prefill_ms = p0.elapsed_time(p1)
-    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms "
-        f"(roofline {prefill_roofline(sh, B, P, int(eng.sizes.prefill_rows), prefill_ms)['frac']:.3f})")
+    prefill_roof = prefill_roofline(sh, B, P, int(eng.sizes.prefill_rows), prefill_ms)
+    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms (roofline {prefill_roof['frac']:.3f})")
     for s in range(W):
         eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
 
@@ -597,7 +597,7 @@ def run_workload(name, S, W, args, headline):
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(B * P / (prefill_ms / 1e3), 1),
-        "prefill_roofline": prefill_roofline(sh, B, P, int(eng.sizes.prefill_rows), prefill_ms),
+        "prefill_roofline": prefill_roof,
         "lossless_vs_greedy": lossless,
         "plain_decoding_tokens_per_s": round(plain_tps, 3),
         "speedup_vs_plain_decoding": round(tokens / (ms / 1e3) / plain_tps, 4),
