@@ -676,14 +676,16 @@ __global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
 //    may share a row block: the workgroup then stages both weight sets.
 //  * Split launches (O, down, QKV) give each K slice its own workgroup and
 //    write the slice partials for the next kernel; unsplit launches run the
-//    SwiGLU or argmax epilogue.
+//    SwiGLU or argmax epilogue, or (O and down in prefill passes, whose row
+//    blocks alone fill the chip) add their sums to the residual in place.
 #define TRW 5    // row tiles of waves 1-3
 #define TRW0 2   // row tiles of wave 0 (the weight loader)
 
 template <int C, int EP, bool SPLIT, bool TWO>
 __global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
-  static_assert(SPLIT ? (EP == EP_RESID || EP == EP_QKV) : (EP == EP_SWIGLU || EP == EP_ARGMAX),
-                "split launches write partials; unsplit ones run SwiGLU or argmax");
+  static_assert(SPLIT ? (EP == EP_RESID || EP == EP_QKV)
+                      : (EP == EP_SWIGLU || EP == EP_ARGMAX || EP == EP_RESID),
+                "split launches write partials; unsplit ones run SwiGLU, argmax or the residual add");
   static_assert(!TWO || SPLIT, "two weight sets: split launches only");
   static_assert(EP != EP_SWIGLU || C % 2 == 0, "SwiGLU pairs gate and up tiles");
   constexpr int NW = TWO ? 2 * C : C;           // weight fragments per k-block
@@ -937,6 +939,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
     }
     return;
   }
+  if constexpr (EP == EP_RESID) {
+    // the residual add in place, h + (slice-ordered sum): the value the
+    // residual-norm kernel forms from a split launch's partials
+#pragma unroll
+    for (int jj = 0; jj < TRW; ++jj) {
+      if (lr >= vrow[jj]) continue;
+      float* yp = a.y + (size_t)(rowb[jj] + lr) * a.ldy + ct0 * 16 + lq * 4;
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (c >= nct) break;
+        floatx4_t hv = *(const floatx4_t*)(yp + c * 16);
+        hv[0] += cur[jj][c][0]; hv[1] += cur[jj][c][1];
+        hv[2] += cur[jj][c][2]; hv[3] += cur[jj][c][3];
+        *(floatx4_t*)(yp + c * 16) = hv;
+      }
+    }
+    return;
+  }
   if constexpr (EP == EP_SWIGLU) {
     // gate (even tile) and up (odd tile) of one 16-column act block
 #pragma unroll
@@ -1072,7 +1092,7 @@ static bool rows144_pad_less(int M) { return (M + 143) / 144 * 144 < (M + 127) /
 // then one workgroup per compute unit at 272 rows), argmax and QKV, 4 for
 // the residual GEMMs (512 workgroups at Qwen3-8B width); row blocks of at
 // most 3 * TRW + TRW0 tiles, balanced.
-struct RowsPlan { int C, two, nrb, tb, ng, wgs; };
+struct RowsPlan { int C, two, split, nrb, tb, ng, wgs; };
 
 static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
   if (M2 < 0) M2 = 0;
@@ -1080,15 +1100,19 @@ static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
   if (T < 16 || N % 32 != 0) return false;
   if ((ep == EP_SWIGLU || ep == EP_ARGMAX) && M2 > 0) return false;
   if (ep != EP_SWIGLU && ep != EP_ARGMAX && ep != EP_RESID && ep != EP_QKV) return false;
-  // split launches keep no running sums, so they take wider column groups:
-  // fewer of them, and fewer reads of the activations (one per group)
-  p.C = ep == EP_RESID ? 8 : (ep == EP_QKV && M2 <= 0 ? 12 : 6);
-  if (ep == EP_SWIGLU && (N / 16) % 6 != 0) p.C = 4;   // whole gate/up pairs per workgroup
   p.two = M2 > 0;
   p.nrb = (T + 3 * TRW + TRW0 - 1) / (3 * TRW + TRW0);
   p.tb = (T + p.nrb - 1) / p.nrb;
+  // QKV always splits K; the residual GEMMs split K unless their row blocks
+  // alone give two full rounds of workgroups at 4 column tiles (prefill
+  // passes), where the slice partials would only add memory traffic
+  p.split = ep == EP_QKV || (ep == EP_RESID && (p.two || (N / 16 + 3) / 4 * p.nrb < 512));
+  // split launches keep no running sums, so they take wider column groups:
+  // fewer of them, and fewer reads of the activations (one per group)
+  p.C = p.split ? (ep == EP_RESID ? 8 : (M2 <= 0 ? 12 : 6)) : (ep == EP_RESID ? 4 : 6);
+  if (ep == EP_SWIGLU && (N / 16) % 6 != 0) p.C = 4;   // whole gate/up pairs per workgroup
   p.ng = (N / 16 + p.C - 1) / p.C;
-  const int ngs = p.ng * ((ep == EP_RESID || ep == EP_QKV) ? NSL : 1);
+  const int ngs = p.ng * (p.split ? NSL : 1);
   p.wgs = (ngs + 7) / 8 * 8 * p.nrb;
   return true;
 }
@@ -1101,7 +1125,7 @@ bool gemm_bf16_rows_form(int M, int N, int ep) {
 int gemm_bf16_split_slices(int M, int M2, int N, int ep) {
   if (M2 < 0) M2 = 0;
   RowsPlan rp;
-  if (rows_plan(M, M2, N, ep, rp)) return (ep == EP_RESID || ep == EP_QKV) ? NSL : 0;
+  if (rows_plan(M, M2, N, ep, rp)) return rp.split ? NSL : 0;
   int rpw = gemm_rows_per_wg(M, M2);
   int gy = (M + rpw - 1) / rpw + (M2 + rpw - 1) / rpw;
   // QKV takes 64-row tiles where 128-row tiles give fewer than 192
@@ -1162,7 +1186,7 @@ extern "C" int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, in
     return ORTHRUS_EINVAL;
   RowsPlan rp;
   if (rows_plan(m, m2, n, epilogue, rp)) {
-    plan[0] = rp.tb; plan[1] = 4; plan[2] = epilogue == EP_RESID || epilogue == EP_QKV;
+    plan[0] = rp.tb; plan[1] = 4; plan[2] = rp.split;
     plan[3] = rp.C; plan[4] = rp.wgs; plan[5] = 1 + rp.two;
     return ORTHRUS_OK;
   }
@@ -1192,7 +1216,8 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
         hipLaunchKernelGGL(k_amax_rows, dim3(a.M), dim3(64), 0, s, a);
         break;
       case EP_RESID:
-        if (rp.two) gemm_launch(k_gemm_rows<8, EP_RESID, true, true>, g, b, s, a);
+        if (!rp.split) gemm_launch(k_gemm_rows<4, EP_RESID, false, false>, g, b, s, a);
+        else if (rp.two) gemm_launch(k_gemm_rows<8, EP_RESID, true, true>, g, b, s, a);
         else gemm_launch(k_gemm_rows<8, EP_RESID, true, false>, g, b, s, a);
         break;
       default:

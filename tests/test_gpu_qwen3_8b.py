@@ -264,3 +264,76 @@ def test_qwen3_8b_single_layer_batch_against_oracle(B):
     g = one_step(cfg, w, prompt, K, V, B)
     del w
     compare_step(H.shape("qwen3_8b", L=1), g, prompt[:1], K)
+
+
+def test_qwen3_8b_single_layer_full_prefill_pass_against_oracle():
+    """One layer at full width, 32 prompts of 61 tokens: the prefill is one
+    pass of 32 x 60 rows, where the O and down projections run unsplit and
+    add their sums to the residual in place (the residual-norm kernel then
+    reads no partials).  Sequence 0's last-row logits within 2e-2 of the
+    oracle's prefill and its first token the oracle's argmax (or, within
+    the near-tie margin, its runner-up).  (The draft rows that follow are
+    held to the oracle by the tests above; the exactness of this pass
+    against the split form is the next test.)"""
+    sh = workloads.SHAPES["qwen3_8b"]
+    V, B, P = sh["V"], 32, 61
+    plan = C.orthrus_gemm_plan(B * (P - 1), 0, sh["d"], sh["F"], C.EP_RESID)
+    assert plan["form"] == 1 and not plan["split"], plan
+    cfg = U.cfg_of("qwen3_8b", max_batch=B, max_ctx=P + 64, n_layers=1)
+    lay, total = C.weight_layout(cfg)
+    w = fill_weights_device(lay, total, True)
+    eng = Engine(cfg, w)
+    assert int(eng.sizes.prefill_rows) >= P - 1
+    lg = torch.zeros(B, V, device="cuda")
+    eng.set_debug(lg, None, B)
+    prompt = workloads.prompts(B, P, V, seed=25)
+    eng.prefill(prompt)
+    torch.cuda.synchronize()
+    got, pend = lg[0].cpu().numpy().astype(np.float64), int(eng.pending[0])
+    eng.close()
+    del w
+    shp = H.shape("qwen3_8b", L=1)
+    _, want = oracle.Model(shp, H.weights(shp)).seq(P + 4).prefill(prompt[0], want_logits=True)
+    d = np.abs(got - want)
+    assert d.max() < TOL and d.mean() < 5e-3, (d.max(), d.mean())
+    check_token(pend, want)
+
+
+def test_qwen3_8b_prefill_one_pass_equals_two_passes():
+    """Two layers at full width, 8 prompts of 256 tokens, prefilled in one
+    pass of 8 x 255 rows (max_batch 8: O and down unsplit, adding to the
+    residual in place) and in two passes of 8 x 128 and 8 x 127 rows
+    (max_batch 16: O and down split into slice partials summed by the
+    residual-norm kernel).  Both forms sum the same slices in the same order
+    and attention folds the same key chunks, so the last rows' logits, the
+    first tokens and every cache slot agree bit for bit."""
+    sh = workloads.SHAPES["qwen3_8b"]
+    V, B, P, L = sh["V"], 8, 256, 2
+    assert not C.orthrus_gemm_plan(B * (P - 1), 0, sh["d"], sh["F"], C.EP_RESID)["split"]
+    assert C.orthrus_gemm_plan(B * 128, 0, sh["d"], sh["F"], C.EP_RESID)["split"]
+    prompt = workloads.prompts(B, P, V, seed=26)
+    w = None
+    got = []
+    for mb, rows in ((8, 256), (16, 128)):
+        cfg = U.cfg_of("qwen3_8b", max_batch=mb, max_ctx=P + 64, n_layers=L)
+        if w is None:
+            lay, total = C.weight_layout(cfg)
+            w = fill_weights_device(lay, total, True)
+        eng = Engine(cfg, w)
+        assert int(eng.sizes.prefill_rows) == rows
+        lg = torch.zeros(mb, V, device="cuda")
+        eng.set_debug(lg, None, mb)
+        eng.prefill(prompt)
+        torch.cuda.synchronize()
+        cap, hkv, hd = int(eng.sizes.kv_slots), sh["hkv"], sh["hd"]
+        kv = eng.kv.view(torch.bfloat16)[:2 * L * mb * hkv * cap * hd].view(2, L, mb, hkv, cap, hd)
+        got.append(dict(logits=lg[:B].cpu().clone(), pending=eng.pending[:B].cpu().clone(),
+                        k=kv[0, :, :B, :, :P].cpu().clone(),
+                        v=kv[1, :, :B].reshape(L, B, hkv, cap // 64, hd, 64)[:, :, :, :P // 64].cpu().clone()))
+        eng.close()
+    del w
+    a, b = got
+    assert torch.equal(a["pending"], b["pending"])
+    assert torch.equal(a["logits"], b["logits"])
+    assert torch.equal(a["k"].view(torch.int16), b["k"].view(torch.int16))
+    assert torch.equal(a["v"].view(torch.int16), b["v"].view(torch.int16))
