@@ -642,13 +642,15 @@ __global__ __launch_bounds__(WV * 64, (SPLIT && MT <= 2) ? 4 : 2) void k_gemm_bf
 // Split QKV projection, second half: one wave per (row, head) adds the 8
 // slice partials in slice order and runs the QK-norm / RoPE / placement
 // epilogue.  Rows [0, M) are segment 0 (from row0), [M, M + M2) segment 1.
+// NS = 1: an unsplit launch stored its slice-ordered sums in slice 0.
+template <int NS>
 __global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
   const int r = blockIdx.x, ng = blockIdx.y, lane = threadIdx.x;
   const int prow = r < a.M ? a.row0 + r : a.row02 + (r - a.M);
   const float* p = a.rpart + (size_t)prow * a.N + ng * 128 + lane;
   float x1 = p[0], x2 = p[64];
 #pragma unroll
-  for (int sl = 1; sl < NSL; ++sl) {
+  for (int sl = 1; sl < NS; ++sl) {
     x1 += p[(size_t)sl * a.rps];
     x2 += p[(size_t)sl * a.rps + 64];
   }
@@ -676,16 +678,18 @@ __global__ __launch_bounds__(64) void k_qkv_finish_bf16(GemmArgs a) {
 //    may share a row block: the workgroup then stages both weight sets.
 //  * Split launches (O, down, QKV) give each K slice its own workgroup and
 //    write the slice partials for the next kernel; unsplit launches run the
-//    SwiGLU or argmax epilogue, or (O and down in prefill passes, whose row
-//    blocks alone fill the chip) add their sums to the residual in place.
+//    SwiGLU or argmax epilogue, or (O, down and QKV in prefill passes, whose
+//    row blocks alone fill the chip) add their sums to the residual in place
+//    or store them for the QKV finish kernel.
 #define TRW 5    // row tiles of waves 1-3
 #define TRW0 2   // row tiles of wave 0 (the weight loader)
 
 template <int C, int EP, bool SPLIT, bool TWO>
 __global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
   static_assert(SPLIT ? (EP == EP_RESID || EP == EP_QKV)
-                      : (EP == EP_SWIGLU || EP == EP_ARGMAX || EP == EP_RESID),
-                "split launches write partials; unsplit ones run SwiGLU, argmax or the residual add");
+                      : (EP == EP_SWIGLU || EP == EP_ARGMAX || EP == EP_RESID || EP == EP_QKV),
+                "split launches write partials; unsplit ones run SwiGLU, argmax, the residual add or "
+                "store QKV sums");
   static_assert(!TWO || SPLIT, "two weight sets: split launches only");
   static_assert(EP != EP_SWIGLU || C % 2 == 0, "SwiGLU pairs gate and up tiles");
   constexpr int NW = TWO ? 2 * C : C;           // weight fragments per k-block
@@ -928,7 +932,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_rows(GemmArgs a) {
 
   // ============================ epilogues
   // lane (lr, lq): rows rowb[jj] + lr, columns (ct0 + c)*16 + lq*4 + i
-  if constexpr (SPLIT) {
+  // split launches: slice sl's partials; unsplit QKV: the slice-ordered
+  // sums, as slice 0 (the finish kernel then adds nothing)
+  if constexpr (SPLIT || EP == EP_QKV) {
 #pragma unroll
     for (int jj = 0; jj < TRW; ++jj) {
       if (lr >= vrow[jj]) continue;
@@ -1103,13 +1109,14 @@ static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
   p.two = M2 > 0;
   p.nrb = (T + 3 * TRW + TRW0 - 1) / (3 * TRW + TRW0);
   p.tb = (T + p.nrb - 1) / p.nrb;
-  // QKV always splits K; the residual GEMMs split K unless their row blocks
-  // alone give two full rounds of workgroups at 4 column tiles (prefill
-  // passes), where the slice partials would only add memory traffic
-  p.split = ep == EP_QKV || (ep == EP_RESID && (p.two || (N / 16 + 3) / 4 * p.nrb < 512));
+  // QKV and the residual GEMMs split K unless their row blocks alone give
+  // two full rounds of workgroups at 4 column tiles (prefill passes), where
+  // the slice partials would only add memory traffic (unsplit QKV still
+  // leaves its sums to the finish kernel, which needs whole heads)
+  p.split = (ep == EP_QKV || ep == EP_RESID) && (p.two || (N / 16 + 3) / 4 * p.nrb < 512);
   // split launches keep no running sums, so they take wider column groups:
   // fewer of them, and fewer reads of the activations (one per group)
-  p.C = p.split ? (ep == EP_RESID ? 8 : (M2 <= 0 ? 12 : 6)) : (ep == EP_RESID ? 4 : 6);
+  p.C = p.split ? (ep == EP_RESID ? 8 : (M2 <= 0 ? 12 : 6)) : (ep == EP_RESID || ep == EP_QKV ? 4 : 6);
   if (ep == EP_SWIGLU && (N / 16) % 6 != 0) p.C = 4;   // whole gate/up pairs per workgroup
   p.ng = (N / 16 + p.C - 1) / p.C;
   const int ngs = p.ng * (p.split ? NSL : 1);
@@ -1221,9 +1228,14 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
         else gemm_launch(k_gemm_rows<8, EP_RESID, true, false>, g, b, s, a);
         break;
       default:
+        if (!rp.split) {
+          gemm_launch(k_gemm_rows<4, EP_QKV, false, false>, g, b, s, a);
+          hipLaunchKernelGGL(k_qkv_finish_bf16<1>, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+          break;
+        }
         if (rp.two) gemm_launch(k_gemm_rows<6, EP_QKV, true, true>, g, b, s, a);
         else gemm_launch(k_gemm_rows<12, EP_QKV, true, false>, g, b, s, a);
-        hipLaunchKernelGGL(k_qkv_finish_bf16, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(k_qkv_finish_bf16<NSL>, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
         break;
     }
     return;
@@ -1249,7 +1261,7 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
       case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
       case EP_QKV:
         dispatch_mt<EP_QKV, 8, true>(MT, grid, a, s);
-        hipLaunchKernelGGL(k_qkv_finish_bf16, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+        hipLaunchKernelGGL(k_qkv_finish_bf16<NSL>, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
         break;
       default: dispatch_mt<EP_ARGMAX, 8, true>(MT, grid, a, s); break;
     }
