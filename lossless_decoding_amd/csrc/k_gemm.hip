@@ -1093,11 +1093,13 @@ static bool rows144_pad_less(int M) { return (M + 143) / 144 * 144 < (M + 127) /
 // + RMSNorm kernel that follows must add that many slice partials.
 // The row-split form (k_gemm_rows) takes launches of at least 16 row tiles
 // (256 rows) with 16-column tiles in whole pairs: SwiGLU and argmax unsplit
-// (one weight set), QKV and the residual GEMMs split into the 8 K slices.
-// Column tiles per workgroup: 6 for SwiGLU (the Qwen3-8B gate/up GEMM is
-// then one workgroup per compute unit at 272 rows), argmax and QKV, 4 for
-// the residual GEMMs (512 workgroups at Qwen3-8B width); row blocks of at
-// most 3 * TRW + TRW0 tiles, balanced.
+// (one weight set); QKV and the residual GEMMs split into the 8 K slices,
+// except in launches whose row blocks alone give two full rounds (prefill
+// passes).  Column tiles per workgroup: 6 for SwiGLU (the Qwen3-8B gate/up
+// GEMM is then one workgroup per compute unit at 272 rows), argmax and
+// two-segment QKV; split, 12 for one-segment QKV and 8 for the residual
+// GEMMs; unsplit, 4 for QKV and the residual GEMMs.  Row blocks of at most
+// 3 * TRW + TRW0 tiles, balanced.
 struct RowsPlan { int C, two, split, nrb, tb, ng, wgs; };
 
 static bool rows_plan(int M, int M2, int N, int ep, RowsPlan& p) {
