@@ -4,20 +4,23 @@ layers, bf16), K = 32, 16 sequences after 8192-token prompts and 8 after
 planted drafts with the workload's accept-length law).
 
 The oracle cannot prefill prompts this long (one layer over 1024 tokens
-takes minutes on the host), so these tests check properties that hold at
-any size:
-  * lossless: draft/verify decoding emits exactly the tokens of the GPU's own
-    greedy decoding (the K = 0 twin), and every planted block is accepted to
-    its planted length;
-  * batch invariance: a sequence decoded inside the full batch gets the same
-    tokens and bit-identical verify logits as the same sequence decoded
-    alone.
-Attention at these shapes is checked against the oracle on sampled rows in
-test_gpu_attention; the layer arithmetic is checked against the oracle at
-the full model shape in test_gpu_qwen3_8b."""
+takes minutes on the host), so two kinds of checks run here:
+  * properties that hold at any size.  Lossless: draft/verify decoding emits
+    exactly the tokens of the GPU's own greedy decoding (the K = 0 twin), and
+    every planted block is accepted to its planted length.  Batch
+    invariance: a sequence decoded inside the full batch gets the same tokens
+    and bit-identical verify logits as the same sequence decoded alone;
+  * oracle parity on samples the oracle can compute: one step, teacher-forced
+    at three layers (the GPU's own layer inputs and committed cache loaded
+    into the oracle) for the first and the last sequence of the batch.
+Attention at these shapes is also checked against the oracle on sampled rows
+in test_gpu_attention; every layer is checked against the oracle at the full
+model shape (batch 1, short prompt) in test_gpu_qwen3_8b."""
 import numpy as np
 import pytest
 import torch
+
+import oracle
 
 from lossless_decoding_amd import _lib as C
 from lossless_decoding_amd.engine import Engine, attn_chunk_for
@@ -110,3 +113,128 @@ def test_full_size_lossless_and_batch_invariant(name, weights8b_full):
     solo.close()
     assert got1[0] == got[0]
     assert torch.equal(lg1, lg[:K])
+
+
+CHECK_LAYERS = (0, 18, 35)
+
+
+@pytest.mark.parametrize("name", ["qwen3_8b_b16_c8192", "qwen3_8b_b8_c32768"])
+def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
+    """Oracle parity at the full sizes, in the launch configuration bench.py
+    times: prefill of the whole batch, then one draft/verify/commit step of
+    every sequence (its own drafts).  For the first and the last sequence,
+    at layers 0, 18 and 35 of both passes, the oracle (float64, the GPU's
+    committed cache of that layer loaded into it) recomputes the attention of
+    the anchor, mask and verify rows from the GPU's layer-input rows and
+    compares it with the GPU's before rounding, and recomputes the rest of
+    the layer from the GPU's layer input and bf16 attention output; the final
+    logits come from the GPU's last residual rows.  All within 2e-2; every
+    token is the oracle's argmax or, at an oracle near-tie, its runner-up;
+    the accept length is the oracle's prefix rule on the GPU's drafts and
+    tokens, and the commit moves the sequence by exactly m + 1."""
+    from lossless_decoding_amd.layout import untile_v
+    from tests import gpu_util as U
+    from tests.test_gpu_qwen3_8b import TOL, check_token
+
+    wl = workloads.WORKLOADS[name]
+    sh = workloads.SHAPES[wl["shape"]]
+    B, P, K, V = wl["B"], wl["P"], sh["K"], sh["V"]
+    L, d, hkv, hd = sh["L"], sh["d"], sh["hkv"], sh["hd"]
+    qd = sh["hq"] * hd
+    max_ctx = P + STEPS * (K + 1) + 64
+    chunk = attn_chunk_for(max_ctx, B, hkv)
+    print(f"[{name}] teacher-forced: B={B} P={P} K={K} chunk={chunk} layers={CHECK_LAYERS}",
+          flush=True)
+    prompts = workloads.prompts(B, P, V)
+    eng = make(sh, K, B, max_ctx, chunk, weights8b_full)
+    RA = U.anchor_row(K, B)
+    rows = RA + B
+    lg = torch.zeros(rows, V, device="cuda")
+    atb = torch.zeros(L, rows, qd, dtype=torch.bfloat16, device="cuda")
+    resid = torch.zeros(L + 1, rows, d, device="cuda")
+    at32 = torch.zeros(L, rows, qd, device="cuda")
+    eng.set_debug(lg, atb, rows)
+    eng.set_debug_layers(resid, at32, rows)
+    eng.prefill(prompts)
+    torch.cuda.synchronize()
+    n0 = eng.seq_len[:B].cpu().numpy().copy()
+    assert (n0 == P).all()
+
+    lay = list(CHECK_LAYERS)
+    lay1 = [l + 1 for l in CHECK_LAYERS]
+
+    def grab(nrows):
+        """The checked layers' taps of one pass, on the host (float64)."""
+        f = lambda t: t.float().cpu().numpy().astype(np.float64)   # noqa: E731
+        return dict(R=f(resid[lay, :nrows]), R1=f(resid[lay1, :nrows]), RL=f(resid[L, :nrows]),
+                    A32=f(at32[lay, :nrows]), AB=f(atb[lay, :nrows]), lg=f(lg[:nrows]))
+
+    eng.draft()
+    torch.cuda.synchronize()
+    gd = grab(rows)
+    drafts = eng.drafts[:B].cpu().numpy().copy()
+    eng.verify()
+    torch.cuda.synchronize()
+    gv = grab(B * K)
+    ar = eng.ar[:B].cpu().numpy().copy()
+    acc = eng.accept[:B].cpu().numpy().copy()
+    eng.commit()
+    torch.cuda.synchronize()
+    assert np.array_equal(eng.commit_start[:B].cpu().numpy(), n0)
+    assert np.array_equal(eng.seq_len[:B].cpu().numpy(), n0 + 1 + acc)
+    assert np.array_equal(eng.pending[:B].cpu().numpy(), ar[np.arange(B), acc])
+
+    cap = int(eng.sizes.kv_slots)
+    kv = eng.kv.view(torch.bfloat16)[:2 * L * eng.cfg.max_batch * hkv * cap * hd]
+    kv = kv.view(2, L, eng.cfg.max_batch, hkv, cap, hd)
+    m = U.oracle_model(wl["shape"])
+    worst = dict(attn=0.0, h=0.0, logits=0.0)
+    events = 0
+    for b in sorted({0, B - 1}):
+        n = int(n0[b])
+        seq = m.seq(n + K + 2)
+        for l in CHECK_LAYERS:
+            k = kv[0, l, b, :, :n].float().cpu().numpy().astype(np.float64)
+            v = untile_v(kv[1, l, b].reshape(hkv, cap // 64, hd, 64))[:, :n]
+            seq.load_kv(l, k, v.float().cpu().numpy().astype(np.float64))
+        seq.len = n
+        mk, an = slice(b * K, (b + 1) * K), slice(RA + b, RA + b + 1)
+
+        def hold(i, g, o_o, sl, diffusion):
+            ea = np.abs(o_o - g["A32"][i, sl]).max()
+            h_o = m.layer_tail(CHECK_LAYERS[i], g["R"][i, sl], g["AB"][i, sl], diffusion=diffusion)
+            eh = np.abs(h_o - g["R1"][i, sl]).max()
+            worst["attn"] = max(worst["attn"], ea)
+            worst["h"] = max(worst["h"], eh)
+            assert ea < TOL and eh < TOL, (b, CHECK_LAYERS[i], ea, eh)
+
+        # draft pass: the anchor at slot n (its K/V into the oracle's slot n
+        # of the layer), then the mask rows over [0, n] and the block
+        for i, l in enumerate(CHECK_LAYERS):
+            _, o_a = seq.ar_layer(l, gd["R"][i, an], n)
+            hold(i, gd, o_a, an, False)
+            _, o_m = seq.draft_layer(l, gd["R"][i, mk], n)
+            hold(i, gd, o_m, mk, True)
+        lo, _ = m.final(np.concatenate([gd["RL"][mk], gd["RL"][an]]))
+        gl = np.concatenate([gd["lg"][mk], gd["lg"][an]])
+        e = np.abs(lo - gl).max()
+        worst["logits"] = max(worst["logits"], e)
+        assert e < TOL, (b, e)
+        events += sum(check_token(drafts[b, i], lo[i]) for i in range(K))
+        events += check_token(ar[b, 0], lo[K])
+        # verify pass: rows at n+1 .. n+K, causal over the cache, the
+        # anchor's slot n included
+        for i, l in enumerate(CHECK_LAYERS):
+            _, o_v = seq.ar_layer(l, gv["R"][i, mk], n + 1)
+            hold(i, gv, o_v, mk, False)
+        lo, _ = m.final(gv["RL"][mk])
+        e = np.abs(lo - gv["lg"][mk]).max()
+        worst["logits"] = max(worst["logits"], e)
+        assert e < TOL, (b, e)
+        events += sum(check_token(ar[b, 1 + i], lo[i]) for i in range(K))
+        assert acc[b] == oracle.accept(drafts[b], ar[b])
+        del seq
+    eng.close()
+    print(f"[{name}] teacher-forced layers {CHECK_LAYERS}: max |attention| {worst['attn']:.2e}, "
+          f"max |layer output| {worst['h']:.2e}, max |logits| {worst['logits']:.2e}, "
+          f"near-tie events {events}", flush=True)
