@@ -65,3 +65,59 @@ def test_small_dynamic_k_equals_gpu_greedy(policy):
     for r in recs:
         assert (r["m"] <= r["k"]).all()
         assert (r["len"] == r["n"] + 1 + r["m"]).all()
+
+
+@pytest.mark.slow
+def test_qwen3_8b_width_dynamic_k_and_refine_with_planted_drafts():
+    """Dynamic K and the 2-step denoising pass at the Qwen3-8B width (one
+    layer, d 4096, vocabulary 151936) and the batch shapes of the 8 x 32768
+    workload (8 sequences: a 264-row draft pass at k = 32 takes the row-split
+    GEMMs, smaller k the column-split ones).  Each step drafts a block of k
+    from a schedule (0 and 32 included), every other step runs the refine
+    pass, then planted drafts with accept lengths min(a, k) (a uniform on
+    0..32) replace the block: every step accepts exactly its planted length,
+    and the emitted tokens are the GPU's own greedy decoding."""
+    from lossless_decoding_amd import _lib as C
+    from lossless_decoding_amd.engine import Engine
+    from synth.device import fill_weights_device
+
+    sh = workloads.SHAPES["qwen3_8b"]
+    K, V, B = sh["K"], sh["V"], 8
+    ks = np.array([32, 5, 17, 0, 32, 9, 1, 32], np.int32)
+    steps = len(ks)
+    cfg = U.cfg_of("qwen3_8b", max_batch=B, max_ctx=512, n_layers=1)
+    lay, total = C.weight_layout(cfg)
+    w = fill_weights_device(lay, total, True)
+    prompt = workloads.prompts(B, 20, V, seed=61)
+    a = np.minimum(workloads.plant_lengths(steps, B, K, "uniform32"), ks[:, None])
+    need = 1 + int((a + 1).sum(0).max()) + K + 2
+    twin = Engine(U.cfg_of("qwen3_8b", K=0, max_batch=B, max_ctx=512, n_layers=1), w)
+    traj, _ = twin.generate(prompt, need)
+    twin.close()
+    planted = workloads.plant_drafts(traj, 1, a, K, V)
+
+    eng = Engine(cfg, w)
+    eng.prefill(prompt)
+    outs = [[int(t)] for t in eng.pending[:B].cpu().tolist()]
+    for s in range(steps):
+        k = int(ks[s])
+        n = eng.seq_len[:B].cpu().numpy().copy()
+        eng.draft(k)
+        if s % 2 == 1 and k > 0:
+            eng.refine()
+        if k > 0:
+            eng.drafts[:B, :k].copy_(torch.as_tensor(planted[s][:, :k], device="cuda"))
+        eng.verify()
+        eng.commit()
+        torch.cuda.synchronize()
+        acc = eng.accept[:B].cpu().numpy()
+        assert np.array_equal(acc, a[s]), (s, k, acc, a[s])
+        assert np.array_equal(eng.seq_len[:B].cpu().numpy(), n + 1 + acc)
+        off = eng.out_off[:B + 1].cpu().numpy()
+        tok = eng.out_tokens[:off[-1]].cpu().numpy()
+        for b in range(B):
+            outs[b].extend(tok[off[b]:off[b + 1]].tolist())
+    eng.close()
+    del w
+    for b in range(B):
+        assert outs[b] == traj[b, :len(outs[b])].tolist(), b

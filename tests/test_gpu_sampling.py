@@ -192,3 +192,74 @@ def test_small_bf16_sampling_steps_are_consistent():
         for b in range(B):
             assert np.array_equal(tok[off[b]:off[b] + acc[b]], drafts[b, :acc[b]])
     assert events <= 2
+
+
+@pytest.mark.slow
+def test_qwen3_8b_width_sampler_matches_oracle():
+    """The sampler at the Qwen3-8B width (vocabulary 151936, one layer, d 4096)
+    and the qwen3_8b_b8_c32768 batch launch shapes (8 sequences: a 264-row
+    draft pass, so the row-split LM head writes the logits the sampler reads):
+    drafts are the oracle's draws on the GPU's logits, acceptance and final
+    tokens the oracle's rule with the same uniforms, and every commit moves a
+    sequence by m + 1.  Boundary cases (u within 1e-5 of the GPU token's
+    interval in the oracle's float64 CDF) are allowed here for up to 3% of
+    the draws: over 151936 tokens the drawn token's interval is about 1e-4
+    of the mass (random-init logits at T = 0.8), and the GPU's float32 running
+    sums over ~600-element chunks are off by a few 1e-7 of the mass, which
+    moves about one draw in a hundred across a boundary (measured: 5 of 536)."""
+    from lossless_decoding_amd import _lib as C
+    from lossless_decoding_amd.engine import Engine
+    from synth.device import fill_weights_device
+
+    sh = workloads.SHAPES["qwen3_8b"]
+    K, V, B, T, seed = sh["K"], sh["V"], 8, 0.8, 4321
+    cfg = U.cfg_of("qwen3_8b", max_batch=B, max_ctx=256, n_layers=1)
+    lay, total = C.weight_layout(cfg)
+    w = fill_weights_device(lay, total, True)
+    eng = Engine(cfg, w)
+    RA = U.anchor_row(K, B)
+    rows = RA + B
+    lg = torch.zeros(rows, V, device="cuda")
+    eng.set_debug(lg, None, rows)
+    eng.set_sampling(T, seed)
+    eng.prefill(workloads.prompts(B, 24, V, seed=57))
+    torch.cuda.synchronize()
+    f64 = lambda t: t.cpu().numpy().astype(np.float64)   # noqa: E731
+    events = 0
+    pre = f64(lg[:B])
+    for b in range(B):
+        events += check_draw(int(eng.pending[b]), pre[b], T, oracle.uniform(seed, 0, 4, 0, b))
+    accepted = 0
+    for step in range(2):
+        n = eng.seq_len[:B].cpu().numpy().copy()
+        eng.draft()
+        torch.cuda.synchronize()
+        gd = f64(lg)
+        drafts = eng.drafts[:B].cpu().numpy()
+        for b in range(B):
+            for i in range(K):
+                events += check_draw(int(drafts[b, i]), gd[b * K + i], T,
+                                     oracle.uniform(seed, step, 1, i, b))
+        eng.verify()
+        torch.cuda.synchronize()
+        gv = f64(lg[:B * K])
+        ar = eng.ar[:B].cpu().numpy()
+        acc = eng.accept[:B].cpu().numpy()
+        for b in range(B):
+            pz = np.concatenate([gd[RA + b:RA + b + 1], gv[b * K:(b + 1) * K]])
+            qz = gd[b * K:(b + 1) * K]
+            ua = [oracle.uniform(seed, step, 2, i + 1, b) for i in range(K)]
+            uf = oracle.uniform(seed, step, 3, 0, b)
+            events += check_accept(pz, qz, drafts[b], T, ua, uf, int(acc[b]), int(ar[b, acc[b]]))
+            assert np.array_equal(ar[b, :acc[b]], drafts[b, :acc[b]])
+            accepted += int(acc[b])
+        eng.commit()
+        torch.cuda.synchronize()
+        assert (eng.seq_len[:B].cpu().numpy() == n + 1 + acc).all()
+        assert (eng.pending[:B].cpu().numpy() == ar[np.arange(B), acc]).all()
+    eng.close()
+    del w
+    decisions = B + 2 * B * K + 2 * B
+    assert events <= 0.03 * decisions, (events, decisions)
+    print(f"sampler parity at vocabulary {V}: {2 * B} steps, {accepted} drafts accepted, "
+          f"{events} boundary events", flush=True)
