@@ -10,9 +10,10 @@ takes minutes on the host), so two kinds of checks run here:
     every planted block is accepted to its planted length.  Batch
     invariance: a sequence decoded inside the full batch gets the same tokens
     and bit-identical verify logits as the same sequence decoded alone;
-  * oracle parity on samples the oracle can compute: one step, teacher-forced
-    at three layers (the GPU's own layer inputs and committed cache loaded
-    into the oracle) for the first and the last sequence of the batch.
+  * oracle parity on samples the oracle can compute: three steps on the
+    planting table, teacher-forced at three layers (the GPU's own layer inputs
+    and committed cache loaded into the oracle) for the first and the last
+    sequence of the batch.
 Attention at these shapes is also checked against the oracle on sampled rows
 in test_gpu_attention; every layer is checked against the oracle at the full
 model shape (batch 1, short prompt) in test_gpu_qwen3_8b."""
@@ -121,17 +122,19 @@ CHECK_LAYERS = (0, 18, 35)
 @pytest.mark.parametrize("name", ["qwen3_8b_b16_c8192", "qwen3_8b_b8_c32768"])
 def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
     """Oracle parity at the full sizes, in the launch configuration bench.py
-    times: prefill of the whole batch, then one draft/verify/commit step of
-    every sequence (its own drafts).  For the first and the last sequence,
-    at layers 0, 18 and 35 of both passes, the oracle (float64, the GPU's
-    committed cache of that layer loaded into it) recomputes the attention of
-    the anchor, mask and verify rows from the GPU's layer-input rows and
-    compares it with the GPU's before rounding, and recomputes the rest of
-    the layer from the GPU's layer input and bf16 attention output; the final
-    logits come from the GPU's last residual rows.  All within 2e-2; every
-    token is the oracle's argmax or, at an oracle near-tie, its runner-up;
-    the accept length is the oracle's prefix rule on the GPU's drafts and
-    tokens, and the commit moves the sequence by exactly m + 1."""
+    times, on the workload's planting table: prefill of the whole batch, then
+    three draft/verify/commit steps whose verify passes take the planted
+    drafts.  At every step, for the first and the last sequence, at layers 0,
+    18 and 35 of both passes, the oracle (float64, the GPU's committed cache
+    of that layer loaded into it) recomputes the attention of the anchor,
+    mask and verify rows from the GPU's layer-input rows and compares it with
+    the GPU's before rounding, and recomputes the rest of the layer from the
+    GPU's layer input and bf16 attention output; the final logits come from
+    the GPU's last residual rows.  All within 2e-2; every draft and AR token
+    is the oracle's argmax or, at an oracle near-tie, its runner-up (counted;
+    the oracle follows the GPU's state); accept lengths are the planted ones
+    and the oracle's prefix rule, and each commit moves a sequence by exactly
+    m + 1 from its length."""
     from lossless_decoding_amd.layout import untile_v
     from tests import gpu_util as U
     from tests.test_gpu_qwen3_8b import TOL, check_token
@@ -141,11 +144,24 @@ def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
     B, P, K, V = wl["B"], wl["P"], sh["K"], sh["V"]
     L, d, hkv, hd = sh["L"], sh["d"], sh["hkv"], sh["hd"]
     qd = sh["hq"] * hd
+    a = workloads.plant_lengths(STEPS, B, K, wl["plant"])
+    need = 1 + int((a + 1).sum(0).max()) + K + 2
     max_ctx = P + STEPS * (K + 1) + 64
     chunk = attn_chunk_for(max_ctx, B, hkv)
-    print(f"[{name}] teacher-forced: B={B} P={P} K={K} chunk={chunk} layers={CHECK_LAYERS}",
-          flush=True)
+    print(f"[{name}] teacher-forced: B={B} P={P} K={K} chunk={chunk} layers={CHECK_LAYERS} "
+          f"steps={STEPS}", flush=True)
     prompts = workloads.prompts(B, P, V)
+    ar0 = make(sh, 0, B, P + need + 8, chunk, weights8b_full)
+    ar0.prefill(prompts)
+    traj = [ar0.pending[:B].clone()]
+    for _ in range(1, need):
+        ar0.step()
+        traj.append(ar0.pending[:B].clone())
+    traj = torch.stack(traj, 1).cpu().numpy()
+    ar0.close()
+    del ar0
+    planted = workloads.plant_drafts(traj, 1, a, K, V)
+
     eng = make(sh, K, B, max_ctx, chunk, weights8b_full)
     RA = U.anchor_row(K, B)
     rows = RA + B
@@ -157,8 +173,7 @@ def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
     eng.set_debug_layers(resid, at32, rows)
     eng.prefill(prompts)
     torch.cuda.synchronize()
-    n0 = eng.seq_len[:B].cpu().numpy().copy()
-    assert (n0 == P).all()
+    assert (eng.seq_len[:B].cpu().numpy() == P).all()
 
     lay = list(CHECK_LAYERS)
     lay1 = [l + 1 for l in CHECK_LAYERS]
@@ -169,29 +184,16 @@ def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
         return dict(R=f(resid[lay, :nrows]), R1=f(resid[lay1, :nrows]), RL=f(resid[L, :nrows]),
                     A32=f(at32[lay, :nrows]), AB=f(atb[lay, :nrows]), lg=f(lg[:nrows]))
 
-    eng.draft()
-    torch.cuda.synchronize()
-    gd = grab(rows)
-    drafts = eng.drafts[:B].cpu().numpy().copy()
-    eng.verify()
-    torch.cuda.synchronize()
-    gv = grab(B * K)
-    ar = eng.ar[:B].cpu().numpy().copy()
-    acc = eng.accept[:B].cpu().numpy().copy()
-    eng.commit()
-    torch.cuda.synchronize()
-    assert np.array_equal(eng.commit_start[:B].cpu().numpy(), n0)
-    assert np.array_equal(eng.seq_len[:B].cpu().numpy(), n0 + 1 + acc)
-    assert np.array_equal(eng.pending[:B].cpu().numpy(), ar[np.arange(B), acc])
-
     cap = int(eng.sizes.kv_slots)
     kv = eng.kv.view(torch.bfloat16)[:2 * L * eng.cfg.max_batch * hkv * cap * hd]
     kv = kv.view(2, L, eng.cfg.max_batch, hkv, cap, hd)
     m = U.oracle_model(wl["shape"])
     worst = dict(attn=0.0, h=0.0, logits=0.0)
     events = 0
-    for b in sorted({0, B - 1}):
-        n = int(n0[b])
+
+    def check_sequence(b, n, gd, gv, drafts, ar, acc):
+        """Sequence b's rows of one step against the oracle (cache [0, n))."""
+        nonlocal events
         seq = m.seq(n + K + 2)
         for l in CHECK_LAYERS:
             k = kv[0, l, b, :, :n].float().cpu().numpy().astype(np.float64)
@@ -206,7 +208,7 @@ def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
             eh = np.abs(h_o - g["R1"][i, sl]).max()
             worst["attn"] = max(worst["attn"], ea)
             worst["h"] = max(worst["h"], eh)
-            assert ea < TOL and eh < TOL, (b, CHECK_LAYERS[i], ea, eh)
+            assert ea < TOL and eh < TOL, (b, n, CHECK_LAYERS[i], ea, eh)
 
         # draft pass: the anchor at slot n (its K/V into the oracle's slot n
         # of the layer), then the mask rows over [0, n] and the block
@@ -216,25 +218,44 @@ def test_full_size_teacher_forced_against_oracle(name, weights8b_full):
             _, o_m = seq.draft_layer(l, gd["R"][i, mk], n)
             hold(i, gd, o_m, mk, True)
         lo, _ = m.final(np.concatenate([gd["RL"][mk], gd["RL"][an]]))
-        gl = np.concatenate([gd["lg"][mk], gd["lg"][an]])
-        e = np.abs(lo - gl).max()
+        e = np.abs(lo - np.concatenate([gd["lg"][mk], gd["lg"][an]])).max()
         worst["logits"] = max(worst["logits"], e)
-        assert e < TOL, (b, e)
+        assert e < TOL, (b, n, e)
         events += sum(check_token(drafts[b, i], lo[i]) for i in range(K))
         events += check_token(ar[b, 0], lo[K])
-        # verify pass: rows at n+1 .. n+K, causal over the cache, the
-        # anchor's slot n included
+        # verify pass over the planted drafts: rows at n+1 .. n+K, causal over
+        # the cache, the anchor's slot n included
         for i, l in enumerate(CHECK_LAYERS):
             _, o_v = seq.ar_layer(l, gv["R"][i, mk], n + 1)
             hold(i, gv, o_v, mk, False)
         lo, _ = m.final(gv["RL"][mk])
         e = np.abs(lo - gv["lg"][mk]).max()
         worst["logits"] = max(worst["logits"], e)
-        assert e < TOL, (b, e)
+        assert e < TOL, (b, n, e)
         events += sum(check_token(ar[b, 1 + i], lo[i]) for i in range(K))
-        assert acc[b] == oracle.accept(drafts[b], ar[b])
         del seq
+
+    for step in range(STEPS):
+        n0 = eng.seq_len[:B].cpu().numpy().copy()
+        eng.draft()
+        torch.cuda.synchronize()
+        gd = grab(rows)
+        drafts = eng.drafts[:B].cpu().numpy().copy()
+        eng.drafts[:B].copy_(torch.as_tensor(planted[step], device="cuda"))
+        eng.verify()
+        torch.cuda.synchronize()
+        gv = grab(B * K)
+        ar = eng.ar[:B].cpu().numpy().copy()
+        acc = eng.accept[:B].cpu().numpy().copy()
+        for b in sorted({0, B - 1}):
+            check_sequence(b, int(n0[b]), gd, gv, drafts, ar, acc)
+            assert acc[b] == oracle.accept(planted[step][b], ar[b]) == a[step, b], (step, b)
+        eng.commit()
+        torch.cuda.synchronize()
+        assert np.array_equal(eng.commit_start[:B].cpu().numpy(), n0)
+        assert np.array_equal(eng.seq_len[:B].cpu().numpy(), n0 + 1 + acc)
+        assert np.array_equal(eng.pending[:B].cpu().numpy(), ar[np.arange(B), acc])
     eng.close()
-    print(f"[{name}] teacher-forced layers {CHECK_LAYERS}: max |attention| {worst['attn']:.2e}, "
-          f"max |layer output| {worst['h']:.2e}, max |logits| {worst['logits']:.2e}, "
-          f"near-tie events {events}", flush=True)
+    print(f"[{name}] teacher-forced layers {CHECK_LAYERS} x {STEPS} steps: max |attention| "
+          f"{worst['attn']:.2e}, max |layer output| {worst['h']:.2e}, max |logits| "
+          f"{worst['logits']:.2e}, near-tie events {events}", flush=True)
