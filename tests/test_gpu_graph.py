@@ -70,3 +70,59 @@ def test_reserve_steps_refuses_past_capacity():
     with pytest.raises(C.OrthrusError) as e:       # a step in flight
         C.orthrus_reserve_steps(eng.ctx, 2, K, 1)
     assert e.value.code == C.ORTHRUS_ESTATE
+
+
+@pytest.mark.slow
+def test_graph_replays_equal_eager_steps_at_the_headline_batch_shapes():
+    """The same at the Qwen3-8B width (one layer) and the 8-sequence shapes of
+    the 8 x 32768 workload, whose passes take the row-split GEMM launches,
+    the row-split LM head with its separate argmax kernel, and the
+    two-tiles-per-wave attention: replays with planted drafts (the first
+    step's start with three tokens of the greedy continuation, the rest are
+    random) give the eager steps' tokens, lengths and pending tokens
+    exactly."""
+    from lossless_decoding_amd.engine import Engine
+    from synth.device import fill_weights_device
+
+    sh = workloads.SHAPES["qwen3_8b"]
+    B, K, V, steps = 8, sh["K"], sh["V"], 4
+    cfg = U.cfg_of("qwen3_8b", max_batch=B, max_ctx=512, n_layers=1)
+    lay, total = C.weight_layout(cfg)
+    w = fill_weights_device(lay, total, True)
+    prompt = workloads.prompts(B, 24, V, seed=63)
+    ref = Engine(cfg, w)
+    want, _ = ref.generate(prompt, 12)
+    ref.close()
+    rng = np.random.default_rng(64)
+    plants = []
+    for s in range(steps):
+        p = rng.integers(0, V, (B, K)).astype(np.int32)
+        if s == 0:
+            p[:, :3] = np.asarray(want)[:, 1:4]
+        plants.append(torch.from_numpy(p).cuda())
+    eager = Engine(cfg, w)
+    eager.prefill(prompt)
+    want_states = []
+    for s in range(steps):
+        eager.step(plants[s])
+        torch.cuda.synchronize()
+        want_states.append(state(eager, B))
+    eager.close()
+
+    eng = Engine(cfg, w)
+    eng.prefill(prompt)
+    torch.cuda.synchronize()
+    buf = torch.zeros(B, K, dtype=torch.int32, device="cuda")
+    g = eng.capture_step(buf)
+    torch.cuda.synchronize()
+    for s in range(steps):
+        buf.copy_(plants[s])
+        eng.replay(g)
+        torch.cuda.synchronize()
+        got = state(eng, B)
+        for a, b in zip(got, want_states[s]):
+            assert np.array_equal(a, b), s
+        _ = (torch.arange(1000, device="cuda") * 3).sum().item()   # eager work between replays
+    assert (want_states[0][2] == 24 + 1 + 3).all()          # the first step accepted its three drafts
+    eng.close()
+    del w
