@@ -82,8 +82,9 @@ enum { ORTHRUS_F32 = 0, ORTHRUS_BF16 = 1 };
  * are shared.
  * BF16 models: bf16 weights, bf16 KV cache, fp32 residual stream, fp32
  * accumulation; requires head_dim 128, d_model, n_q_heads*head_dim and
- * ffn_dim multiples of 256, d_model <= 8192, vocab a multiple of 128, and
- * (block_k + 1) * group <= 144 (group = n_q_heads / n_kv_heads).
+ * ffn_dim multiples of 256, d_model <= 8192 and vocab a multiple of 128.
+ * block_k is at most 63 for both dtypes (the draft block is one 64-key
+ * attention tile, and acceptance is one 64-lane ballot).
  * F32 models: everything fp32 (small check models). */
 typedef struct orthrus_config {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim, vocab;
@@ -322,8 +323,8 @@ int orthrus_set_debug_layers(orthrus_ctx* ctx, float* resid, float* attn32, int3
  * (kpad = block_len rounded up to 32).  Each row sees cache keys
  * [0, ctx_len) and all block_len block keys (the pages' mask-row view).
  * out: [batch][rows][n_q_heads][128] bf16.  workspace: at least
- * orthrus_attention_workspace(...) bytes.  cap must be a multiple of 64.
- * Errors: EINVAL, EHIP. */
+ * orthrus_attention_workspace(...) bytes.  cap must be a multiple of 64;
+ * rows and block_len at most 64.  Errors: EINVAL, EHIP. */
 int orthrus_block_attention(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t n_kv_heads,
                             const void* q, const void* k_cache, const void* v_cache, int32_t cap,
                             int32_t ctx_len, const void* k_block, const void* v_block,

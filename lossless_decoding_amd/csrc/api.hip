@@ -116,14 +116,12 @@ int validate(const orthrus_config* c) {
   if (c->attn_chunk != 0 &&
       (c->attn_chunk < 64 || c->attn_chunk > 4096 || (c->attn_chunk & (c->attn_chunk - 1))))
     return ORTHRUS_EINVAL;
-  int G = c->n_q_heads / c->n_kv_heads;
   if (c->dtype == ORTHRUS_BF16) {
     if (c->head_dim != 128) return ORTHRUS_EINVAL;
     if (c->d_model % 256 || (c->n_q_heads * c->head_dim) % 256 || c->ffn_dim % 256)
       return ORTHRUS_EINVAL;
     if (c->vocab % 128) return ORTHRUS_EINVAL;
     if (c->d_model > 8192) return ORTHRUS_EINVAL;
-    if ((c->block_k + 1) * G > 144) return ORTHRUS_EINVAL;
   } else if (c->dtype != ORTHRUS_F32) {
     return ORTHRUS_EINVAL;
   }
@@ -1011,8 +1009,7 @@ int block_attention_args(int32_t batch, int32_t rows, int32_t n_q_heads, int32_t
                          int32_t block_len, void* out) {
   if (batch < 1 || rows < 1 || n_q_heads < 1 || n_kv_heads < 1 || n_q_heads % n_kv_heads)
     return ORTHRUS_EINVAL;
-  int G = n_q_heads / n_kv_heads;
-  if (rows * G > 144 || cap % 64 || ctx_len < 0 || ctx_len > cap || block_len < 0 ||
+  if (rows > 64 || cap % 64 || ctx_len < 0 || ctx_len > cap || block_len < 0 ||
       block_len > 64 || ctx_len + block_len < 1)
     return ORTHRUS_EINVAL;
   if (!q || !out || (ctx_len > 0 && (!k_cache || !v_cache)) ||

@@ -104,17 +104,20 @@ def plant_drafts(traj: np.ndarray, first_emitted: int, a: np.ndarray, K: int, V:
     (first_emitted + sum(a+1) + K + 1 tokens)."""
     steps, B = a.shape
     out = np.zeros((steps, B, K), np.int32)
+    # Philox blocks (4 words) per step: 24 up to K = 32 (x[64] the wrong
+    # token, x[65..95] the fillers), more for larger blocks
+    nblk = max(24, (64 + K + 3) // 4)
     for b in range(B):
         e = first_emitted
         for s in range(steps):
-            x = np.stack(uniform_u32(24, seed, b, P_PLANT, start=s * 24)).T.reshape(-1)
+            x = np.stack(uniform_u32(nblk, seed, b, P_PLANT, start=s * nblk)).T.reshape(-1)
             k = int(a[s, b])
             t = traj[b, e:e + K + 1]          # true continuation t_1..t_{K+1}
             out[s, b, :k] = t[:k]
             if k < K:
                 u = int((int(x[64]) * (V - 1)) >> 32)
                 out[s, b, k] = (int(t[k]) + 1 + u) % V
-                for i in range(k + 1, K):      # at most 31 words: x[65..95]
+                for i in range(k + 1, K):      # at most K - 1 words: x[65..]
                     out[s, b, i] = int((int(x[65 + (i - k - 1)]) * V) >> 32)
             e += k + 1
     return out

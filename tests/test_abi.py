@@ -85,6 +85,14 @@ def test_invalid_configs_rejected(field, val):
     assert e.value.code == C.ORTHRUS_EINVAL
 
 
+def test_largest_block_accepted():
+    """block_k up to 63 (one 64-key block tile, one 64-lane acceptance
+    ballot) at the Qwen3-8B group of 4 query heads per KV head."""
+    c = cfg_of("qwen3_8b")
+    c.block_k = 63
+    assert C.orthrus_query_sizes(c).kv_bytes > 0
+
+
 def test_create_rejects_null_and_misaligned_pointers():
     c = cfg_of("tiny")
     with pytest.raises(C.OrthrusError) as e:

@@ -169,3 +169,21 @@ def test_block_attention_microbenchmark_grid(lk, B):
         n += len(qrows)
     assert n >= (B * rows * hq if B <= 4 else 256)
     assert err < TOL, err
+
+
+@pytest.mark.parametrize("lk,kb", [(700, 64), (0, 64)])
+def test_block_attention_64_rows_all_rows(lk, kb):
+    """The largest block: 64 query tokens and 64 block keys (256 rows per KV
+    head at a group of 4), every output against the oracle."""
+    B, rows, hq, hkv = 2, 64, 8, 2
+    q, kc, vc, kbk, vbk, cap = make(B, rows, hq, hkv, lk, kb, 5)
+    out = run(B, rows, hq, hkv, lk, kb, q, kc, vc, kbk, vbk, cap).float().cpu().numpy()
+    qn, kn, vn = q.float().cpu().numpy(), kc.float().cpu().numpy(), vc.float().cpu().numpy()
+    kbn, vbn = kbk.float().cpu().numpy(), vbk.float().cpu().numpy()
+    err = 0.0
+    for b in range(B):
+        for r in range(rows):
+            for h in range(hq):
+                want = oracle_row(qn, kn, vn, kbn, vbn, b, r, h, lk, kb, hq // hkv)
+                err = max(err, float(np.abs(out[b, r, h] - want).max()))
+    assert err < TOL, err

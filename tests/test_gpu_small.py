@@ -203,3 +203,60 @@ def test_launch_timing_classes_and_capacity():
     eng.draft(); eng.verify(); eng.commit()
     tim, dropped = C.orthrus_timing_read(eng.ctx)
     assert tim == {} and not dropped
+
+
+def test_small_block_of_63_masks():
+    """The largest block (K = 63: 64 tokens x 4 heads = 256 attention rows per
+    sequence and KV head in the draft pass, i.e. two row groups of eight
+    16-row tiles).  Planted drafts, lengths uniform on 0..63, all accepted
+    exactly, output equal to the GPU's greedy decoding; and one step against
+    the oracle: anchor, mask and verify logits within 2e-2, drafts and AR
+    tokens under the near-tie rule, the same accept length."""
+    sh = workloads.SHAPES["small"]
+    K, V, B, steps = 63, sh["V"], 3, 5
+    prompt = workloads.prompts(B, 30, V, seed=65)
+    ar = U.engine("small", K=0, max_batch=B, max_ctx=1024)
+    traj, _ = ar.generate(prompt, 1 + steps * (K + 1) + K + 2)
+    a = workloads.plant_lengths(steps, B, K, "uniform32")   # uniform on 0..K
+    planted = workloads.plant_drafts(traj, 1, a, K, V)
+    eng = U.engine("small", K=K, max_batch=B, max_ctx=1024)
+    n_new = 1 + int((a + 1).sum(0).min())
+    got, recs = eng.generate(prompt, n_new, planted=planted, record=True)
+    assert np.array_equal(got, traj[:, :n_new])
+    for s, r in enumerate(recs):
+        assert np.array_equal(r["m"], a[s])
+
+    # one free-running step of sequence 0 against the oracle
+    om = U.oracle_model("small")
+    seq = om.seq(256)
+    pend_o, _ = seq.prefill(prompt[0], want_logits=True)
+    one = U.engine("small", K=K, max_batch=1, max_ctx=256)
+    RA = U.anchor_row(K)
+    lg = torch.zeros(RA + 1, V, device="cuda")
+    one.set_debug(lg, None, RA + 1)
+    one.prefill(prompt[:1])
+    torch.cuda.synchronize()
+    assert int(one.pending[0]) == pend_o
+    one.draft()
+    torch.cuda.synchronize()
+    gd = lg.cpu().numpy().astype(np.float64)
+    drafts = one.drafts[0].cpu().numpy().copy()
+    one.verify()
+    torch.cuda.synchronize()
+    gv = lg[:K].cpu().numpy().astype(np.float64)
+    g_ar = one.ar[0].cpu().numpy().copy()
+    g_m = int(one.accept[0])
+    r = seq.step(pend_o, K)
+    assert np.abs(gd[RA] - r["logits_anchor"]).max() < TOL
+    assert np.abs(gd[:K] - r["logits_draft"]).max() < TOL
+    ties = 0
+    for i in range(K):
+        if drafts[i] != r["drafts"][i]:
+            row = r["logits_draft"][i]
+            assert U.margin(row) <= TOL and np.argsort(row)[-2] == drafts[i]
+            ties += 1
+    if ties == 0:
+        m = r["m"]
+        assert g_m == m
+        assert np.abs(gv[:m + 1] - r["logits_verify"][:m + 1]).max() < TOL
+        assert g_ar[0] == r["ar"][0] or U.margin(r["logits_anchor"]) <= TOL
