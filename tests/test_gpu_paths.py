@@ -144,3 +144,40 @@ def test_call_order_and_capacity_errors():
     with pytest.raises(C.OrthrusError) as e:           # a bound above the host's is refused
         C.orthrus_sync_lengths(eng.ctx, 2, np.array([79, 79], np.int32))
     assert e.value.code == C.ORTHRUS_EINVAL
+
+
+def test_prompt_length_edges():
+    """Prompts of 1 and 2 tokens and of exactly one prefill pass and one token
+    more (prefill_rows, the prompt rows per sequence of one pass), ragged in
+    one batch: each sequence's output equals its own greedy decoding alone,
+    and the one-token prompt's first token comes from prefill logits within
+    2e-2 of the oracle's."""
+    sh = workloads.SHAPES["small"]
+    V, B = sh["V"], 4
+    eng = U.engine("small", max_batch=B, max_ctx=1024)
+    pr = int(eng.sizes.prefill_rows)
+    plens = [1, 2, pr, pr + 1]
+    full = workloads.prompts(B, pr + 1, V, seed=17)
+    lg = torch.zeros(B, V, device="cuda")
+    eng.set_debug(lg, None, B)
+    eng.prefill(full, prompt_len=plens)
+    torch.cuda.synchronize()
+    first = lg[0].cpu().numpy().astype(np.float64)      # the last prefill pass: one row per sequence
+    outs = [[int(t)] for t in eng.pending[:B].cpu().tolist()]
+    eng.set_debug(None, None, 0)
+    while min(len(o) for o in outs) < 40:
+        eng.draft(); eng.verify(); eng.commit()
+        off = eng.out_off[:B + 1].cpu().numpy()
+        tok = eng.out_tokens[:off[-1]].cpu().numpy()
+        for b in range(B):
+            outs[b].extend(tok[off[b]:off[b + 1]].tolist())
+        C.orthrus_sync_lengths(eng.ctx, B, eng.seq_len[:B].cpu().numpy())
+    for b in range(B):
+        alone = U.engine("small", K=0, max_batch=1, max_ctx=1024)
+        want, _ = alone.generate(full[b:b + 1, :plens[b]], 40)
+        assert np.array_equal(np.array(outs[b][:40]), want[0]), (b, plens[b])
+    om = U.oracle_model("small")
+    pend, lo = om.seq(64).prefill(full[0, :1], want_logits=True)
+    lo = np.asarray(lo, np.float64).reshape(-1)[-V:]
+    assert np.abs(first - lo).max() < 2e-2
+    assert outs[0][0] == pend or U.margin(lo) <= 2e-2
