@@ -423,7 +423,10 @@ def run_workload(name, S, W, args, headline):
     prompts = workloads.prompts(B, P, V)
     # greedy trajectory from the plain-decoding context (same kernels, K = 0)
     t0 = time.time()
-    ar.prefill(prompts)
+    q0, q1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    q0.record()
+    ar.prefill(prompts)                    # the plain-decoding context's time to first token
+    q1.record()
     traj = torch.zeros(need, B, dtype=torch.int32, device=dev)
     traj[0] = ar.pending[:B]
     a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -434,6 +437,7 @@ def run_workload(name, S, W, args, headline):
     a1.record()
     torch.cuda.synchronize()
     plain_tps = B * (need - 1) / (a0.elapsed_time(a1) / 1e3)
+    plain_prefill_ms = q0.elapsed_time(q1)
     traj = traj.t().contiguous().cpu().numpy()
     log(f"[setup] greedy trajectory of {need} tokens x {B} in {time.time() - t0:.1f}s "
         f"(plain decoding {plain_tps:.1f} tokens/s)")
@@ -451,7 +455,8 @@ def run_workload(name, S, W, args, headline):
     torch.cuda.synchronize()
     prefill_ms = p0.elapsed_time(p1)
     prefill_roof = prefill_roofline(sh, B, P, int(eng.sizes.prefill_rows), prefill_ms)
-    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms (roofline {prefill_roof['frac']:.3f})")
+    log(f"[prefill] {B} x {P} prompt tokens in {prefill_ms:.1f} ms (roofline {prefill_roof['frac']:.3f}; "
+        f"plain-decoding context {plain_prefill_ms:.1f} ms)")
     for s in range(W):
         eng.draft(); eng.drafts[:B].copy_(planted[s]); eng.verify(); eng.commit()
 
@@ -597,6 +602,10 @@ def run_workload(name, S, W, args, headline):
         "tpf": round(tpf_from_accept(tokens / S / B - 1.0), 4),
         "prefill_ms": round(prefill_ms, 3),
         "prefill_tokens_per_s": round(B * P / (prefill_ms / 1e3), 1),
+        # the same prompts prefilled by the plain-decoding (K = 0) context: the
+        # time-to-first-token ratio of draft/verify decoding to plain decoding
+        "prefill_plain_decoding_ms": round(plain_prefill_ms, 3),
+        "ttft_vs_plain_decoding": round(prefill_ms / plain_prefill_ms, 4),
         "prefill_roofline": prefill_roof,
         "lossless_vs_greedy": lossless,
         "plain_decoding_tokens_per_s": round(plain_tps, 3),
