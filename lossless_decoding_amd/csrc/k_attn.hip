@@ -105,9 +105,12 @@ template <int N> struct IntC { static constexpr int value = N; };
 #define ATT_SLOTS 5
 
 // The kernel body, for TPW query tiles per wave (four waves per workgroup,
-// two workgroups per compute unit).  It is a device template behind plain
+// two workgroups per compute unit), with cache policy KVPOL on the K/V tile
+// loads (0: default; 2: non-temporal, for launches in which every key tile
+// is read by one workgroup only -- a single row group -- so that the
+// streamed keys do not hold L2 lines).  It is a device template behind plain
 // kernels, so only the device pass instantiates it.
-template <int TPW>
+template <int TPW, int KVPOL>
 __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
   constexpr int NW = 4;
   // each 16 KB unit is 16 one-kilobyte loads, LPU of them per wave
@@ -236,7 +239,8 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
 #pragma unroll
     for (int j = 0; j < LPU; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16, koff[j], 0, 0, 0);
+          r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16, koff[j], 0, 0,
+          KVPOL);
   };
   // V^T: a cache tile is 128 rows of 64 keys; the block's rows are kpad
   // keys long (pieces past kpad belong to the next row; they are zeroed in
@@ -254,7 +258,7 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
       const int d = (wv * LPU + j) * 8 + (lane >> 3);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           r, (__attribute__((address_space(3))) void*)(dst + (wv * LPU + j) * 512), 16,
-          voff[j] + d * row_extra, 0, 0, 0);
+          voff[j] + d * row_extra, 0, 0, KVPOL);
     }
   };
   // zero the V^T columns of keys >= nvalid (the last, partial tile)
@@ -573,8 +577,11 @@ __device__ __forceinline__ void attn_bf16_body(const AttnArgs& a) {
 }
 
 // one query tile per wave (launches with few workgroups), two per wave
-__global__ __launch_bounds__(256, 2) void k_attn_bf16_t1(AttnArgs a) { attn_bf16_body<1>(a); }
-__global__ __launch_bounds__(256, 2) void k_attn_bf16_t2(AttnArgs a) { attn_bf16_body<2>(a); }
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_t1(AttnArgs a) { attn_bf16_body<1, 0>(a); }
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_t2(AttnArgs a) { attn_bf16_body<2, 0>(a); }
+// the same with non-temporal K/V loads (launches of a single row group)
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_t1_stream(AttnArgs a) { attn_bf16_body<1, 2>(a); }
+__global__ __launch_bounds__(256, 2) void k_attn_bf16_t2_stream(AttnArgs a) { attn_bf16_body<2, 2>(a); }
 
 // Combine the chunk partials of one (row, query head); one wave each, four
 // per block.  Phase 1: the maximum M of the chunk maxima the row sees.
@@ -697,10 +704,17 @@ void launch_attention_bf16(const AttnArgs& a0, hipStream_t s) {
   const int act = a.active_chunks > 0 && a.active_chunks < a.nc ? a.active_chunks : a.nc;
   if (a.tpw != 1 && a.tpw != 2) a.tpw = (long)B * a.hkv * act * attn_row_groups(QR, 2) < 512 ? 1 : 2;
   const int nrg = attn_row_groups(QR, a.tpw);
+  // one row group: every key tile is read by one workgroup, so the tiles are
+  // streamed past L2 (measured at 8 x 32768: verify attention 10.08 -> 9.53 ms
+  // per step); with several row groups the later ones re-read the keys from
+  // L2 and the default policy keeps them (the draft pass took 11.5 -> 14.5 ms
+  // with non-temporal loads)
+  const bool stream = nrg == 1;
+  const dim3 g1((a.nc + 1) * a.hkv * B * nrg), g2(a.nc * a.hkv * B * nrg);
   if (a.tpw == 1)
-    hipLaunchKernelGGL(k_attn_bf16_t1, dim3((a.nc + 1) * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(stream ? k_attn_bf16_t1_stream : k_attn_bf16_t1, g1, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_attn_bf16_t2, dim3(a.nc * a.hkv * B * nrg), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(stream ? k_attn_bf16_t2_stream : k_attn_bf16_t2, g2, dim3(256), 0, s, a);
   const int rows = a.fixed_ctx >= 0 ? B * a.P.Kx : a.P.rows();
   const int npairs = rows * a.hq;
   hipLaunchKernelGGL(k_attn_merge, dim3((npairs + 3) / 4), dim3(256), 0, s, a, npairs);
