@@ -542,9 +542,18 @@ void run_pass_bf16(orthrus_ctx* c, const PassInfo& P, const int32_t* anchor_tok,
       if (P.kind == PASS_DRAFT && NA > 0 && gemm_bf16_rows_form(BK, y.nqkv, EP_QKV)) {
         // many mask rows: their own row-split launch (wider column groups than
         // a two-segment one) and a small launch for the anchor rows; every
-        // row's arithmetic is the same in either form
+        // row's arithmetic is the same in either form.  When both write slice
+        // partials (disjoint rows of the partial buffer), one finish kernel
+        // takes both row ranges.
+        const bool one_finish = gemm_bf16_split_slices(BK, 0, y.nqkv, EP_QKV) > 0 &&
+                                gemm_bf16_split_slices(NA, 0, y.nqkv, EP_QKV) > 0;
+        g.defer_finish = one_finish;
         run(g, y.p_dqkv[l], 0, BK, y.d, y.nqkv, EP_QKV);
         run(g, y.p_qkv[l], RM, NA, y.d, y.nqkv, EP_QKV);
+        if (one_finish) {
+          g.row0 = 0; g.M = BK; g.row02 = RM; g.M2 = NA; g.N = y.nqkv;
+          launch_qkv_finish_bf16(g, s);
+        }
       } else if (P.kind == PASS_DRAFT) {
         run2(g, y.p_dqkv[l], y.p_qkv[l], y.d, y.nqkv, EP_QKV);
       } else {

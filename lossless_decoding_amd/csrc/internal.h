@@ -162,8 +162,12 @@ struct GemmArgs {
   float2* amax; float* logits; int ldl; int Kb;       // EP_ARGMAX
   int32_t* drafts; int32_t* ar; int32_t* pending;
   int tnrb, ttb, tng;           // row-split launches: row blocks, row tiles per block, column groups (set by the launcher)
+  int defer_finish;             // EP_QKV launches that write slice partials: the caller runs the finish kernel
 };
 void launch_gemm_bf16(const GemmArgs& a, hipStream_t s);
+// QKV finish over the slice partials of one or two earlier split launches
+// (rows [0, M) from row0, [M, M + M2) from row02)
+void launch_qkv_finish_bf16(const GemmArgs& a, hipStream_t s);
 // Profiling: the next bf16 GEMM kernel launched from this host thread
 // records start / stop itself (hipExtLaunchKernel); pending until taken.
 void gemm_time_next_launch(hipEvent_t start, hipEvent_t stop);

@@ -1204,6 +1204,11 @@ extern "C" int orthrus_gemm_plan(int32_t m, int32_t m2, int32_t n, int32_t k, in
   return ORTHRUS_OK;
 }
 
+void launch_qkv_finish_bf16(const GemmArgs& a, hipStream_t s) {
+  const int rows = (a.M > 0 ? a.M : 0) + (a.M2 > 0 ? a.M2 : 0);
+  if (rows > 0) hipLaunchKernelGGL(k_qkv_finish_bf16<NSL>, dim3(rows, a.N / 128), dim3(64), 0, s, a);
+}
+
 // Shape rules: N a multiple of 128, K a multiple of 256 (8 slices of whole
 // k-blocks).  A second segment (W2, M2, row02: same N, K and input buffer)
 // runs in the same launch; the argmax epilogue takes one segment only.
@@ -1237,7 +1242,7 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
         }
         if (rp.two) gemm_launch(k_gemm_rows<6, EP_QKV, true, true>, g, b, s, a);
         else gemm_launch(k_gemm_rows<12, EP_QKV, true, false>, g, b, s, a);
-        hipLaunchKernelGGL(k_qkv_finish_bf16<NSL>, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+        if (!a.defer_finish) launch_qkv_finish_bf16(a, s);
         break;
     }
     return;
@@ -1263,7 +1268,7 @@ void launch_gemm_bf16(const GemmArgs& a0, hipStream_t s) {
       case EP_SWIGLU: dispatch_mt<EP_SWIGLU, 8, true>(MT, grid, a, s); break;
       case EP_QKV:
         dispatch_mt<EP_QKV, 8, true>(MT, grid, a, s);
-        hipLaunchKernelGGL(k_qkv_finish_bf16<NSL>, dim3(a.M + a.M2, a.N / 128), dim3(64), 0, s, a);
+        if (!a.defer_finish) launch_qkv_finish_bf16(a, s);
         break;
       default: dispatch_mt<EP_ARGMAX, 8, true>(MT, grid, a, s); break;
     }
